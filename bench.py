@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Benchmark of the PowerSGD step (compress + finite check + decompress/error update) on one
+MI355X, on the 64-resblock d_model=3968 per-GPU gradient shard at rank 112.
+
+    python bench.py [--steps K] [--warmup W] [--workload 3] [--no-out] [--no-cpu-baseline]
+
+Prints ONE JSON line. `value` is gradient GB/s: the fp16 gradient bytes of the whole shard
+(256 matrices, 1.51e9 elements, 3.02 GB) times K, over the wall time of K steps bracketed by
+device synchronisation, inputs resident in HBM. Per-kernel durations come from HIP events the
+library records around each launch on the step's stream (psgd_profile_events), over the same
+timed steps. The `roofline` object is for the streaming kernel with the longest average
+duration. `cpu_baseline` times the float64 oracle on a bounded sample of the same workload
+(whole resblocks, on this host's cores).
+
+One GPU only: --gpus above 1 exits with an error (the path has no multi-GPU leg here; the factor
+all-reduces are the identity on one GPU).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "gradient GB/s compressed+decompressed (rank 112) and % HBM roofline, 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+# algorithmic bytes per gradient element of each streaming kernel (gradient dtype size g):
+#   ef_mq       reads G and E                         g + 4
+#   mtp         reads G and E again                   g + 4
+#   decompress  reads G and E, writes E (and D)       g + 8 (+ 4)
+STREAMING = ("ef_mq", "mtp", "decompress")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3, choices=(2, 3))
+    ap.add_argument("--n-blocks", type=int, default=None, help="resblocks of workload 3 (default 64)")
+    ap.add_argument("--no-out", action="store_true", help="do not write the decompressed gradient")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="time budget of the CPU oracle sample (whole resblocks)")
+    return ap.parse_args(argv)
+
+
+class Hip:
+    """The few HIP runtime calls the timing needs (the runtime torch already loaded)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self) -> int:
+        h = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(h)) == 0
+        return h.value
+
+    def record(self, ev: int, stream: int):
+        assert self.lib.hipEventRecord(ev, stream) == 0
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        err = self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        assert err == 0, err
+        return float(ms.value)
+
+    def destroy(self, ev: int):
+        self.lib.hipEventDestroy(ev)
+
+
+def build_workload(config: int, n_blocks, write_out: bool):
+    import torch
+    import workloads as wl
+    from rank_gradient_compression_powersgd_amd import PowerSGDGroup
+    w = wl.workload(config, n_blocks) if config == 3 else wl.workload(config)
+    dev = torch.device("cuda", 0)
+    grads, q0 = [], []
+    for s in w.matrices:
+        grads.append(wl.gradient_torch(w, s, 0, dev))
+        q0.append(wl.initial_q_torch(w, s, dev))
+    scale = torch.tensor(wl.scales_np(w), device=dev)
+    group = PowerSGDGroup(grads, [s.block for s in w.matrices], scale, w.rank, q0, None, write_out)
+    passthrough = [torch.from_numpy(wl.passthrough_np(config, w.n_blocks)).to(dev).reshape(-1)]
+    torch.cuda.synchronize()
+    return w, group, passthrough
+
+
+def cpu_baseline(seconds: float):
+    """The float64 oracle, as it is, on whole resblocks of the same per-GPU shard shapes
+    (numpy-generated, rank 112, cold start) until `seconds` of oracle time have passed."""
+    import numpy as np
+    import oracle
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((i.get("num_threads", 0) for i in threadpool_info()), default=0)
+    except Exception:  # pragma: no cover
+        blas_threads = 0
+    w = wl.workload(3)
+    per_block = [s for s in w.matrices if s.block == 0]
+    t_total, nbytes, blocks = 0.0, 0, 0
+    while t_total < seconds and blocks < w.n_blocks:
+        specs = [s for s in w.matrices if s.block == blocks]
+        grads = [wl.gradient_np(w, s, 0).astype(np.float32) for s in specs]
+        errs = [np.zeros((s.m, s.n), np.float32) for s in specs]
+        qs = [wl.initial_q_np(w, s) for s in specs]
+        t0 = time.perf_counter()
+        oracle.step_group(grads, errs, qs, [0] * len(specs), wl.scales_np(w)[blocks:blocks + 1])
+        t_total += time.perf_counter() - t0
+        nbytes += sum(s.m * s.n * 2 for s in specs)
+        blocks += 1
+    cores = len(os.sched_getaffinity(0))
+    return {"value": nbytes / t_total / 1e9, "unit": "GB/s", "cores": cores,
+            "blas_threads": blas_threads, "kind": "oracle",
+            "sample": f"{blocks} of 64 resblocks ({blocks * len(per_block)} matrices, "
+                      f"{nbytes / 1e9:.3f} GB fp16 gradient), float64 numpy oracle, cold start, "
+                      f"{t_total:.1f} s"}
+
+
+def main(argv=None) -> int:
+    a = parse(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (--gpus {a.gpus}, WORLD_SIZE {world}): the "
+              "PowerSGD path here has no multi-GPU leg; run with --gpus 1", file=sys.stderr)
+        return 2
+    import torch
+    import rank_gradient_compression_powersgd_amd as psgd
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    psgd.load_library()
+    hip = Hip()
+    log(f"building workload {a.workload} ...")
+    w, group, passthrough = build_workload(a.workload, a.n_blocks, not a.no_out)
+    stream = int(torch.cuda.current_stream().cuda_stream)
+    nslot = len(psgd.PROFILE_SLOTS)
+
+    for _ in range(a.warmup):
+        group.step(passthrough)
+    torch.cuda.synchronize()
+
+    K = a.steps
+    kev = [[hip.event() for _ in range(2 * nslot)] for _ in range(K)]
+    sev = [(hip.event(), hip.event()) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        psgd.psgd_profile_events(group.ctx, kev[k])
+        hip.record(sev[k][0], stream)
+        group.step(passthrough)
+        hip.record(sev[k][1], stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    psgd.psgd_profile_events(group.ctx, None)
+    assert int(group.skip.item()) == 0, "a timed step was skipped"
+
+    step_ms = sorted(hip.elapsed_ms(s0, s1) for s0, s1 in sev)
+    kern = {}
+    for j, name in enumerate(psgd.PROFILE_SLOTS):
+        vals = [hip.elapsed_ms(kev[k][2 * j], kev[k][2 * j + 1]) for k in range(K)]
+        kern[name] = statistics.mean(vals)
+    for evs in kev:
+        for e in evs:
+            hip.destroy(e)
+    for s0, s1 in sev:
+        hip.destroy(s0)
+        hip.destroy(s1)
+
+    gsz = 2 if w.dtype in ("f16", "bf16") else 4
+    numel = w.numel
+    per_elem = {"ef_mq": gsz + 4, "mtp": gsz + 4, "decompress": gsz + 8 + (0 if a.no_out else 4)}
+    rooflines = {}
+    for name in STREAMING:
+        nbytes = per_elem[name] * numel
+        gbs = nbytes / (kern[name] * 1e-3) / 1e9
+        rooflines[name] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                           "bytes_per_launch": nbytes, "avg_ms": round(kern[name], 4)}
+    dom = max(STREAMING, key=lambda n: kern[n])
+    roof = dict(rooflines[dom])
+    roof["kernel"] = dom
+
+    ms_per_step = wall * 1e3 / K
+    value = w.grad_bytes * K / wall / 1e9
+    flops = 6 * w.rank * numel * 3       # three bf16/fp16 products per GEMM, three GEMMs
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{w.n_blocks}-resblock d_model=3968 per-GPU shard: {len(w.matrices)} "
+                         f"{w.dtype} matrices (qkv 3968x1488, attn-out 496x3968, mlp-in 3968x1984, "
+                         f"mlp-out 1984x3968), {numel} elements, rank {w.rank}"),
+            "grad_dtype": w.dtype, "rank": w.rank, "matrices": len(w.matrices),
+            "grad_bytes": w.grad_bytes, "decompressed_out": not a.no_out,
+            "arithmetic": "M and E fp32; products as split bf16/fp16 MFMA with fp32 accumulation; "
+                          "orthonormalisation fp64",
+        },
+        "step_ms_median": round(statistics.median(step_ms), 4),
+        "step_ms_p90": round(step_ms[min(K - 1, int(math.ceil(0.9 * K)) - 1)], 4),
+        "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
+        "streaming": rooflines,
+        "mfma_equivalent_tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 1),
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    group.close()
+    del group
+    torch.cuda.empty_cache()
+    if not a.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        line["cpu_baseline"] = cpu_baseline(a.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,190 @@
+/*
+ * psgd.h — C ABI of the MI355X PowerSGD gradient-compression library (libpsgd.so).
+ *
+ * The operation. Data-parallel training of the DALL·E 12B transformer averages gradients across
+ * machines by all-reducing low-rank factors instead of the full gradient matrices. Each GPU
+ * compresses its own parameter shard at rank 112 (total rank 896). An error buffer carries what
+ * the factors miss. Finite-value checks guard the step, and the decompressed gradient is formed
+ * with 32-bit products. Gains, biases, embeddings and unembeddings are reduced uncompressed in
+ * 32-bit. Sources: "Zero-Shot Text-to-Image Generation — 中文验证版" (ai-papers.xuzou.cn reading
+ * card), sections 方法适配 and 证据; the Korean summary of the same paper (only-wanna.tistory.com),
+ * section "Distributed Optimization".
+ *
+ * Per gradient matrix i (m x n, row-major) with per-resblock scale s_b, error buffer E (m x n,
+ * fp32) and warm start Q (n x r, fp32), one step computes
+ *     M  = s_b * G + E
+ *     P  = orthonormalise(M Q)          thin-QR factor with positive R diagonal
+ *     Q' = M^T P                        next warm start
+ *     D  = P Q'^T                       decompressed gradient
+ *     E  = M - D
+ * On one GPU the two factor all-reduces of the multi-GPU method (of M Q and of Q') are the
+ * identity, so this library computes the whole step locally.
+ *
+ * Call order per step, all asynchronous on the caller's stream:
+ *     psgd_compress            -> P (orthonormal), q_next, per-matrix non-finite flags
+ *     psgd_check_finite        -> skip word (device; optional host copy, the only host sync)
+ *     psgd_decompress_update   -> not skipped: E = M - D, optional D out, q <- q_next
+ *                                 skipped:     E = 0 for every matrix, q kept, D not written
+ *
+ * Conventions
+ *  - All data pointers are device memory owned by the caller (torch tensors, hipMalloc, ...).
+ *    The library owns only its context, its plans and the plan workspace.
+ *  - Every call is asynchronous on `stream`. Only psgd_check_finite with a non-NULL skip_host
+ *    synchronises the stream.
+ *  - Errors are status codes; nothing is thrown across the ABI. psgd_last_error gives the
+ *    message of the last failure on a context. There is no CPU fallback: a failure is reported,
+ *    never hidden.
+ *  - Non-finite data is not an error: it is reported through the flags and the skip word.
+ *  - A context and its plans are not thread-safe. Calls that overlap on one plan race.
+ */
+#ifndef PSGD_H
+#define PSGD_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PSGD_ABI_VERSION 1
+
+typedef enum psgd_status {
+  PSGD_OK = 0,
+  PSGD_EINVAL = 1,        /* bad argument: null pointer, shape, leading dimension, alignment */
+  PSGD_EDTYPE = 2,        /* unknown gradient dtype */
+  PSGD_ENOMEM = 3,        /* workspace allocation failed */
+  PSGD_EHIP = 4,          /* a HIP runtime call or kernel launch failed */
+  PSGD_EUNSUPPORTED = 5   /* valid request this build does not implement (rank above 128) */
+} psgd_status;
+
+typedef enum psgd_dtype {
+  PSGD_F16 = 1,           /* IEEE binary16 gradients */
+  PSGD_BF16 = 2,          /* bfloat16 gradients */
+  PSGD_F32 = 3            /* float32 gradients */
+} psgd_dtype;
+
+/*
+ * One gradient matrix and its state. Row-major, element (i, j) of G at grad[i * ld_grad + j].
+ *  grad    m x n gradient, dtype of the plan (read only). ld_grad >= n, ld_grad % 8 == 0.
+ *  err     m x n fp32 error buffer E (read and written by psgd_decompress_update; read by
+ *          psgd_compress). ld_err >= n, ld_err % 4 == 0.
+ *  q       n x r fp32 warm start (row-major, leading dimension r). Read by psgd_compress,
+ *          overwritten with q_next by a non-skipped psgd_decompress_update.
+ *  q_next  n x r fp32, written by psgd_compress.
+ *  p       m x r fp32, written by psgd_compress with the orthonormal factor.
+ *  out     m x n fp32 decompressed gradient D, or NULL to skip writing it. ld_out >= n,
+ *          ld_out % 4 == 0.
+ *  m, n    shape; n % 8 == 0; 1 <= r <= min(m, n).
+ *  block   index into the per-resblock scale array (0 <= block < n_blocks).
+ * Every pointer must be 16-byte aligned. Buffers of different matrices must not overlap.
+ */
+typedef struct psgd_matrix {
+  const void* grad;   int64_t ld_grad;
+  float* err;         int64_t ld_err;
+  float* q;
+  float* q_next;
+  float* p;
+  float* out;         int64_t ld_out;
+  int64_t m, n;
+  int32_t block;
+  int32_t reserved;   /* must be 0 */
+} psgd_matrix;
+
+/* An uncompressed fp32 tensor (gain, bias, embedding, unembedding): only finite-checked here;
+ * its 32-bit reduction is the identity on one GPU. */
+typedef struct psgd_tensor {
+  const float* data;
+  int64_t numel;
+} psgd_tensor;
+
+typedef struct psgd_ctx psgd_ctx;
+typedef struct psgd_plan psgd_plan;
+
+/* Library ABI version (PSGD_ABI_VERSION). */
+int psgd_version(void);
+
+/* Create a context on HIP device `device` for compression rank `rank` (1..128 in this build).
+ * Writes *ctx; on failure *ctx is NULL. */
+psgd_status psgd_create(psgd_ctx** ctx, int device, int rank);
+
+/* Destroy a context. Plans created on it must be destroyed first. NULL is accepted. */
+psgd_status psgd_destroy(psgd_ctx* ctx);
+
+/*
+ * Describe a group of gradient matrices that are compressed together in grouped launches
+ * (the grouped all-reduce of "Zero-Shot Text-to-Image Generation — 中文验证版", section 证据).
+ * Validates every matrix, allocates and zeroes the plan workspace, and uploads the descriptor
+ * tables once (synchronously, on the null stream). The pointers in `mats` are captured: the
+ * same buffers are used by every later call on the plan. n_blocks is the length of the scale
+ * array later calls pass.
+ */
+psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
+                             psgd_dtype grad_dtype, int n_blocks, psgd_plan** plan);
+
+/* Free a plan and its workspace (synchronises the device). NULL is accepted. */
+psgd_status psgd_plan_destroy(psgd_plan* plan);
+
+/*
+ * Compression: for every matrix, M = s_b G + E, P = orthonormalise(M q), q_next = M^T P.
+ * Writes p, q_next and flags[i] = 1 when any element of G_i or E_i is +-inf or NaN (else 0).
+ * Reads E and q without modifying them.
+ *  scale  device fp32[n_blocks], the per-resblock multipliers s_b.
+ *  flags  device uint8[n_mats].
+ */
+psgd_status psgd_compress(psgd_ctx* ctx, psgd_plan* plan, const float* scale, uint8_t* flags,
+                          hipStream_t stream);
+
+/*
+ * Skip decision ("Zero-Shot Text-to-Image Generation — 中文验证版", section 方法适配: the
+ * skip-update rule for non-finite values). *skip_dev = 1 when any flags[i] is set, any element
+ * of the pass-through tensors is non-finite, or any of scale[0..n_blocks) is non-finite;
+ * otherwise 0.
+ *  pass/n_pass  host array of fp32 device tensors (n_pass may be 0, pass may then be NULL).
+ *  skip_dev     device int32, written.
+ *  skip_host    NULL, or a host int32 that receives the skip word; the call then synchronises
+ *               the stream.
+ */
+psgd_status psgd_check_finite(psgd_ctx* ctx, psgd_plan* plan, const uint8_t* flags,
+                              const psgd_tensor* pass, int n_pass, const float* scale,
+                              int32_t* skip_dev, int32_t* skip_host, hipStream_t stream);
+
+/*
+ * Decompression and error feedback, gated on the device-side skip word (no host sync).
+ *  not skipped: D = P q_next^T formed with fp32-accurate products; E = M - D; out = D when the
+ *               matrix has an out buffer; q <- q_next.
+ *  skipped:     E = 0 for every matrix of the plan; q unchanged; out untouched
+ *               (the error buffer is zeroed on non-finite values: Korean summary, section
+ *               "Distributed Optimization").
+ * Must follow psgd_compress on the same plan with the same scale array.
+ */
+psgd_status psgd_decompress_update(psgd_ctx* ctx, psgd_plan* plan, const float* scale,
+                                   const int32_t* skip_dev, hipStream_t stream);
+
+/*
+ * Tracing hook. Install an array of n HIP events created by the caller with timing enabled.
+ * While installed, the launch of each kernel in slot k is bracketed by hipEventRecord of
+ * events[2k] (before) and events[2k+1] (after) on the call's stream; elapsed times between the
+ * pair give that kernel's duration. Slots: 0 flag clear, 1 warm-start operand, 2 M Q with
+ * error feedback, 3 Gram partials, 4 Gram-Schmidt, 5 orthonormal P, 6 M^T P, 7 skip clear,
+ * 8 finite check, 9 decompression + error update, 10 q commit. n must be at least 22.
+ * events == NULL (n ignored) removes the hook. The events stay owned by the caller.
+ */
+psgd_status psgd_profile_events(psgd_ctx* ctx, hipEvent_t* events, int n);
+
+/* Message of the last failed call on ctx ("" if none). Valid until the next call on ctx. */
+const char* psgd_last_error(const psgd_ctx* ctx);
+
+/*
+ * Diagnostics for tests: device address and byte size of an internal per-matrix buffer of a
+ * plan. which: 0 = raw factor M q (m x rpad fp32, before orthonormalisation),
+ * 1 = orthonormalising coefficient matrix T (rpad x rpad fp64, upper triangular, P = (M q) T).
+ * *rpad receives the padded rank (r rounded up to 16).
+ */
+psgd_status psgd_debug_buffer(psgd_plan* plan, int which, int mat, void** ptr, int64_t* bytes,
+                              int32_t* rpad);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PSGD_H */

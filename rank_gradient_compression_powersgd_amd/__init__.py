@@ -1,0 +1,14 @@
+"""MI355X-native PowerSGD gradient compression (the data-parallel hot path of DALL·E training).
+
+The PowerSGD step runs in hand-written gfx950 HIP kernels inside libpsgd.so (C ABI:
+include/psgd.h). This package is the thin Python binding over it:
+  * binding  - ctypes wrappers with the ABI's names (psgd_create, psgd_compress, ...);
+  * group    - a convenience holder of one group of gradient matrices and their state.
+"""
+from .binding import (  # noqa: F401
+    LIB_PATH, PROFILE_SLOTS, PSGD_BF16, PSGD_F16, PSGD_F32, PsgdError, load_library,
+    make_matrix, psgd_check_finite, psgd_compress, psgd_create, psgd_debug_buffer,
+    psgd_decompress_update, psgd_destroy, psgd_last_error, psgd_plan_create, psgd_plan_destroy,
+    psgd_profile_events, psgd_version,
+)
+from .group import PowerSGDGroup  # noqa: F401

@@ -1,0 +1,213 @@
+"""ctypes binding of libpsgd.so: the C ABI of include/psgd.h, under the same names.
+
+Argument marshalling only. Every step of the PowerSGD path runs in the HIP kernels of the
+library; torch tensors are used for device memory and streams. If the library is missing the
+import of this module's functions raises: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Iterable, List, Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpsgd.so")
+
+PSGD_OK, PSGD_EINVAL, PSGD_EDTYPE, PSGD_ENOMEM, PSGD_EHIP, PSGD_EUNSUPPORTED = range(6)
+PSGD_F16, PSGD_BF16, PSGD_F32 = 1, 2, 3
+STATUS_NAMES = {0: "PSGD_OK", 1: "PSGD_EINVAL", 2: "PSGD_EDTYPE", 3: "PSGD_ENOMEM",
+                4: "PSGD_EHIP", 5: "PSGD_EUNSUPPORTED"}
+
+# Names of the profiling slots (order of psgd_profile_events).
+PROFILE_SLOTS = ("zero_flags", "prep_qt", "ef_mq", "gs_gram", "gs_factor", "gs_apply", "mtp",
+                 "zero_skip", "check_finite", "decompress", "commit_q")
+
+
+class psgd_matrix(ctypes.Structure):
+    _fields_ = [
+        ("grad", ctypes.c_void_p), ("ld_grad", ctypes.c_int64),
+        ("err", ctypes.c_void_p), ("ld_err", ctypes.c_int64),
+        ("q", ctypes.c_void_p),
+        ("q_next", ctypes.c_void_p),
+        ("p", ctypes.c_void_p),
+        ("out", ctypes.c_void_p), ("ld_out", ctypes.c_int64),
+        ("m", ctypes.c_int64), ("n", ctypes.c_int64),
+        ("block", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class psgd_tensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("numel", ctypes.c_int64)]
+
+
+class PsgdError(RuntimeError):
+    def __init__(self, call: str, status: int, message: str):
+        super().__init__(f"{call} failed: {STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libpsgd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    # torch first: its HIP runtime is then the one libpsgd.so binds to (same soname), so the
+    # streams and events torch hands out are valid inside the library.
+    import torch  # noqa: F401
+    if not os.path.exists(p):
+        raise ImportError(
+            f"{p} is missing: build it with `python -m rank_gradient_compression_powersgd_amd.build` "
+            "(there is no CPU fallback for the PowerSGD kernels)")
+    lib = ctypes.CDLL(p)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.psgd_version.restype = ctypes.c_int
+    lib.psgd_create.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.c_int]
+    lib.psgd_destroy.argtypes = [vp]
+    lib.psgd_plan_create.argtypes = [vp, ctypes.POINTER(psgd_matrix), ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, ctypes.POINTER(vp)]
+    lib.psgd_plan_destroy.argtypes = [vp]
+    lib.psgd_compress.argtypes = [vp, vp, vp, vp, vp]
+    lib.psgd_check_finite.argtypes = [vp, vp, vp, ctypes.POINTER(psgd_tensor), ctypes.c_int, vp, vp,
+                                      ctypes.POINTER(i32), vp]
+    lib.psgd_decompress_update.argtypes = [vp, vp, vp, vp, vp]
+    lib.psgd_last_error.argtypes = [vp]
+    lib.psgd_last_error.restype = ctypes.c_char_p
+    lib.psgd_debug_buffer.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp),
+                                      ctypes.POINTER(i64), ctypes.POINTER(i32)]
+    lib.psgd_profile_events.argtypes = [vp, ctypes.POINTER(vp), ctypes.c_int]
+    for name in ("psgd_create", "psgd_destroy", "psgd_plan_create", "psgd_plan_destroy",
+                 "psgd_compress", "psgd_check_finite", "psgd_decompress_update",
+                 "psgd_debug_buffer", "psgd_profile_events"):
+        getattr(lib, name).restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(ctx, call: str, status: int):
+    if status != PSGD_OK:
+        msg = ""
+        if ctx:
+            raw = load_library().psgd_last_error(ctx)
+            msg = raw.decode() if raw else ""
+        raise PsgdError(call, status, msg)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+# --------------------------------------------------------------------------------------
+# the C ABI, one function per entry point
+# --------------------------------------------------------------------------------------
+def psgd_version() -> int:
+    return int(load_library().psgd_version())
+
+
+def psgd_create(device: int, rank: int) -> int:
+    h = ctypes.c_void_p()
+    _check(None, "psgd_create", load_library().psgd_create(ctypes.byref(h), device, rank))
+    return h.value
+
+
+def psgd_destroy(ctx: int) -> None:
+    load_library().psgd_destroy(ctx)
+
+
+def dtype_code(torch_dtype) -> int:
+    import torch
+    return {torch.float16: PSGD_F16, torch.bfloat16: PSGD_BF16, torch.float32: PSGD_F32}[torch_dtype]
+
+
+def make_matrix(grad, err, q, q_next, p, block: int, out=None) -> psgd_matrix:
+    """psgd_matrix over torch tensors (row-major; leading dimensions from the strides)."""
+    m, n = grad.shape
+    for name, t, shape in (("err", err, (m, n)), ("q", q, None), ("q_next", q_next, None),
+                           ("p", p, None), ("out", out, (m, n))):
+        if t is None:
+            continue
+        if shape is not None and tuple(t.shape) != shape:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+        if t.stride(-1) != 1:
+            raise ValueError(f"{name} must have unit stride along rows")
+    for name, t in (("q", q), ("q_next", q_next), ("p", p)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    return psgd_matrix(
+        grad=_ptr(grad), ld_grad=grad.stride(0),
+        err=_ptr(err), ld_err=err.stride(0),
+        q=_ptr(q), q_next=_ptr(q_next), p=_ptr(p),
+        out=_ptr(out), ld_out=out.stride(0) if out is not None else 0,
+        m=m, n=n, block=block, reserved=0)
+
+
+def psgd_plan_create(ctx: int, mats: Sequence[psgd_matrix], grad_dtype: int, n_blocks: int) -> int:
+    arr = (psgd_matrix * len(mats))(*mats)
+    h = ctypes.c_void_p()
+    _check(ctx, "psgd_plan_create",
+           load_library().psgd_plan_create(ctx, arr, len(mats), grad_dtype, n_blocks, ctypes.byref(h)))
+    return h.value
+
+
+def psgd_plan_destroy(plan: int) -> None:
+    load_library().psgd_plan_destroy(plan)
+
+
+def psgd_compress(ctx: int, plan: int, scale, flags, stream=None) -> None:
+    _check(ctx, "psgd_compress",
+           load_library().psgd_compress(ctx, plan, _ptr(scale), _ptr(flags), _stream(stream)))
+
+
+def psgd_check_finite(ctx: int, plan: int, flags, passthrough: Iterable, scale, skip_dev,
+                      host: bool = False, stream=None) -> Optional[int]:
+    pts = [t for t in passthrough]
+    arr = (psgd_tensor * max(1, len(pts)))(*[psgd_tensor(_ptr(t), t.numel()) for t in pts])
+    skip_host = ctypes.c_int32(-1)
+    _check(ctx, "psgd_check_finite",
+           load_library().psgd_check_finite(ctx, plan, _ptr(flags), arr, len(pts), _ptr(scale),
+                                            _ptr(skip_dev), ctypes.byref(skip_host) if host else None,
+                                            _stream(stream)))
+    return int(skip_host.value) if host else None
+
+
+def psgd_decompress_update(ctx: int, plan: int, scale, skip_dev, stream=None) -> None:
+    _check(ctx, "psgd_decompress_update",
+           load_library().psgd_decompress_update(ctx, plan, _ptr(scale), _ptr(skip_dev), _stream(stream)))
+
+
+def psgd_last_error(ctx: int) -> str:
+    raw = load_library().psgd_last_error(ctx)
+    return raw.decode() if raw else ""
+
+
+def psgd_debug_buffer(plan: int, which: int, mat: int):
+    """(device address, bytes, rpad) of an internal buffer of a plan."""
+    ptr, nbytes, rpad = ctypes.c_void_p(), ctypes.c_int64(), ctypes.c_int32()
+    _check(None, "psgd_debug_buffer",
+           load_library().psgd_debug_buffer(plan, which, mat, ctypes.byref(ptr), ctypes.byref(nbytes),
+                                            ctypes.byref(rpad)))
+    return ptr.value, nbytes.value, rpad.value
+
+
+def psgd_profile_events(ctx: int, events: Optional[List[int]]) -> None:
+    """Install (or with None remove) HIP events recorded around every kernel launch: event
+    2*k before and 2*k+1 after the launch of slot k of PROFILE_SLOTS."""
+    if events is None:
+        _check(ctx, "psgd_profile_events", load_library().psgd_profile_events(ctx, None, 0))
+        return
+    arr = (ctypes.c_void_p * len(events))(*events)
+    _check(ctx, "psgd_profile_events", load_library().psgd_profile_events(ctx, arr, len(events)))

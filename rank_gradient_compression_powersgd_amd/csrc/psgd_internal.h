@@ -1,0 +1,175 @@
+// Internal definitions shared by the HIP kernels and the runtime of libpsgd.so (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace psgd {
+
+// ------------------------------------------------------------------------------------------
+// vector types for the gfx950 MFMA builtins
+// ------------------------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+enum GradType : int { G_F16 = 1, G_BF16 = 2, G_F32 = 3 };
+
+constexpr int kWave = 64;
+constexpr int kMaxRankTiles = 8;          // r <= 128 in this build
+constexpr int kXcds = 8;                  // MI355X: 8 XCDs, 32 CUs each
+constexpr int kGramRows = 256;            // rows per Gram partial
+constexpr double kDegenerate = 9.094947017729282e-13;   // 2^-40: relative squared residual
+
+// ------------------------------------------------------------------------------------------
+// device-side description of one gradient matrix and its plan workspace
+// ------------------------------------------------------------------------------------------
+struct DevMat {
+  const void* grad;  int64_t ld_grad;
+  float* err;        int64_t ld_err;
+  float* q;          float* q_next;    float* p;
+  float* out;        int64_t ld_out;
+  int32_t m, n, block, r;
+  int32_t rpad;      // r rounded up to 16 (MFMA tile)
+  int32_t kpad3;     // r rounded up to 32 (K of the fp16 decompression MFMA)
+  int32_t npad;      // n rounded up to 32
+  int32_t mpad;      // m rounded up to 32
+  int32_t gram_parts;
+  int32_t pad_;
+  // workspace (library owned)
+  float* p_raw;                        // m x rpad fp32: M q before orthonormalisation
+  uint16_t* qt_hi; uint16_t* qt_lo;    // rpad x npad bf16: q^T split into hi + lo
+  uint16_t* pt_hi; uint16_t* pt_lo;    // rpad x mpad bf16: P^T split into hi + lo
+  uint16_t* p3_hi; uint16_t* p3_lo;    // m x kpad3 fp16: P * 2^p3_exp[row], split hi + lo
+  int32_t* p3_exp;                     // m
+  uint16_t* q3_hi; uint16_t* q3_lo;    // n x kpad3 fp16: q_next * 2^q3_exp[row], split hi + lo
+  int32_t* q3_exp;                     // n
+  double* gram;                        // gram_parts x rpad x rpad fp64 partial Gram matrices
+  double* tmat;                        // rpad x rpad fp64 upper-triangular T, P = (M q) T
+};
+
+// One unit of grouped work: a matrix and a block of it. Unused slots have mat = -1.
+struct Work {
+  int32_t mat;
+  int32_t a;   // first row (K1, Gram, apply, decompress) or first column (K2)
+  int32_t b;   // rank chunk (K1, K2) / first column (decompress) / Gram part
+  int32_t c;
+};
+
+// ------------------------------------------------------------------------------------------
+// helpers
+// ------------------------------------------------------------------------------------------
+// Workgroups are dispatched round-robin over the 8 XCDs. Remap so that each XCD walks one
+// contiguous range of the work list (neighbouring blocks of one matrix share its factor in L2).
+// `grid` is a multiple of 8.
+__device__ __forceinline__ int xcd_remap(int bid, int grid) {
+  const int per = grid >> 3;
+  return (bid & (kXcds - 1)) * per + (bid >> 3);
+}
+
+// class mask: signalling NaN | quiet NaN | -inf | +inf
+__device__ __forceinline__ bool nonfinite(float x) { return __builtin_amdgcn_classf(x, 1 | 2 | 4 | 512); }
+
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f64x4 mfma_f64(double a, double b, f64x4 c) {
+  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
+// x = hi + lo with hi, lo bfloat16 (round to nearest even); |x - hi - lo| <= 2^-17 |x|.
+__device__ __forceinline__ void split_bf16(const f32x8& x, bf16x8& hi, bf16x8& lo) {
+  hi = __builtin_convertvector(x, bf16x8);
+  const f32x8 rest = x - __builtin_convertvector(hi, f32x8);
+  lo = __builtin_convertvector(rest, bf16x8);
+}
+
+// Power-of-two exponent e with |x| * 2^e in [2^13, 2^14) for the largest |x| of a row; 0 for
+// rows that are all zero or not finite.
+__device__ __forceinline__ int fp16_row_exponent(float amax) {
+  if (!(amax > 0.0f) || nonfinite(amax)) return 0;
+  int ex;
+  (void)frexpf(amax, &ex);           // amax = f * 2^ex, f in [0.5, 1)
+  return 14 - ex;
+}
+
+// 16-bit patterns of float values
+__device__ __forceinline__ uint16_t bf16_bits(__bf16 v) { return __builtin_bit_cast(uint16_t, v); }
+__device__ __forceinline__ uint16_t f16_bits(_Float16 v) { return __builtin_bit_cast(uint16_t, v); }
+
+// Load 8 gradient elements as fp32 (16-byte aligned source of the gradient dtype).
+template <int GT> struct GradIO;
+template <> struct GradIO<G_F16> {
+  static constexpr int kBytes = 2;
+  __device__ __forceinline__ static f32x8 load8(const void* base) {
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(base);
+    return __builtin_convertvector(__builtin_bit_cast(f16x8, raw), f32x8);
+  }
+  __device__ __forceinline__ static f32x4 load4(const void* base) {
+    const u32x2 raw = *reinterpret_cast<const u32x2*>(base);
+    return __builtin_convertvector(__builtin_bit_cast(f16x4, raw), f32x4);
+  }
+};
+template <> struct GradIO<G_BF16> {
+  static constexpr int kBytes = 2;
+  __device__ __forceinline__ static f32x8 load8(const void* base) {
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(base);
+    return __builtin_convertvector(__builtin_bit_cast(bf16x8, raw), f32x8);
+  }
+  __device__ __forceinline__ static f32x4 load4(const void* base) {
+    const u32x2 raw = *reinterpret_cast<const u32x2*>(base);
+    return __builtin_convertvector(__builtin_bit_cast(bf16x4, raw), f32x4);
+  }
+};
+template <> struct GradIO<G_F32> {
+  static constexpr int kBytes = 4;
+  __device__ __forceinline__ static f32x8 load8(const void* base) {
+    const f32x4 a = reinterpret_cast<const f32x4*>(base)[0];
+    const f32x4 b = reinterpret_cast<const f32x4*>(base)[1];
+    return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
+  __device__ __forceinline__ static f32x4 load4(const void* base) {
+    return *reinterpret_cast<const f32x4*>(base);
+  }
+};
+
+__device__ __forceinline__ f32x8 load_f32x8(const float* p) {
+  const f32x4 a = reinterpret_cast<const f32x4*>(p)[0];
+  const f32x4 b = reinterpret_cast<const f32x4*>(p)[1];
+  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+}  // namespace psgd
+
+// ------------------------------------------------------------------------------------------
+// host-side launchers (one translation unit per kernel family)
+// ------------------------------------------------------------------------------------------
+namespace psgd {
+hipError_t launch_zero_u8(uint8_t* p, int n, hipStream_t s);
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
+hipError_t launch_prep_qt(const DevMat* mats, const Work* work, int n_work, int rpad_max, hipStream_t s);
+hipError_t launch_ef_mq(int gt, int rtc, const DevMat* mats, const Work* work, int n_work,
+                        const float* scale, uint8_t* flags, hipStream_t s);
+hipError_t launch_gs_gram(int rt, const DevMat* mats, const Work* work, int n_work, hipStream_t s);
+hipError_t launch_gs_factor(const DevMat* mats, const Work* work, int n_work, hipStream_t s);
+hipError_t launch_gs_apply(int rt, const DevMat* mats, const Work* work, int n_work, hipStream_t s);
+hipError_t launch_mtp(int gt, int rtc, const DevMat* mats, const Work* work, int n_work,
+                      const float* scale, hipStream_t s);
+hipError_t launch_decompress(int gt, const DevMat* mats, const Work* work, int n_work,
+                             const float* scale, const int32_t* skip, hipStream_t s);
+hipError_t launch_commit_q(const DevMat* mats, const Work* work, int n_work, const int32_t* skip,
+                           hipStream_t s);
+struct PassList;
+hipError_t launch_check_finite(const uint8_t* flags, int n_flags, const float* scale, int n_scale,
+                               const float* const* pass_ptr, const int64_t* pass_n, int n_pass,
+                               int32_t* skip, hipStream_t s);
+}  // namespace psgd

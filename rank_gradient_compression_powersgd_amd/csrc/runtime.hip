@@ -1,0 +1,394 @@
+// C ABI of libpsgd.so: contexts, plans (validated descriptor tables + workspace) and the three
+// step calls, each enqueuing grouped kernels on the caller's stream.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <memory>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/psgd.h"
+#include "psgd_internal.h"
+
+namespace psgd {
+int ef_mq_rows_per_block();
+int mtp_cols_per_block();
+int gs_apply_rows_per_block();
+int decomp_tile_m();
+int decomp_tile_n();
+}  // namespace psgd
+
+using psgd::DevMat;
+using psgd::Work;
+
+struct psgd_ctx {
+  int device = 0;
+  int rank = 0;
+  std::string err;
+  std::vector<hipEvent_t> events;   // tracing hook: 2 per slot, empty when off
+};
+
+namespace {
+
+enum WorkKind { W_PREP, W_K1, W_GRAM, W_FACTOR, W_APPLY, W_K2, W_K3, W_COMMIT, W_KINDS };
+
+}  // namespace
+
+struct psgd_plan {
+  psgd_ctx* ctx = nullptr;
+  int n_mats = 0, n_blocks = 0, gt = 0, rt = 0, rtc = 0, chunks = 0;
+  std::vector<DevMat> mats;
+  DevMat* d_mats = nullptr;
+  void* workspace = nullptr;
+  size_t ws_bytes = 0;
+  Work* d_work = nullptr;
+  int off[W_KINDS] = {0};
+  int cnt[W_KINDS] = {0};
+};
+
+namespace {
+
+psgd_status fail(psgd_ctx* ctx, psgd_status st, const char* fmt, ...) __attribute__((format(printf, 3, 4)));
+psgd_status fail(psgd_ctx* ctx, psgd_status st, const char* fmt, ...) {
+  if (ctx) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    ctx->err = buf;
+  }
+  return st;
+}
+
+psgd_status hip_fail(psgd_ctx* ctx, hipError_t e, const char* what) {
+  return fail(ctx, PSGD_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+enum Slot { S_ZERO_FLAGS, S_PREP, S_K1, S_GRAM, S_FACTOR, S_APPLY, S_K2, S_ZERO_SKIP, S_CHECK,
+            S_K3, S_COMMIT, S_SLOTS };
+
+// Launch `expr` in tracing slot `slot`, bracketed by the hook's events when installed.
+template <typename F>
+hipError_t traced(psgd_ctx* ctx, int slot, hipStream_t s, F&& launch) {
+  if (!ctx->events.empty()) {
+    const hipError_t e = hipEventRecord(ctx->events[2 * slot], s);
+    if (e != hipSuccess) return e;
+  }
+  const hipError_t e = launch();
+  if (e != hipSuccess || ctx->events.empty()) return e;
+  return hipEventRecord(ctx->events[2 * slot + 1], s);
+}
+
+#define HIPCHK(ctx, expr, what)                         \
+  do {                                                  \
+    hipError_t e_ = (expr);                             \
+    if (e_ != hipSuccess) return hip_fail(ctx, e_, what); \
+  } while (0)
+
+inline int64_t rup(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int psgd_version(void) { return PSGD_ABI_VERSION; }
+
+psgd_status psgd_create(psgd_ctx** out, int device, int rank) {
+  if (!out) return PSGD_EINVAL;
+  *out = nullptr;
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || device < 0 || device >= n) return PSGD_EINVAL;
+  if (rank < 1) return PSGD_EINVAL;
+  if (rank > 16 * psgd::kMaxRankTiles) return PSGD_EUNSUPPORTED;
+  psgd_ctx* c = new (std::nothrow) psgd_ctx;
+  if (!c) return PSGD_ENOMEM;
+  c->device = device;
+  c->rank = rank;
+  *out = c;
+  return PSGD_OK;
+}
+
+psgd_status psgd_destroy(psgd_ctx* ctx) {
+  delete ctx;
+  return PSGD_OK;
+}
+
+const char* psgd_last_error(const psgd_ctx* ctx) { return ctx ? ctx->err.c_str() : ""; }
+
+psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
+                             psgd_dtype grad_dtype, int n_blocks, psgd_plan** plan_out) {
+  if (!ctx) return PSGD_EINVAL;
+  ctx->err.clear();
+  if (!plan_out) return fail(ctx, PSGD_EINVAL, "plan pointer is NULL");
+  *plan_out = nullptr;
+  if (!mats || n_mats < 1) return fail(ctx, PSGD_EINVAL, "need at least one matrix");
+  if (n_blocks < 1) return fail(ctx, PSGD_EINVAL, "n_blocks must be >= 1");
+  int gt = 0;
+  switch (grad_dtype) {
+    case PSGD_F16: gt = psgd::G_F16; break;
+    case PSGD_BF16: gt = psgd::G_BF16; break;
+    case PSGD_F32: gt = psgd::G_F32; break;
+    default: return fail(ctx, PSGD_EDTYPE, "unknown gradient dtype %d", (int)grad_dtype);
+  }
+  HIPCHK(ctx, hipSetDevice(ctx->device), "hipSetDevice");
+
+  const int r = ctx->rank;
+  const int rpad = (int)rup(r, 16);
+  const int kpad3 = (int)rup(r, 32);
+  const int rt = rpad / 16;
+  std::unique_ptr<psgd_plan> p(new (std::nothrow) psgd_plan);
+  if (!p) return fail(ctx, PSGD_ENOMEM, "out of host memory");
+  p->ctx = ctx;
+  p->n_mats = n_mats;
+  p->n_blocks = n_blocks;
+  p->gt = gt;
+  p->rt = rt;
+  p->rtc = rt;       // rank <= 128: one chunk
+  p->chunks = 1;
+
+  // ---- validate and lay out the workspace ---------------------------------------------
+  size_t ws = 0;
+  auto take = [&](size_t bytes) { size_t o = ws; ws += (size_t)rup((int64_t)bytes, 256); return o; };
+  struct Off { size_t p_raw, qth, qtl, pth, ptl, p3h, p3l, p3e, q3h, q3l, q3e, gram, tmat; };
+  std::vector<Off> offs(n_mats);
+  p->mats.resize(n_mats);
+  for (int i = 0; i < n_mats; ++i) {
+    const psgd_matrix& a = mats[i];
+    if (!a.grad || !a.err || !a.q || !a.q_next || !a.p)
+      return fail(ctx, PSGD_EINVAL, "matrix %d: grad, err, q, q_next and p are required", i);
+    if (a.m < 1 || a.n < 1 || a.m > (1 << 28) || a.n > (1 << 28))
+      return fail(ctx, PSGD_EINVAL, "matrix %d: bad shape %lld x %lld", i, (long long)a.m, (long long)a.n);
+    if (a.n % 8 != 0) return fail(ctx, PSGD_EINVAL, "matrix %d: n = %lld is not a multiple of 8", i, (long long)a.n);
+    if (r > a.m || r > a.n)
+      return fail(ctx, PSGD_EINVAL, "matrix %d: rank %d exceeds min(m, n)", i, r);
+    if (a.ld_grad < a.n || a.ld_grad % 8 != 0)
+      return fail(ctx, PSGD_EINVAL, "matrix %d: ld_grad must be >= n and a multiple of 8", i);
+    if (a.ld_err < a.n || a.ld_err % 4 != 0)
+      return fail(ctx, PSGD_EINVAL, "matrix %d: ld_err must be >= n and a multiple of 4", i);
+    if (a.out && (a.ld_out < a.n || a.ld_out % 4 != 0))
+      return fail(ctx, PSGD_EINVAL, "matrix %d: ld_out must be >= n and a multiple of 4", i);
+    if (!aligned16(a.grad) || !aligned16(a.err) || !aligned16(a.q) || !aligned16(a.q_next) ||
+        !aligned16(a.p) || (a.out && !aligned16(a.out)))
+      return fail(ctx, PSGD_EINVAL, "matrix %d: every pointer must be 16-byte aligned", i);
+    if (a.block < 0 || a.block >= n_blocks)
+      return fail(ctx, PSGD_EINVAL, "matrix %d: block %d outside [0, %d)", i, a.block, n_blocks);
+    if (a.reserved != 0) return fail(ctx, PSGD_EINVAL, "matrix %d: reserved field must be 0", i);
+
+    DevMat& d = p->mats[i];
+    std::memset(&d, 0, sizeof d);
+    d.grad = a.grad; d.ld_grad = a.ld_grad;
+    d.err = a.err; d.ld_err = a.ld_err;
+    d.q = a.q; d.q_next = a.q_next; d.p = a.p;
+    d.out = a.out; d.ld_out = a.ld_out;
+    d.m = (int)a.m; d.n = (int)a.n; d.block = a.block; d.r = r;
+    d.rpad = rpad; d.kpad3 = kpad3;
+    d.npad = (int)rup(a.n, 32); d.mpad = (int)rup(a.m, 32);
+    d.gram_parts = (int)((a.m + psgd::kGramRows - 1) / psgd::kGramRows);
+    Off& o = offs[i];
+    o.p_raw = take((size_t)a.m * rpad * 4);
+    o.qth = take((size_t)rpad * d.npad * 2);
+    o.qtl = take((size_t)rpad * d.npad * 2);
+    o.pth = take((size_t)rpad * d.mpad * 2);
+    o.ptl = take((size_t)rpad * d.mpad * 2);
+    o.p3h = take((size_t)a.m * kpad3 * 2);
+    o.p3l = take((size_t)a.m * kpad3 * 2);
+    o.p3e = take((size_t)a.m * 4);
+    o.q3h = take((size_t)a.n * kpad3 * 2);
+    o.q3l = take((size_t)a.n * kpad3 * 2);
+    o.q3e = take((size_t)a.n * 4);
+    o.gram = take((size_t)d.gram_parts * rpad * rpad * 8);
+    o.tmat = take((size_t)rpad * rpad * 8);
+  }
+
+  // ---- work lists -------------------------------------------------------------------------
+  std::vector<Work> all;
+  auto begin_kind = [&](int k) { p->off[k] = (int)all.size(); };
+  auto end_kind = [&](int k, bool pad8) {
+    if (pad8) while ((all.size() - p->off[k]) % psgd::kXcds) all.push_back(Work{-1, 0, 0, 0});
+    p->cnt[k] = (int)all.size() - p->off[k];
+  };
+  const int k1rows = psgd::ef_mq_rows_per_block();
+  const int k2cols = psgd::mtp_cols_per_block();
+  const int aprows = psgd::gs_apply_rows_per_block();
+  const int tm = psgd::decomp_tile_m(), tn = psgd::decomp_tile_n();
+  begin_kind(W_PREP);
+  for (int i = 0; i < n_mats; ++i)
+    for (int n0 = 0; n0 < p->mats[i].npad; n0 += 32)
+      for (int r0 = 0; r0 < rpad; r0 += 32) all.push_back(Work{i, n0, r0, 0});
+  end_kind(W_PREP, false);
+  begin_kind(W_K1);
+  for (int i = 0; i < n_mats; ++i)
+    for (int ch = 0; ch < p->chunks; ++ch)
+      for (int r0 = 0; r0 < p->mats[i].m; r0 += k1rows) all.push_back(Work{i, r0, ch, 0});
+  end_kind(W_K1, true);
+  begin_kind(W_GRAM);
+  for (int i = 0; i < n_mats; ++i)
+    for (int pt = 0; pt < p->mats[i].gram_parts; ++pt) all.push_back(Work{i, pt * psgd::kGramRows, pt, 0});
+  end_kind(W_GRAM, true);
+  begin_kind(W_FACTOR);
+  for (int i = 0; i < n_mats; ++i) all.push_back(Work{i, 0, 0, 0});
+  end_kind(W_FACTOR, false);
+  begin_kind(W_APPLY);
+  for (int i = 0; i < n_mats; ++i)
+    for (int r0 = 0; r0 < p->mats[i].m; r0 += aprows) all.push_back(Work{i, r0, 0, 0});
+  end_kind(W_APPLY, true);
+  begin_kind(W_K2);
+  for (int i = 0; i < n_mats; ++i)
+    for (int ch = 0; ch < p->chunks; ++ch)
+      for (int c0 = 0; c0 < p->mats[i].n; c0 += k2cols) all.push_back(Work{i, c0, ch, 0});
+  end_kind(W_K2, true);
+  begin_kind(W_K3);
+  for (int i = 0; i < n_mats; ++i)
+    for (int m0 = 0; m0 < p->mats[i].m; m0 += tm)
+      for (int n0 = 0; n0 < p->mats[i].n; n0 += tn) all.push_back(Work{i, m0, n0, 0});
+  end_kind(W_K3, true);
+  begin_kind(W_COMMIT);
+  for (int i = 0; i < n_mats; ++i) {
+    const int64_t tot = (int64_t)p->mats[i].n * r;
+    for (int64_t c0 = 0; c0 * 4096 < tot; ++c0) all.push_back(Work{i, (int)c0, 0, 0});
+  }
+  end_kind(W_COMMIT, false);
+  for (int k = 0; k < W_KINDS; ++k)
+    if (p->cnt[k] > 0x7fffffff / 2) return fail(ctx, PSGD_EINVAL, "work list too long");
+
+  // ---- device allocations -----------------------------------------------------------------
+  hipError_t e = hipMalloc(&p->workspace, ws ? ws : 256);
+  if (e != hipSuccess) return fail(ctx, PSGD_ENOMEM, "workspace of %zu bytes: %s", ws, hipGetErrorString(e));
+  p->ws_bytes = ws;
+  auto cleanup = [&]() {
+    if (p->workspace) (void)hipFree(p->workspace);
+    if (p->d_mats) (void)hipFree(p->d_mats);
+    if (p->d_work) (void)hipFree(p->d_work);
+    p->workspace = nullptr;
+    p->d_mats = nullptr;
+    p->d_work = nullptr;
+  };
+  char* base = static_cast<char*>(p->workspace);
+  for (int i = 0; i < n_mats; ++i) {
+    DevMat& d = p->mats[i];
+    const Off& o = offs[i];
+    d.p_raw = reinterpret_cast<float*>(base + o.p_raw);
+    d.qt_hi = reinterpret_cast<uint16_t*>(base + o.qth);
+    d.qt_lo = reinterpret_cast<uint16_t*>(base + o.qtl);
+    d.pt_hi = reinterpret_cast<uint16_t*>(base + o.pth);
+    d.pt_lo = reinterpret_cast<uint16_t*>(base + o.ptl);
+    d.p3_hi = reinterpret_cast<uint16_t*>(base + o.p3h);
+    d.p3_lo = reinterpret_cast<uint16_t*>(base + o.p3l);
+    d.p3_exp = reinterpret_cast<int32_t*>(base + o.p3e);
+    d.q3_hi = reinterpret_cast<uint16_t*>(base + o.q3h);
+    d.q3_lo = reinterpret_cast<uint16_t*>(base + o.q3l);
+    d.q3_exp = reinterpret_cast<int32_t*>(base + o.q3e);
+    d.gram = reinterpret_cast<double*>(base + o.gram);
+    d.tmat = reinterpret_cast<double*>(base + o.tmat);
+  }
+  if ((e = hipMemset(p->workspace, 0, ws ? ws : 256)) != hipSuccess) { cleanup(); return hip_fail(ctx, e, "workspace clear"); }
+  if ((e = hipMalloc(&p->d_mats, sizeof(DevMat) * n_mats)) != hipSuccess) { cleanup(); return fail(ctx, PSGD_ENOMEM, "descriptor table"); }
+  if ((e = hipMemcpy(p->d_mats, p->mats.data(), sizeof(DevMat) * n_mats, hipMemcpyHostToDevice)) != hipSuccess) { cleanup(); return hip_fail(ctx, e, "descriptor upload"); }
+  if ((e = hipMalloc(&p->d_work, sizeof(Work) * all.size())) != hipSuccess) { cleanup(); return fail(ctx, PSGD_ENOMEM, "work lists"); }
+  if ((e = hipMemcpy(p->d_work, all.data(), sizeof(Work) * all.size(), hipMemcpyHostToDevice)) != hipSuccess) { cleanup(); return hip_fail(ctx, e, "work list upload"); }
+  if ((e = hipDeviceSynchronize()) != hipSuccess) { cleanup(); return hip_fail(ctx, e, "plan upload"); }
+  *plan_out = p.release();
+  return PSGD_OK;
+}
+
+psgd_status psgd_plan_destroy(psgd_plan* plan) {
+  if (!plan) return PSGD_OK;
+  (void)hipSetDevice(plan->ctx->device);
+  (void)hipDeviceSynchronize();
+  if (plan->workspace) (void)hipFree(plan->workspace);
+  if (plan->d_mats) (void)hipFree(plan->d_mats);
+  if (plan->d_work) (void)hipFree(plan->d_work);
+  delete plan;
+  return PSGD_OK;
+}
+
+psgd_status psgd_compress(psgd_ctx* ctx, psgd_plan* plan, const float* scale, uint8_t* flags,
+                          hipStream_t stream) {
+  if (!ctx) return PSGD_EINVAL;
+  ctx->err.clear();
+  if (!plan || plan->ctx != ctx) return fail(ctx, PSGD_EINVAL, "plan does not belong to this context");
+  if (!scale || !flags) return fail(ctx, PSGD_EINVAL, "scale and flags are required");
+  HIPCHK(ctx, hipSetDevice(ctx->device), "hipSetDevice");
+  const DevMat* dm = plan->d_mats;
+  auto W = [&](int k) { return plan->d_work + plan->off[k]; };
+  HIPCHK(ctx, traced(ctx, S_ZERO_FLAGS, stream, [&] { return psgd::launch_zero_u8(flags, plan->n_mats, stream); }), "flag clear");
+  HIPCHK(ctx, traced(ctx, S_PREP, stream, [&] { return psgd::launch_prep_qt(dm, W(W_PREP), plan->cnt[W_PREP], 0, stream); }), "warm-start operand");
+  HIPCHK(ctx, traced(ctx, S_K1, stream, [&] { return psgd::launch_ef_mq(plan->gt, plan->rtc, dm, W(W_K1), plan->cnt[W_K1], scale, flags, stream); }), "M Q");
+  HIPCHK(ctx, traced(ctx, S_GRAM, stream, [&] { return psgd::launch_gs_gram(plan->rt, dm, W(W_GRAM), plan->cnt[W_GRAM], stream); }), "Gram");
+  HIPCHK(ctx, traced(ctx, S_FACTOR, stream, [&] { return psgd::launch_gs_factor(dm, W(W_FACTOR), plan->cnt[W_FACTOR], stream); }), "Gram-Schmidt");
+  HIPCHK(ctx, traced(ctx, S_APPLY, stream, [&] { return psgd::launch_gs_apply(plan->rt, dm, W(W_APPLY), plan->cnt[W_APPLY], stream); }), "orthonormal P");
+  HIPCHK(ctx, traced(ctx, S_K2, stream, [&] { return psgd::launch_mtp(plan->gt, plan->rtc, dm, W(W_K2), plan->cnt[W_K2], scale, stream); }), "M^T P");
+  return PSGD_OK;
+}
+
+psgd_status psgd_check_finite(psgd_ctx* ctx, psgd_plan* plan, const uint8_t* flags,
+                              const psgd_tensor* pass, int n_pass, const float* scale,
+                              int32_t* skip_dev, int32_t* skip_host, hipStream_t stream) {
+  if (!ctx) return PSGD_EINVAL;
+  ctx->err.clear();
+  if (!plan || plan->ctx != ctx) return fail(ctx, PSGD_EINVAL, "plan does not belong to this context");
+  if (!flags || !scale || !skip_dev) return fail(ctx, PSGD_EINVAL, "flags, scale and skip_dev are required");
+  if (n_pass < 0 || (n_pass > 0 && !pass)) return fail(ctx, PSGD_EINVAL, "bad pass-through list");
+  std::vector<const float*> ptrs;
+  std::vector<int64_t> ns;
+  for (int i = 0; i < n_pass; ++i) {
+    if (pass[i].numel < 0 || (pass[i].numel > 0 && !pass[i].data))
+      return fail(ctx, PSGD_EINVAL, "pass-through tensor %d: bad pointer or size", i);
+    if (pass[i].numel == 0) continue;
+    ptrs.push_back(pass[i].data);
+    ns.push_back(pass[i].numel);
+  }
+  HIPCHK(ctx, hipSetDevice(ctx->device), "hipSetDevice");
+  HIPCHK(ctx, traced(ctx, S_ZERO_SKIP, stream, [&] { return psgd::launch_zero_i32(skip_dev, 1, stream); }), "skip clear");
+  HIPCHK(ctx, traced(ctx, S_CHECK, stream, [&] {
+                return psgd::launch_check_finite(flags, plan->n_mats, scale, plan->n_blocks, ptrs.data(),
+                                                 ns.data(), (int)ptrs.size(), skip_dev, stream); }), "finite check");
+  if (skip_host) {
+    HIPCHK(ctx, hipMemcpyAsync(skip_host, skip_dev, sizeof(int32_t), hipMemcpyDeviceToHost, stream), "skip copy");
+    HIPCHK(ctx, hipStreamSynchronize(stream), "skip sync");
+  }
+  return PSGD_OK;
+}
+
+psgd_status psgd_decompress_update(psgd_ctx* ctx, psgd_plan* plan, const float* scale,
+                                   const int32_t* skip_dev, hipStream_t stream) {
+  if (!ctx) return PSGD_EINVAL;
+  ctx->err.clear();
+  if (!plan || plan->ctx != ctx) return fail(ctx, PSGD_EINVAL, "plan does not belong to this context");
+  if (!scale || !skip_dev) return fail(ctx, PSGD_EINVAL, "scale and skip_dev are required");
+  HIPCHK(ctx, hipSetDevice(ctx->device), "hipSetDevice");
+  const DevMat* dm = plan->d_mats;
+  auto W = [&](int k) { return plan->d_work + plan->off[k]; };
+  HIPCHK(ctx, traced(ctx, S_K3, stream, [&] { return psgd::launch_decompress(plan->gt, dm, W(W_K3), plan->cnt[W_K3], scale, skip_dev, stream); }), "decompress");
+  HIPCHK(ctx, traced(ctx, S_COMMIT, stream, [&] { return psgd::launch_commit_q(dm, W(W_COMMIT), plan->cnt[W_COMMIT], skip_dev, stream); }), "commit q");
+  return PSGD_OK;
+}
+
+psgd_status psgd_profile_events(psgd_ctx* ctx, hipEvent_t* events, int n) {
+  if (!ctx) return PSGD_EINVAL;
+  ctx->err.clear();
+  if (!events) {
+    ctx->events.clear();
+    return PSGD_OK;
+  }
+  if (n < 2 * S_SLOTS) return fail(ctx, PSGD_EINVAL, "need at least %d events, got %d", 2 * S_SLOTS, n);
+  ctx->events.assign(events, events + 2 * S_SLOTS);
+  return PSGD_OK;
+}
+
+psgd_status psgd_debug_buffer(psgd_plan* plan, int which, int mat, void** ptr, int64_t* bytes,
+                              int32_t* rpad) {
+  if (!plan || !ptr || !bytes || mat < 0 || mat >= plan->n_mats) return PSGD_EINVAL;
+  const DevMat& d = plan->mats[mat];
+  if (rpad) *rpad = d.rpad;
+  switch (which) {
+    case 0: *ptr = d.p_raw; *bytes = (int64_t)d.m * d.rpad * 4; return PSGD_OK;
+    case 1: *ptr = d.tmat; *bytes = (int64_t)d.rpad * d.rpad * 8; return PSGD_OK;
+  }
+  return PSGD_EINVAL;
+}
+
+}  // extern "C"

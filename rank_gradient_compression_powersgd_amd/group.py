@@ -1,0 +1,77 @@
+"""One group of gradient matrices compressed together, over torch device tensors.
+
+Holds the context, the plan and the per-step device words (flags, skip), and calls the three
+entry points in order. All compute happens in libpsgd.so.
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Sequence
+
+from . import binding as B
+
+
+class PowerSGDGroup:
+    """State of a group: per matrix G (caller-filled each step), E, Q, Q_next, P, optional D.
+
+    grads: list of 2-D device tensors (fp16, bf16 or fp32, all the same dtype, unit row stride)
+    blocks: per matrix index into `scale`
+    scale: device fp32 tensor of per-resblock multipliers
+    q0: list of n x r fp32 initial warm starts (copied)
+    err: optional list of m x n fp32 device tensors used in place as the error buffers
+         (unit row stride; default: new zero buffers)
+    write_out: allocate D buffers and have the decompression write them
+    """
+
+    def __init__(self, grads: Sequence, blocks: Sequence[int], scale, rank: int, q0: Sequence,
+                 err: Optional[Sequence] = None, write_out: bool = True, device: int = 0):
+        import torch
+        self.torch = torch
+        self.rank = rank
+        self.grads = list(grads)
+        self.blocks = list(blocks)
+        self.scale = scale
+        dev = self.grads[0].device
+        self.err = ([torch.zeros(g.shape, dtype=torch.float32, device=dev) for g in self.grads]
+                    if err is None else list(err))
+        self.q = [q.to(device=dev, dtype=torch.float32).contiguous().clone() for q in q0]
+        self.q_next = [torch.empty_like(q) for q in self.q]
+        self.p = [torch.empty((g.shape[0], rank), dtype=torch.float32, device=dev) for g in self.grads]
+        self.out = [torch.empty(g.shape, dtype=torch.float32, device=dev) if write_out else None
+                    for g in self.grads]
+        self.flags = torch.zeros(len(self.grads), dtype=torch.uint8, device=dev)
+        self.skip = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.ctx = B.psgd_create(device, rank)
+        mats = [B.make_matrix(g, e, q, qn, p, b, o) for g, e, q, qn, p, b, o in
+                zip(self.grads, self.err, self.q, self.q_next, self.p, self.blocks, self.out)]
+        self.plan = B.psgd_plan_create(self.ctx, mats, B.dtype_code(self.grads[0].dtype),
+                                       int(scale.numel()))
+
+    def compress(self, stream=None):
+        B.psgd_compress(self.ctx, self.plan, self.scale, self.flags, stream)
+
+    def check_finite(self, passthrough: Sequence = (), host: bool = False, stream=None):
+        return B.psgd_check_finite(self.ctx, self.plan, self.flags, passthrough, self.scale,
+                                   self.skip, host, stream)
+
+    def decompress_update(self, stream=None):
+        B.psgd_decompress_update(self.ctx, self.plan, self.scale, self.skip, stream)
+
+    def step(self, passthrough: Sequence = (), host: bool = False, stream=None):
+        self.compress(stream)
+        s = self.check_finite(passthrough, host, stream)
+        self.decompress_update(stream)
+        return s
+
+    def close(self):
+        if getattr(self, "plan", None):
+            B.psgd_plan_destroy(self.plan)
+            self.plan = None
+        if getattr(self, "ctx", None):
+            B.psgd_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

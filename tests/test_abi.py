@@ -1,0 +1,79 @@
+"""The C-ABI library loads and exports every entry point include/psgd.h declares (CPU only),
+and the ctypes structures match the C layout."""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "psgd.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(psgd_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_step_calls():
+    names = _declared()
+    for n in ("psgd_compress", "psgd_check_finite", "psgd_decompress_update", "psgd_create",
+              "psgd_destroy", "psgd_plan_create", "psgd_plan_destroy", "psgd_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    from rank_gradient_compression_powersgd_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail("libpsgd.so is not built (run python -m rank_gradient_compression_powersgd_amd.build)")
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert binding.load_library().psgd_version() == 1
+
+
+def test_binding_names_match_header():
+    import rank_gradient_compression_powersgd_amd as pkg
+    for n in _declared():
+        assert hasattr(pkg, n) or n in ("psgd_debug_buffer",), n
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+def test_struct_layout_matches_c(tmp_path):
+    from rank_gradient_compression_powersgd_amd.binding import psgd_matrix, psgd_tensor
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "psgd.h"\n'
+        "int main(void){\n"
+        ' printf("%zu %zu\\n", sizeof(psgd_matrix), sizeof(psgd_tensor));\n'
+        + "".join(f' printf("%zu\\n", offsetof(psgd_matrix, {f}));\n' for f, _ in psgd_matrix._fields_)
+        + " return 0; }\n")
+    exe = tmp_path / "layout"
+    r = subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                        "-I", "/opt/rocm/include", str(src), "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    vals = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()
+    assert int(vals[0]) == ctypes.sizeof(psgd_matrix)
+    assert int(vals[1]) == ctypes.sizeof(psgd_tensor)
+    for (f, _), off in zip(psgd_matrix._fields_, vals[2:]):
+        assert getattr(psgd_matrix, f).offset == int(off), f
+
+
+def test_product_path_fails_loudly_without_library(tmp_path):
+    from rank_gradient_compression_powersgd_amd import binding
+    with pytest.raises(ImportError):
+        binding.load_library(str(tmp_path / "missing.so"))
+
+
+def test_oracle_is_not_imported_by_the_product():
+    pkg = os.path.join(ROOT, "rank_gradient_compression_powersgd_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f), errors="ignore").read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), f
+                assert "oracle/" not in text, f

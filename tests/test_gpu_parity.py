@@ -1,0 +1,299 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle on the same inputs.
+
+Every input is seeded and synthetic (workloads/). The oracle never sees a value produced by
+the HIP path: it starts from the same generated state and evolves its own state.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from tests.gpu_helpers import Case, compare_step, log, orth_err, rel, REL_TOL, ORTH_TOL
+
+pytestmark = pytest.mark.gpu
+
+
+def _shard_case(config, n_blocks, err_warm=False, write_out=True, rank=None):
+    w = wl.workload(config, n_blocks) if config in (3, 4) else wl.workload(config)
+    specs = w.matrices
+    r = rank or w.rank
+    q0 = [wl.initial_q_np(w, s, r) for s in specs]
+    err0 = [wl.warm_error_np(w, s) for s in specs] if err_warm else None
+    case = Case([(s.m, s.n) for s in specs], [s.block for s in specs], w.dtype, r,
+                wl.scales_np(w), q0, err0, write_out)
+    return w, specs, case
+
+
+# ------------------------------------------------------------------------------------------
+# tiny 256x128 fp32 workload at rank 4
+# ------------------------------------------------------------------------------------------
+def test_tiny_single_step_and_exact_rank():
+    w = wl.workload(1)
+    spec = w.matrices[0]
+    G = wl.gradient_np(w, spec, 0)
+    Q0 = wl.initial_q_np(w, spec)
+    log("tiny 256x128 fp32 r=4: one step")
+    case = Case([(256, 128)], [0], "f32", 4, np.ones(1, np.float32), [Q0])
+    case.set_grads([G])
+    assert case.gpu_step() == 0
+    compare_step(case.fetch(), case.oracle_step(), "tiny step 0")
+    case.close()
+
+    log("tiny exact rank-4 matrix recovered in one step")
+    M = wl.exact_rank_np(256, 128, 4, seed=wl.step_seed(1, 0)).astype(np.float32)
+    case = Case([(256, 128)], [0], "f32", 4, np.ones(1, np.float32), [Q0])
+    case.set_grads([M])
+    case.gpu_step()
+    res = case.fetch()
+    st = case.oracle_step()
+    compare_step(res, st, "exact rank 4", exact_rank=True)
+    assert np.linalg.norm(res["E"][0]) / np.linalg.norm(M) <= 1e-5
+    case.close()
+
+
+def test_tiny_subspace_iteration_against_svd():
+    """Error buffer reset to zero before every step: the steps are subspace iterations on a
+    fixed matrix. After 1 and 20 iterations the error is bounded below by Eckart-Young and the
+    20-iteration excess is at most 5e-3; both match the oracle's iterations."""
+    import torch
+    w = wl.workload(1)
+    spec = w.matrices[0]
+    G = wl.gradient_np(w, spec, 0)
+    Q0 = wl.initial_q_np(w, spec)
+    M = G.astype(np.float64)
+    sv = np.linalg.svd(M, compute_uv=False)
+    floor = math.sqrt(float(np.sum(sv[4:] ** 2)))
+    case = Case([(256, 128)], [0], "f32", 4, np.ones(1, np.float32), [Q0])
+    case.set_grads([G])
+    for it in range(1, 21):
+        case.group.err[0].zero_()
+        case.gpu_step()
+        if it in (1, 20):
+            D = case.fetch()["D"][0]
+            _, _, Dor = oracle.subspace_iteration(M, Q0, it)
+            err = float(np.linalg.norm(M - D))
+            log(f"  iters={it}: |M-D|/floor - 1 = {err / floor - 1:.3e}, rel to oracle {rel(D, Dor):.2e}")
+            assert err >= floor * (1 - 1e-6)
+            assert rel(D, Dor) <= REL_TOL
+            if it == 20:
+                assert err / floor - 1 <= 5e-3
+    case.close()
+
+
+# ------------------------------------------------------------------------------------------
+# one resblock shard (fp16, rank 112)
+# ------------------------------------------------------------------------------------------
+def test_shard_cold_start_one_step():
+    w, specs, case = _shard_case(2, None)
+    log("resblock shard fp16 r=112, E0 = 0, one step")
+    case.set_grads([wl.gradient_np(w, s, 0) for s in specs])
+    assert case.gpu_step() == 0
+    res = case.fetch()
+    assert not res["flags"].any()
+    compare_step(res, case.oracle_step(), "shard cold")
+    case.close()
+
+
+def test_shard_warm_state_one_step():
+    w, specs, case = _shard_case(2, None, err_warm=True)
+    log("resblock shard fp16 r=112, generated warm E0, one step")
+    case.set_grads([wl.gradient_np(w, s, 3) for s in specs])
+    case.gpu_step()
+    compare_step(case.fetch(), case.oracle_step(), "shard warm")
+    case.close()
+
+
+def test_shard_free_running_ten_steps():
+    w, specs, case = _shard_case(2, None)
+    log("resblock shard fp16 r=112, 10 warm-started steps, independent trajectories")
+    for t in range(10):
+        case.set_grads([wl.gradient_np(w, s, t) for s in specs])
+        case.gpu_step()
+        compare_step(case.fetch(), case.oracle_step(), f"shard step {t}")
+    case.close()
+
+
+def test_shard_without_output_buffer():
+    w, specs, case = _shard_case(2, None, write_out=False)
+    case.set_grads([wl.gradient_np(w, s, 0) for s in specs])
+    case.gpu_step()
+    res = case.fetch()
+    st = case.oracle_step()
+    for i in range(len(specs)):
+        assert rel(res["E"][i], st.E_next[i]) <= REL_TOL
+    case.close()
+
+
+# ------------------------------------------------------------------------------------------
+# ragged shapes, padded leading dimensions, other ranks and dtypes
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,rank", [("f16", 20), ("bf16", 37), ("f32", 128), ("f16", 1)])
+def test_ragged_shapes(dtype, rank):
+    shapes = [(1000, 200), (37, 1048), (513, 264), (300, 128), (129, 136)]
+    shapes = [(m, n) for m, n in shapes if min(m, n) >= rank]
+    rng = np.random.default_rng(7000 + rank)
+    blocks = [i % 2 for i in range(len(shapes))]
+    scales = np.array([1.0, 0.3125], np.float32)
+    q0 = [rng.standard_normal((n, rank)).astype(np.float32) for _, n in shapes]
+    err0 = [(rng.standard_normal((m, n)) * 0.05).astype(np.float32) for m, n in shapes]
+    log(f"ragged {dtype} r={rank} shapes={shapes}, ld padded by 24")
+    case = Case(shapes, blocks, dtype, rank, scales, q0, err0, ld_pad=24)
+    for t in range(3):
+        gs = []
+        for m, n in shapes:
+            x = rng.standard_normal((m, n)) * np.exp(rng.uniform(-3, 0, size=(m, 1)))
+            gs.append(wl.to_bf16_bits(x) if dtype == "bf16" else
+                      (wl.to_fp16(x) if dtype == "f16" else x.astype(np.float32)))
+        case.set_grads(gs)
+        case.gpu_step()
+        compare_step(case.fetch(), case.oracle_step(), f"ragged step {t}", check_p=rank > 1)
+    # padding columns between n and ld are never touched
+    for gte in case.group.err:
+        base = gte.as_strided((gte.shape[0], gte.shape[1] + 24), gte.stride())
+        assert float(base[:, gte.shape[1]:].abs().max()) == 0.0
+    case.close()
+
+
+# ------------------------------------------------------------------------------------------
+# non-finite values: flags and skip bit-exact, error buffers zeroed, q kept
+# ------------------------------------------------------------------------------------------
+def test_nonfinite_flags_skip_and_zeroing():
+    import torch
+    shapes = [(300, 256), (64, 512), (200, 104)]
+    rank = 16
+    rng = np.random.default_rng(99)
+    q0 = [rng.standard_normal((n, rank)).astype(np.float32) for _, n in shapes]
+    err0 = [(rng.standard_normal((m, n)) * 0.1).astype(np.float32) for m, n in shapes]
+    scales = np.array([1.0, 0.5], np.float32)
+    case = Case(shapes, [0, 1, 1], "f16", rank, scales, q0, err0)
+    base = [wl.to_fp16(rng.standard_normal((m, n))) for m, n in shapes]
+
+    # clean step first
+    case.set_grads(base)
+    assert case.gpu_step(passthrough=[np.ones(10)]) == 0
+    compare_step(case.fetch(), case.oracle_step([np.ones(10)]), "clean")
+
+    events = [
+        ("grad +inf", dict(grad=(1, 5, 7, np.inf))),
+        ("grad nan", dict(grad=(2, 199, 103, np.nan))),
+        ("grad -inf", dict(grad=(0, 0, 0, -np.inf))),
+        ("err nan", dict(err=(1, 63, 511, np.nan))),
+        ("pass nan", dict(passthrough=np.array([0.0, np.nan, 1.0]))),
+        ("scale inf", dict(scale=(1, np.inf))),
+    ]
+    for name, ev in events:
+        log(f"  inject {name}")
+        gs = [g.copy() for g in base]
+        if "grad" in ev:
+            i, r, c, v = ev["grad"]
+            gs[i][r, c] = v
+        case.set_grads(gs)
+        if "err" in ev:
+            i, r, c, v = ev["err"]
+            case.group.err[i][r, c] = float(v)
+        if "scale" in ev:
+            b, v = ev["scale"]
+            case.group.scale[b] = float(v)
+        q_before = [q.clone() for q in case.group.q]
+        out_before = [o.clone() for o in case.group.out]
+        pt = [ev["passthrough"]] if "passthrough" in ev else [np.ones(10)]
+        skip = case.gpu_step(passthrough=pt)
+        res = case.fetch()
+        expect_flags = np.zeros(len(shapes), np.uint8)
+        if "grad" in ev:
+            expect_flags[ev["grad"][0]] = 1
+        if "err" in ev:
+            expect_flags[ev["err"][0]] = 1
+        assert np.array_equal(res["flags"], expect_flags), (name, res["flags"])
+        assert skip == 1, name
+        assert int(case.group.skip.item()) == 1
+        for e in res["E"]:
+            assert np.all(e == 0.0), name
+        for qb, qa in zip(q_before, case.group.q):
+            assert torch.equal(qb, qa), name
+        for ob, oa in zip(out_before, case.group.out):
+            assert torch.equal(ob, oa), name
+        if "scale" in ev:
+            case.group.scale[ev["scale"][0]] = float(scales[ev["scale"][0]])
+        # oracle agrees on the decision and zeroing
+        Es = [np.asarray(e, np.float64) for e in case.E_or]
+        if "err" in ev:
+            i, r, c, v = ev["err"]
+            Es[i] = Es[i].copy()
+            Es[i][r, c] = v
+        sc = scales.copy()
+        if "scale" in ev:
+            sc[ev["scale"][0]] = ev["scale"][1]
+        st = oracle.step_group(case.cur_grads, Es, case.Q_or, case.blocks, sc, pt)
+        assert st.skip and [bool(f) for f in res["flags"]] == st.flags
+        case.E_or = st.E_next
+        case.Q_or = st.Q_next
+
+    # recovery: a clean step after the skips, from zeroed error buffers and the kept q
+    case.set_grads(base)
+    assert case.gpu_step(passthrough=[np.ones(10)]) == 0
+    compare_step(case.fetch(), case.oracle_step([np.ones(10)]), "after skips")
+    case.close()
+
+
+# ------------------------------------------------------------------------------------------
+# near-underflow heavy-tailed workload at rank 80 (2 resblocks)
+# ------------------------------------------------------------------------------------------
+def test_underflow_workload_two_resblocks():
+    w, specs, case = _shard_case(4, 2)
+    log("Student-t(3) near fp16 underflow, r=80, 2 resblocks, 3 steps")
+    for t in range(3):
+        case.set_grads([wl.gradient_np(w, s, t) for s in specs])
+        assert case.gpu_step() == 0
+        compare_step(case.fetch(), case.oracle_step(), f"underflow step {t}")
+    case.close()
+
+
+# ------------------------------------------------------------------------------------------
+# determinism: the same inputs give bitwise identical outputs
+# ------------------------------------------------------------------------------------------
+def test_bitwise_deterministic():
+    import torch
+    w, specs, _ = _shard_case(2, None)
+    outs = []
+    for rep in range(2):
+        w, specs, case = _shard_case(2, None, err_warm=True)
+        case.set_grads([wl.gradient_np(w, s, 1) for s in specs])
+        case.gpu_step()
+        outs.append(case.fetch())
+        case.close()
+    for k in ("E", "Q", "P", "D"):
+        for a, b in zip(outs[0][k], outs[1][k]):
+            assert np.array_equal(a, b), k
+
+
+# ------------------------------------------------------------------------------------------
+# argument validation
+# ------------------------------------------------------------------------------------------
+def test_invalid_arguments_rejected():
+    import torch
+    from rank_gradient_compression_powersgd_amd import binding as B
+    ctx = B.psgd_create(0, 8)
+    try:
+        g = torch.zeros((64, 60), dtype=torch.float16, device="cuda")   # n not a multiple of 8
+        e = torch.zeros((64, 60), dtype=torch.float32, device="cuda")
+        q = torch.zeros((60, 8), device="cuda")
+        p = torch.zeros((64, 8), device="cuda")
+        with pytest.raises(B.PsgdError) as ei:
+            B.psgd_plan_create(ctx, [B.make_matrix(g, e, q, q.clone(), p, 0)], B.PSGD_F16, 1)
+        assert ei.value.status == B.PSGD_EINVAL and "multiple of 8" in str(ei.value)
+        g = torch.zeros((64, 64), dtype=torch.float16, device="cuda")
+        e = torch.zeros((64, 64), dtype=torch.float32, device="cuda")
+        q = torch.zeros((64, 8), device="cuda")
+        with pytest.raises(B.PsgdError):   # block outside the scale array
+            B.psgd_plan_create(ctx, [B.make_matrix(g, e, q, q.clone(), p, 3)], B.PSGD_F16, 2)
+        with pytest.raises(B.PsgdError):   # unknown dtype
+            B.psgd_plan_create(ctx, [B.make_matrix(g, e, q, q.clone(), p, 0)], 9, 1)
+    finally:
+        B.psgd_destroy(ctx)
+    with pytest.raises(B.PsgdError):
+        B.psgd_create(0, 0)
+    with pytest.raises(B.PsgdError):
+        B.psgd_create(0, 129)
