@@ -65,6 +65,7 @@ void k_gs_gram(const DevMat* __restrict__ mats, const Work* __restrict__ work)
         if (p % NW == wv) acc[p / NW] = mfma_f64(v[ti], v[tj], acc[p / NW]);
   }
 
+  // C layout of v_mfma_f64_16x16x4f64: lane 16g + c, register i holds C[g + 4i][c].
   double* __restrict__ out = d.gram + (int64_t)wi.b * rpad * rpad;
   int p = 0;
 #pragma unroll
@@ -74,7 +75,7 @@ void k_gs_gram(const DevMat* __restrict__ mats, const Work* __restrict__ work)
       if (p % NW == wv) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          out[(int64_t)(ti * 16 + 4 * g + i) * rpad + tj * 16 + c] = acc[p / NW][i];
+          out[(int64_t)(ti * 16 + g + 4 * i) * rpad + tj * 16 + c] = acc[p / NW][i];
       }
 }
 
@@ -183,42 +184,27 @@ void k_gs_apply(const DevMat* __restrict__ mats, const Work* __restrict__ work)
     }
   }
 
-  // lane holds P_hat[rbase + 4g + i][tj*16 + c]
+  // C layout of v_mfma_f64_16x16x4f64: lane 16g + c, register i holds P_hat[rbase + g + 4i][tj*16 + c]
   float x32[RT][4];
 #pragma unroll
   for (int t = 0; t < RT; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) x32[t][i] = (float)acc[t][i];
 
-  // (a) fp32 P_hat, m x r row-major
 #pragma unroll
-  for (int t = 0; t < RT; ++t) {
-    const int col = t * 16 + c;
-    if (col < r) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = rbase + 4 * g + i;
-        if (row < m) d.p[(int64_t)row * r + col] = x32[t][i];
-      }
-    }
-  }
-  // (b) P_hat^T split bf16 hi/lo, rpad x mpad: 4 consecutive rows per lane
-  const int row4 = rbase + 4 * g;
-  if (row4 < mpad) {
+  for (int i = 0; i < 4; ++i) {
+    const int row = rbase + g + 4 * i;
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const int col = t * 16 + c;
-      uint16_t h[4], l[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      // (a) fp32 P_hat, m x r row-major
+      if (row < m && col < r) d.p[(int64_t)row * r + col] = x32[t][i];
+      // (b) P_hat^T split bf16 hi/lo, rpad x mpad (rows m..mpad hold zeros)
+      if (row < mpad) {
         const __bf16 hb = (__bf16)x32[t][i];
-        h[i] = bf16_bits(hb);
-        l[i] = bf16_bits((__bf16)(x32[t][i] - (float)hb));
+        d.pt_hi[(int64_t)col * mpad + row] = bf16_bits(hb);
+        d.pt_lo[(int64_t)col * mpad + row] = bf16_bits((__bf16)(x32[t][i] - (float)hb));
       }
-      *reinterpret_cast<u32x2*>(d.pt_hi + (int64_t)col * mpad + row4) =
-          u32x2{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16)};
-      *reinterpret_cast<u32x2*>(d.pt_lo + (int64_t)col * mpad + row4) =
-          u32x2{l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16)};
     }
   }
   // (c) rows scaled by 2^e (largest entry in [2^13, 2^14)) and split fp16 hi/lo, m x kpad3
@@ -232,7 +218,7 @@ void k_gs_apply(const DevMat* __restrict__ mats, const Work* __restrict__ work)
     amax = fmaxf(amax, __shfl_xor(amax, 4));
     amax = fmaxf(amax, __shfl_xor(amax, 8));
     const int ex = fp16_row_exponent(amax);
-    const int row = rbase + 4 * g + i;
+    const int row = rbase + g + 4 * i;
     if (row < m) {
 #pragma unroll
       for (int t = 0; t < RT; ++t) {

@@ -147,9 +147,11 @@ def compare_step(res, st, what="", exact_rank: bool = False, check_p: bool = Tru
     worst = {}
     for i in range(len(res["E"])):
         rD = rel(res["D"][i], st.D[i]) if res["D"][i] is not None else 0.0
-        if exact_rank:
-            nm = np.linalg.norm(st.D[i] + st.E_next[i])
-            rE = float(np.linalg.norm(res["E"][i]) / nm)
+        nm = float(np.linalg.norm(st.D[i] + st.E_next[i]))       # ||M||
+        if exact_rank or np.linalg.norm(st.E_next[i]) <= 1e-8 * nm:
+            # M lies in span(P) (rank(M) <= r): the oracle's E is round-off, so E is measured
+            # against ||M|| instead of against itself
+            rE = float(np.linalg.norm(res["E"][i] - st.E_next[i]) / nm)
         else:
             rE = rel(res["E"][i], st.E_next[i])
         rQ = rel(res["Q"][i], st.Q_next[i])

@@ -1,0 +1,114 @@
+"""Full-size parity: the 64-resblock d_model=3968 per-GPU shard (256 matrices, 1.51e9
+gradient elements) in the launch configuration bench.py times.
+
+The oracle cannot afford every matrix, so sampled matrices (one of each shape, spread over the
+depth) are compared one by one; the non-finite flags are checked for all 256 matrices.
+Inputs are generated on the device from seeds (workloads.gradient_torch) and copied to the host
+for the oracle before the step runs.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from tests.gpu_helpers import REL_TOL, ORTH_TOL, log, orth_err, rel
+
+pytestmark = pytest.mark.gpu
+
+SAMPLES = (0, 4 * 17 + 1, 4 * 40 + 2, 4 * 63 + 3)   # rb0.qkv, rb17.attn_out, rb40.mlp_in, rb63.mlp_out
+
+
+def _build(config, write_out=True):
+    import torch
+    from rank_gradient_compression_powersgd_amd import PowerSGDGroup
+    w = wl.workload(config)
+    dev = torch.device("cuda", 0)
+    grads = [wl.gradient_torch(w, s, 0, dev) for s in w.matrices]
+    q0 = [wl.initial_q_torch(w, s, dev) for s in w.matrices]
+    scale = torch.tensor(wl.scales_np(w), device=dev)
+    group = PowerSGDGroup(grads, [s.block for s in w.matrices], scale, w.rank, q0, None, write_out)
+    torch.cuda.synchronize()
+    return w, grads, group
+
+
+def _host_flags(grads):
+    return np.array([0 if bool(np.isfinite(g.cpu().numpy()).all()) else 1 for g in grads], np.uint8)
+
+
+def test_full_shard_sampled_against_oracle():
+    import torch
+    w, grads, group = _build(3)
+    scales = wl.scales_np(w)
+    pt = [torch.from_numpy(wl.passthrough_np(3, w.n_blocks)).cuda().reshape(-1)]
+    E_or = {i: np.zeros((w.matrices[i].m, w.matrices[i].n)) for i in SAMPLES}
+    Q_or = {i: group.q[i].cpu().numpy().astype(np.float64) for i in SAMPLES}
+    for step in range(3):
+        if step:
+            for s, g in zip(w.matrices, grads):
+                wl.gradient_torch(w, s, step, g.device, out=g)
+        G = {i: grads[i].float().cpu().numpy() for i in SAMPLES}
+        expect_flags = _host_flags(grads)
+        log(f"full shard step {step}: 256 matrices, r=112")
+        skip = group.step(pt, host=True)
+        torch.cuda.synchronize()
+        assert skip == 0
+        assert np.array_equal(group.flags.cpu().numpy(), expect_flags)
+        for i in SAMPLES:
+            s = w.matrices[i]
+            st = oracle.step_matrix(G[i], float(scales[s.block]), E_or[i], Q_or[i])
+            D = group.out[i].cpu().numpy()
+            E = group.err[i].cpu().numpy()
+            P = group.p[i].cpu().numpy()
+            Q = group.q[i].cpu().numpy()
+            r = dict(D=rel(D, st.D), E=rel(E, st.E_next), Q=rel(Q, st.Q_next), P=rel(P, st.P),
+                     orth=orth_err(P))
+            log(f"  {s.name}: " + " ".join(f"{k}={v:.2e}" for k, v in r.items()))
+            for k in ("D", "E", "Q", "P"):
+                assert r[k] <= REL_TOL, (step, s.name, k, r[k])
+            assert r["orth"] <= ORTH_TOL
+            E_or[i], Q_or[i] = st.E_next, st.Q_next
+    group.close()
+
+
+def test_full_underflow_shard_injections():
+    """Rank 80, Student-t(3) gradients near fp16 underflow over all 64 resblocks, with non-finite
+    values injected into gradients, a pass-through tensor and a scale: flags (all 256 matrices)
+    and skip bit-exact, error buffers zeroed on skipped steps, q kept."""
+    import torch
+    w, grads, group = _build(4, write_out=False)
+    scales = wl.scales_np(w)
+    pt = torch.from_numpy(wl.passthrough_np(4, w.n_blocks)).cuda().reshape(-1)
+    sched = {1: ("grad", 7, 100, 200, np.inf), 3: ("grad", 201, 5, 9, np.nan),
+             4: ("pass", 0, 1234, 0, np.nan), 5: ("scale", 13, 0, 0, np.inf),
+             6: ("grad", 255, 1983, 3967, -np.inf)}
+    for step in range(8):
+        for s, g in zip(w.matrices, grads):
+            wl.gradient_torch(w, s, step, g.device, out=g)
+        ev = sched.get(step)
+        ptx = pt.clone()
+        if ev and ev[0] == "grad":
+            grads[ev[1]][ev[2], ev[3]] = float(ev[4])
+        if ev and ev[0] == "pass":
+            ptx[ev[2]] = float(ev[4])
+        if ev and ev[0] == "scale":
+            group.scale[ev[1]] = float(ev[4])
+        expect_flags = _host_flags(grads)
+        expect_skip = int(expect_flags.any() or not bool(np.isfinite(ptx.cpu().numpy()).all())
+                          or not bool(np.isfinite(group.scale.cpu().numpy()).all()))
+        q_before = [q.clone() for q in group.q[:8]] + [group.q[255].clone()]
+        log(f"underflow shard step {step}: event {ev}")
+        skip = group.step([ptx], host=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(group.flags.cpu().numpy(), expect_flags), step
+        assert skip == expect_skip, step
+        if skip:
+            for e in group.err:
+                assert float(e.abs().max()) == 0.0
+            for qb, qa in zip(q_before, group.q[:8] + [group.q[255]]):
+                assert torch.equal(qb, qa)
+        else:
+            for e in group.err[::37]:
+                assert bool(torch.isfinite(e).all())
+        if ev and ev[0] == "scale":
+            group.scale[ev[1]] = float(scales[ev[1]])
+    group.close()

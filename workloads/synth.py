@@ -329,6 +329,8 @@ def gradient_torch(wl: WorkloadSpec, spec: MatrixSpec, step: int, device, out=No
         dt = torch.float16
     elif wl.config == 5:
         x = torch.randn(spec.m, spec.n, generator=g, device=device, dtype=torch.float32)
+        A, B = planted_torch(spec, device)
+        x.add_(A @ B)
         dt = torch.bfloat16
     else:
         x = torch.randn(spec.m, spec.n, generator=g, device=device, dtype=torch.float32)
