@@ -77,7 +77,8 @@ typedef enum psgd_dtype {
  *          ld_out % 4 == 0.
  *  m, n    shape; n % 8 == 0; 1 <= r <= min(m, n).
  *  block   index into the per-resblock scale array (0 <= block < n_blocks).
- * Every pointer must be 16-byte aligned. Buffers of different matrices must not overlap.
+ * Every pointer must be 16-byte aligned. Buffers of different matrices must not overlap. The
+ * byte span of each of G, E and out ((m - 1) * ld + n elements) must be below 2 GiB.
  */
 typedef struct psgd_matrix {
   const void* grad;   int64_t ld_grad;

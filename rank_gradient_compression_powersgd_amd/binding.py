@@ -55,7 +55,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    p = path or os.environ.get("PSGD_LIBRARY") or LIB_PATH
     # torch first: its HIP runtime is then the one libpsgd.so binds to (same soname), so the
     # streams and events torch hands out are valid inside the library.
     import torch  # noqa: F401

@@ -9,7 +9,9 @@
 //
 // The tile is computed transposed, D^T = Q' P^T. In that form the MFMA C layout gives every
 // lane 4 consecutive columns of one row of D, so the G/E/out traffic is 8- and 16-byte vector
-// accesses along rows.
+// accesses along rows. G, E and out go through buffer descriptors: ragged edges read zeros
+// and drop their stores in hardware, so the epilogue issues the loads of all its tiles at
+// once and has no branches.
 //
 // Skip: the device-side skip word is read first. A skipped step zeroes the error buffer over
 // the tile and writes nothing else (the error buffer is zeroed on non-finite values: Korean
@@ -19,10 +21,32 @@
 namespace psgd {
 namespace {
 
-constexpr int K3_WM = 2, K3_WN = 2;      // waves along m and n; wave tile 64 x 64
+#ifndef K3_WM
+#define K3_WM 2      // waves along m
+#endif
+#ifndef K3_WN
+#define K3_WN 2      // waves along n; each wave computes a 64 x 64 tile
+#endif
 constexpr int K3_TM = K3_WM * 64, K3_TN = K3_WN * 64;
 constexpr int K3_THREADS = K3_WM * K3_WN * kWave;
 constexpr int LDS_K = 40;                // fp16 elements per LDS row (32 + 8 padding)
+
+template <int GT> struct Raw4;
+template <> struct Raw4<G_F16> {
+  u32x2 v;
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { v = bload8(r, off); }
+  __device__ __forceinline__ f32x4 f32() const { return __builtin_convertvector(__builtin_bit_cast(f16x4, v), f32x4); }
+};
+template <> struct Raw4<G_BF16> {
+  u32x2 v;
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { v = bload8(r, off); }
+  __device__ __forceinline__ f32x4 f32() const { return __builtin_convertvector(__builtin_bit_cast(bf16x4, v), f32x4); }
+};
+template <> struct Raw4<G_F32> {
+  u32x4 v;
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { v = bload16(r, off); }
+  __device__ __forceinline__ f32x4 f32() const { return __builtin_bit_cast(f32x4, v); }
+};
 
 template <int GT>
 __global__ __launch_bounds__(K3_THREADS)
@@ -34,19 +58,16 @@ void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   const DevMat& d = mats[wi.mat];
   const int m = d.m, n = d.n, kpad3 = d.kpad3;
   const int m0 = wi.a, n0 = wi.b;
-  float* __restrict__ E = d.err;
-  const int64_t lde = d.ld_err;
+  const int lde = (int)d.ld_err;
+  const rsrc_t re = make_rsrc(d.err, d.e_bytes);
 
   if (*skip != 0) {
-    // zero E over the tile: 2 threads per row, 64 columns each
-    const int row = m0 + threadIdx.x / 2;
-    if (row < m) {
-      const int cb = n0 + (threadIdx.x & 1) * 64;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int col = cb + 4 * j;
-        if (col < n) *reinterpret_cast<f32x4*>(E + (int64_t)row * lde + col) = f32x4{0, 0, 0, 0};
-      }
+    // zero E over the tile, 4 columns per store
+    constexpr int C4 = K3_TN / 4;
+    for (int idx = threadIdx.x; idx < K3_TM * C4; idx += K3_THREADS) {
+      const int row = m0 + idx / C4, col = n0 + 4 * (idx % C4);
+      const bool ok = row < m && col < n;
+      bstore16(u32x4{0, 0, 0, 0}, re, ok ? (uint32_t)(row * lde + col) * 4u : kOOB);
     }
     return;
   }
@@ -59,34 +80,41 @@ void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   __shared__ __attribute__((aligned(16))) uint16_t ldq[2][2][K3_TN][LDS_K];
   __shared__ __attribute__((aligned(16))) uint16_t ldp[2][2][K3_TM][LDS_K];
 
-  // staging: (K3_TN + K3_TM) rows x 32 k x {hi, lo} in 16-byte units
-  constexpr int UNITS = (K3_TN + K3_TM) * 4 * 2;
-  constexpr int UPT = UNITS / K3_THREADS;
-  static_assert(UNITS % K3_THREADS == 0, "staging units");
-  u32x4 stage[UPT];
+  // staging: K3_TN rows of Q' and K3_TM rows of P x 32 k x {hi, lo}, in 16-byte units. The
+  // operand arrays are padded with zero rows to whole tiles, so no staging load is masked.
+  constexpr int QU = K3_TN * 8 / K3_THREADS, PU = K3_TM * 8 / K3_THREADS;
+  static_assert(QU * K3_THREADS == K3_TN * 8 && PU * K3_THREADS == K3_TM * 8, "staging units");
+  const GLOBAL uint16_t* __restrict__ q3h = gbl(d.q3_hi) + (int64_t)n0 * kpad3;
+  const GLOBAL uint16_t* __restrict__ q3l = gbl(d.q3_lo) + (int64_t)n0 * kpad3;
+  const GLOBAL uint16_t* __restrict__ p3h = gbl(d.p3_hi) + (int64_t)m0 * kpad3;
+  const GLOBAL uint16_t* __restrict__ p3l = gbl(d.p3_lo) + (int64_t)m0 * kpad3;
+  u32x4 sq[QU], sp[PU];
   auto load_stage = [&](int k0) {
 #pragma unroll
-    for (int j = 0; j < UPT; ++j) {
+    for (int j = 0; j < QU; ++j) {
+      const int u = threadIdx.x + j * K3_THREADS;          // u = (arr * K3_TN + row) * 4 + q4
+      const int q4 = u & 3, rr = (u >> 2) % K3_TN, arr = (u >> 2) / K3_TN;
+      sq[j] = *gcast<u32x4>((arr ? q3l : q3h) + (int64_t)rr * kpad3 + k0 + 8 * q4);
+    }
+#pragma unroll
+    for (int j = 0; j < PU; ++j) {
       const int u = threadIdx.x + j * K3_THREADS;
-      const bool isq = u < K3_TN * 8;
-      const int v = isq ? u : u - K3_TN * 8;
-      const int arr = v & 1, q4 = (v >> 1) & 3, rr = v >> 3;
-      const int row = (isq ? n0 : m0) + rr;
-      const int lim = isq ? n : m;
-      const uint16_t* base = isq ? (arr ? d.q3_lo : d.q3_hi) : (arr ? d.p3_lo : d.p3_hi);
-      stage[j] = row < lim ? *reinterpret_cast<const u32x4*>(base + (int64_t)row * kpad3 + k0 + 8 * q4)
-                           : u32x4{0, 0, 0, 0};
+      const int q4 = u & 3, rr = (u >> 2) % K3_TM, arr = (u >> 2) / K3_TM;
+      sp[j] = *gcast<u32x4>((arr ? p3l : p3h) + (int64_t)rr * kpad3 + k0 + 8 * q4);
     }
   };
   auto store_stage = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < UPT; ++j) {
+    for (int j = 0; j < QU; ++j) {
       const int u = threadIdx.x + j * K3_THREADS;
-      const bool isq = u < K3_TN * 8;
-      const int v = isq ? u : u - K3_TN * 8;
-      const int arr = v & 1, q4 = (v >> 1) & 3, rr = v >> 3;
-      uint16_t* dst = isq ? &ldq[buf][arr][rr][8 * q4] : &ldp[buf][arr][rr][8 * q4];
-      *reinterpret_cast<u32x4*>(dst) = stage[j];
+      const int q4 = u & 3, rr = (u >> 2) % K3_TN, arr = (u >> 2) / K3_TN;
+      *reinterpret_cast<u32x4*>(&ldq[buf][arr][rr][8 * q4]) = sq[j];
+    }
+#pragma unroll
+    for (int j = 0; j < PU; ++j) {
+      const int u = threadIdx.x + j * K3_THREADS;
+      const int q4 = u & 3, rr = (u >> 2) % K3_TM, arr = (u >> 2) / K3_TM;
+      *reinterpret_cast<u32x4*>(&ldp[buf][arr][rr][8 * q4]) = sp[j];
     }
   };
 
@@ -96,14 +124,7 @@ void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0, 0, 0, 0};
 
-  const int nsteps = kpad3 / 32;
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-  for (int ks = 0; ks < nsteps; ++ks) {
-    const int buf = ks & 1;
-    const bool more = ks + 1 < nsteps;
-    if (more) load_stage((ks + 1) * 32);
+  auto compute = [&](int buf) {
     f16x8 bh[4], bl[4];
 #pragma unroll
     for (int im = 0; im < 4; ++im) {
@@ -121,35 +142,64 @@ void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
         acc[jn][im] = mfma_f16(al, bh[im], acc[jn][im]);
       }
     }
-    if (more) store_stage(buf ^ 1);
+  };
+
+  const int nsteps = kpad3 / 32;
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+  int ks = 0;
+  for (; ks + 1 < nsteps; ++ks) {
+    load_stage((ks + 1) * 32);
+    compute(ks & 1);
+    store_stage((ks & 1) ^ 1);
     __syncthreads();
   }
+  compute(ks & 1);
 
-  // acc[jn][im]: lane holds D[m = m0 + wm*64 + im*16 + c][n = n0 + wn*64 + jn*16 + 4g + {0..3}]
-  const char* __restrict__ G = reinterpret_cast<const char*>(d.grad);
-  const int64_t ldg = d.ld_grad, ldo = d.ld_out;
-  float* __restrict__ out = d.out;
+  // Epilogue. acc[jn][im]: lane holds D[row = m0 + wm*64 + im*16 + c][n0 + wn*64 + jn*16 + 4g
+  // + {0..3}]. All G/E loads of the wave's 16 tiles are issued before any is used.
+  const rsrc_t rg = make_rsrc(d.grad, d.g_bytes);
+  const rsrc_t ro = make_rsrc(d.out, d.out ? d.o_bytes : 0u);   // no out buffer: stores dropped
+  const int ldg = (int)d.ld_grad, ldo = (int)d.ld_out;
+  const GLOBAL int32_t* __restrict__ pexp = gbl(d.p3_exp);     // padded to whole tiles
+  const GLOBAL int32_t* __restrict__ qexp = gbl(d.q3_exp);
   const float s = scale[d.block];
-#pragma unroll
-  for (int im = 0; im < 4; ++im) {
+  constexpr int GB = GradIO<GT>::kBytes;
+  Raw4<GT> gv[4][4];
+  u32x4 ev[4][4];
+  auto offset = [&](int im, int jn, int ld, uint32_t bytes) -> uint32_t {
     const int row = m0 + wm * 64 + im * 16 + c;
-    if (row >= m) continue;
-    const int ep = d.p3_exp[row];
+    const int col = n0 + wn * 64 + jn * 16 + 4 * g;
+    return (row < m && col < n) ? (uint32_t)(row * ld + col) * bytes : kOOB;
+  };
+#pragma unroll
+  for (int im = 0; im < 4; ++im)
 #pragma unroll
     for (int jn = 0; jn < 4; ++jn) {
-      const int col = n0 + wn * 64 + jn * 16 + 4 * g;
-      if (col >= n) continue;
-      const f32x4 gf = GradIO<GT>::load4(G + ((int64_t)row * ldg + col) * GradIO<GT>::kBytes);
-      float* ep4 = E + (int64_t)row * lde + col;
-      const f32x4 ev = *reinterpret_cast<const f32x4*>(ep4);
+      gv[im][jn].load(rg, offset(im, jn, ldg, GB));
+      ev[im][jn] = bload16(re, offset(im, jn, lde, 4u));
+    }
+  int ep[4];
+  u32x4 eqv[4];
+#pragma unroll
+  for (int im = 0; im < 4; ++im) ep[im] = pexp[m0 + wm * 64 + im * 16 + c];
+#pragma unroll
+  for (int jn = 0; jn < 4; ++jn) eqv[jn] = *gcast<u32x4>(qexp + n0 + wn * 64 + jn * 16 + 4 * g);
+#pragma unroll
+  for (int im = 0; im < 4; ++im) {
+#pragma unroll
+    for (int jn = 0; jn < 4; ++jn) {
+      const f32x4 gf = gv[im][jn].f32();
+      const f32x4 ef = __builtin_bit_cast(f32x4, ev[im][jn]);
       f32x4 dv, en;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        dv[i] = ldexpf(acc[jn][im][i], -(ep + d.q3_exp[col + i]));
-        en[i] = __builtin_fmaf(s, gf[i], ev[i]) - dv[i];
+        dv[i] = ldexpf(acc[jn][im][i], -(ep[im] + (int)eqv[jn][i]));
+        en[i] = __builtin_fmaf(s, gf[i], ef[i]) - dv[i];
       }
-      *reinterpret_cast<f32x4*>(ep4) = en;
-      if (out) *reinterpret_cast<f32x4*>(out + (int64_t)row * ldo + col) = dv;
+      bstore16(__builtin_bit_cast(u32x4, en), re, offset(im, jn, lde, 4u));
+      bstore16(__builtin_bit_cast(u32x4, dv), ro, offset(im, jn, ldo, 4u));
     }
   }
 }
@@ -165,7 +215,9 @@ void k_commit_q(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   const int64_t total = (int64_t)d.n * d.r;
   const int64_t beg = (int64_t)wi.a * 4096;
   const int64_t end = beg + 4096 < total ? beg + 4096 : total;
-  for (int64_t i = beg + threadIdx.x; i < end; i += 256) d.q[i] = d.q_next[i];
+  GLOBAL float* __restrict__ q = gbl(d.q);
+  const GLOBAL float* __restrict__ qn = gbl(d.q_next);
+  for (int64_t i = beg + threadIdx.x; i < end; i += 256) q[i] = qn[i];
 }
 
 template <int GT>

@@ -10,39 +10,61 @@
 //
 // Data flow per workgroup (a block of rows of one matrix, one rank chunk):
 //   * every lane streams its own MFMA A-fragments straight from HBM: 8 consecutive columns of
-//     one row of G (16 B of fp16) and of E (32 B), so no LDS round trip is needed for M;
+//     one row of G (16 B of fp16) and of E (32 B), so M needs no LDS round trip. The loads go
+//     through buffer descriptors: out-of-range lanes use an offset past the range and read
+//     zeros, so the loop body has no branches and the next stage's loads stay in flight while
+//     the current stage computes;
 //   * the shared operand, Q^T split into bf16 hi/lo (prepared once per step), is staged in LDS
-//     32 columns of k at a time and double-buffered;
-//   * the flag test runs on M (one class test per element); only when M is non-finite are the
-//     inputs G and E themselves examined, so the flag is exactly "G or E holds inf/NaN".
+//     one pipeline stage (K1_KSUB x 32 columns of k) at a time, double-buffered;
+//   * the flag test runs on M (one class test per element); only when a wave met a non-finite
+//     M are the inputs G and E of its rows examined, after the main loop, so the flag is
+//     exactly "G or E holds inf/NaN".
 #include "psgd_internal.h"
+
+#ifndef K1_RA
+#define K1_RA 2      // 16-row tiles per wave
+#endif
+#ifndef K1_W
+#define K1_W 4       // waves per workgroup
+#endif
+#ifndef K1_KSUB
+#define K1_KSUB 2    // 32-column MFMA k groups per pipeline stage
+#endif
 
 namespace psgd {
 namespace {
 
-constexpr int K1_RA = 2;     // 16-row tiles per wave
-constexpr int K1_W = 4;      // waves per workgroup
 constexpr int K1_ROWS = K1_RA * 16 * K1_W;
-constexpr int LDS_K = 40;    // 32 k values + 8 padding (bf16 elements per LDS row)
+constexpr int KS = 32 * K1_KSUB;       // k columns per stage
+constexpr int LDS_K = KS + 8;          // + 8 bf16 padding per LDS row
 
 template <int GT> struct Raw8;
 template <> struct Raw8<G_F16> {
   u32x4 v;
-  __device__ __forceinline__ void load(const void* p) { v = *reinterpret_cast<const u32x4*>(p); }
-  __device__ __forceinline__ void zero() { v = u32x4{0, 0, 0, 0}; }
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { v = bload16(r, off); }
   __device__ __forceinline__ f32x8 f32() const { return __builtin_convertvector(__builtin_bit_cast(f16x8, v), f32x8); }
 };
 template <> struct Raw8<G_BF16> {
   u32x4 v;
-  __device__ __forceinline__ void load(const void* p) { v = *reinterpret_cast<const u32x4*>(p); }
-  __device__ __forceinline__ void zero() { v = u32x4{0, 0, 0, 0}; }
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { v = bload16(r, off); }
   __device__ __forceinline__ f32x8 f32() const { return __builtin_convertvector(__builtin_bit_cast(bf16x8, v), f32x8); }
 };
 template <> struct Raw8<G_F32> {
-  f32x8 v;
-  __device__ __forceinline__ void load(const void* p) { v = load_f32x8(reinterpret_cast<const float*>(p)); }
-  __device__ __forceinline__ void zero() { v = f32x8{0, 0, 0, 0, 0, 0, 0, 0}; }
-  __device__ __forceinline__ f32x8 f32() const { return v; }
+  u32x4 a, b;
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { a = bload16(r, off); b = bload16(r, off + 16); }
+  __device__ __forceinline__ f32x8 f32() const {
+    const f32x4 x = __builtin_bit_cast(f32x4, a), y = __builtin_bit_cast(f32x4, b);
+    return f32x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  }
+};
+
+struct Raw8E {
+  u32x4 a, b;
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { a = bload16(r, off); b = bload16(r, off + 16); }
+  __device__ __forceinline__ f32x8 f32() const {
+    const f32x4 x = __builtin_bit_cast(f32x4, a), y = __builtin_bit_cast(f32x4, b);
+    return f32x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  }
 };
 
 template <int GT, int RTC>
@@ -54,12 +76,13 @@ void k_ef_mq(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   if (wi.mat < 0) return;
   const DevMat& d = mats[wi.mat];
   const int m = d.m, n = d.n, npad = d.npad, rpad = d.rpad;
-  const char* __restrict__ G = reinterpret_cast<const char*>(d.grad);
-  const float* __restrict__ E = d.err;
-  const int64_t ldg = d.ld_grad, lde = d.ld_err;
-  const uint16_t* __restrict__ qth = d.qt_hi;
-  const uint16_t* __restrict__ qtl = d.qt_lo;
+  const int ldg = (int)d.ld_grad, lde = (int)d.ld_err;
+  const rsrc_t rg = make_rsrc(d.grad, d.g_bytes);
+  const rsrc_t re = make_rsrc(d.err, d.e_bytes);
+  const GLOBAL uint16_t* __restrict__ qth = gbl(d.qt_hi);
+  const GLOBAL uint16_t* __restrict__ qtl = gbl(d.qt_lo);
   const float s = scale[d.block];
+  constexpr int GB = GradIO<GT>::kBytes;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
@@ -69,50 +92,51 @@ void k_ef_mq(const DevMat* __restrict__ mats, const Work* __restrict__ work,
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][RTC * 16][LDS_K];
 
-  // Q^T chunk staging: RTC*16 rank rows x 32 k x {hi, lo}, in 16-byte units.
-  constexpr int UNITS = RTC * 16 * 4 * 2;
+  // Q^T staging: RTC*16 rank rows x KS k x {hi, lo} in 16-byte units. Threads past the last
+  // unit repeat it (same value to the same LDS address), so the code has no branch.
+  constexpr int QPR = KS / 8;                   // 16-byte units per rank row
+  constexpr int UNITS = RTC * 16 * QPR * 2;
   constexpr int THREADS = K1_W * kWave;
   constexpr int UPT = (UNITS + THREADS - 1) / THREADS;
   u32x4 stage[UPT];
+  auto unit = [&](int j, int& arr, int& rr, int& q) {
+    int u = threadIdx.x + j * THREADS;
+    u = u < UNITS ? u : UNITS - 1;
+    arr = u / (RTC * 16 * QPR);
+    const int rem = u - arr * (RTC * 16 * QPR);
+    rr = rem / QPR;
+    q = rem % QPR;
+  };
   auto load_stage = [&](int k0) {
 #pragma unroll
     for (int j = 0; j < UPT; ++j) {
-      const int u = threadIdx.x + j * THREADS;
-      if (UNITS % THREADS == 0 || u < UNITS) {
-        const int arr = u / (RTC * 64);
-        const int rem = u - arr * (RTC * 64);
-        const int rr = rem >> 2, q4 = rem & 3;
-        const uint16_t* src = (arr ? qtl : qth) + (int64_t)(rc0 + rr) * npad + k0 + 8 * q4;
-        stage[j] = *reinterpret_cast<const u32x4*>(src);
-      }
+      int arr, rr, q;
+      unit(j, arr, rr, q);
+      stage[j] = *gcast<u32x4>((arr ? qtl : qth) + (int64_t)(rc0 + rr) * npad + k0 + 8 * q);
     }
   };
   auto store_stage = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < UPT; ++j) {
-      const int u = threadIdx.x + j * THREADS;
-      if (UNITS % THREADS == 0 || u < UNITS) {
-        const int arr = u / (RTC * 64);
-        const int rem = u - arr * (RTC * 64);
-        const int rr = rem >> 2, q4 = rem & 3;
-        *reinterpret_cast<u32x4*>(&lds[buf][arr][rr][8 * q4]) = stage[j];
-      }
+      int arr, rr, q;
+      unit(j, arr, rr, q);
+      *reinterpret_cast<u32x4*>(&lds[buf][arr][rr][8 * q]) = stage[j];
     }
   };
 
-  Raw8<GT> gcur[K1_RA];
-  f32x8 ecur[K1_RA];
-  auto load_m = [&](int k0, Raw8<GT>* gq, f32x8* eq) {
-    const int col = k0 + 8 * g;
+  // A-fragments of one stage: row tile a, k group j -> 8 columns k0 + 32j + 8g of row
+  // row0 + 16a + c. Out-of-range rows/columns read zeros.
+  struct Frag { Raw8<GT> gr[K1_RA][K1_KSUB]; Raw8E er[K1_RA][K1_KSUB]; };
+  auto load_m = [&](int k0, Frag& f) {
 #pragma unroll
-    for (int a = 0; a < K1_RA; ++a) {
-      const int row = row0 + a * 16 + c;
-      if (row < m && col < n) {
-        gq[a].load(G + ((int64_t)row * ldg + col) * GradIO<GT>::kBytes);
-        eq[a] = load_f32x8(E + (int64_t)row * lde + col);
-      } else {
-        gq[a].zero();
-        eq[a] = f32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < K1_KSUB; ++j) {
+      const int col = k0 + 32 * j + 8 * g;
+#pragma unroll
+      for (int a = 0; a < K1_RA; ++a) {
+        const int row = row0 + a * 16 + c;
+        const bool ok = row < m && col < n;
+        f.gr[a][j].load(rg, ok ? (uint32_t)(row * ldg + col) * GB : kOOB);
+        f.er[a][j].load(re, ok ? (uint32_t)(row * lde + col) * 4u : kOOB);
       }
     }
   };
@@ -122,75 +146,99 @@ void k_ef_mq(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   for (int a = 0; a < K1_RA; ++a)
 #pragma unroll
     for (int cc = 0; cc < RTC; ++cc) acc[a][cc] = f32x4{0, 0, 0, 0};
-  bool bad = false;
+  bool mbad = false;     // some M element of this lane was not finite
 
-  const int nsteps = npad / 32;
-  load_stage(0);
-  store_stage(0);
-  load_m(0, gcur, ecur);
-  __syncthreads();
-
-  for (int ks = 0; ks < nsteps; ++ks) {
-    const int buf = ks & 1;
-    const bool more = ks + 1 < nsteps;
-    Raw8<GT> gnxt[K1_RA];
-    f32x8 enxt[K1_RA];
-    if (more) {
-      load_stage((ks + 1) * 32);
-      load_m((ks + 1) * 32, gnxt, enxt);
-    }
-
-    bf16x8 ah[K1_RA], al[K1_RA];
+  auto compute = [&](int buf, const Frag& f) {
 #pragma unroll
-    for (int a = 0; a < K1_RA; ++a) {
-      const f32x8 gf = gcur[a].f32();
-      f32x8 mv;
-      bool mb = false;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        mv[e] = __builtin_fmaf(s, gf[e], ecur[a][e]);
-        mb |= nonfinite(mv[e]);
-      }
-      if (mb) {
-        // rare: decide on the inputs, not on M (M may also be inf through s or overflow)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) bad |= nonfinite(gf[e]) || nonfinite(ecur[a][e]);
-      }
-      split_bf16(mv, ah[a], al[a]);
-    }
-
-#pragma unroll
-    for (int cc = 0; cc < RTC; ++cc) {
-      const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&lds[buf][0][cc * 16 + c][8 * g]);
-      const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&lds[buf][1][cc * 16 + c][8 * g]);
+    for (int j = 0; j < K1_KSUB; ++j) {
+      bf16x8 ah[K1_RA], al[K1_RA];
 #pragma unroll
       for (int a = 0; a < K1_RA; ++a) {
-        acc[a][cc] = mfma_bf16(ah[a], bh, acc[a][cc]);
-        acc[a][cc] = mfma_bf16(ah[a], bl, acc[a][cc]);
-        acc[a][cc] = mfma_bf16(al[a], bh, acc[a][cc]);
+        const f32x8 gf = f.gr[a][j].f32();
+        const f32x8 ef = f.er[a][j].f32();
+        f32x8 mv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          mv[e] = __builtin_fmaf(s, gf[e], ef[e]);
+          mbad |= nonfinite(mv[e]);
+        }
+        split_bf16(mv, ah[a], al[a]);
+      }
+#pragma unroll
+      for (int cc = 0; cc < RTC; ++cc) {
+        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&lds[buf][0][cc * 16 + c][32 * j + 8 * g]);
+        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&lds[buf][1][cc * 16 + c][32 * j + 8 * g]);
+#pragma unroll
+        for (int a = 0; a < K1_RA; ++a) {
+          acc[a][cc] = mfma_bf16(ah[a], bh, acc[a][cc]);
+          acc[a][cc] = mfma_bf16(ah[a], bl, acc[a][cc]);
+          acc[a][cc] = mfma_bf16(al[a], bh, acc[a][cc]);
+        }
       }
     }
+  };
 
-    if (more) {
-      store_stage(buf ^ 1);
-#pragma unroll
-      for (int a = 0; a < K1_RA; ++a) { gcur[a] = gnxt[a]; ecur[a] = enxt[a]; }
-    }
+  const int nsteps = (npad + KS - 1) / KS;       // Q^T rows are padded to a whole stage
+  Frag cur;
+  load_stage(0);
+  load_m(0, cur);
+  store_stage(0);
+  __syncthreads();
+  int ks = 0;
+  for (; ks + 1 < nsteps; ++ks) {
+    Frag nxt;
+    load_stage((ks + 1) * KS);
+    load_m((ks + 1) * KS, nxt);
+    compute(ks & 1, cur);
+    store_stage((ks & 1) ^ 1);
+    cur = nxt;
     __syncthreads();
   }
+  compute(ks & 1, cur);
 
   // C layout of v_mfma_f32_16x16x32: lane holds rows 4g..4g+3, column c of the 16x16 tile.
-  float* __restrict__ praw = d.p_raw;
+  GLOBAL float* __restrict__ praw = gbl(d.p_raw);
+  if (row0 + K1_RA * 16 <= m) {
 #pragma unroll
-  for (int a = 0; a < K1_RA; ++a)
+    for (int a = 0; a < K1_RA; ++a)
 #pragma unroll
-    for (int cc = 0; cc < RTC; ++cc)
+      for (int cc = 0; cc < RTC; ++cc)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = row0 + a * 16 + 4 * g + i;
-        if (row < m) praw[(int64_t)row * rpad + rc0 + cc * 16 + c] = acc[a][cc][i];
+        for (int i = 0; i < 4; ++i)
+          praw[(int64_t)(row0 + a * 16 + 4 * g + i) * rpad + rc0 + cc * 16 + c] = acc[a][cc][i];
+  } else {
+#pragma unroll
+    for (int a = 0; a < K1_RA; ++a)
+#pragma unroll
+      for (int cc = 0; cc < RTC; ++cc)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = row0 + a * 16 + 4 * g + i;
+          if (row < m) praw[(int64_t)row * rpad + rc0 + cc * 16 + c] = acc[a][cc][i];
+        }
+  }
+
+  // Flag: M non-finite somewhere in this wave's rows is rare; only then are the inputs G and
+  // E of those rows examined, so the flag is exactly "G or E holds inf/NaN" (M may also be
+  // non-finite through s or fp32 overflow).
+  if (__builtin_amdgcn_ballot_w64(mbad) != 0) {
+    bool bad = false;
+    for (int col = 8 * g; col < n; col += 32) {
+#pragma unroll
+      for (int a = 0; a < K1_RA; ++a) {
+        const int row = row0 + a * 16 + c;
+        const bool ok = row < m;
+        Raw8<GT> gr;
+        Raw8E er;
+        gr.load(rg, ok ? (uint32_t)(row * ldg + col) * GB : kOOB);
+        er.load(re, ok ? (uint32_t)(row * lde + col) * 4u : kOOB);
+        const f32x8 gf = gr.f32(), ef = er.f32();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bad |= nonfinite(gf[e]) || nonfinite(ef[e]);
       }
-  if (bad) flags[wi.mat] = 1;
+    }
+    if (bad) flags[wi.mat] = 1;
+  }
 }
 
 template <int GT>
@@ -208,6 +256,7 @@ hipError_t launch_gt(int rtc, dim3 grid, dim3 block, hipStream_t s, const DevMat
 }  // namespace
 
 int ef_mq_rows_per_block() { return K1_ROWS; }
+int ef_mq_k_per_stage() { return KS; }
 
 hipError_t launch_ef_mq(int gt, int rtc, const DevMat* mats, const Work* work, int n_work,
                         const float* scale, uint8_t* flags, hipStream_t s) {

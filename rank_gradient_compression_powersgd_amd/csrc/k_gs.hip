@@ -38,7 +38,7 @@ void k_gs_gram(const DevMat* __restrict__ mats, const Work* __restrict__ work)
   if (wi.mat < 0) return;
   const DevMat& d = mats[wi.mat];
   const int m = d.m, rpad = d.rpad;
-  const float* __restrict__ P = d.p_raw;
+  const GLOBAL float* __restrict__ P = gbl(d.p_raw);
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
   const int c = lane & 15, g = lane >> 4;
@@ -66,7 +66,7 @@ void k_gs_gram(const DevMat* __restrict__ mats, const Work* __restrict__ work)
   }
 
   // C layout of v_mfma_f64_16x16x4f64: lane 16g + c, register i holds C[g + 4i][c].
-  double* __restrict__ out = d.gram + (int64_t)wi.b * rpad * rpad;
+  GLOBAL double* __restrict__ out = gbl(d.gram) + (int64_t)wi.b * rpad * rpad;
   int p = 0;
 #pragma unroll
   for (int ti = 0; ti < RT; ++ti)
@@ -97,6 +97,8 @@ void k_gs_factor(const DevMat* __restrict__ mats, const Work* __restrict__ work)
   const int rp = d.rpad;
   const int parts = d.gram_parts;
   const int tid = threadIdx.x;
+  const GLOBAL double* __restrict__ gram = gbl(d.gram);
+  GLOBAL double* __restrict__ tmat = gbl(d.tmat);
 
   __shared__ double W[kPackMax];
   __shared__ double T[kPackMax];
@@ -108,7 +110,7 @@ void k_gs_factor(const DevMat* __restrict__ mats, const Work* __restrict__ work)
   for (int i = 0; i < rp; ++i) {
     for (int j = i + tid; j < rp; j += GS_THREADS) {
       double sum = 0.0;
-      for (int pt = 0; pt < parts; ++pt) sum += d.gram[((int64_t)pt * rp + i) * rp + j];
+      for (int pt = 0; pt < parts; ++pt) sum += gram[((int64_t)pt * rp + i) * rp + j];
       W[pidx(i, j, rp)] = sum;
       T[pidx(i, j, rp)] = (i == j) ? 1.0 : 0.0;
     }
@@ -142,7 +144,7 @@ void k_gs_factor(const DevMat* __restrict__ mats, const Work* __restrict__ work)
 
   for (int idx = tid; idx < rp * rp; idx += GS_THREADS) {
     const int i = idx / rp, j = idx % rp;
-    d.tmat[idx] = (i <= j) ? T[pidx(i, j, rp)] : 0.0;
+    tmat[idx] = (i <= j) ? T[pidx(i, j, rp)] : 0.0;
   }
   (void)np;
 }
@@ -158,8 +160,14 @@ void k_gs_apply(const DevMat* __restrict__ mats, const Work* __restrict__ work)
   if (wi.mat < 0) return;
   const DevMat& d = mats[wi.mat];
   const int m = d.m, r = d.r, rpad = d.rpad, mpad = d.mpad, kpad3 = d.kpad3;
-  const float* __restrict__ P = d.p_raw;
-  const double* __restrict__ Tm = d.tmat;
+  const GLOBAL float* __restrict__ P = gbl(d.p_raw);
+  const GLOBAL double* __restrict__ Tm = gbl(d.tmat);
+  GLOBAL float* __restrict__ pout = gbl(d.p);
+  GLOBAL uint16_t* __restrict__ pth = gbl(d.pt_hi);
+  GLOBAL uint16_t* __restrict__ ptl = gbl(d.pt_lo);
+  GLOBAL uint16_t* __restrict__ p3h = gbl(d.p3_hi);
+  GLOBAL uint16_t* __restrict__ p3l = gbl(d.p3_lo);
+  GLOBAL int32_t* __restrict__ p3e = gbl(d.p3_exp);
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
   const int c = lane & 15, g = lane >> 4;
@@ -198,12 +206,12 @@ void k_gs_apply(const DevMat* __restrict__ mats, const Work* __restrict__ work)
     for (int t = 0; t < RT; ++t) {
       const int col = t * 16 + c;
       // (a) fp32 P_hat, m x r row-major
-      if (row < m && col < r) d.p[(int64_t)row * r + col] = x32[t][i];
+      if (row < m && col < r) pout[(int64_t)row * r + col] = x32[t][i];
       // (b) P_hat^T split bf16 hi/lo, rpad x mpad (rows m..mpad hold zeros)
       if (row < mpad) {
         const __bf16 hb = (__bf16)x32[t][i];
-        d.pt_hi[(int64_t)col * mpad + row] = bf16_bits(hb);
-        d.pt_lo[(int64_t)col * mpad + row] = bf16_bits((__bf16)(x32[t][i] - (float)hb));
+        pth[(int64_t)col * mpad + row] = bf16_bits(hb);
+        ptl[(int64_t)col * mpad + row] = bf16_bits((__bf16)(x32[t][i] - (float)hb));
       }
     }
   }
@@ -224,10 +232,10 @@ void k_gs_apply(const DevMat* __restrict__ mats, const Work* __restrict__ work)
       for (int t = 0; t < RT; ++t) {
         const float x = ldexpf(x32[t][i], ex);
         const _Float16 h = (_Float16)x;
-        d.p3_hi[(int64_t)row * kpad3 + t * 16 + c] = f16_bits(h);
-        d.p3_lo[(int64_t)row * kpad3 + t * 16 + c] = f16_bits((_Float16)(x - (float)h));
+        p3h[(int64_t)row * kpad3 + t * 16 + c] = f16_bits(h);
+        p3l[(int64_t)row * kpad3 + t * 16 + c] = f16_bits((_Float16)(x - (float)h));
       }
-      if (c == 0) d.p3_exp[row] = ex;
+      if (c == 0) p3e[row] = ex;
     }
   }
 }

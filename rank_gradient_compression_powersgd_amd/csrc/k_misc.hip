@@ -19,7 +19,7 @@ void k_prep_qt(const DevMat* __restrict__ mats, const Work* __restrict__ work)
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int nn = n0 + ty + 8 * j, rr = r0 + tx;
-    tile[ty + 8 * j][tx] = (nn < n && rr < r) ? d.q[(int64_t)nn * r + rr] : 0.0f;
+    tile[ty + 8 * j][tx] = (nn < n && rr < r) ? gbl(d.q)[(int64_t)nn * r + rr] : 0.0f;
   }
   __syncthreads();
 #pragma unroll
@@ -28,8 +28,8 @@ void k_prep_qt(const DevMat* __restrict__ mats, const Work* __restrict__ work)
     if (rr < rpad && nn < npad) {
       const float x = tile[tx][ty + 8 * j];
       const __bf16 h = (__bf16)x;
-      d.qt_hi[(int64_t)rr * npad + nn] = bf16_bits(h);
-      d.qt_lo[(int64_t)rr * npad + nn] = bf16_bits((__bf16)(x - (float)h));
+      gbl(d.qt_hi)[(int64_t)rr * npad + nn] = bf16_bits(h);
+      gbl(d.qt_lo)[(int64_t)rr * npad + nn] = bf16_bits((__bf16)(x - (float)h));
     }
   }
 }

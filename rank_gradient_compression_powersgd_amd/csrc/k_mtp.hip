@@ -9,7 +9,8 @@
 // Column tile t of a wave holds columns {4j + t : j = 0..15} of its 64-column strip.
 // The shared operand P^T, split into bf16 hi/lo by the orthonormalisation kernel, is staged
 // in LDS 32 rows of m at a time and double-buffered. Products use the same three-term bf16
-// split as K1.
+// split as K1. G and E are read through buffer descriptors (out-of-range reads give zeros),
+// so the loop body has no branches and the next rows' loads overlap the current MFMAs.
 //
 // Epilogue: Q' is written in fp32 (the caller's q_next). When the whole rank fits one chunk
 // the kernel also writes the decompression operand: each row of Q' scaled by a power of two
@@ -19,27 +20,27 @@
 namespace psgd {
 namespace {
 
-constexpr int K2_W = 4;       // waves per workgroup, 64 columns each
+#ifndef K2_W
+#define K2_W 4       // waves per workgroup, 64 columns each
+#endif
 constexpr int LDS_K = 40;
 
+// 4 consecutive gradient elements of one row, loaded through a buffer descriptor.
 template <int GT> struct Raw4;
 template <> struct Raw4<G_F16> {
   u32x2 v;
-  __device__ __forceinline__ void load(const void* p) { v = *reinterpret_cast<const u32x2*>(p); }
-  __device__ __forceinline__ void zero() { v = u32x2{0, 0}; }
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { v = bload8(r, off); }
   __device__ __forceinline__ f32x4 f32() const { return __builtin_convertvector(__builtin_bit_cast(f16x4, v), f32x4); }
 };
 template <> struct Raw4<G_BF16> {
   u32x2 v;
-  __device__ __forceinline__ void load(const void* p) { v = *reinterpret_cast<const u32x2*>(p); }
-  __device__ __forceinline__ void zero() { v = u32x2{0, 0}; }
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { v = bload8(r, off); }
   __device__ __forceinline__ f32x4 f32() const { return __builtin_convertvector(__builtin_bit_cast(bf16x4, v), f32x4); }
 };
 template <> struct Raw4<G_F32> {
-  f32x4 v;
-  __device__ __forceinline__ void load(const void* p) { v = *reinterpret_cast<const f32x4*>(p); }
-  __device__ __forceinline__ void zero() { v = f32x4{0, 0, 0, 0}; }
-  __device__ __forceinline__ f32x4 f32() const { return v; }
+  u32x4 v;
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { v = bload16(r, off); }
+  __device__ __forceinline__ f32x4 f32() const { return __builtin_bit_cast(f32x4, v); }
 };
 
 template <int GT, int RTC>
@@ -51,12 +52,13 @@ void k_mtp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   if (wi.mat < 0) return;
   const DevMat& d = mats[wi.mat];
   const int m = d.m, n = d.n, mpad = d.mpad, r = d.r, rpad = d.rpad;
-  const char* __restrict__ G = reinterpret_cast<const char*>(d.grad);
-  const float* __restrict__ E = d.err;
-  const int64_t ldg = d.ld_grad, lde = d.ld_err;
-  const uint16_t* __restrict__ pth = d.pt_hi;
-  const uint16_t* __restrict__ ptl = d.pt_lo;
+  const int ldg = (int)d.ld_grad, lde = (int)d.ld_err;
+  const rsrc_t rg = make_rsrc(d.grad, d.g_bytes);
+  const rsrc_t re = make_rsrc(d.err, d.e_bytes);
+  const GLOBAL uint16_t* __restrict__ pth = gbl(d.pt_hi);
+  const GLOBAL uint16_t* __restrict__ ptl = gbl(d.pt_lo);
   const float s = scale[d.block];
+  constexpr int GB = GradIO<GT>::kBytes;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
@@ -67,49 +69,45 @@ void k_mtp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][RTC * 16][LDS_K];
 
+  // P^T staging: RTC*16 rank rows x 32 m x {hi, lo}; threads past the last unit repeat it.
   constexpr int UNITS = RTC * 16 * 4 * 2;
   constexpr int THREADS = K2_W * kWave;
   constexpr int UPT = (UNITS + THREADS - 1) / THREADS;
   u32x4 stage[UPT];
+  auto unit = [&](int j, int& arr, int& rr, int& q4) {
+    int u = threadIdx.x + j * THREADS;
+    u = u < UNITS ? u : UNITS - 1;
+    arr = u / (RTC * 64);
+    const int rem = u - arr * (RTC * 64);
+    rr = rem >> 2;
+    q4 = rem & 3;
+  };
   auto load_stage = [&](int k0) {
 #pragma unroll
     for (int j = 0; j < UPT; ++j) {
-      const int u = threadIdx.x + j * THREADS;
-      if (UNITS % THREADS == 0 || u < UNITS) {
-        const int arr = u / (RTC * 64);
-        const int rem = u - arr * (RTC * 64);
-        const int rr = rem >> 2, q4 = rem & 3;
-        const uint16_t* src = (arr ? ptl : pth) + (int64_t)(rc0 + rr) * mpad + k0 + 8 * q4;
-        stage[j] = *reinterpret_cast<const u32x4*>(src);
-      }
+      int arr, rr, q4;
+      unit(j, arr, rr, q4);
+      stage[j] = *gcast<u32x4>((arr ? ptl : pth) + (int64_t)(rc0 + rr) * mpad + k0 + 8 * q4);
     }
   };
   auto store_stage = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < UPT; ++j) {
-      const int u = threadIdx.x + j * THREADS;
-      if (UNITS % THREADS == 0 || u < UNITS) {
-        const int arr = u / (RTC * 64);
-        const int rem = u - arr * (RTC * 64);
-        const int rr = rem >> 2, q4 = rem & 3;
-        *reinterpret_cast<u32x4*>(&lds[buf][arr][rr][8 * q4]) = stage[j];
-      }
+      int arr, rr, q4;
+      unit(j, arr, rr, q4);
+      *reinterpret_cast<u32x4*>(&lds[buf][arr][rr][8 * q4]) = stage[j];
     }
   };
 
-  Raw4<GT> gcur[8];
-  f32x4 ecur[8];
-  auto load_m = [&](int k0, Raw4<GT>* gq, f32x4* eq) {
+  // 8 rows k0 + 8g + kk, 4 columns colbase..colbase+3; out-of-range reads give zeros.
+  struct Frag { Raw4<GT> gr[8]; u32x4 er[8]; };
+  auto load_m = [&](int k0, Frag& f) {
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const int row = k0 + 8 * g + kk;
-      if (colok && row < m) {
-        gq[kk].load(G + ((int64_t)row * ldg + colbase) * GradIO<GT>::kBytes);
-        eq[kk] = *reinterpret_cast<const f32x4*>(E + (int64_t)row * lde + colbase);
-      } else {
-        gq[kk].zero();
-        eq[kk] = f32x4{0, 0, 0, 0};
-      }
+      const bool ok = colok && row < m;
+      f.gr[kk].load(rg, ok ? (uint32_t)(row * ldg + colbase) * GB : kOOB);
+      f.er[kk] = bload16(re, ok ? (uint32_t)(row * lde + colbase) * 4u : kOOB);
     }
   };
 
@@ -119,34 +117,19 @@ void k_mtp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[i][t] = f32x4{0, 0, 0, 0};
 
-  const int nsteps = mpad / 32;
-  load_stage(0);
-  store_stage(0);
-  load_m(0, gcur, ecur);
-  __syncthreads();
-
-  for (int ks = 0; ks < nsteps; ++ks) {
-    const int buf = ks & 1;
-    const bool more = ks + 1 < nsteps;
-    Raw4<GT> gnxt[8];
-    f32x4 enxt[8];
-    if (more) {
-      load_stage((ks + 1) * 32);
-      load_m((ks + 1) * 32, gnxt, enxt);
-    }
-
+  auto compute = [&](int buf, const Frag& f) {
     // B-fragments: tile t takes column t of every loaded row (k = 8g + kk).
     f32x8 mt[4];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const f32x4 gf = gcur[kk].f32();
+      const f32x4 gf = f.gr[kk].f32();
+      const f32x4 ef = __builtin_bit_cast(f32x4, f.er[kk]);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) mt[t][kk] = __builtin_fmaf(s, gf[t], ecur[kk][t]);
+      for (int t = 0; t < 4; ++t) mt[t][kk] = __builtin_fmaf(s, gf[t], ef[t]);
     }
     bf16x8 bh[4], bl[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) split_bf16(mt[t], bh[t], bl[t]);
-
 #pragma unroll
     for (int i = 0; i < RTC; ++i) {
       const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&lds[buf][0][i * 16 + c][8 * g]);
@@ -158,38 +141,54 @@ void k_mtp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
         acc[i][t] = mfma_bf16(al, bh[t], acc[i][t]);
       }
     }
+  };
 
-    if (more) {
-      store_stage(buf ^ 1);
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) { gcur[kk] = gnxt[kk]; ecur[kk] = enxt[kk]; }
-    }
+  const int nsteps = mpad / 32;
+  Frag cur;
+  load_stage(0);
+  load_m(0, cur);
+  store_stage(0);
+  __syncthreads();
+  int ks = 0;
+  for (; ks + 1 < nsteps; ++ks) {
+    Frag nxt;
+    load_stage((ks + 1) * 32);
+    load_m((ks + 1) * 32, nxt);
+    compute(ks & 1, cur);
+    store_stage((ks & 1) ^ 1);
+    cur = nxt;
     __syncthreads();
   }
+  compute(ks & 1, cur);
 
   // Output tile (i, t): lane holds Q'^T rows rc0 + 16i + 4g + {0..3}, i.e. Q'[colbase + t][..].
-  if (!colok) return;
-  float* __restrict__ qn = d.q_next;
+  GLOBAL float* __restrict__ qn = gbl(d.q_next);
+  const bool full = (wi.a + wv * 64 + 64 <= n) && (r & 3) == 0 && rc0 + RTC * 16 <= r;
+  if (full) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int ncol = colbase + t;
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int i = 0; i < RTC; ++i) {
-      const int rr = rc0 + i * 16 + 4 * g;
-      float* dst = qn + (int64_t)ncol * r + rr;
-      if (rr + 3 < r && (r & 3) == 0) {
-        *reinterpret_cast<f32x4*>(dst) = acc[i][t];
-      } else {
+      for (int i = 0; i < RTC; ++i)
+        *gcast<f32x4>(qn + (int64_t)(colbase + t) * r + rc0 + i * 16 + 4 * g) = acc[i][t];
+  } else if (colok) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < RTC; ++i) {
+        const int rr = rc0 + i * 16 + 4 * g;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
-          if (rr + ii < r) dst[ii] = acc[i][t][ii];
+          if (rr + ii < r) qn[(int64_t)(colbase + t) * r + rr + ii] = acc[i][t][ii];
       }
-    }
   }
 
-  // Decompression operand (only when this chunk covers the whole padded rank).
+  // Decompression operand (only when this chunk covers the whole padded rank): each row of Q'
+  // scaled by a power of two and split into fp16 hi + lo.
   if (RTC * 16 != rpad) return;
   const int kpad3 = d.kpad3;
+  GLOBAL uint16_t* __restrict__ q3h = gbl(d.q3_hi);
+  GLOBAL uint16_t* __restrict__ q3l = gbl(d.q3_lo);
+  GLOBAL int32_t* __restrict__ q3e = gbl(d.q3_exp);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     float amax = 0.0f;
@@ -201,8 +200,7 @@ void k_mtp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
     amax = fmaxf(amax, __shfl_xor(amax, 32));
     const int ex = fp16_row_exponent(amax);
     const int ncol = colbase + t;
-    uint16_t* hi = d.q3_hi + (int64_t)ncol * kpad3;
-    uint16_t* lo = d.q3_lo + (int64_t)ncol * kpad3;
+    if (!colok) continue;
 #pragma unroll
     for (int i = 0; i < RTC; ++i) {
       const int rr = i * 16 + 4 * g;
@@ -214,10 +212,10 @@ void k_mtp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
         h4[ii] = f16_bits(h);
         l4[ii] = f16_bits((_Float16)(x - (float)h));
       }
-      *reinterpret_cast<u32x2*>(hi + rr) = u32x2{h4[0] | ((uint32_t)h4[1] << 16), h4[2] | ((uint32_t)h4[3] << 16)};
-      *reinterpret_cast<u32x2*>(lo + rr) = u32x2{l4[0] | ((uint32_t)l4[1] << 16), l4[2] | ((uint32_t)l4[3] << 16)};
+      *gcast<u32x2>(q3h + (int64_t)ncol * kpad3 + rr) = u32x2{h4[0] | ((uint32_t)h4[1] << 16), h4[2] | ((uint32_t)h4[3] << 16)};
+      *gcast<u32x2>(q3l + (int64_t)ncol * kpad3 + rr) = u32x2{l4[0] | ((uint32_t)l4[1] << 16), l4[2] | ((uint32_t)l4[3] << 16)};
     }
-    if (g == 0) d.q3_exp[ncol] = ex;
+    if (g == 0) q3e[ncol] = ex;
   }
 }
 

@@ -21,6 +21,40 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 enum GradType : int { G_F16 = 1, G_BF16 = 2, G_F32 = 3 };
 
+// Pointers read out of the descriptor table are generic; accesses through them would compile
+// to FLAT instructions (which wait on both the vector-memory and the LDS counters). Every
+// kernel casts them to the global address space first so the compiler emits global_load /
+// global_store.
+#define GLOBAL __attribute__((address_space(1)))
+template <typename T> __device__ __forceinline__ GLOBAL T* gbl(T* p) { return (GLOBAL T*)p; }
+template <typename T> __device__ __forceinline__ const GLOBAL T* gbl(const T* p) { return (const GLOBAL T*)p; }
+template <typename T, typename U> __device__ __forceinline__ const GLOBAL T* gcast(const GLOBAL U* p) {
+  return reinterpret_cast<const GLOBAL T*>(p);
+}
+template <typename T, typename U> __device__ __forceinline__ GLOBAL T* gcast(GLOBAL U* p) {
+  return reinterpret_cast<GLOBAL T*>(p);
+}
+
+// Buffer resources. The streamed gradient, error and output matrices are accessed through a
+// per-matrix buffer descriptor whose range is the matrix's byte span. A lane whose element is
+// out of range uses the offset kOOB: the hardware returns zero for such loads and drops such
+// stores, so ragged edges need no branches and the compiler keeps every load in flight.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOOB = 0x80000000u;          // beyond every range (spans are < 2^31 bytes)
+constexpr int kRsrcWord3 = 0x00020000;          // raw 32-bit data format (gfx9 family)
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ u32x2 bload8(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ void bstore16(u32x4 v, rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v), r, off, 0, 0);
+}
+
 constexpr int kWave = 64;
 constexpr int kMaxRankTiles = 8;          // r <= 128 in this build
 constexpr int kXcds = 8;                  // MI355X: 8 XCDs, 32 CUs each
@@ -38,18 +72,20 @@ struct DevMat {
   int32_t m, n, block, r;
   int32_t rpad;      // r rounded up to 16 (MFMA tile)
   int32_t kpad3;     // r rounded up to 32 (K of the fp16 decompression MFMA)
-  int32_t npad;      // n rounded up to 32
+  int32_t npad;      // n rounded up to the k extent of one K1 stage
   int32_t mpad;      // m rounded up to 32
   int32_t gram_parts;
   int32_t pad_;
+  uint32_t g_bytes, e_bytes, o_bytes;   // byte spans of G, E and out (buffer ranges, < 2^31)
+  uint32_t pad2_;
   // workspace (library owned)
   float* p_raw;                        // m x rpad fp32: M q before orthonormalisation
   uint16_t* qt_hi; uint16_t* qt_lo;    // rpad x npad bf16: q^T split into hi + lo
   uint16_t* pt_hi; uint16_t* pt_lo;    // rpad x mpad bf16: P^T split into hi + lo
-  uint16_t* p3_hi; uint16_t* p3_lo;    // m x kpad3 fp16: P * 2^p3_exp[row], split hi + lo
-  int32_t* p3_exp;                     // m
-  uint16_t* q3_hi; uint16_t* q3_lo;    // n x kpad3 fp16: q_next * 2^q3_exp[row], split hi + lo
-  int32_t* q3_exp;                     // n
+  uint16_t* p3_hi; uint16_t* p3_lo;    // m3 x kpad3 fp16: P * 2^p3_exp[row], split hi + lo
+  int32_t* p3_exp;                     // m3 (m rounded up to a decompression tile; zero rows)
+  uint16_t* q3_hi; uint16_t* q3_lo;    // n3 x kpad3 fp16: q_next * 2^q3_exp[row], split hi + lo
+  int32_t* q3_exp;                     // n3 (n rounded up to a decompression tile; zero rows)
   double* gram;                        // gram_parts x rpad x rpad fp64 partial Gram matrices
   double* tmat;                        // rpad x rpad fp64 upper-triangular T, P = (M q) T
 };
@@ -110,41 +146,41 @@ __device__ __forceinline__ uint16_t f16_bits(_Float16 v) { return __builtin_bit_
 template <int GT> struct GradIO;
 template <> struct GradIO<G_F16> {
   static constexpr int kBytes = 2;
-  __device__ __forceinline__ static f32x8 load8(const void* base) {
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(base);
+  __device__ __forceinline__ static f32x8 load8(const GLOBAL char* base) {
+    const u32x4 raw = *gcast<u32x4>(base);
     return __builtin_convertvector(__builtin_bit_cast(f16x8, raw), f32x8);
   }
-  __device__ __forceinline__ static f32x4 load4(const void* base) {
-    const u32x2 raw = *reinterpret_cast<const u32x2*>(base);
+  __device__ __forceinline__ static f32x4 load4(const GLOBAL char* base) {
+    const u32x2 raw = *gcast<u32x2>(base);
     return __builtin_convertvector(__builtin_bit_cast(f16x4, raw), f32x4);
   }
 };
 template <> struct GradIO<G_BF16> {
   static constexpr int kBytes = 2;
-  __device__ __forceinline__ static f32x8 load8(const void* base) {
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(base);
+  __device__ __forceinline__ static f32x8 load8(const GLOBAL char* base) {
+    const u32x4 raw = *gcast<u32x4>(base);
     return __builtin_convertvector(__builtin_bit_cast(bf16x8, raw), f32x8);
   }
-  __device__ __forceinline__ static f32x4 load4(const void* base) {
-    const u32x2 raw = *reinterpret_cast<const u32x2*>(base);
+  __device__ __forceinline__ static f32x4 load4(const GLOBAL char* base) {
+    const u32x2 raw = *gcast<u32x2>(base);
     return __builtin_convertvector(__builtin_bit_cast(bf16x4, raw), f32x4);
   }
 };
 template <> struct GradIO<G_F32> {
   static constexpr int kBytes = 4;
-  __device__ __forceinline__ static f32x8 load8(const void* base) {
-    const f32x4 a = reinterpret_cast<const f32x4*>(base)[0];
-    const f32x4 b = reinterpret_cast<const f32x4*>(base)[1];
+  __device__ __forceinline__ static f32x8 load8(const GLOBAL char* base) {
+    const f32x4 a = gcast<f32x4>(base)[0];
+    const f32x4 b = gcast<f32x4>(base)[1];
     return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   }
-  __device__ __forceinline__ static f32x4 load4(const void* base) {
-    return *reinterpret_cast<const f32x4*>(base);
+  __device__ __forceinline__ static f32x4 load4(const GLOBAL char* base) {
+    return *gcast<f32x4>(base);
   }
 };
 
-__device__ __forceinline__ f32x8 load_f32x8(const float* p) {
-  const f32x4 a = reinterpret_cast<const f32x4*>(p)[0];
-  const f32x4 b = reinterpret_cast<const f32x4*>(p)[1];
+__device__ __forceinline__ f32x8 load_f32x8(const GLOBAL float* p) {
+  const f32x4 a = gcast<f32x4>(p)[0];
+  const f32x4 b = gcast<f32x4>(p)[1];
   return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 

@@ -13,6 +13,7 @@
 
 namespace psgd {
 int ef_mq_rows_per_block();
+int ef_mq_k_per_stage();
 int mtp_cols_per_block();
 int gs_apply_rows_per_block();
 int decomp_tile_m();
@@ -185,20 +186,31 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
     d.out = a.out; d.ld_out = a.ld_out;
     d.m = (int)a.m; d.n = (int)a.n; d.block = a.block; d.r = r;
     d.rpad = rpad; d.kpad3 = kpad3;
-    d.npad = (int)rup(a.n, 32); d.mpad = (int)rup(a.m, 32);
+    d.npad = (int)rup(a.n, psgd::ef_mq_k_per_stage());   // Q^T covers whole K1 stages
+    d.mpad = (int)rup(a.m, 32);
     d.gram_parts = (int)((a.m + psgd::kGramRows - 1) / psgd::kGramRows);
+    const int gsz = gt == psgd::G_F32 ? 4 : 2;
+    const int64_t gb = ((a.m - 1) * a.ld_grad + a.n) * gsz;
+    const int64_t eb = ((a.m - 1) * a.ld_err + a.n) * 4;
+    const int64_t ob = a.out ? ((a.m - 1) * a.ld_out + a.n) * 4 : 0;
+    if (gb >= (int64_t(1) << 31) || eb >= (int64_t(1) << 31) || ob >= (int64_t(1) << 31))
+      return fail(ctx, PSGD_EINVAL, "matrix %d: G, E and out must each span less than 2 GiB", i);
+    d.g_bytes = (uint32_t)gb;
+    d.e_bytes = (uint32_t)eb;
+    d.o_bytes = (uint32_t)ob;
     Off& o = offs[i];
     o.p_raw = take((size_t)a.m * rpad * 4);
     o.qth = take((size_t)rpad * d.npad * 2);
     o.qtl = take((size_t)rpad * d.npad * 2);
     o.pth = take((size_t)rpad * d.mpad * 2);
     o.ptl = take((size_t)rpad * d.mpad * 2);
-    o.p3h = take((size_t)a.m * kpad3 * 2);
-    o.p3l = take((size_t)a.m * kpad3 * 2);
-    o.p3e = take((size_t)a.m * 4);
-    o.q3h = take((size_t)a.n * kpad3 * 2);
-    o.q3l = take((size_t)a.n * kpad3 * 2);
-    o.q3e = take((size_t)a.n * 4);
+    const int64_t m3 = rup(a.m, psgd::decomp_tile_m()), n3 = rup(a.n, psgd::decomp_tile_n());
+    o.p3h = take((size_t)m3 * kpad3 * 2);      // zero rows up to a whole decompression tile
+    o.p3l = take((size_t)m3 * kpad3 * 2);
+    o.p3e = take((size_t)m3 * 4);
+    o.q3h = take((size_t)n3 * kpad3 * 2);
+    o.q3l = take((size_t)n3 * kpad3 * 2);
+    o.q3e = take((size_t)n3 * 4);
     o.gram = take((size_t)d.gram_parts * rpad * rpad * 8);
     o.tmat = take((size_t)rpad * rpad * 8);
   }
