@@ -55,6 +55,10 @@ def parse(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the CPU oracle sample (whole resblocks)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of 2 GiB (reads 2 GiB, writes 2 GiB) three "
+                         "times; under rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE scale the "
+                         "traffic counters of the library kernels")
     return ap.parse_args(argv)
 
 
@@ -147,6 +151,15 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if a.copy_calibration:
+        x = torch.ones(1 << 29, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.neg(x, out=y)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"kernel": "elementwise neg", "bytes_read": x.numel() * 4,
+                                               "bytes_written": y.numel() * 4, "launches": 3}}))
+        return 0
     psgd.load_library()
     hip = Hip()
     log(f"building workload {a.workload} ...")

@@ -48,28 +48,35 @@ def _run(cmd, verbose):
         print(out)
 
 
-def build(jobs: int = 0, verbose: bool = False) -> str:
+def build(jobs: int = 0, verbose: bool = False, defines=(), out: str = "") -> str:
+    """Compile every csrc/*.hip and link libpsgd.so (or `out`). `defines` are extra -D macros
+    (kernel tile parameters) for alternative builds."""
     cc = hipcc()
-    os.makedirs(BUILD, exist_ok=True)
+    lib = os.path.abspath(out) if out else LIB
+    bdir = BUILD if not defines else os.path.join(BUILD, "v_" + "_".join(d.replace("=", "") for d in defines))
+    os.makedirs(bdir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    objs = [os.path.join(bdir, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    dflags = [f"-D{d}" for d in defines]
     jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 4)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        futs = [ex.submit(_run, [cc, *COMMON, "-c", s, "-o", o], verbose) for s, o in zip(srcs, objs)]
+        futs = [ex.submit(_run, [cc, *COMMON, *dflags, "-c", s, "-o", o], verbose) for s, o in zip(srcs, objs)]
         for f in futs:
             f.result()
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=0)
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--define", action="append", default=[], help="extra -D macro, e.g. K2_TC=2")
+    ap.add_argument("--out", default="", help="output library path (default: in-tree libpsgd.so)")
     a = ap.parse_args(argv)
-    print(build(a.jobs, a.verbose))
+    print(build(a.jobs, a.verbose, a.define, a.out))
     return 0
 
 

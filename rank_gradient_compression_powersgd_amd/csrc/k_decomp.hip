@@ -27,9 +27,15 @@ namespace {
 #ifndef K3_WN
 #define K3_WN 2      // waves along n; each wave computes a 64 x 64 tile
 #endif
+#ifndef K3_OCC
+#define K3_OCC 2     // workgroups per CU the register budget is sized for
+#endif
 constexpr int K3_TM = K3_WM * 64, K3_TN = K3_WN * 64;
 constexpr int K3_THREADS = K3_WM * K3_WN * kWave;
-constexpr int LDS_K = 40;                // fp16 elements per LDS row (32 + 8 padding)
+constexpr int LDS_K = 32;                // LDS row = 32 fp16 = 4 16-byte units, XOR-swizzled
+// Physical unit of logical unit q in row rr: 16 lanes reading 16 consecutive rows (one unit
+// each) or writing 4 rows (4 units each) hit 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz3(int rr, int q) { return q ^ ((rr >> 2) & 3); }
 
 template <int GT> struct Raw4;
 template <> struct Raw4<G_F16> {
@@ -49,7 +55,7 @@ template <> struct Raw4<G_F32> {
 };
 
 template <int GT>
-__global__ __launch_bounds__(K3_THREADS)
+__global__ __launch_bounds__(K3_THREADS, K3_OCC)
 void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
               const float* __restrict__ scale, const int32_t* __restrict__ skip)
 {
@@ -89,32 +95,40 @@ void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   const GLOBAL uint16_t* __restrict__ p3h = gbl(d.p3_hi) + (int64_t)m0 * kpad3;
   const GLOBAL uint16_t* __restrict__ p3l = gbl(d.p3_lo) + (int64_t)m0 * kpad3;
   u32x4 sq[QU], sp[PU];
+  // unit u of a `rows`-row operand: array (hi/lo), row, 16-byte unit; consecutive threads take
+  // consecutive units of a row (coalesced global reads).
+  auto unit = [](int u, int rows, int& arr, int& rr, int& q4) {
+    arr = u / (rows * 4);
+    const int v = u - arr * rows * 4;
+    rr = v >> 2;
+    q4 = v & 3;
+  };
   auto load_stage = [&](int k0) {
 #pragma unroll
     for (int j = 0; j < QU; ++j) {
-      const int u = threadIdx.x + j * K3_THREADS;          // u = (arr * K3_TN + row) * 4 + q4
-      const int q4 = u & 3, rr = (u >> 2) % K3_TN, arr = (u >> 2) / K3_TN;
+      int arr, rr, q4;
+      unit(threadIdx.x + j * K3_THREADS, K3_TN, arr, rr, q4);
       sq[j] = *gcast<u32x4>((arr ? q3l : q3h) + (int64_t)rr * kpad3 + k0 + 8 * q4);
     }
 #pragma unroll
     for (int j = 0; j < PU; ++j) {
-      const int u = threadIdx.x + j * K3_THREADS;
-      const int q4 = u & 3, rr = (u >> 2) % K3_TM, arr = (u >> 2) / K3_TM;
+      int arr, rr, q4;
+      unit(threadIdx.x + j * K3_THREADS, K3_TM, arr, rr, q4);
       sp[j] = *gcast<u32x4>((arr ? p3l : p3h) + (int64_t)rr * kpad3 + k0 + 8 * q4);
     }
   };
   auto store_stage = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < QU; ++j) {
-      const int u = threadIdx.x + j * K3_THREADS;
-      const int q4 = u & 3, rr = (u >> 2) % K3_TN, arr = (u >> 2) / K3_TN;
-      *reinterpret_cast<u32x4*>(&ldq[buf][arr][rr][8 * q4]) = sq[j];
+      int arr, rr, q4;
+      unit(threadIdx.x + j * K3_THREADS, K3_TN, arr, rr, q4);
+      *reinterpret_cast<u32x4*>(&ldq[buf][arr][rr][8 * swz3(rr, q4)]) = sq[j];
     }
 #pragma unroll
     for (int j = 0; j < PU; ++j) {
-      const int u = threadIdx.x + j * K3_THREADS;
-      const int q4 = u & 3, rr = (u >> 2) % K3_TM, arr = (u >> 2) / K3_TM;
-      *reinterpret_cast<u32x4*>(&ldp[buf][arr][rr][8 * q4]) = sp[j];
+      int arr, rr, q4;
+      unit(threadIdx.x + j * K3_THREADS, K3_TM, arr, rr, q4);
+      *reinterpret_cast<u32x4*>(&ldp[buf][arr][rr][8 * swz3(rr, q4)]) = sp[j];
     }
   };
 
@@ -128,13 +142,15 @@ void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
     f16x8 bh[4], bl[4];
 #pragma unroll
     for (int im = 0; im < 4; ++im) {
-      bh[im] = *reinterpret_cast<const f16x8*>(&ldp[buf][0][wm * 64 + im * 16 + c][8 * g]);
-      bl[im] = *reinterpret_cast<const f16x8*>(&ldp[buf][1][wm * 64 + im * 16 + c][8 * g]);
+      const int rp = wm * 64 + im * 16 + c;
+      bh[im] = *reinterpret_cast<const f16x8*>(&ldp[buf][0][rp][8 * swz3(rp, g)]);
+      bl[im] = *reinterpret_cast<const f16x8*>(&ldp[buf][1][rp][8 * swz3(rp, g)]);
     }
 #pragma unroll
     for (int jn = 0; jn < 4; ++jn) {
-      const f16x8 ah = *reinterpret_cast<const f16x8*>(&ldq[buf][0][wn * 64 + jn * 16 + c][8 * g]);
-      const f16x8 al = *reinterpret_cast<const f16x8*>(&ldq[buf][1][wn * 64 + jn * 16 + c][8 * g]);
+      const int rq = wn * 64 + jn * 16 + c;
+      const f16x8 ah = *reinterpret_cast<const f16x8*>(&ldq[buf][0][rq][8 * swz3(rq, g)]);
+      const f16x8 al = *reinterpret_cast<const f16x8*>(&ldq[buf][1][rq][8 * swz3(rq, g)]);
 #pragma unroll
       for (int im = 0; im < 4; ++im) {
         acc[jn][im] = mfma_f16(ah, bh[im], acc[jn][im]);

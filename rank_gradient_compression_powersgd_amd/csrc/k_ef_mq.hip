@@ -22,10 +22,13 @@
 #include "psgd_internal.h"
 
 #ifndef K1_RA
-#define K1_RA 2      // 16-row tiles per wave
+#define K1_RA 4      // 16-row tiles per wave
 #endif
 #ifndef K1_W
 #define K1_W 4       // waves per workgroup
+#endif
+#ifndef K1_OCC
+#define K1_OCC 1     // workgroups per CU the register budget is sized for
 #endif
 #ifndef K1_KSUB
 #define K1_KSUB 2    // 32-column MFMA k groups per pipeline stage
@@ -36,7 +39,12 @@ namespace {
 
 constexpr int K1_ROWS = K1_RA * 16 * K1_W;
 constexpr int KS = 32 * K1_KSUB;       // k columns per stage
-constexpr int LDS_K = KS + 8;          // + 8 bf16 padding per LDS row
+constexpr int LDS_K = KS;              // LDS row = KS bf16; 16-byte units XOR-swizzled by row
+static_assert(KS == 64, "the LDS swizzle assumes 8 units per row");
+// Physical 16-byte unit of logical unit q in rank row rr: with 128-byte rows, the 16 lanes of a
+// read (16 consecutive rows, one unit each) and of a write (2 rows, 8 units each) hit 16
+// distinct 16-byte bank groups.
+__device__ __forceinline__ int swz1(int rr, int q) { return q ^ ((rr >> 1) & 7); }
 
 template <int GT> struct Raw8;
 template <> struct Raw8<G_F16> {
@@ -68,7 +76,7 @@ struct Raw8E {
 };
 
 template <int GT, int RTC>
-__global__ __launch_bounds__(K1_W * kWave)
+__global__ __launch_bounds__(K1_W * kWave, K1_OCC)
 void k_ef_mq(const DevMat* __restrict__ mats, const Work* __restrict__ work,
              const float* __restrict__ scale, uint8_t* __restrict__ flags)
 {
@@ -92,8 +100,9 @@ void k_ef_mq(const DevMat* __restrict__ mats, const Work* __restrict__ work,
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][RTC * 16][LDS_K];
 
-  // Q^T staging: RTC*16 rank rows x KS k x {hi, lo} in 16-byte units. Threads past the last
-  // unit repeat it (same value to the same LDS address), so the code has no branch.
+  // Q^T staging: RTC*16 rank rows x KS k x {hi, lo} in 16-byte units; consecutive threads take
+  // consecutive units of a row (coalesced global reads). Threads past the last unit repeat it
+  // (same value to the same LDS address), so the code has no branch.
   constexpr int QPR = KS / 8;                   // 16-byte units per rank row
   constexpr int UNITS = RTC * 16 * QPR * 2;
   constexpr int THREADS = K1_W * kWave;
@@ -120,7 +129,7 @@ void k_ef_mq(const DevMat* __restrict__ mats, const Work* __restrict__ work,
     for (int j = 0; j < UPT; ++j) {
       int arr, rr, q;
       unit(j, arr, rr, q);
-      *reinterpret_cast<u32x4*>(&lds[buf][arr][rr][8 * q]) = stage[j];
+      *reinterpret_cast<u32x4*>(&lds[buf][arr][rr][8 * swz1(rr, q)]) = stage[j];
     }
   };
 
@@ -166,8 +175,9 @@ void k_ef_mq(const DevMat* __restrict__ mats, const Work* __restrict__ work,
       }
 #pragma unroll
       for (int cc = 0; cc < RTC; ++cc) {
-        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&lds[buf][0][cc * 16 + c][32 * j + 8 * g]);
-        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&lds[buf][1][cc * 16 + c][32 * j + 8 * g]);
+        const int pq = 8 * swz1(cc * 16 + c, 4 * j + g);
+        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&lds[buf][0][cc * 16 + c][pq]);
+        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&lds[buf][1][cc * 16 + c][pq]);
 #pragma unroll
         for (int a = 0; a < K1_RA; ++a) {
           acc[a][cc] = mfma_bf16(ah[a], bh, acc[a][cc]);

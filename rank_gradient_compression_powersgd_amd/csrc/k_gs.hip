@@ -51,18 +51,30 @@ void k_gs_gram(const DevMat* __restrict__ mats, const Work* __restrict__ work)
   for (int j = 0; j < PPW; ++j) acc[j] = f64x4{0, 0, 0, 0};
 
   const int row0 = wi.a;
-  for (int ks = 0; ks < kGramRows / 4; ++ks) {
-    const int row = row0 + 4 * ks + g;
-    double v[RT];
+  constexpr int KB = 4;                      // k steps (of 4 rows) whose loads are batched
+  for (int ks = 0; ks < kGramRows / 4; ks += KB) {
+    float v[KB][RT];
 #pragma unroll
-    for (int t = 0; t < RT; ++t) v[t] = row < m ? (double)P[(int64_t)row * rpad + t * 16 + c] : 0.0;
+    for (int b = 0; b < KB; ++b) {
+      const int row = row0 + 4 * (ks + b) + g;
+      const int rr = row < m ? row : 0;
+#pragma unroll
+      for (int t = 0; t < RT; ++t) v[b][t] = P[(int64_t)rr * rpad + t * 16 + c];
+      if (row >= m) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t) v[b][t] = 0.0f;
+      }
+    }
     // lane supplies A[c][g] = P[row][ti*16 + c] and B[g][c] = P[row][tj*16 + c]
-    int p = 0;
 #pragma unroll
-    for (int ti = 0; ti < RT; ++ti)
+    for (int b = 0; b < KB; ++b) {
+      int p = 0;
 #pragma unroll
-      for (int tj = ti; tj < RT; ++tj, ++p)
-        if (p % NW == wv) acc[p / NW] = mfma_f64(v[ti], v[tj], acc[p / NW]);
+      for (int ti = 0; ti < RT; ++ti)
+#pragma unroll
+        for (int tj = ti; tj < RT; ++tj, ++p)
+          if (p % NW == wv) acc[p / NW] = mfma_f64((double)v[b][ti], (double)v[b][tj], acc[p / NW]);
+    }
   }
 
   // C layout of v_mfma_f64_16x16x4f64: lane 16g + c, register i holds C[g + 4i][c].
@@ -88,7 +100,9 @@ __device__ __forceinline__ int pidx(int i, int j, int rp) {   // packed upper, i
   return i * rp - (i * (i - 1)) / 2 + (j - i);
 }
 
-__global__ __launch_bounds__(GS_THREADS)
+constexpr int GSF_THREADS = 1024;     // 32 x 32 thread grid over the r x r problem
+
+__global__ __launch_bounds__(GSF_THREADS)
 void k_gs_factor(const DevMat* __restrict__ mats, const Work* __restrict__ work)
 {
   const Work wi = work[blockIdx.x];
@@ -96,7 +110,7 @@ void k_gs_factor(const DevMat* __restrict__ mats, const Work* __restrict__ work)
   const DevMat& d = mats[wi.mat];
   const int rp = d.rpad;
   const int parts = d.gram_parts;
-  const int tid = threadIdx.x;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   const GLOBAL double* __restrict__ gram = gbl(d.gram);
   GLOBAL double* __restrict__ tmat = gbl(d.tmat);
 
@@ -106,17 +120,17 @@ void k_gs_factor(const DevMat* __restrict__ mats, const Work* __restrict__ work)
   __shared__ double rrow[128];
 
   // W = sum of the partial Gram matrices in part order; T = I.
-  const int np = rp * (rp + 1) / 2;
-  for (int i = 0; i < rp; ++i) {
-    for (int j = i + tid; j < rp; j += GS_THREADS) {
+  for (int i = ty; i < rp; i += 32) {
+    const int base = i * rp - (i * (i - 1)) / 2 - i;
+    for (int j = i + tx; j < rp; j += 32) {
       double sum = 0.0;
       for (int pt = 0; pt < parts; ++pt) sum += gram[((int64_t)pt * rp + i) * rp + j];
-      W[pidx(i, j, rp)] = sum;
-      T[pidx(i, j, rp)] = (i == j) ? 1.0 : 0.0;
+      W[base + j] = sum;
+      T[base + j] = (i == j) ? 1.0 : 0.0;
     }
   }
   __syncthreads();
-  for (int i = tid; i < rp; i += GS_THREADS) diag0[i] = W[pidx(i, i, rp)];
+  if (threadIdx.x < rp) diag0[threadIdx.x] = W[pidx(threadIdx.x, threadIdx.x, rp)];
   __syncthreads();
 
   for (int j = 0; j < rp; ++j) {
@@ -125,33 +139,36 @@ void k_gs_factor(const DevMat* __restrict__ mats, const Work* __restrict__ work)
     const bool ok = (d0 > 0.0) && (dj > kDegenerate * d0) && (dj <= 1.0e300);
     const double inv = ok ? 1.0 / sqrt(dj) : 0.0;
     // r_jk = <q_j, v_k> = W[j][k] / ||v_j||; t_j = u_j / ||v_j||
-    for (int k = j + 1 + tid; k < rp; k += GS_THREADS) rrow[k] = W[pidx(j, k, rp)] * inv;
-    for (int i = tid; i <= j; i += GS_THREADS) T[pidx(i, j, rp)] *= inv;
+    const int k1 = j + 1 + (int)threadIdx.x;
+    if (k1 < rp) rrow[k1] = W[pidx(j, k1, rp)] * inv;
+    if ((int)threadIdx.x <= j) T[pidx(threadIdx.x, j, rp)] *= inv;
     __syncthreads();
     // v_k -= r_jk q_j for k > j: Gram update and coefficient update
-    const int L = rp - j - 1;
-    for (int idx = tid; idx < L * L; idx += GS_THREADS) {
-      const int k = j + 1 + idx / L, l = j + 1 + idx % L;
-      if (l >= k) W[pidx(k, l, rp)] -= rrow[k] * rrow[l];
+    for (int k = j + 1 + ty; k < rp; k += 32) {
+      const int base = k * rp - (k * (k - 1)) / 2 - k;
+      const double rk = rrow[k];
+      for (int l = k + ((tx - (k - j - 1)) & 31); l < rp; l += 32) W[base + l] -= rk * rrow[l];
     }
-    const int nt = (j + 1) * L;
-    for (int idx = tid; idx < nt; idx += GS_THREADS) {
-      const int i = idx / L, k = j + 1 + idx % L;
-      T[pidx(i, k, rp)] -= rrow[k] * T[pidx(i, j, rp)];
+    for (int i = ty; i <= j; i += 32) {
+      const int base = i * rp - (i * (i - 1)) / 2 - i;
+      const double tij = T[base + j];
+      for (int k = j + 1 + tx; k < rp; k += 32) T[base + k] -= rrow[k] * tij;
     }
     __syncthreads();
   }
 
-  for (int idx = tid; idx < rp * rp; idx += GS_THREADS) {
-    const int i = idx / rp, j = idx % rp;
-    tmat[idx] = (i <= j) ? T[pidx(i, j, rp)] : 0.0;
+  for (int i = ty; i < rp; i += 32) {
+    const int base = i * rp - (i * (i - 1)) / 2 - i;
+    for (int j = tx; j < rp; j += 32) tmat[(int64_t)i * rp + j] = (j >= i) ? T[base + j] : 0.0;
   }
-  (void)np;
 }
 
 // ------------------------------------------------------------------------------------------
 // P_hat = P T and the operand layouts of the two products that follow
 // ------------------------------------------------------------------------------------------
+constexpr int GSA_RA = 2;                          // 16-row tiles per wave
+constexpr int GSA_ROWS = GSA_RA * 16 * (GS_THREADS / kWave);   // 128 rows per workgroup
+
 template <int RT>
 __global__ __launch_bounds__(GS_THREADS)
 void k_gs_apply(const DevMat* __restrict__ mats, const Work* __restrict__ work)
@@ -162,82 +179,102 @@ void k_gs_apply(const DevMat* __restrict__ mats, const Work* __restrict__ work)
   const int m = d.m, r = d.r, rpad = d.rpad, mpad = d.mpad, kpad3 = d.kpad3;
   const GLOBAL float* __restrict__ P = gbl(d.p_raw);
   const GLOBAL double* __restrict__ Tm = gbl(d.tmat);
-  GLOBAL float* __restrict__ pout = gbl(d.p);
-  GLOBAL uint16_t* __restrict__ pth = gbl(d.pt_hi);
-  GLOBAL uint16_t* __restrict__ ptl = gbl(d.pt_lo);
-  GLOBAL uint16_t* __restrict__ p3h = gbl(d.p3_hi);
-  GLOBAL uint16_t* __restrict__ p3l = gbl(d.p3_lo);
-  GLOBAL int32_t* __restrict__ p3e = gbl(d.p3_exp);
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
   const int c = lane & 15, g = lane >> 4;
-  const int rbase = wi.a + wv * 16;        // this wave's 16 rows
-  const int rowA = rbase + c;              // A-fragment row supplied by this lane
+  const int row0 = wi.a;                   // this workgroup's GSA_ROWS rows
+  constexpr int SP = RT * 16 + 1;          // LDS row pitch (floats); odd, so column reads spread over banks
 
-  f64x4 acc[RT];
+  __shared__ float S[GSA_ROWS * SP];
+  __shared__ int sexp[GSA_ROWS];
+
+  f64x4 acc[GSA_RA][RT];
 #pragma unroll
-  for (int t = 0; t < RT; ++t) acc[t] = f64x4{0, 0, 0, 0};
+  for (int a = 0; a < GSA_RA; ++a)
+#pragma unroll
+    for (int t = 0; t < RT; ++t) acc[a][t] = f64x4{0, 0, 0, 0};
 
+  // P_hat = P T with T upper triangular: k tile kt only feeds column tiles tj >= kt.
 #pragma unroll
   for (int kt = 0; kt < RT; ++kt) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int k = kt * 16 + ks * 4 + g;
-      const double a = rowA < m ? (double)P[(int64_t)rowA * rpad + k] : 0.0;
+      double av[GSA_RA];
 #pragma unroll
-      for (int tj = kt; tj < RT; ++tj) {       // T is upper triangular
+      for (int a = 0; a < GSA_RA; ++a) {
+        const int rowA = row0 + (wv * GSA_RA + a) * 16 + c;     // A-fragment row of this lane
+        av[a] = rowA < m ? (double)P[(int64_t)rowA * rpad + k] : 0.0;
+      }
+#pragma unroll
+      for (int tj = kt; tj < RT; ++tj) {
         const double b = Tm[(int64_t)k * rpad + tj * 16 + c];
-        acc[tj] = mfma_f64(a, b, acc[tj]);
+#pragma unroll
+        for (int a = 0; a < GSA_RA; ++a) acc[a][tj] = mfma_f64(av[a], b, acc[a][tj]);
       }
     }
   }
 
-  // C layout of v_mfma_f64_16x16x4f64: lane 16g + c, register i holds P_hat[rbase + g + 4i][tj*16 + c]
-  float x32[RT][4];
+  // C layout of v_mfma_f64_16x16x4f64: lane 16g + c, register i holds C[g + 4i][c].
 #pragma unroll
-  for (int t = 0; t < RT; ++t)
+  for (int a = 0; a < GSA_RA; ++a)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x32[t][i] = (float)acc[t][i];
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        S[((wv * GSA_RA + a) * 16 + g + 4 * i) * SP + t * 16 + c] = (float)acc[a][t][i];
+  __syncthreads();
 
+  // (a) fp32 P_hat, m x r row-major
+  GLOBAL float* __restrict__ pout = gbl(d.p);
+  for (int idx = threadIdx.x; idx < GSA_ROWS * r; idx += GS_THREADS) {
+    const int rr = idx / r, cc = idx - rr * r;
+    if (row0 + rr < m) pout[(int64_t)(row0 + rr) * r + cc] = S[rr * SP + cc];
+  }
+  // (b) P_hat^T split bf16 hi/lo, rpad x mpad: 8 consecutive rows of one column per store
+  GLOBAL uint16_t* __restrict__ pth = gbl(d.pt_hi);
+  GLOBAL uint16_t* __restrict__ ptl = gbl(d.pt_lo);
+  for (int idx = threadIdx.x; idx < rpad * (GSA_ROWS / 8); idx += GS_THREADS) {
+    const int col = idx / (GSA_ROWS / 8), r8 = (idx % (GSA_ROWS / 8)) * 8;
+    if (row0 + r8 >= mpad) continue;
+    uint32_t h[4], l[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = rbase + g + 4 * i;
-#pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      const int col = t * 16 + c;
-      // (a) fp32 P_hat, m x r row-major
-      if (row < m && col < r) pout[(int64_t)row * r + col] = x32[t][i];
-      // (b) P_hat^T split bf16 hi/lo, rpad x mpad (rows m..mpad hold zeros)
-      if (row < mpad) {
-        const __bf16 hb = (__bf16)x32[t][i];
-        pth[(int64_t)col * mpad + row] = bf16_bits(hb);
-        ptl[(int64_t)col * mpad + row] = bf16_bits((__bf16)(x32[t][i] - (float)hb));
-      }
+    for (int e = 0; e < 4; ++e) {
+      const float x0 = S[(r8 + 2 * e) * SP + col], x1 = S[(r8 + 2 * e + 1) * SP + col];
+      const __bf16 h0 = (__bf16)x0, h1 = (__bf16)x1;
+      h[e] = bf16_bits(h0) | ((uint32_t)bf16_bits(h1) << 16);
+      l[e] = bf16_bits((__bf16)(x0 - (float)h0)) | ((uint32_t)bf16_bits((__bf16)(x1 - (float)h1)) << 16);
     }
+    *gcast<u32x4>(pth + (int64_t)col * mpad + row0 + r8) = u32x4{h[0], h[1], h[2], h[3]};
+    *gcast<u32x4>(ptl + (int64_t)col * mpad + row0 + r8) = u32x4{l[0], l[1], l[2], l[3]};
   }
   // (c) rows scaled by 2^e (largest entry in [2^13, 2^14)) and split fp16 hi/lo, m x kpad3
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  if (threadIdx.x < GSA_ROWS) {
     float amax = 0.0f;
-#pragma unroll
-    for (int t = 0; t < RT; ++t) amax = fmaxf(amax, fabsf(x32[t][i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
-    amax = fmaxf(amax, __shfl_xor(amax, 2));
-    amax = fmaxf(amax, __shfl_xor(amax, 4));
-    amax = fmaxf(amax, __shfl_xor(amax, 8));
-    const int ex = fp16_row_exponent(amax);
-    const int row = rbase + g + 4 * i;
-    if (row < m) {
-#pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        const float x = ldexpf(x32[t][i], ex);
-        const _Float16 h = (_Float16)x;
-        p3h[(int64_t)row * kpad3 + t * 16 + c] = f16_bits(h);
-        p3l[(int64_t)row * kpad3 + t * 16 + c] = f16_bits((_Float16)(x - (float)h));
-      }
-      if (c == 0) p3e[row] = ex;
-    }
+    for (int cc = 0; cc < RT * 16; ++cc) amax = fmaxf(amax, fabsf(S[threadIdx.x * SP + cc]));
+    sexp[threadIdx.x] = fp16_row_exponent(amax);
   }
+  __syncthreads();
+  GLOBAL uint16_t* __restrict__ p3h = gbl(d.p3_hi);
+  GLOBAL uint16_t* __restrict__ p3l = gbl(d.p3_lo);
+  GLOBAL int32_t* __restrict__ p3e = gbl(d.p3_exp);
+  constexpr int U8 = RT * 2;                         // 8-column units per row (rpad / 8)
+  for (int idx = threadIdx.x; idx < GSA_ROWS * U8; idx += GS_THREADS) {
+    const int rr = idx / U8, c8 = (idx % U8) * 8;
+    if (row0 + rr >= m) continue;
+    const int ex = sexp[rr];
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x0 = ldexpf(S[rr * SP + c8 + 2 * e], ex), x1 = ldexpf(S[rr * SP + c8 + 2 * e + 1], ex);
+      const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+      h[e] = f16_bits(h0) | ((uint32_t)f16_bits(h1) << 16);
+      l[e] = f16_bits((_Float16)(x0 - (float)h0)) | ((uint32_t)f16_bits((_Float16)(x1 - (float)h1)) << 16);
+    }
+    *gcast<u32x4>(p3h + (int64_t)(row0 + rr) * kpad3 + c8) = u32x4{h[0], h[1], h[2], h[3]};
+    *gcast<u32x4>(p3l + (int64_t)(row0 + rr) * kpad3 + c8) = u32x4{l[0], l[1], l[2], l[3]};
+  }
+  if (threadIdx.x < GSA_ROWS && row0 + (int)threadIdx.x < m) p3e[row0 + threadIdx.x] = sexp[threadIdx.x];
 }
 
 }  // namespace
@@ -256,7 +293,7 @@ hipError_t launch_gs_gram(int rt, const DevMat* mats, const Work* work, int n_wo
 
 hipError_t launch_gs_factor(const DevMat* mats, const Work* work, int n_work, hipStream_t s) {
   if (n_work <= 0) return hipSuccess;
-  k_gs_factor<<<dim3(n_work), dim3(GS_THREADS), 0, s>>>(mats, work);
+  k_gs_factor<<<dim3(n_work), dim3(GSF_THREADS), 0, s>>>(mats, work);
   return hipGetLastError();
 }
 
@@ -272,6 +309,6 @@ hipError_t launch_gs_apply(int rt, const DevMat* mats, const Work* work, int n_w
   return hipGetLastError();
 }
 
-int gs_apply_rows_per_block() { return (GS_THREADS / kWave) * 16; }
+int gs_apply_rows_per_block() { return GSA_ROWS; }
 
 }  // namespace psgd

@@ -21,30 +21,23 @@ namespace psgd {
 namespace {
 
 #ifndef K2_W
-#define K2_W 4       // waves per workgroup, 64 columns each
+#define K2_W 4       // waves per workgroup
 #endif
-constexpr int LDS_K = 40;
-
-// 4 consecutive gradient elements of one row, loaded through a buffer descriptor.
-template <int GT> struct Raw4;
-template <> struct Raw4<G_F16> {
-  u32x2 v;
-  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { v = bload8(r, off); }
-  __device__ __forceinline__ f32x4 f32() const { return __builtin_convertvector(__builtin_bit_cast(f16x4, v), f32x4); }
-};
-template <> struct Raw4<G_BF16> {
-  u32x2 v;
-  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { v = bload8(r, off); }
-  __device__ __forceinline__ f32x4 f32() const { return __builtin_convertvector(__builtin_bit_cast(bf16x4, v), f32x4); }
-};
-template <> struct Raw4<G_F32> {
-  u32x4 v;
-  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { v = bload16(r, off); }
-  __device__ __forceinline__ f32x4 f32() const { return __builtin_bit_cast(f32x4, v); }
-};
+#ifndef K2_TC
+#define K2_TC 4      // consecutive columns per lane = column tiles per wave (2 or 4)
+#endif
+#ifndef K2_OCC
+#define K2_OCC 1     // workgroups per CU the register budget is sized for
+#endif
+constexpr int LDS_K = 32;                 // LDS row = 32 bf16 = 4 16-byte units, XOR-swizzled
+// Physical unit of logical unit q in row rr: 16 lanes reading 16 consecutive rows (one unit
+// each) or writing 4 rows (4 units each) hit 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz2(int rr, int q) { return q ^ ((rr >> 2) & 3); }
+constexpr int TC = K2_TC;
+constexpr int WCOLS = 16 * TC;            // columns per wave
 
 template <int GT, int RTC>
-__global__ __launch_bounds__(K2_W * kWave)
+__global__ __launch_bounds__(K2_W * kWave, K2_OCC)
 void k_mtp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
            const float* __restrict__ scale)
 {
@@ -63,8 +56,8 @@ void k_mtp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
   const int c = lane & 15, g = lane >> 4;
-  const int colbase = wi.a + wv * 64 + 4 * c;
-  const bool colok = colbase < n;              // n % 8 == 0: 4-column groups are all in or out
+  const int colbase = wi.a + wv * WCOLS + TC * c;
+  const bool colok = colbase < n;              // n % 8 == 0: TC-column groups are all in or out
   const int rc0 = wi.b * RTC * 16;
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][RTC * 16][LDS_K];
@@ -74,6 +67,7 @@ void k_mtp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   constexpr int THREADS = K2_W * kWave;
   constexpr int UPT = (UNITS + THREADS - 1) / THREADS;
   u32x4 stage[UPT];
+  // consecutive threads take consecutive units of a row; threads past the last unit repeat it
   auto unit = [&](int j, int& arr, int& rr, int& q4) {
     int u = threadIdx.x + j * THREADS;
     u = u < UNITS ? u : UNITS - 1;
@@ -95,47 +89,48 @@ void k_mtp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
     for (int j = 0; j < UPT; ++j) {
       int arr, rr, q4;
       unit(j, arr, rr, q4);
-      *reinterpret_cast<u32x4*>(&lds[buf][arr][rr][8 * q4]) = stage[j];
+      *reinterpret_cast<u32x4*>(&lds[buf][arr][rr][8 * swz2(rr, q4)]) = stage[j];
     }
   };
 
-  // 8 rows k0 + 8g + kk, 4 columns colbase..colbase+3; out-of-range reads give zeros.
-  struct Frag { Raw4<GT> gr[8]; u32x4 er[8]; };
+  // 8 rows k0 + 8g + kk, TC columns colbase..; out-of-range reads give zeros.
+  struct Frag { GradVec<GT, TC> gr[8]; GradVec<G_F32, TC> er[8]; };
   auto load_m = [&](int k0, Frag& f) {
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const int row = k0 + 8 * g + kk;
       const bool ok = colok && row < m;
       f.gr[kk].load(rg, ok ? (uint32_t)(row * ldg + colbase) * GB : kOOB);
-      f.er[kk] = bload16(re, ok ? (uint32_t)(row * lde + colbase) * 4u : kOOB);
+      f.er[kk].load(re, ok ? (uint32_t)(row * lde + colbase) * 4u : kOOB);
     }
   };
 
-  f32x4 acc[RTC][4];
+  f32x4 acc[RTC][TC];
 #pragma unroll
   for (int i = 0; i < RTC; ++i)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[i][t] = f32x4{0, 0, 0, 0};
+    for (int t = 0; t < TC; ++t) acc[i][t] = f32x4{0, 0, 0, 0};
 
   auto compute = [&](int buf, const Frag& f) {
     // B-fragments: tile t takes column t of every loaded row (k = 8g + kk).
-    f32x8 mt[4];
+    f32x8 mt[TC];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const f32x4 gf = f.gr[kk].f32();
-      const f32x4 ef = __builtin_bit_cast(f32x4, f.er[kk]);
+      const auto gf = f.gr[kk].f32();
+      const auto ef = f.er[kk].f32();
 #pragma unroll
-      for (int t = 0; t < 4; ++t) mt[t][kk] = __builtin_fmaf(s, gf[t], ef[t]);
+      for (int t = 0; t < TC; ++t) mt[t][kk] = __builtin_fmaf(s, gf[t], ef[t]);
     }
-    bf16x8 bh[4], bl[4];
+    bf16x8 bh[TC], bl[TC];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) split_bf16(mt[t], bh[t], bl[t]);
+    for (int t = 0; t < TC; ++t) split_bf16(mt[t], bh[t], bl[t]);
 #pragma unroll
     for (int i = 0; i < RTC; ++i) {
-      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&lds[buf][0][i * 16 + c][8 * g]);
-      const bf16x8 al = *reinterpret_cast<const bf16x8*>(&lds[buf][1][i * 16 + c][8 * g]);
+      const int pq = 8 * swz2(i * 16 + c, g);
+      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&lds[buf][0][i * 16 + c][pq]);
+      const bf16x8 al = *reinterpret_cast<const bf16x8*>(&lds[buf][1][i * 16 + c][pq]);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < TC; ++t) {
         acc[i][t] = mfma_bf16(ah, bh[t], acc[i][t]);
         acc[i][t] = mfma_bf16(ah, bl[t], acc[i][t]);
         acc[i][t] = mfma_bf16(al, bh[t], acc[i][t]);
@@ -163,16 +158,16 @@ void k_mtp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
 
   // Output tile (i, t): lane holds Q'^T rows rc0 + 16i + 4g + {0..3}, i.e. Q'[colbase + t][..].
   GLOBAL float* __restrict__ qn = gbl(d.q_next);
-  const bool full = (wi.a + wv * 64 + 64 <= n) && (r & 3) == 0 && rc0 + RTC * 16 <= r;
+  const bool full = (wi.a + wv * WCOLS + WCOLS <= n) && (r & 3) == 0 && rc0 + RTC * 16 <= r;
   if (full) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < TC; ++t)
 #pragma unroll
       for (int i = 0; i < RTC; ++i)
         *gcast<f32x4>(qn + (int64_t)(colbase + t) * r + rc0 + i * 16 + 4 * g) = acc[i][t];
   } else if (colok) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < TC; ++t)
 #pragma unroll
       for (int i = 0; i < RTC; ++i) {
         const int rr = rc0 + i * 16 + 4 * g;
@@ -190,7 +185,7 @@ void k_mtp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   GLOBAL uint16_t* __restrict__ q3l = gbl(d.q3_lo);
   GLOBAL int32_t* __restrict__ q3e = gbl(d.q3_exp);
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < TC; ++t) {
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < RTC; ++i)
@@ -233,7 +228,7 @@ hipError_t launch_gt(int rtc, dim3 grid, dim3 block, hipStream_t s, const DevMat
 
 }  // namespace
 
-int mtp_cols_per_block() { return K2_W * 64; }
+int mtp_cols_per_block() { return K2_W * WCOLS; }
 
 hipError_t launch_mtp(int gt, int rtc, const DevMat* mats, const Work* work, int n_work,
                       const float* scale, hipStream_t s) {
