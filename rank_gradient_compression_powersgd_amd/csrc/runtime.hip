@@ -4,6 +4,7 @@
 #include <cstdio>
 #include <cstring>
 #include <memory>
+#include <algorithm>
 #include <new>
 #include <string>
 #include <vector>
@@ -217,10 +218,33 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
 
   // ---- work lists -------------------------------------------------------------------------
   std::vector<Work> all;
+  std::vector<int64_t> cost;   // bytes one item streams (same index as `all`)
   auto begin_kind = [&](int k) { p->off[k] = (int)all.size(); };
-  auto end_kind = [&](int k, bool pad8) {
+  // Padded lists are launched with xcd_remap: XCD x walks the x-th eighth of the list in order.
+  // For the two long-running product kernels, whose items differ in length by up to 2.7x, the
+  // items within each eighth are sorted by decreasing cost (stable, so the blocks of one
+  // matrix stay together and share its factor in that XCD's L2): the longest items start first
+  // and the short ones fill the tail (longest-processing-time-first list scheduling).
+  auto end_kind = [&](int k, bool pad8, bool sort = false) {
     if (pad8) while ((all.size() - p->off[k]) % psgd::kXcds) all.push_back(Work{-1, 0, 0, 0});
     p->cnt[k] = (int)all.size() - p->off[k];
+    cost.resize(all.size(), 0);
+    if (!sort) return;
+    const int per = p->cnt[k] / psgd::kXcds;
+    std::vector<int> idx(per);
+    std::vector<Work> tmp(per);
+    for (int x = 0; x < psgd::kXcds; ++x) {
+      const int b = p->off[k] + x * per;
+      for (int j = 0; j < per; ++j) idx[j] = b + j;
+      std::stable_sort(idx.begin(), idx.end(), [&](int u, int v) { return cost[u] > cost[v]; });
+      for (int j = 0; j < per; ++j) tmp[j] = all[idx[j]];
+      for (int j = 0; j < per; ++j) all[b + j] = tmp[j];
+    }
+  };
+  auto push = [&](Work w, int64_t c) {
+    all.push_back(w);
+    cost.resize(all.size(), 0);
+    cost.back() = c;
   };
   const int k1rows = psgd::ef_mq_rows_per_block();
   const int k2cols = psgd::mtp_cols_per_block();
@@ -234,28 +258,32 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
   begin_kind(W_K1);
   for (int i = 0; i < n_mats; ++i)
     for (int ch = 0; ch < p->chunks; ++ch)
-      for (int r0 = 0; r0 < p->mats[i].m; r0 += k1rows) all.push_back(Work{i, r0, ch, 0});
-  end_kind(W_K1, true);
+      for (int r0 = 0; r0 < p->mats[i].m; r0 += k1rows)
+        push(Work{i, r0, ch, 0}, (int64_t)std::min(k1rows, p->mats[i].m - r0) * p->mats[i].n);
+  end_kind(W_K1, true, true);
   begin_kind(W_GRAM);
   for (int i = 0; i < n_mats; ++i)
-    for (int pt = 0; pt < p->mats[i].gram_parts; ++pt) all.push_back(Work{i, pt * psgd::kGramRows, pt, 0});
+    for (int pt = 0; pt < p->mats[i].gram_parts; ++pt)
+      push(Work{i, pt * psgd::kGramRows, pt, 0}, std::min(psgd::kGramRows, p->mats[i].m - pt * psgd::kGramRows));
   end_kind(W_GRAM, true);
   begin_kind(W_FACTOR);
   for (int i = 0; i < n_mats; ++i) all.push_back(Work{i, 0, 0, 0});
   end_kind(W_FACTOR, false);
   begin_kind(W_APPLY);
   for (int i = 0; i < n_mats; ++i)
-    for (int r0 = 0; r0 < p->mats[i].m; r0 += aprows) all.push_back(Work{i, r0, 0, 0});
+    for (int r0 = 0; r0 < p->mats[i].m; r0 += aprows) push(Work{i, r0, 0, 0}, std::min(aprows, p->mats[i].m - r0));
   end_kind(W_APPLY, true);
   begin_kind(W_K2);
   for (int i = 0; i < n_mats; ++i)
     for (int ch = 0; ch < p->chunks; ++ch)
-      for (int c0 = 0; c0 < p->mats[i].n; c0 += k2cols) all.push_back(Work{i, c0, ch, 0});
-  end_kind(W_K2, true);
+      for (int c0 = 0; c0 < p->mats[i].n; c0 += k2cols)
+        push(Work{i, c0, ch, 0}, (int64_t)std::min(k2cols, p->mats[i].n - c0) * p->mats[i].m);
+  end_kind(W_K2, true, true);
   begin_kind(W_K3);
   for (int i = 0; i < n_mats; ++i)
     for (int m0 = 0; m0 < p->mats[i].m; m0 += tm)
-      for (int n0 = 0; n0 < p->mats[i].n; n0 += tn) all.push_back(Work{i, m0, n0, 0});
+      for (int n0 = 0; n0 < p->mats[i].n; n0 += tn)
+        push(Work{i, m0, n0, 0}, (int64_t)std::min(tm, p->mats[i].m - m0) * std::min(tn, p->mats[i].n - n0));
   end_kind(W_K3, true);
   begin_kind(W_COMMIT);
   for (int i = 0; i < n_mats; ++i) {
