@@ -80,11 +80,12 @@ class Hip:
     def record(self, ev: int, stream: int):
         assert self.lib.hipEventRecord(ev, stream) == 0
 
-    def elapsed_ms(self, a: int, b: int) -> float:
+    def elapsed_ms(self, a: int, b: int):
+        """Milliseconds between two recorded events; None when either was never recorded (a
+        profiling slot whose kernel the step did not launch)."""
         ms = ctypes.c_float()
         err = self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b)
-        assert err == 0, err
-        return float(ms.value)
+        return float(ms.value) if err == 0 else None
 
     def destroy(self, ev: int):
         self.lib.hipEventDestroy(ev)
@@ -190,7 +191,8 @@ def main(argv=None) -> int:
     kern = {}
     for j, name in enumerate(psgd.PROFILE_SLOTS):
         vals = [hip.elapsed_ms(kev[k][2 * j], kev[k][2 * j + 1]) for k in range(K)]
-        kern[name] = statistics.mean(vals)
+        if all(v is not None for v in vals):
+            kern[name] = statistics.mean(vals)
     for evs in kev:
         for e in evs:
             hip.destroy(e)

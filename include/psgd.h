@@ -55,7 +55,7 @@ typedef enum psgd_status {
   PSGD_EDTYPE = 2,        /* unknown gradient dtype */
   PSGD_ENOMEM = 3,        /* workspace allocation failed */
   PSGD_EHIP = 4,          /* a HIP runtime call or kernel launch failed */
-  PSGD_EUNSUPPORTED = 5   /* valid request this build does not implement (rank above 128) */
+  PSGD_EUNSUPPORTED = 5   /* valid request this build does not implement (rank above 1024) */
 } psgd_status;
 
 typedef enum psgd_dtype {
@@ -105,8 +105,10 @@ typedef struct psgd_plan psgd_plan;
 /* Library ABI version (PSGD_ABI_VERSION). */
 int psgd_version(void);
 
-/* Create a context on HIP device `device` for compression rank `rank` (1..128 in this build).
- * Writes *ctx; on failure *ctx is NULL. */
+/* Create a context on HIP device `device` for compression rank `rank` (1..1024). Ranks above
+ * 128 are processed in rank chunks of at most 128 columns by the two products (each chunk
+ * re-reads the gradient and error buffer) and orthonormalised blockwise.
+ * Writes *ctx; on failure *ctx is NULL (rank above 1024: PSGD_EUNSUPPORTED). */
 psgd_status psgd_create(psgd_ctx** ctx, int device, int rank);
 
 /* Destroy a context. Plans created on it must be destroyed first. NULL is accepted. */
@@ -168,7 +170,10 @@ psgd_status psgd_decompress_update(psgd_ctx* ctx, psgd_plan* plan, const float* 
  * events[2k] (before) and events[2k+1] (after) on the call's stream; elapsed times between the
  * pair give that kernel's duration. Slots: 0 flag clear, 1 warm-start operand, 2 M Q with
  * error feedback, 3 Gram partials, 4 Gram-Schmidt, 5 orthonormal P, 6 M^T P, 7 skip clear,
- * 8 finite check, 9 decompression + error update, 10 q commit. n must be at least 22.
+ * 8 finite check, 9 decompression + error update, 10 q commit, 11 Gram sum (rank > 128 only),
+ * 12 decompression operands (rank > 128 only), 13 second orthonormalisation pass (all four of
+ * its launches; they return at once for matrices whose first pass was well conditioned).
+ * Slots a call does not launch keep their events unrecorded. n must be at least 28.
  * events == NULL (n ignored) removes the hook. The events stay owned by the caller.
  */
 psgd_status psgd_profile_events(psgd_ctx* ctx, hipEvent_t* events, int n);
@@ -179,8 +184,10 @@ const char* psgd_last_error(const psgd_ctx* ctx);
 /*
  * Diagnostics for tests: device address and byte size of an internal per-matrix buffer of a
  * plan. which: 0 = raw factor M q (m x rpad fp32, before orthonormalisation),
- * 1 = orthonormalising coefficient matrix T (rpad x rpad fp64, upper triangular, P = (M q) T).
- * *rpad receives the padded rank (r rounded up to 16).
+ * 1 = orthonormalising coefficient matrix T of the last pass (rpad x rpad fp64, upper
+ * triangular; P = (M q) T after one pass, P = ((M q) T1) T after two).
+ * *rpad receives the padded rank: a multiple of 16 that is at least r (ranks above 128 are padded
+ * to whole rank chunks).
  */
 psgd_status psgd_debug_buffer(psgd_plan* plan, int which, int mat, void** ptr, int64_t* bytes,
                               int32_t* rpad);

@@ -8,7 +8,7 @@
 // reductions are done once, as the Gram matrix W = P^T P, and the Gram-Schmidt recurrence runs
 // on the small r x r side:
 //
-//   gs_gram    W = P^T P per 256-row block, v_mfma_f64_16x16x4 (products of fp32 values are
+//   gs_gram    W = P^T P per block of rows, v_mfma_f64_16x16x4 (products of fp32 values are
 //              exact in fp64); partial sums are added later in a fixed order (deterministic).
 //   gs_factor  modified Gram-Schmidt carried out on coefficient vectors. Column j of the
 //              result is P t_j. The inner products <q_i, v_j> and the norms ||v_j|| are read
@@ -17,9 +17,24 @@
 //              QR. fp64, one workgroup per matrix, W and T resident in LDS.
 //              A column whose remaining squared norm is at most 2^-40 of its original squared
 //              norm (or zero, or not finite) is dependent: its column of T is set to zero.
+//   second pass The Gram form loses orthogonality as eps_64 times the squared condition
+//              number of M q. gs_factor records whether some kept column retained less than
+//              2^-20 of its squared norm; for such a matrix gs_apply stores the first result
+//              in p2 instead of the outputs, and gram/factor/apply run again on p2 (the product
+//              of the two triangular factors is again the thin-QR factor, so the result is the
+//              same P). Matrices that need no second pass leave those launches at once.
 //   gs_apply   P_hat = P T with fp64 MFMA accumulation, then the stores the products need:
 //              P_hat in fp32 (caller's p), P_hat^T split bf16 hi/lo for K2, and P_hat rows
 //              scaled by a power of two and split fp16 hi/lo for the decompression kernel.
+//
+// Ranks above 128 (r x r no longer fits in LDS) take the blocked form of the same recurrence,
+// on 128-column blocks: the Gram matrix is formed block pair by block pair and summed
+// (gs_reduce); gs_factor_blk then walks the diagonal blocks. Each diagonal block is factored
+// in LDS by the same column recurrence (giving T_kk = R_kk^-1), the block row of R to its right
+// is R_kj = T_kk^T W_kj, and the trailing Gram blocks lose R_ki^T R_kj (a right-looking blocked
+// Cholesky factorisation W = R^T R). The off-diagonal blocks of T = R^-1 follow from
+// T_ij = -T_ii (sum_{i<k<=j} R_ik T_kj). gs_apply forms P_hat by 128-column blocks and
+// split3 builds the scaled fp16 operands of the decompression from the fp32 factors.
 #include "psgd_internal.h"
 
 namespace psgd {
@@ -30,19 +45,27 @@ constexpr int GS_THREADS = 256;
 // ------------------------------------------------------------------------------------------
 // Gram partials
 // ------------------------------------------------------------------------------------------
-template <int RT>
+// One work item: rows [a, a + gram_rows) of one matrix, partial index b. Small ranks (FULL =
+// false) form the upper-triangular tile pairs of the whole rpad x rpad Gram matrix. Large ranks
+// (FULL = true, RT = 8) form the full 128 x 128 block (bi, bj) packed in c = bi | bj << 16.
+template <int RT, bool FULL>
 __global__ __launch_bounds__(GS_THREADS)
-void k_gs_gram(const DevMat* __restrict__ mats, const Work* __restrict__ work)
+void k_gs_gram(const DevMat* __restrict__ mats, const Work* __restrict__ work, int pass)
 {
   const Work wi = work[xcd_remap(blockIdx.x, gridDim.x)];
   if (wi.mat < 0) return;
   const DevMat& d = mats[wi.mat];
-  const int m = d.m, rpad = d.rpad;
-  const GLOBAL float* __restrict__ P = gbl(d.p_raw);
+  if (pass && *d.reorth == 0) return;
+  const int m = d.m, rpad = d.rpad, rows = d.gram_rows;
+  const int ci0 = FULL ? (wi.c & 0xffff) * kBlk : 0;
+  const int cj0 = FULL ? (wi.c >> 16) * kBlk : 0;
+  const int nti = FULL ? min(RT, (rpad - ci0) / 16) : RT;    // tiles present in each block
+  const int ntj = FULL ? min(RT, (rpad - cj0) / 16) : RT;
+  const GLOBAL float* __restrict__ P = gbl(pass ? d.p2 : d.p_raw);
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
   const int c = lane & 15, g = lane >> 4;
-  constexpr int NP = RT * (RT + 1) / 2;
+  constexpr int NP = FULL ? RT * RT : RT * (RT + 1) / 2;
   constexpr int NW = GS_THREADS / kWave;
   constexpr int PPW = (NP + NW - 1) / NW;
 
@@ -52,28 +75,41 @@ void k_gs_gram(const DevMat* __restrict__ mats, const Work* __restrict__ work)
 
   const int row0 = wi.a;
   constexpr int KB = 4;                      // k steps (of 4 rows) whose loads are batched
-  for (int ks = 0; ks < kGramRows / 4; ks += KB) {
-    float v[KB][RT];
+  for (int ks = 0; ks < rows / 4; ks += KB) {
+    float vi[KB][RT], vj[FULL ? KB : 1][RT];
 #pragma unroll
     for (int b = 0; b < KB; ++b) {
       const int row = row0 + 4 * (ks + b) + g;
       const int rr = row < m ? row : 0;
 #pragma unroll
-      for (int t = 0; t < RT; ++t) v[b][t] = P[(int64_t)rr * rpad + t * 16 + c];
+      for (int t = 0; t < RT; ++t) {
+        const int ti = t < nti ? t : 0;
+        vi[b][t] = P[(int64_t)rr * rpad + ci0 + ti * 16 + c];
+        if constexpr (FULL) {
+          const int tj = t < ntj ? t : 0;
+          vj[b][t] = P[(int64_t)rr * rpad + cj0 + tj * 16 + c];
+        }
+      }
       if (row >= m) {
 #pragma unroll
-        for (int t = 0; t < RT; ++t) v[b][t] = 0.0f;
+        for (int t = 0; t < RT; ++t) {
+          vi[b][t] = 0.0f;
+          if constexpr (FULL) vj[b][t] = 0.0f;
+        }
       }
     }
-    // lane supplies A[c][g] = P[row][ti*16 + c] and B[g][c] = P[row][tj*16 + c]
+    // lane supplies A[c][g] = P[row][ci0 + ti*16 + c] and B[g][c] = P[row][cj0 + tj*16 + c]
 #pragma unroll
     for (int b = 0; b < KB; ++b) {
       int p = 0;
 #pragma unroll
       for (int ti = 0; ti < RT; ++ti)
 #pragma unroll
-        for (int tj = ti; tj < RT; ++tj, ++p)
-          if (p % NW == wv) acc[p / NW] = mfma_f64((double)v[b][ti], (double)v[b][tj], acc[p / NW]);
+        for (int tj = FULL ? 0 : ti; tj < RT; ++tj, ++p)
+          if (p % NW == wv) {
+            const float bv = FULL ? vj[FULL ? b : 0][tj] : vi[b][tj];
+            acc[p / NW] = mfma_f64((double)vi[b][ti], (double)bv, acc[p / NW]);
+          }
     }
   }
 
@@ -83,31 +119,88 @@ void k_gs_gram(const DevMat* __restrict__ mats, const Work* __restrict__ work)
 #pragma unroll
   for (int ti = 0; ti < RT; ++ti)
 #pragma unroll
-    for (int tj = ti; tj < RT; ++tj, ++p)
-      if (p % NW == wv) {
+    for (int tj = FULL ? 0 : ti; tj < RT; ++tj, ++p)
+      if (p % NW == wv && ti < nti && tj < ntj) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          out[(int64_t)(ti * 16 + g + 4 * i) * rpad + tj * 16 + c] = acc[p / NW][i];
+          out[(int64_t)(ci0 + ti * 16 + g + 4 * i) * rpad + cj0 + tj * 16 + c] = acc[p / NW][i];
       }
 }
 
+// W = sum of the Gram partials in part order (large ranks). One work item: 4096 consecutive
+// elements of the rpad x rpad matrix starting at a * 4096. Elements of blocks below the
+// diagonal were never written and sum to zero.
+__global__ __launch_bounds__(256)
+void k_gs_reduce(const DevMat* __restrict__ mats, const Work* __restrict__ work, int pass)
+{
+  const Work wi = work[blockIdx.x];
+  if (wi.mat < 0) return;
+  const DevMat& d = mats[wi.mat];
+  if (pass && *d.reorth == 0) return;
+  const int64_t tot = (int64_t)d.rpad * d.rpad;
+  const int parts = d.gram_parts;
+  const GLOBAL double* __restrict__ gram = gbl(d.gram);
+  GLOBAL double* __restrict__ wsum = gbl(d.wsum);
+  for (int64_t e = (int64_t)wi.a * 4096 + threadIdx.x; e < tot && e < (int64_t)(wi.a + 1) * 4096; e += 256) {
+    double sum = 0.0;
+    for (int pt = 0; pt < parts; ++pt) sum += gram[(int64_t)pt * tot + e];
+    wsum[e] = sum;
+  }
+}
+
 // ------------------------------------------------------------------------------------------
-// Gram-Schmidt on the Gram matrix (rpad <= 128)
+// Gram-Schmidt on a Gram matrix block resident in LDS (block size <= 128)
 // ------------------------------------------------------------------------------------------
-constexpr int kPackMax = 128 * 129 / 2;
+constexpr int kPackMax = kBlk * (kBlk + 1) / 2;
+constexpr int GSF_THREADS = 1024;     // 32 x 32 thread grid over the r x r problem
 
 __device__ __forceinline__ int pidx(int i, int j, int rp) {   // packed upper, i <= j
   return i * rp - (i * (i - 1)) / 2 + (j - i);
 }
 
-constexpr int GSF_THREADS = 1024;     // 32 x 32 thread grid over the r x r problem
+// Column recurrence on packed W (bs x bs, updated in place) and T (packed, initialised to I):
+// on return P T has orthonormal columns when W = P^T P; dependent columns of T are zero.
+// diag0[j] is column j's squared norm before any projection. All GSF_THREADS threads call it
+// and all return the smallest squared residual ratio of a kept column (1 if none is kept).
+__device__ double factor_block(double* W, double* T, const double* diag0, double* rrow, int bs)
+{
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  double minratio = 1.0;
+  for (int j = 0; j < bs; ++j) {
+    const double dj = W[pidx(j, j, bs)];
+    const double d0 = diag0[j];
+    const bool ok = (d0 > 0.0) && (dj > kDegenerate * d0) && (dj <= 1.0e300);
+    const double inv = ok ? 1.0 / sqrt(dj) : 0.0;
+    if (ok) minratio = fmin(minratio, dj / d0);
+    // r_jk = <q_j, v_k> = W[j][k] / ||v_j||; t_j = u_j / ||v_j||
+    const int k1 = j + 1 + (int)threadIdx.x;
+    if (k1 < bs) rrow[k1] = W[pidx(j, k1, bs)] * inv;
+    if ((int)threadIdx.x <= j) T[pidx(threadIdx.x, j, bs)] *= inv;
+    __syncthreads();
+    // v_k -= r_jk q_j for k > j: Gram update and coefficient update
+    for (int k = j + 1 + ty; k < bs; k += 32) {
+      const int base = k * bs - (k * (k - 1)) / 2 - k;
+      const double rk = rrow[k];
+      for (int l = k + ((tx - (k - j - 1)) & 31); l < bs; l += 32) W[base + l] -= rk * rrow[l];
+    }
+    for (int i = ty; i <= j; i += 32) {
+      const int base = i * bs - (i * (i - 1)) / 2 - i;
+      const double tij = T[base + j];
+      for (int k = j + 1 + tx; k < bs; k += 32) T[base + k] -= rrow[k] * tij;
+    }
+    __syncthreads();
+  }
+  return minratio;
+}
 
+// Ranks up to 128: W summed from the partials straight into LDS.
 __global__ __launch_bounds__(GSF_THREADS)
-void k_gs_factor(const DevMat* __restrict__ mats, const Work* __restrict__ work)
+void k_gs_factor(const DevMat* __restrict__ mats, const Work* __restrict__ work, int pass)
 {
   const Work wi = work[blockIdx.x];
   if (wi.mat < 0) return;
   const DevMat& d = mats[wi.mat];
+  if (pass && *d.reorth == 0) return;
   const int rp = d.rpad;
   const int parts = d.gram_parts;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
@@ -116,8 +209,8 @@ void k_gs_factor(const DevMat* __restrict__ mats, const Work* __restrict__ work)
 
   __shared__ double W[kPackMax];
   __shared__ double T[kPackMax];
-  __shared__ double diag0[128];
-  __shared__ double rrow[128];
+  __shared__ double diag0[kBlk];
+  __shared__ double rrow[kBlk];
 
   // W = sum of the partial Gram matrices in part order; T = I.
   for (int i = ty; i < rp; i += 32) {
@@ -133,34 +226,144 @@ void k_gs_factor(const DevMat* __restrict__ mats, const Work* __restrict__ work)
   if (threadIdx.x < rp) diag0[threadIdx.x] = W[pidx(threadIdx.x, threadIdx.x, rp)];
   __syncthreads();
 
-  for (int j = 0; j < rp; ++j) {
-    const double dj = W[pidx(j, j, rp)];
-    const double d0 = diag0[j];
-    const bool ok = (d0 > 0.0) && (dj > kDegenerate * d0) && (dj <= 1.0e300);
-    const double inv = ok ? 1.0 / sqrt(dj) : 0.0;
-    // r_jk = <q_j, v_k> = W[j][k] / ||v_j||; t_j = u_j / ||v_j||
-    const int k1 = j + 1 + (int)threadIdx.x;
-    if (k1 < rp) rrow[k1] = W[pidx(j, k1, rp)] * inv;
-    if ((int)threadIdx.x <= j) T[pidx(threadIdx.x, j, rp)] *= inv;
-    __syncthreads();
-    // v_k -= r_jk q_j for k > j: Gram update and coefficient update
-    for (int k = j + 1 + ty; k < rp; k += 32) {
-      const int base = k * rp - (k * (k - 1)) / 2 - k;
-      const double rk = rrow[k];
-      for (int l = k + ((tx - (k - j - 1)) & 31); l < rp; l += 32) W[base + l] -= rk * rrow[l];
-    }
-    for (int i = ty; i <= j; i += 32) {
-      const int base = i * rp - (i * (i - 1)) / 2 - i;
-      const double tij = T[base + j];
-      for (int k = j + 1 + tx; k < rp; k += 32) T[base + k] -= rrow[k] * tij;
-    }
-    __syncthreads();
-  }
+  const double minratio = factor_block(W, T, diag0, rrow, rp);
+  if (pass == 0 && threadIdx.x == 0) *gbl(d.reorth) = minratio < kReorth ? 1 : 0;
 
   for (int i = ty; i < rp; i += 32) {
     const int base = i * rp - (i * (i - 1)) / 2 - i;
     for (int j = tx; j < rp; j += 32) tmat[(int64_t)i * rp + j] = (j >= i) ? T[base + j] : 0.0;
   }
+}
+
+// C (bi x bj, ld) = alpha * op(A) op(B) (+ C when accumulate), with op(A) bi x bk and op(B)
+// bk x bj, all fp64 in global memory (leading dimension ld). transA: A is stored bk x bi and
+// op(A) = A^T. transB likewise. Blocks are at most 128 x 128; GSF_THREADS threads, each
+// owning a 4 x 4 piece of C; 16-deep k slices staged in LDS (As, Bs: 16 x 128 each). Every
+// thread reads all of A and B before any thread writes C, so C may alias A or B.
+__device__ void block_gemm(GLOBAL double* C, const GLOBAL double* A, bool transA,
+                           const GLOBAL double* B, bool transB, int ld, int bi, int bj, int bk,
+                           double alpha, bool accumulate, double* As, double* Bs)
+{
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  double acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+  for (int k0 = 0; k0 < bk; k0 += 16) {
+    for (int e = threadIdx.x; e < 16 * kBlk; e += GSF_THREADS) {
+      const int kk = e / kBlk, ii = e % kBlk, k = k0 + kk;
+      double av = 0.0, bv = 0.0;
+      if (k < bk && ii < bi) av = transA ? A[(int64_t)k * ld + ii] : A[(int64_t)ii * ld + k];
+      if (k < bk && ii < bj) bv = transB ? B[(int64_t)ii * ld + k] : B[(int64_t)k * ld + ii];
+      As[kk * kBlk + ii] = av;
+      Bs[kk * kBlk + ii] = bv;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int kk = 0; kk < 16; ++kk) {
+      double av[4], bv[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) av[a] = As[kk * kBlk + 4 * ty + a];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) bv[b] = Bs[kk * kBlk + 4 * tx + b];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = fma(av[a], bv[b], acc[a][b]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int i = 4 * ty + a, j = 4 * tx + b;
+      if (i < bi && j < bj) {
+        GLOBAL double* cp = C + (int64_t)i * ld + j;
+        *cp = alpha * acc[a][b] + (accumulate ? *cp : 0.0);
+      }
+    }
+  __syncthreads();
+}
+
+// Ranks above 128: blocked factorisation of the summed Gram matrix (see the file comment).
+// One workgroup per matrix. wsum's upper blocks are overwritten by R's off-diagonal blocks; the
+// first 128 x 128 doubles of the (no longer needed) partial buffer serve as scratch.
+__global__ __launch_bounds__(GSF_THREADS)
+void k_gs_factor_blk(const DevMat* __restrict__ mats, const Work* __restrict__ work, int pass)
+{
+  const Work wi = work[blockIdx.x];
+  if (wi.mat < 0) return;
+  const DevMat& d = mats[wi.mat];
+  if (pass && *d.reorth == 0) return;
+  const int rp = d.rpad;
+  const int nb = (rp + kBlk - 1) / kBlk;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  GLOBAL double* __restrict__ W = gbl(d.wsum);
+  GLOBAL double* __restrict__ Tg = gbl(d.tmat);
+  GLOBAL double* __restrict__ S = gbl(d.gram);
+
+  __shared__ double lW[kPackMax];          // packed diagonal block; staging of block_gemm
+  __shared__ double lT[kPackMax];
+  __shared__ double diag0[kMaxRank];
+  __shared__ double rrow[kBlk];
+
+  for (int i = threadIdx.x; i < rp; i += GSF_THREADS) diag0[i] = W[(int64_t)i * rp + i];
+  __syncthreads();
+
+  double minratio = 1.0;
+  for (int kb = 0; kb < nb; ++kb) {
+    const int k0 = kb * kBlk, bs = min(kBlk, rp - k0);
+    // diagonal block in LDS
+    for (int i = ty; i < bs; i += 32) {
+      const int base = i * bs - (i * (i - 1)) / 2 - i;
+      for (int j = i + tx; j < bs; j += 32) {
+        lW[base + j] = W[(int64_t)(k0 + i) * rp + k0 + j];
+        lT[base + j] = (i == j) ? 1.0 : 0.0;
+      }
+    }
+    __syncthreads();
+    minratio = fmin(minratio, factor_block(lW, lT, diag0 + k0, rrow, bs));
+    for (int i = ty; i < bs; i += 32) {
+      const int base = i * bs - (i * (i - 1)) / 2 - i;
+      for (int j = tx; j < bs; j += 32) Tg[(int64_t)(k0 + i) * rp + k0 + j] = (j >= i) ? lT[base + j] : 0.0;
+    }
+    __syncthreads();
+    // block row of R: R_kj = T_kk^T W_kj (in place)
+    for (int jb = kb + 1; jb < nb; ++jb) {
+      const int j0 = jb * kBlk, bj = min(kBlk, rp - j0);
+      block_gemm(W + (int64_t)k0 * rp + j0, Tg + (int64_t)k0 * rp + k0, true,
+                 W + (int64_t)k0 * rp + j0, false, rp, bs, bj, bs, 1.0, false, lW, lT);
+    }
+    // trailing Gram blocks: W_ij -= R_ki^T R_kj
+    for (int ib = kb + 1; ib < nb; ++ib)
+      for (int jb = ib; jb < nb; ++jb) {
+        const int i0 = ib * kBlk, j0 = jb * kBlk;
+        block_gemm(W + (int64_t)i0 * rp + j0, W + (int64_t)k0 * rp + i0, true,
+                   W + (int64_t)k0 * rp + j0, false, rp, min(kBlk, rp - i0), min(kBlk, rp - j0), bs,
+                   -1.0, true, lW, lT);
+      }
+  }
+  if (pass == 0 && threadIdx.x == 0) *gbl(d.reorth) = minratio < kReorth ? 1 : 0;
+  // T = R^-1, block column by block column: T_ij = -T_ii sum_{i<k<=j} R_ik T_kj
+  for (int jb = 1; jb < nb; ++jb) {
+    const int j0 = jb * kBlk, bj = min(kBlk, rp - j0);
+    for (int ib = jb - 1; ib >= 0; --ib) {
+      const int i0 = ib * kBlk, bi = min(kBlk, rp - i0);
+      for (int kb = ib + 1; kb <= jb; ++kb) {
+        const int q0 = kb * kBlk, bq = min(kBlk, rp - q0);
+        block_gemm(S, W + (int64_t)i0 * rp + q0, false, Tg + (int64_t)q0 * rp + j0, false, rp,
+                   bi, bj, bq, 1.0, kb > ib + 1, lW, lT);
+      }
+      block_gemm(Tg + (int64_t)i0 * rp + j0, Tg + (int64_t)i0 * rp + i0, false, S, false, rp,
+                 bi, bj, bi, -1.0, false, lW, lT);
+    }
+  }
+  // blocks below the diagonal of T
+  for (int i = ty; i < rp; i += 32)
+    for (int j = tx; j < rp; j += 32)
+      if (j / kBlk < i / kBlk) Tg[(int64_t)i * rp + j] = 0.0;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -169,20 +372,28 @@ void k_gs_factor(const DevMat* __restrict__ mats, const Work* __restrict__ work)
 constexpr int GSA_RA = 2;                          // 16-row tiles per wave
 constexpr int GSA_ROWS = GSA_RA * 16 * (GS_THREADS / kWave);   // 128 rows per workgroup
 
-template <int RT>
+// Small ranks (BIG = false): all RT column tiles of P_hat for rows [a, a + 128). Large ranks
+// (BIG = true, RT = 8): the 128-column block b of P_hat; its fp16 decompression operand is
+// built afterwards by split3 (its row scale needs every column).
+template <int RT, bool BIG>
 __global__ __launch_bounds__(GS_THREADS)
-void k_gs_apply(const DevMat* __restrict__ mats, const Work* __restrict__ work)
+void k_gs_apply(const DevMat* __restrict__ mats, const Work* __restrict__ work, int pass)
 {
   const Work wi = work[xcd_remap(blockIdx.x, gridDim.x)];
   if (wi.mat < 0) return;
   const DevMat& d = mats[wi.mat];
+  const bool again = *d.reorth != 0;      // a second pass follows (pass 0) / runs (pass 1)
+  if (pass && !again) return;
   const int m = d.m, r = d.r, rpad = d.rpad, mpad = d.mpad, kpad3 = d.kpad3;
-  const GLOBAL float* __restrict__ P = gbl(d.p_raw);
+  const GLOBAL float* __restrict__ P = gbl(pass ? d.p2 : d.p_raw);
   const GLOBAL double* __restrict__ Tm = gbl(d.tmat);
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
   const int c = lane & 15, g = lane >> 4;
   const int row0 = wi.a;                   // this workgroup's GSA_ROWS rows
+  const int t0 = BIG ? wi.b * RT : 0;      // first output column tile
+  const int nto = BIG ? min(RT, rpad / 16 - t0) : RT;   // output tiles present
+  const int c0 = t0 * 16;
   constexpr int SP = RT * 16 + 1;          // LDS row pitch (floats); odd, so column reads spread over banks
 
   __shared__ float S[GSA_ROWS * SP];
@@ -194,25 +405,33 @@ void k_gs_apply(const DevMat* __restrict__ mats, const Work* __restrict__ work)
 #pragma unroll
     for (int t = 0; t < RT; ++t) acc[a][t] = f64x4{0, 0, 0, 0};
 
-  // P_hat = P T with T upper triangular: k tile kt only feeds column tiles tj >= kt.
+  auto kstep = [&](int k, int tfirst) {
+    double av[GSA_RA];
+#pragma unroll
+    for (int a = 0; a < GSA_RA; ++a) {
+      const int rowA = row0 + (wv * GSA_RA + a) * 16 + c;     // A-fragment row of this lane
+      av[a] = rowA < m ? (double)P[(int64_t)rowA * rpad + k] : 0.0;
+    }
+#pragma unroll
+    for (int tj = 0; tj < RT; ++tj) {
+      if (tj < tfirst || tj >= nto) continue;
+      const double b = Tm[(int64_t)k * rpad + c0 + tj * 16 + c];
+#pragma unroll
+      for (int a = 0; a < GSA_RA; ++a) acc[a][tj] = mfma_f64(av[a], b, acc[a][tj]);
+    }
+  };
+  if constexpr (BIG) {
+    // k tiles left of the block feed every output tile
+    for (int kt = 0; kt < t0; ++kt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kstep(kt * 16 + ks * 4 + g, 0);
+  }
+  // P_hat = P T with T upper triangular: k tile t0 + kt only feeds column tiles tj >= kt.
 #pragma unroll
   for (int kt = 0; kt < RT; ++kt) {
+    if (kt >= nto) break;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int k = kt * 16 + ks * 4 + g;
-      double av[GSA_RA];
-#pragma unroll
-      for (int a = 0; a < GSA_RA; ++a) {
-        const int rowA = row0 + (wv * GSA_RA + a) * 16 + c;     // A-fragment row of this lane
-        av[a] = rowA < m ? (double)P[(int64_t)rowA * rpad + k] : 0.0;
-      }
-#pragma unroll
-      for (int tj = kt; tj < RT; ++tj) {
-        const double b = Tm[(int64_t)k * rpad + tj * 16 + c];
-#pragma unroll
-        for (int a = 0; a < GSA_RA; ++a) acc[a][tj] = mfma_f64(av[a], b, acc[a][tj]);
-      }
-    }
+    for (int ks = 0; ks < 4; ++ks) kstep((t0 + kt) * 16 + ks * 4 + g, kt);
   }
 
   // C layout of v_mfma_f64_16x16x4f64: lane 16g + c, register i holds C[g + 4i][c].
@@ -225,16 +444,28 @@ void k_gs_apply(const DevMat* __restrict__ mats, const Work* __restrict__ work)
         S[((wv * GSA_RA + a) * 16 + g + 4 * i) * SP + t * 16 + c] = (float)acc[a][t][i];
   __syncthreads();
 
-  // (a) fp32 P_hat, m x r row-major
+  if (pass == 0 && again) {
+    // first pass of a matrix that needs two: the result is the second pass's input
+    GLOBAL float* __restrict__ p2 = gbl(d.p2);
+    const int nc = nto * 16;
+    for (int idx = threadIdx.x; idx < GSA_ROWS * nc; idx += GS_THREADS) {
+      const int rr = idx / nc, cc = idx - rr * nc;
+      if (row0 + rr < m) p2[(int64_t)(row0 + rr) * rpad + c0 + cc] = S[rr * SP + cc];
+    }
+    return;
+  }
+
+  // (a) fp32 P_hat, m x r row-major (this block's columns)
   GLOBAL float* __restrict__ pout = gbl(d.p);
-  for (int idx = threadIdx.x; idx < GSA_ROWS * r; idx += GS_THREADS) {
-    const int rr = idx / r, cc = idx - rr * r;
-    if (row0 + rr < m) pout[(int64_t)(row0 + rr) * r + cc] = S[rr * SP + cc];
+  const int ncol = max(0, min(nto * 16, r - c0));
+  for (int idx = threadIdx.x; idx < GSA_ROWS * ncol; idx += GS_THREADS) {
+    const int rr = idx / ncol, cc = idx - rr * ncol;
+    if (row0 + rr < m) pout[(int64_t)(row0 + rr) * r + c0 + cc] = S[rr * SP + cc];
   }
   // (b) P_hat^T split bf16 hi/lo, rpad x mpad: 8 consecutive rows of one column per store
   GLOBAL uint16_t* __restrict__ pth = gbl(d.pt_hi);
   GLOBAL uint16_t* __restrict__ ptl = gbl(d.pt_lo);
-  for (int idx = threadIdx.x; idx < rpad * (GSA_ROWS / 8); idx += GS_THREADS) {
+  for (int idx = threadIdx.x; idx < nto * 16 * (GSA_ROWS / 8); idx += GS_THREADS) {
     const int col = idx / (GSA_ROWS / 8), r8 = (idx % (GSA_ROWS / 8)) * 8;
     if (row0 + r8 >= mpad) continue;
     uint32_t h[4], l[4];
@@ -245,9 +476,10 @@ void k_gs_apply(const DevMat* __restrict__ mats, const Work* __restrict__ work)
       h[e] = bf16_bits(h0) | ((uint32_t)bf16_bits(h1) << 16);
       l[e] = bf16_bits((__bf16)(x0 - (float)h0)) | ((uint32_t)bf16_bits((__bf16)(x1 - (float)h1)) << 16);
     }
-    *gcast<u32x4>(pth + (int64_t)col * mpad + row0 + r8) = u32x4{h[0], h[1], h[2], h[3]};
-    *gcast<u32x4>(ptl + (int64_t)col * mpad + row0 + r8) = u32x4{l[0], l[1], l[2], l[3]};
+    *gcast<u32x4>(pth + (int64_t)(c0 + col) * mpad + row0 + r8) = u32x4{h[0], h[1], h[2], h[3]};
+    *gcast<u32x4>(ptl + (int64_t)(c0 + col) * mpad + row0 + r8) = u32x4{l[0], l[1], l[2], l[3]};
   }
+  if constexpr (BIG) return;
   // (c) rows scaled by 2^e (largest entry in [2^13, 2^14)) and split fp16 hi/lo, m x kpad3
   if (threadIdx.x < GSA_ROWS) {
     float amax = 0.0f;
@@ -261,7 +493,7 @@ void k_gs_apply(const DevMat* __restrict__ mats, const Work* __restrict__ work)
   constexpr int U8 = RT * 2;                         // 8-column units per row (rpad / 8)
   for (int idx = threadIdx.x; idx < GSA_ROWS * U8; idx += GS_THREADS) {
     const int rr = idx / U8, c8 = (idx % U8) * 8;
-    if (row0 + rr >= m) continue;
+    if (row0 + rr >= m || c8 >= kpad3) continue;
     const int ex = sexp[rr];
     uint32_t h[4], l[4];
 #pragma unroll
@@ -277,13 +509,53 @@ void k_gs_apply(const DevMat* __restrict__ mats, const Work* __restrict__ work)
   if (threadIdx.x < GSA_ROWS && row0 + (int)threadIdx.x < m) p3e[row0 + threadIdx.x] = sexp[threadIdx.x];
 }
 
+// Decompression operands from the fp32 factors (large ranks): each row of P_hat (which = 0,
+// from p) or of Q' (which = 1, from q_next) scaled by a power of two so that its largest entry
+// lies in [2^13, 2^14), split into fp16 hi + lo over kpad3 columns (zero beyond r), and the
+// exponent stored. One work item: 64 rows [a, a + 64) of matrix `mat`, which = b; one wave per
+// row at a time.
+__global__ __launch_bounds__(256)
+void k_split3(const DevMat* __restrict__ mats, const Work* __restrict__ work)
+{
+  const Work wi = work[blockIdx.x];
+  if (wi.mat < 0) return;
+  const DevMat& d = mats[wi.mat];
+  const int r = d.r, kpad3 = d.kpad3;
+  const bool isq = wi.b != 0;
+  const int rows = isq ? d.n : d.m;
+  const GLOBAL float* __restrict__ src = gbl(isq ? d.q_next : d.p);
+  GLOBAL uint16_t* __restrict__ hi = gbl(isq ? d.q3_hi : d.p3_hi);
+  GLOBAL uint16_t* __restrict__ lo = gbl(isq ? d.q3_lo : d.p3_lo);
+  GLOBAL int32_t* __restrict__ ex = gbl(isq ? d.q3_exp : d.p3_exp);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  for (int row = wi.a + wv; row < wi.a + 64 && row < rows; row += 4) {
+    float amax = 0.0f;
+    for (int col = lane; col < r; col += kWave) amax = fmaxf(amax, fabsf(src[(int64_t)row * r + col]));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    const int e = fp16_row_exponent(amax);
+    for (int col = lane; col < kpad3; col += kWave) {
+      const float x = col < r ? ldexpf(src[(int64_t)row * r + col], e) : 0.0f;
+      const _Float16 h = (_Float16)x;
+      hi[(int64_t)row * kpad3 + col] = f16_bits(h);
+      lo[(int64_t)row * kpad3 + col] = f16_bits((_Float16)(x - (float)h));
+    }
+    if (lane == 0) ex[row] = e;
+  }
+}
+
 }  // namespace
 
-hipError_t launch_gs_gram(int rt, const DevMat* mats, const Work* work, int n_work, hipStream_t s) {
+hipError_t launch_gs_gram(int rt, bool big, int pass, const DevMat* mats, const Work* work, int n_work, hipStream_t s) {
   if (n_work <= 0) return hipSuccess;
   const dim3 grid(n_work), block(GS_THREADS);
+  if (big) {
+    k_gs_gram<kMaxRankTiles, true><<<grid, block, 0, s>>>(mats, work, pass);
+    return hipGetLastError();
+  }
   switch (rt) {
-#define CASE(R) case R: k_gs_gram<R><<<grid, block, 0, s>>>(mats, work); break;
+#define CASE(R) case R: k_gs_gram<R, false><<<grid, block, 0, s>>>(mats, work, pass); break;
     CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
 #undef CASE
     default: return hipErrorInvalidValue;
@@ -291,21 +563,38 @@ hipError_t launch_gs_gram(int rt, const DevMat* mats, const Work* work, int n_wo
   return hipGetLastError();
 }
 
-hipError_t launch_gs_factor(const DevMat* mats, const Work* work, int n_work, hipStream_t s) {
+hipError_t launch_gs_reduce(int pass, const DevMat* mats, const Work* work, int n_work, hipStream_t s) {
   if (n_work <= 0) return hipSuccess;
-  k_gs_factor<<<dim3(n_work), dim3(GSF_THREADS), 0, s>>>(mats, work);
+  k_gs_reduce<<<dim3(n_work), dim3(256), 0, s>>>(mats, work, pass);
   return hipGetLastError();
 }
 
-hipError_t launch_gs_apply(int rt, const DevMat* mats, const Work* work, int n_work, hipStream_t s) {
+hipError_t launch_gs_factor(bool big, int pass, const DevMat* mats, const Work* work, int n_work, hipStream_t s) {
+  if (n_work <= 0) return hipSuccess;
+  if (big) k_gs_factor_blk<<<dim3(n_work), dim3(GSF_THREADS), 0, s>>>(mats, work, pass);
+  else k_gs_factor<<<dim3(n_work), dim3(GSF_THREADS), 0, s>>>(mats, work, pass);
+  return hipGetLastError();
+}
+
+hipError_t launch_gs_apply(int rt, bool big, int pass, const DevMat* mats, const Work* work, int n_work, hipStream_t s) {
   if (n_work <= 0) return hipSuccess;
   const dim3 grid(n_work), block(GS_THREADS);
+  if (big) {
+    k_gs_apply<kMaxRankTiles, true><<<grid, block, 0, s>>>(mats, work, pass);
+    return hipGetLastError();
+  }
   switch (rt) {
-#define CASE(R) case R: k_gs_apply<R><<<grid, block, 0, s>>>(mats, work); break;
+#define CASE(R) case R: k_gs_apply<R, false><<<grid, block, 0, s>>>(mats, work, pass); break;
     CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
 #undef CASE
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_split3(const DevMat* mats, const Work* work, int n_work, hipStream_t s) {
+  if (n_work <= 0) return hipSuccess;
+  k_split3<<<dim3(n_work), dim3(256), 0, s>>>(mats, work);
   return hipGetLastError();
 }
 

@@ -92,10 +92,19 @@ __device__ __forceinline__ void bstore16(u32x4 v, rsrc_t r, uint32_t off) {
 }
 
 constexpr int kWave = 64;
-constexpr int kMaxRankTiles = 8;          // r <= 128 in this build
+constexpr int kMaxRankTiles = 8;          // 16-column rank tiles one product pass carries (128)
+constexpr int kMaxRank = 1024;            // largest compression rank
+constexpr int kBlk = 128;                 // column block of the blocked orthonormalisation (r > 128)
 constexpr int kXcds = 8;                  // MI355X: 8 XCDs, 32 CUs each
-constexpr int kGramRows = 256;            // rows per Gram partial
-constexpr double kDegenerate = 9.094947017729282e-13;   // 2^-40: relative squared residual
+constexpr int kGramRows = 256;            // rows per Gram partial, r <= 128
+constexpr int kGramRowsBig = 1024;        // rows per Gram partial, r > 128
+// A column of M q whose squared norm after projecting out the earlier columns is at most
+// 2^-40 of its squared norm before is dependent (its direction is lost to rounding).
+constexpr double kDegenerate = 9.094947017729282e-13;   // 2^-40
+// The Gram (Cholesky) form loses orthogonality as eps_64 times the squared condition number of
+// M q. When a kept column's squared residual ratio falls below 2^-20 the orthonormalisation is
+// repeated on its own result (a second pass restores orthogonality to rounding level).
+constexpr double kReorth = 9.5367431640625e-07;         // 2^-20
 
 // ------------------------------------------------------------------------------------------
 // device-side description of one gradient matrix and its plan workspace
@@ -111,7 +120,7 @@ struct DevMat {
   int32_t npad;      // n rounded up to the k extent of one K1 stage
   int32_t mpad;      // m rounded up to 32
   int32_t gram_parts;
-  int32_t pad_;
+  int32_t gram_rows;   // rows per Gram partial (multiple of 16)
   uint32_t g_bytes, e_bytes, o_bytes;   // byte spans of G, E and out (buffer ranges, < 2^31)
   uint32_t pad2_;
   // workspace (library owned)
@@ -124,6 +133,11 @@ struct DevMat {
   int32_t* q3_exp;                     // n3 (n rounded up to a decompression tile; zero rows)
   double* gram;                        // gram_parts x rpad x rpad fp64 partial Gram matrices
   double* tmat;                        // rpad x rpad fp64 upper-triangular T, P = (M q) T
+  double* wsum;                        // rpad x rpad fp64 summed Gram matrix, overwritten by the
+                                       // off-diagonal blocks of R (r > 128 only; else unused)
+  float* p2;                           // m x rpad fp32: first-pass orthonormal factor, the input
+                                       // of the second pass when one is needed
+  int32_t* reorth;                     // 1: this step's factor needs a second pass
 };
 
 // One unit of grouped work: a matrix and a block of it. Unused slots have mat = -1.
@@ -231,9 +245,11 @@ hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
 hipError_t launch_prep_qt(const DevMat* mats, const Work* work, int n_work, int rpad_max, hipStream_t s);
 hipError_t launch_ef_mq(int gt, int rtc, const DevMat* mats, const Work* work, int n_work,
                         const float* scale, uint8_t* flags, hipStream_t s);
-hipError_t launch_gs_gram(int rt, const DevMat* mats, const Work* work, int n_work, hipStream_t s);
-hipError_t launch_gs_factor(const DevMat* mats, const Work* work, int n_work, hipStream_t s);
-hipError_t launch_gs_apply(int rt, const DevMat* mats, const Work* work, int n_work, hipStream_t s);
+hipError_t launch_gs_gram(int rt, bool big, int pass, const DevMat* mats, const Work* work, int n_work, hipStream_t s);
+hipError_t launch_gs_reduce(int pass, const DevMat* mats, const Work* work, int n_work, hipStream_t s);
+hipError_t launch_gs_factor(bool big, int pass, const DevMat* mats, const Work* work, int n_work, hipStream_t s);
+hipError_t launch_gs_apply(int rt, bool big, int pass, const DevMat* mats, const Work* work, int n_work, hipStream_t s);
+hipError_t launch_split3(const DevMat* mats, const Work* work, int n_work, hipStream_t s);
 hipError_t launch_mtp(int gt, int rtc, const DevMat* mats, const Work* work, int n_work,
                       const float* scale, hipStream_t s);
 hipError_t launch_decompress(int gt, const DevMat* mats, const Work* work, int n_work,

@@ -33,13 +33,15 @@ struct psgd_ctx {
 
 namespace {
 
-enum WorkKind { W_PREP, W_K1, W_GRAM, W_FACTOR, W_APPLY, W_K2, W_K3, W_COMMIT, W_KINDS };
+enum WorkKind { W_PREP, W_K1, W_GRAM, W_REDUCE, W_FACTOR, W_APPLY, W_K2, W_SPLIT3, W_K3, W_COMMIT,
+                W_KINDS };
 
 }  // namespace
 
 struct psgd_plan {
   psgd_ctx* ctx = nullptr;
   int n_mats = 0, n_blocks = 0, gt = 0, rt = 0, rtc = 0, chunks = 0;
+  bool big = false;   // rank above one 128-column block: blocked orthonormalisation
   std::vector<DevMat> mats;
   DevMat* d_mats = nullptr;
   void* workspace = nullptr;
@@ -69,7 +71,7 @@ psgd_status hip_fail(psgd_ctx* ctx, hipError_t e, const char* what) {
 }
 
 enum Slot { S_ZERO_FLAGS, S_PREP, S_K1, S_GRAM, S_FACTOR, S_APPLY, S_K2, S_ZERO_SKIP, S_CHECK,
-            S_K3, S_COMMIT, S_SLOTS };
+            S_K3, S_COMMIT, S_REDUCE, S_SPLIT3, S_REORTH, S_SLOTS };
 
 // Launch `expr` in tracing slot `slot`, bracketed by the hook's events when installed.
 template <typename F>
@@ -104,7 +106,7 @@ psgd_status psgd_create(psgd_ctx** out, int device, int rank) {
   int n = 0;
   if (hipGetDeviceCount(&n) != hipSuccess || device < 0 || device >= n) return PSGD_EINVAL;
   if (rank < 1) return PSGD_EINVAL;
-  if (rank > 16 * psgd::kMaxRankTiles) return PSGD_EUNSUPPORTED;
+  if (rank > psgd::kMaxRank) return PSGD_EUNSUPPORTED;
   psgd_ctx* c = new (std::nothrow) psgd_ctx;
   if (!c) return PSGD_ENOMEM;
   c->device = device;
@@ -137,10 +139,17 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
   }
   HIPCHK(ctx, hipSetDevice(ctx->device), "hipSetDevice");
 
+  // Rank layout. The two product kernels carry at most kMaxRankTiles 16-column tiles per pass,
+  // so larger ranks are split into `chunks` equal chunks of `rtc` tiles (each chunk re-reads M);
+  // rpad = chunks * rtc * 16 >= r, the extra columns of the factors stay zero.
   const int r = ctx->rank;
-  const int rpad = (int)rup(r, 16);
+  const int rt0 = (int)(rup(r, 16) / 16);
+  const int chunks = (rt0 + psgd::kMaxRankTiles - 1) / psgd::kMaxRankTiles;
+  const int rtc = (rt0 + chunks - 1) / chunks;
+  const int rt = chunks * rtc;
+  const int rpad = rt * 16;
   const int kpad3 = (int)rup(r, 32);
-  const int rt = rpad / 16;
+  const bool big = rpad > psgd::kBlk;
   std::unique_ptr<psgd_plan> p(new (std::nothrow) psgd_plan);
   if (!p) return fail(ctx, PSGD_ENOMEM, "out of host memory");
   p->ctx = ctx;
@@ -148,13 +157,14 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
   p->n_blocks = n_blocks;
   p->gt = gt;
   p->rt = rt;
-  p->rtc = rt;       // rank <= 128: one chunk
-  p->chunks = 1;
+  p->rtc = rtc;
+  p->chunks = chunks;
+  p->big = big;
 
   // ---- validate and lay out the workspace ---------------------------------------------
   size_t ws = 0;
   auto take = [&](size_t bytes) { size_t o = ws; ws += (size_t)rup((int64_t)bytes, 256); return o; };
-  struct Off { size_t p_raw, qth, qtl, pth, ptl, p3h, p3l, p3e, q3h, q3l, q3e, gram, tmat; };
+  struct Off { size_t p_raw, qth, qtl, pth, ptl, p3h, p3l, p3e, q3h, q3l, q3e, gram, tmat, wsum, p2, reorth; };
   std::vector<Off> offs(n_mats);
   p->mats.resize(n_mats);
   for (int i = 0; i < n_mats; ++i) {
@@ -189,7 +199,8 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
     d.rpad = rpad; d.kpad3 = kpad3;
     d.npad = (int)rup(a.n, psgd::ef_mq_k_per_stage());   // Q^T covers whole K1 stages
     d.mpad = (int)rup(a.m, 32);
-    d.gram_parts = (int)((a.m + psgd::kGramRows - 1) / psgd::kGramRows);
+    d.gram_rows = big ? psgd::kGramRowsBig : psgd::kGramRows;
+    d.gram_parts = (int)((a.m + d.gram_rows - 1) / d.gram_rows);
     const int gsz = gt == psgd::G_F32 ? 4 : 2;
     const int64_t gb = ((a.m - 1) * a.ld_grad + a.n) * gsz;
     const int64_t eb = ((a.m - 1) * a.ld_err + a.n) * 4;
@@ -214,6 +225,9 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
     o.q3e = take((size_t)n3 * 4);
     o.gram = take((size_t)d.gram_parts * rpad * rpad * 8);
     o.tmat = take((size_t)rpad * rpad * 8);
+    o.wsum = big ? take((size_t)rpad * rpad * 8) : 0;
+    o.p2 = take((size_t)a.m * rpad * 4);
+    o.reorth = take(4);
   }
 
   // ---- work lists -------------------------------------------------------------------------
@@ -262,16 +276,27 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
         push(Work{i, r0, ch, 0}, (int64_t)std::min(k1rows, p->mats[i].m - r0) * p->mats[i].n);
   end_kind(W_K1, true, true);
   begin_kind(W_GRAM);
-  for (int i = 0; i < n_mats; ++i)
+  const int nblk = (rpad + psgd::kBlk - 1) / psgd::kBlk;
+  for (int i = 0; i < n_mats; ++i) {
+    const int gr = p->mats[i].gram_rows;
     for (int pt = 0; pt < p->mats[i].gram_parts; ++pt)
-      push(Work{i, pt * psgd::kGramRows, pt, 0}, std::min(psgd::kGramRows, p->mats[i].m - pt * psgd::kGramRows));
+      for (int bi = 0; bi < (big ? nblk : 1); ++bi)
+        for (int bj = bi; bj < (big ? nblk : 1); ++bj)
+          push(Work{i, pt * gr, pt, bi | (bj << 16)}, std::min(gr, p->mats[i].m - pt * gr));
+  }
   end_kind(W_GRAM, true);
+  begin_kind(W_REDUCE);
+  if (big)
+    for (int i = 0; i < n_mats; ++i)
+      for (int64_t e0 = 0; e0 * 4096 < (int64_t)rpad * rpad; ++e0) all.push_back(Work{i, (int)e0, 0, 0});
+  end_kind(W_REDUCE, false);
   begin_kind(W_FACTOR);
   for (int i = 0; i < n_mats; ++i) all.push_back(Work{i, 0, 0, 0});
   end_kind(W_FACTOR, false);
   begin_kind(W_APPLY);
   for (int i = 0; i < n_mats; ++i)
-    for (int r0 = 0; r0 < p->mats[i].m; r0 += aprows) push(Work{i, r0, 0, 0}, std::min(aprows, p->mats[i].m - r0));
+    for (int r0 = 0; r0 < p->mats[i].m; r0 += aprows)
+      for (int cb = 0; cb < (big ? nblk : 1); ++cb) push(Work{i, r0, cb, 0}, std::min(aprows, p->mats[i].m - r0));
   end_kind(W_APPLY, true);
   begin_kind(W_K2);
   for (int i = 0; i < n_mats; ++i)
@@ -279,6 +304,13 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
       for (int c0 = 0; c0 < p->mats[i].n; c0 += k2cols)
         push(Work{i, c0, ch, 0}, (int64_t)std::min(k2cols, p->mats[i].n - c0) * p->mats[i].m);
   end_kind(W_K2, true, true);
+  begin_kind(W_SPLIT3);
+  if (big)
+    for (int i = 0; i < n_mats; ++i) {
+      for (int r0 = 0; r0 < p->mats[i].m; r0 += 64) all.push_back(Work{i, r0, 0, 0});
+      for (int r0 = 0; r0 < p->mats[i].n; r0 += 64) all.push_back(Work{i, r0, 1, 0});
+    }
+  end_kind(W_SPLIT3, false);
   begin_kind(W_K3);
   for (int i = 0; i < n_mats; ++i)
     for (int m0 = 0; m0 < p->mats[i].m; m0 += tm)
@@ -323,6 +355,9 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
     d.q3_exp = reinterpret_cast<int32_t*>(base + o.q3e);
     d.gram = reinterpret_cast<double*>(base + o.gram);
     d.tmat = reinterpret_cast<double*>(base + o.tmat);
+    d.wsum = big ? reinterpret_cast<double*>(base + o.wsum) : nullptr;
+    d.p2 = reinterpret_cast<float*>(base + o.p2);
+    d.reorth = reinterpret_cast<int32_t*>(base + o.reorth);
   }
   if ((e = hipMemset(p->workspace, 0, ws ? ws : 256)) != hipSuccess) { cleanup(); return hip_fail(ctx, e, "workspace clear"); }
   if ((e = hipMalloc(&p->d_mats, sizeof(DevMat) * n_mats)) != hipSuccess) { cleanup(); return fail(ctx, PSGD_ENOMEM, "descriptor table"); }
@@ -357,10 +392,22 @@ psgd_status psgd_compress(psgd_ctx* ctx, psgd_plan* plan, const float* scale, ui
   HIPCHK(ctx, traced(ctx, S_ZERO_FLAGS, stream, [&] { return psgd::launch_zero_u8(flags, plan->n_mats, stream); }), "flag clear");
   HIPCHK(ctx, traced(ctx, S_PREP, stream, [&] { return psgd::launch_prep_qt(dm, W(W_PREP), plan->cnt[W_PREP], 0, stream); }), "warm-start operand");
   HIPCHK(ctx, traced(ctx, S_K1, stream, [&] { return psgd::launch_ef_mq(plan->gt, plan->rtc, dm, W(W_K1), plan->cnt[W_K1], scale, flags, stream); }), "M Q");
-  HIPCHK(ctx, traced(ctx, S_GRAM, stream, [&] { return psgd::launch_gs_gram(plan->rt, dm, W(W_GRAM), plan->cnt[W_GRAM], stream); }), "Gram");
-  HIPCHK(ctx, traced(ctx, S_FACTOR, stream, [&] { return psgd::launch_gs_factor(dm, W(W_FACTOR), plan->cnt[W_FACTOR], stream); }), "Gram-Schmidt");
-  HIPCHK(ctx, traced(ctx, S_APPLY, stream, [&] { return psgd::launch_gs_apply(plan->rt, dm, W(W_APPLY), plan->cnt[W_APPLY], stream); }), "orthonormal P");
+  const bool big = plan->big;
+  HIPCHK(ctx, traced(ctx, S_GRAM, stream, [&] { return psgd::launch_gs_gram(plan->rt, big, 0, dm, W(W_GRAM), plan->cnt[W_GRAM], stream); }), "Gram");
+  if (big)
+    HIPCHK(ctx, traced(ctx, S_REDUCE, stream, [&] { return psgd::launch_gs_reduce(0, dm, W(W_REDUCE), plan->cnt[W_REDUCE], stream); }), "Gram sum");
+  HIPCHK(ctx, traced(ctx, S_FACTOR, stream, [&] { return psgd::launch_gs_factor(big, 0, dm, W(W_FACTOR), plan->cnt[W_FACTOR], stream); }), "Gram-Schmidt");
+  HIPCHK(ctx, traced(ctx, S_APPLY, stream, [&] { return psgd::launch_gs_apply(plan->rt, big, 0, dm, W(W_APPLY), plan->cnt[W_APPLY], stream); }), "orthonormal P");
+  // second pass, for the matrices whose first pass flagged it (the others return at once)
+  HIPCHK(ctx, traced(ctx, S_REORTH, stream, [&] {
+    hipError_t e = psgd::launch_gs_gram(plan->rt, big, 1, dm, W(W_GRAM), plan->cnt[W_GRAM], stream);
+    if (e == hipSuccess && big) e = psgd::launch_gs_reduce(1, dm, W(W_REDUCE), plan->cnt[W_REDUCE], stream);
+    if (e == hipSuccess) e = psgd::launch_gs_factor(big, 1, dm, W(W_FACTOR), plan->cnt[W_FACTOR], stream);
+    if (e == hipSuccess) e = psgd::launch_gs_apply(plan->rt, big, 1, dm, W(W_APPLY), plan->cnt[W_APPLY], stream);
+    return e; }), "second orthonormalisation pass");
   HIPCHK(ctx, traced(ctx, S_K2, stream, [&] { return psgd::launch_mtp(plan->gt, plan->rtc, dm, W(W_K2), plan->cnt[W_K2], scale, stream); }), "M^T P");
+  if (big)
+    HIPCHK(ctx, traced(ctx, S_SPLIT3, stream, [&] { return psgd::launch_split3(dm, W(W_SPLIT3), plan->cnt[W_SPLIT3], stream); }), "decompression operands");
   return PSGD_OK;
 }
 

@@ -112,3 +112,52 @@ def test_full_underflow_shard_injections():
         if ev and ev[0] == "scale":
             group.scale[ev[1]] = float(scales[ev[1]])
     group.close()
+
+
+def test_unsharded_rank896():
+    """The unsharded resblock (3968x11904, 3968x3968, 3968x15872, 15872x3968 bf16, planted rank-64
+    component at 10x energy) at rank 896 over 5 warm-started steps. The 3968x3968 matrix is
+    compared with the oracle at every step; for all four matrices the properties that hold at
+    any size are checked: orthonormal P, E + D = M element by element, P^T E = 0, q_next =
+    M^T P on sampled columns."""
+    import torch
+    w, grads, group = _build(5)
+    r = w.rank
+    PROJ = 1
+    E_or = np.zeros((w.matrices[PROJ].m, w.matrices[PROJ].n))
+    Q_or = group.q[PROJ].cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(5)
+    for step in range(5):
+        if step:
+            for s, g in zip(w.matrices, grads):
+                wl.gradient_torch(w, s, step, g.device, out=g)
+        Gs = [g.float().cpu().numpy().astype(np.float64) for g in grads]
+        Es = [e.cpu().numpy().astype(np.float64) for e in group.err]
+        log(f"unsharded rank 896 step {step}")
+        skip = group.step([], host=True)
+        torch.cuda.synchronize()
+        assert skip == 0
+        for i, s in enumerate(w.matrices):
+            M = Gs[i] + Es[i]
+            P = group.p[i].cpu().numpy().astype(np.float64)
+            E = group.err[i].cpu().numpy().astype(np.float64)
+            D = group.out[i].cpu().numpy().astype(np.float64)
+            Q = group.q[i].cpu().numpy().astype(np.float64)
+            oe = orth_err(P)
+            ident = float(np.abs(E + D - M).max() / np.abs(M).max())
+            pe = float(np.linalg.norm(P.T @ E) / np.linalg.norm(E))
+            cols = rng.choice(r, size=8, replace=False)
+            qs = rel(Q[:, cols], M.T @ P[:, cols])
+            log(f"  {s.name}: orth={oe:.2e} |E+D-M|/|M|max={ident:.2e} |P^T E|/|E|={pe:.2e} q_next={qs:.2e}")
+            assert oe <= ORTH_TOL
+            assert ident <= 2.0 ** -20
+            assert pe <= REL_TOL
+            assert qs <= REL_TOL
+        st = oracle.step_matrix(Gs[PROJ], 1.0, E_or, Q_or)
+        r_ = dict(D=rel(group.out[PROJ].cpu().numpy(), st.D), E=rel(group.err[PROJ].cpu().numpy(), st.E_next),
+                  Q=rel(group.q[PROJ].cpu().numpy(), st.Q_next), P=rel(group.p[PROJ].cpu().numpy(), st.P))
+        log("  oracle proj: " + " ".join(f"{k}={v:.2e}" for k, v in r_.items()))
+        for k in ("D", "E", "Q", "P"):
+            assert r_[k] <= REL_TOL, (step, k, r_[k])
+        E_or, Q_or = st.E_next, st.Q_next
+    group.close()

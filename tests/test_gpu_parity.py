@@ -296,4 +296,49 @@ def test_invalid_arguments_rejected():
     with pytest.raises(B.PsgdError):
         B.psgd_create(0, 0)
     with pytest.raises(B.PsgdError):
-        B.psgd_create(0, 129)
+        B.psgd_create(0, 1025)
+
+
+# ------------------------------------------------------------------------------------------
+# ranks above 128: rank chunks in the two products, blocked orthonormalisation
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,rank", [("f16", 200), ("bf16", 260)])
+def test_large_rank_ragged(dtype, rank):
+    shapes = [(1000, 1536), (700, 520), (300, 264)]
+    rng = np.random.default_rng(8000 + rank)
+    blocks = [0, 1, 0]
+    scales = np.array([1.0, 0.75], np.float32)
+    q0 = [rng.standard_normal((n, rank)).astype(np.float32) for _, n in shapes]
+    err0 = [(rng.standard_normal((m, n)) * 0.05).astype(np.float32) for m, n in shapes]
+    log(f"large rank {dtype} r={rank} shapes={shapes}")
+    case = Case(shapes, blocks, dtype, rank, scales, q0, err0)
+    for t in range(3):
+        gs = []
+        for m, n in shapes:
+            x = rng.standard_normal((m, n)) * np.exp(rng.uniform(-3, 0, size=(m, 1)))
+            gs.append(wl.to_bf16_bits(x) if dtype == "bf16" else wl.to_fp16(x))
+        case.set_grads(gs)
+        assert case.gpu_step() == 0
+        compare_step(case.fetch(), case.oracle_step(), f"large rank step {t}")
+    case.close()
+
+
+@pytest.mark.parametrize("rank,true_rank", [(100, 60), (200, 150)])
+def test_rank_deficient_second_pass(rank, true_rank):
+    """rank(M) < r: one step recovers M (E vanishes relative to M). The surplus columns of M q
+    are rounding noise, which leaves the Gram form ill-conditioned, so the orthonormalisation
+    takes its second pass; P must come out orthonormal. Which completion fills the surplus
+    columns is rounding-dependent on both sides, so D and E are compared, not P."""
+    m, n = 600, 512
+    M = wl.exact_rank_np(m, n, true_rank, seed=4242).astype(np.float32)
+    rng = np.random.default_rng(4243)
+    q0 = [rng.standard_normal((n, rank)).astype(np.float32)]
+    case = Case([(m, n)], [0], "f32", rank, np.ones(1, np.float32), q0)
+    case.set_grads([M])
+    assert case.gpu_step() == 0
+    res = case.fetch()
+    compare_step(res, case.oracle_step(), f"rank-{true_rank} matrix at r={rank}", exact_rank=True,
+                 check_p=False)
+    log(f"  |E|/|M| {np.linalg.norm(res['E'][0]) / np.linalg.norm(M):.2e}")
+    assert np.linalg.norm(res["E"][0]) / np.linalg.norm(M) <= 1e-4
+    case.close()
