@@ -220,7 +220,9 @@ void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   }
 }
 
-// q <- q_next when the step is not skipped
+// q <- q_next when the step is not skipped. One work item: 4096 consecutive floats of q (a
+// 16-byte aligned range: q is n x r contiguous); each thread moves four 16-byte vectors, all
+// loads issued before the stores.
 __global__ __launch_bounds__(256)
 void k_commit_q(const DevMat* __restrict__ mats, const Work* __restrict__ work,
                 const int32_t* __restrict__ skip)
@@ -231,9 +233,21 @@ void k_commit_q(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   const int64_t total = (int64_t)d.n * d.r;
   const int64_t beg = (int64_t)wi.a * 4096;
   const int64_t end = beg + 4096 < total ? beg + 4096 : total;
+  const int64_t vend = beg + ((end - beg) & ~int64_t(3));
   GLOBAL float* __restrict__ q = gbl(d.q);
   const GLOBAL float* __restrict__ qn = gbl(d.q_next);
-  for (int64_t i = beg + threadIdx.x; i < end; i += 256) q[i] = qn[i];
+  f32x4 v[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int64_t i = beg + 4 * ((int64_t)threadIdx.x + 256 * b);
+    if (i < vend) v[b] = *gcast<f32x4>(qn + i);
+  }
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int64_t i = beg + 4 * ((int64_t)threadIdx.x + 256 * b);
+    if (i < vend) *gcast<f32x4>(q + i) = v[b];
+  }
+  if ((int)threadIdx.x < end - vend) q[vend + threadIdx.x] = qn[vend + threadIdx.x];
 }
 
 template <int GT>

@@ -266,8 +266,7 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
   const int tm = psgd::decomp_tile_m(), tn = psgd::decomp_tile_n();
   begin_kind(W_PREP);
   for (int i = 0; i < n_mats; ++i)
-    for (int n0 = 0; n0 < p->mats[i].npad; n0 += 32)
-      for (int r0 = 0; r0 < rpad; r0 += 32) all.push_back(Work{i, n0, r0, 0});
+    for (int n0 = 0; n0 < p->mats[i].n; n0 += 64) all.push_back(Work{i, n0, 0, 0});
   end_kind(W_PREP, false);
   begin_kind(W_K1);
   for (int i = 0; i < n_mats; ++i)
