@@ -7,11 +7,12 @@
 // lo*hi) with fp32 accumulation reproduce fp32 products to about 2^-21. The power-of-two row
 // scales are removed exactly with ldexp.
 //
-// The tile is computed transposed, D^T = Q' P^T. In that form the MFMA C layout gives every
-// lane 4 consecutive columns of one row of D, so the G/E/out traffic is 8- and 16-byte vector
-// accesses along rows. G, E and out go through buffer descriptors: ragged edges read zeros
-// and drop their stores in hardware, so the epilogue issues the loads of all its tiles at
-// once and has no branches.
+// The tile is computed transposed, D^T = Q' P^T, so the MFMA C layout gives every lane 4
+// consecutive columns of one row of D. The finished tile is passed through LDS so that the
+// G/E/out traffic runs in whole 128-byte lines: in the C layout one wave instruction would
+// touch half of a line in each of 16 rows, which HBM serves at a markedly lower rate. G, E and
+// out go through buffer descriptors: ragged edges read zeros and drop their stores in
+// hardware, so the epilogue issues the loads of all its rows at once and has no branches.
 //
 // Skip: the device-side skip word is read first. A skipped step zeroes the error buffer over
 // the tile and writes nothing else (the error buffer is zeroed on non-finite values: Korean
@@ -33,6 +34,11 @@ namespace {
 constexpr int K3_TM = K3_WM * 64, K3_TN = K3_WN * 64;
 constexpr int K3_THREADS = K3_WM * K3_WN * kWave;
 constexpr int LDS_K = 32;                // LDS row = 32 fp16 = 4 16-byte units, XOR-swizzled
+constexpr int K3_DTP = K3_TN + 4;        // D tile row pitch (floats), rows 16-byte aligned
+constexpr int kStageQBytes = 2 * 2 * K3_TN * LDS_K * 2;
+constexpr int kStageBytes = kStageQBytes + 2 * 2 * K3_TM * LDS_K * 2;
+constexpr int kTileBytes = K3_TM * K3_DTP * 4;
+constexpr int kLdsBytes = kStageBytes > kTileBytes ? kStageBytes : kTileBytes;
 // Physical unit of logical unit q in row rr: 16 lanes reading 16 consecutive rows (one unit
 // each) or writing 4 rows (4 units each) hit 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int swz3(int rr, int q) { return q ^ ((rr >> 2) & 3); }
@@ -83,8 +89,11 @@ void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   const int wm = wv % K3_WM, wn = wv / K3_WM;
   const int c = lane & 15, g = lane >> 4;
 
-  __shared__ __attribute__((aligned(16))) uint16_t ldq[2][2][K3_TN][LDS_K];
-  __shared__ __attribute__((aligned(16))) uint16_t ldp[2][2][K3_TM][LDS_K];
+  // One LDS arena: the double-buffered factor stages during the products, then the finished
+  // D tile (K3_TM x K3_DTP fp32) for the epilogue.
+  __shared__ __attribute__((aligned(16))) char lds_raw[kLdsBytes];
+  auto ldq = reinterpret_cast<uint16_t(*)[2][K3_TN][LDS_K]>(lds_raw);
+  auto ldp = reinterpret_cast<uint16_t(*)[2][K3_TM][LDS_K]>(lds_raw + kStageQBytes);
 
   // staging: K3_TN rows of Q' and K3_TM rows of P x 32 k x {hi, lo}, in 16-byte units. The
   // operand arrays are padded with zero rows to whole tiles, so no staging load is masked.
@@ -174,7 +183,9 @@ void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   compute(ks & 1);
 
   // Epilogue. acc[jn][im]: lane holds D[row = m0 + wm*64 + im*16 + c][n0 + wn*64 + jn*16 + 4g
-  // + {0..3}]. All G/E loads of the wave's 16 tiles are issued before any is used.
+  // + {0..3}] times 2^(row exponent + column exponent). The exponents are removed and the tile
+  // is written to LDS; G, E and out are then streamed in whole 128-byte lines (each wave
+  // instruction covers 2 rows x 128 columns), all G/E loads issued before any is used.
   const rsrc_t rg = make_rsrc(d.grad, d.g_bytes);
   const rsrc_t ro = make_rsrc(d.out, d.out ? d.o_bytes : 0u);   // no out buffer: stores dropped
   const int ldg = (int)d.ld_grad, ldo = (int)d.ld_out;
@@ -182,41 +193,53 @@ void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   const GLOBAL int32_t* __restrict__ qexp = gbl(d.q3_exp);
   const float s = scale[d.block];
   constexpr int GB = GradIO<GT>::kBytes;
-  Raw4<GT> gv[4][4];
-  u32x4 ev[4][4];
-  auto offset = [&](int im, int jn, int ld, uint32_t bytes) -> uint32_t {
-    const int row = m0 + wm * 64 + im * 16 + c;
-    const int col = n0 + wn * 64 + jn * 16 + 4 * g;
+  constexpr int CQ = K3_TN / 4;                      // 4-column groups per row
+  constexpr int RSTEP = K3_THREADS / CQ;             // rows covered by one pass of the workgroup
+  constexpr int NS = K3_TM / RSTEP;                  // passes over the tile
+  static_assert(RSTEP * CQ == K3_THREADS && NS * RSTEP == K3_TM, "epilogue mapping");
+  const int cq = threadIdx.x % CQ, rs = threadIdx.x / CQ;
+  auto offset = [&](int st, int ld, uint32_t bytes) -> uint32_t {
+    const int row = m0 + rs + RSTEP * st, col = n0 + 4 * cq;
     return (row < m && col < n) ? (uint32_t)(row * ld + col) * bytes : kOOB;
   };
+  Raw4<GT> gv[NS];
+  u32x4 ev[NS];
 #pragma unroll
-  for (int im = 0; im < 4; ++im)
+  for (int st = 0; st < NS; ++st) {
+    gv[st].load(rg, offset(st, ldg, GB));
+    ev[st] = bload16(re, offset(st, lde, 4u));
+  }
+  {
+    int ep[4];
+    u32x4 eqv[4];
 #pragma unroll
-    for (int jn = 0; jn < 4; ++jn) {
-      gv[im][jn].load(rg, offset(im, jn, ldg, GB));
-      ev[im][jn] = bload16(re, offset(im, jn, lde, 4u));
-    }
-  int ep[4];
-  u32x4 eqv[4];
+    for (int im = 0; im < 4; ++im) ep[im] = pexp[m0 + wm * 64 + im * 16 + c];
 #pragma unroll
-  for (int im = 0; im < 4; ++im) ep[im] = pexp[m0 + wm * 64 + im * 16 + c];
+    for (int jn = 0; jn < 4; ++jn) eqv[jn] = *gcast<u32x4>(qexp + n0 + wn * 64 + jn * 16 + 4 * g);
+    __syncthreads();                                  // every wave is done with the stages
+    float* Dt = reinterpret_cast<float*>(lds_raw);
 #pragma unroll
-  for (int jn = 0; jn < 4; ++jn) eqv[jn] = *gcast<u32x4>(qexp + n0 + wn * 64 + jn * 16 + 4 * g);
+    for (int im = 0; im < 4; ++im)
 #pragma unroll
-  for (int im = 0; im < 4; ++im) {
+      for (int jn = 0; jn < 4; ++jn) {
+        f32x4 dv;
 #pragma unroll
-    for (int jn = 0; jn < 4; ++jn) {
-      const f32x4 gf = gv[im][jn].f32();
-      const f32x4 ef = __builtin_bit_cast(f32x4, ev[im][jn]);
-      f32x4 dv, en;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        dv[i] = ldexpf(acc[jn][im][i], -(ep[im] + (int)eqv[jn][i]));
-        en[i] = __builtin_fmaf(s, gf[i], ef[i]) - dv[i];
+        for (int i = 0; i < 4; ++i) dv[i] = ldexpf(acc[jn][im][i], -(ep[im] + (int)eqv[jn][i]));
+        *reinterpret_cast<f32x4*>(&Dt[(wm * 64 + im * 16 + c) * K3_DTP + wn * 64 + jn * 16 + 4 * g]) = dv;
       }
-      bstore16(__builtin_bit_cast(u32x4, en), re, offset(im, jn, lde, 4u));
-      bstore16(__builtin_bit_cast(u32x4, dv), ro, offset(im, jn, ldo, 4u));
-    }
+    __syncthreads();
+  }
+  const float* Dt = reinterpret_cast<const float*>(lds_raw);
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    const f32x4 gf = gv[st].f32();
+    const f32x4 ef = __builtin_bit_cast(f32x4, ev[st]);
+    const f32x4 dv = *reinterpret_cast<const f32x4*>(&Dt[(rs + RSTEP * st) * K3_DTP + 4 * cq]);
+    f32x4 en;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) en[i] = __builtin_fmaf(s, gf[i], ef[i]) - dv[i];
+    bstore16(__builtin_bit_cast(u32x4, en), re, offset(st, lde, 4u));
+    bstore16(__builtin_bit_cast(u32x4, dv), ro, offset(st, ldo, 4u));
   }
 }
 
