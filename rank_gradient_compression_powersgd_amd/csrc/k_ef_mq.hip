@@ -1,82 +1,62 @@
 // K1: fused error-feedback accumulate, P = M Q and the per-matrix non-finite flag.
 //
-// M = s_b * G + E is formed in fp32 registers and never stored. The error buffer and its
-// finite checks come from "Zero-Shot Text-to-Image Generation — 中文验证版" (section 证据);
-// the per-resblock multiplier s_b reflects per-resblock gradient scaling (same card, section
-// 方法适配). The product is a tall-skinny GEMM on gfx950 MFMA (v_mfma_f32_16x16x32_bf16)
-// with fp32 accumulation. Each operand is split into two bfloat16 halves, x = hi + lo, and
-// three products hi*hi + hi*lo + lo*hi keep the result within about 2^-16 of fp32 products
-// while the kernel stays bound by HBM bandwidth.
+// M = s_b * G + E is formed in fp32 registers and never stored in HBM. The error buffer and
+// its finite checks come from "Zero-Shot Text-to-Image Generation — 中文验证版" (section
+// 证据); the per-resblock multiplier s_b reflects per-resblock gradient scaling (same card,
+// section 方法适配). The product is a tall-skinny GEMM on gfx950 MFMA
+// (v_mfma_f32_16x16x32_bf16) with fp32 accumulation. Each operand is split into two bfloat16
+// halves, x = hi + lo, and three products hi*hi + hi*lo + lo*hi keep the result within about
+// 2^-16 of fp32 products while the kernel stays bound by HBM bandwidth.
 //
-// Data flow per workgroup (a block of rows of one matrix, one rank chunk):
-//   * every lane streams its own MFMA A-fragments straight from HBM: 8 consecutive columns of
-//     one row of G (16 B of fp16) and of E (32 B), so M needs no LDS round trip. The loads go
-//     through buffer descriptors: out-of-range lanes use an offset past the range and read
-//     zeros, so the loop body has no branches and the next stage's loads stay in flight while
-//     the current stage computes;
+// Data flow per workgroup (K1_ROWS rows of one matrix, one rank chunk), per stage of 64
+// columns:
+//   * G and E are read in whole 128-byte lines: 16 lanes cover one row (4 consecutive
+//     elements each: 8 bytes of fp16 G, 16 bytes of E), so a wave instruction covers 4 rows.
+//     (Reading the MFMA A-fragments straight from HBM would touch half a line in each of 16
+//     rows per instruction, which HBM serves markedly slower.) The loads go through buffer
+//     descriptors: out-of-range lanes use an offset past the range and read zeros, so the
+//     loop has no branches. The next stage's loads are in flight while this stage computes;
+//   * each lane forms M for its elements, tests them, splits them into bf16 hi/lo and writes
+//     them to an LDS tile (rows x 64 columns, 16-byte units XOR-swizzled by row); the MFMA
+//     A-fragments are read from there;
 //   * the shared operand, Q^T split into bf16 hi/lo (prepared once per step), is staged in LDS
-//     one pipeline stage (K1_KSUB x 32 columns of k) at a time, double-buffered;
-//   * the flag test runs on M (one class test per element); only when a wave met a non-finite
-//     M are the inputs G and E of its rows examined, after the main loop, so the flag is
-//     exactly "G or E holds inf/NaN".
+//     beside it;
+//   * the flag test runs on M (one class test per element); only when the workgroup met a
+//     non-finite M are the inputs G and E of its rows examined, after the main loop, so the
+//     flag is exactly "G or E holds inf/NaN".
 #include "psgd_internal.h"
 
 #ifndef K1_RA
-#define K1_RA 4      // 16-row tiles per wave
+#define K1_RA 2      // 16-row MFMA tiles per wave
 #endif
 #ifndef K1_W
 #define K1_W 4       // waves per workgroup
 #endif
 #ifndef K1_OCC
-#define K1_OCC 1     // workgroups per CU the register budget is sized for
+#define K1_OCC 2     // workgroups per CU the register budget is sized for (one converts while the other multiplies)
 #endif
-#ifndef K1_KSUB
 #define K1_KSUB 2    // 32-column MFMA k groups per pipeline stage
-#endif
 
 namespace psgd {
 namespace {
 
 constexpr int K1_ROWS = K1_RA * 16 * K1_W;
+constexpr int K1_THREADS = K1_W * kWave;
 constexpr int KS = 32 * K1_KSUB;       // k columns per stage
 constexpr int LDS_K = KS;              // LDS row = KS bf16; 16-byte units XOR-swizzled by row
 static_assert(KS == 64, "the LDS swizzle assumes 8 units per row");
-// Physical 16-byte unit of logical unit q in rank row rr: with 128-byte rows, the 16 lanes of a
-// read (16 consecutive rows, one unit each) and of a write (2 rows, 8 units each) hit 16
-// distinct 16-byte bank groups.
+// Physical 16-byte unit of logical unit q in row rr: with 128-byte rows, the 16 lanes of an
+// MFMA fragment read (16 consecutive rows, one unit each) hit 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int swz1(int rr, int q) { return q ^ ((rr >> 1) & 7); }
 
-template <int GT> struct Raw8;
-template <> struct Raw8<G_F16> {
-  u32x4 v;
-  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { v = bload16(r, off); }
-  __device__ __forceinline__ f32x8 f32() const { return __builtin_convertvector(__builtin_bit_cast(f16x8, v), f32x8); }
-};
-template <> struct Raw8<G_BF16> {
-  u32x4 v;
-  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { v = bload16(r, off); }
-  __device__ __forceinline__ f32x8 f32() const { return __builtin_convertvector(__builtin_bit_cast(bf16x8, v), f32x8); }
-};
-template <> struct Raw8<G_F32> {
-  u32x4 a, b;
-  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { a = bload16(r, off); b = bload16(r, off + 16); }
-  __device__ __forceinline__ f32x8 f32() const {
-    const f32x4 x = __builtin_bit_cast(f32x4, a), y = __builtin_bit_cast(f32x4, b);
-    return f32x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-  }
-};
-
-struct Raw8E {
-  u32x4 a, b;
-  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { a = bload16(r, off); b = bload16(r, off + 16); }
-  __device__ __forceinline__ f32x8 f32() const {
-    const f32x4 x = __builtin_bit_cast(f32x4, a), y = __builtin_bit_cast(f32x4, b);
-    return f32x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-  }
-};
+// coalesced M loads: 16 lanes per row, 4 columns per lane
+constexpr int LCOL = KS / 4;                    // lanes per row (16)
+constexpr int LROWS = K1_THREADS / LCOL;        // rows per load step
+constexpr int NST = K1_ROWS / LROWS;            // load steps per stage
+static_assert(LROWS * LCOL == K1_THREADS && NST * LROWS == K1_ROWS, "load mapping");
 
 template <int GT, int RTC>
-__global__ __launch_bounds__(K1_W * kWave, K1_OCC)
+__global__ __launch_bounds__(K1_THREADS, K1_OCC)
 void k_ef_mq(const DevMat* __restrict__ mats, const Work* __restrict__ work,
              const float* __restrict__ scale, uint8_t* __restrict__ flags)
 {
@@ -95,21 +75,23 @@ void k_ef_mq(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
   const int c = lane & 15, g = lane >> 4;
-  const int row0 = wi.a + wv * (K1_RA * 16);
+  const int row0 = wi.a;                        // first row of the workgroup
   const int rc0 = wi.b * RTC * 16;
+  const int lu = threadIdx.x % LCOL, lr = threadIdx.x / LCOL;
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][RTC * 16][LDS_K];
+  __shared__ __attribute__((aligned(16))) uint16_t ldq[2][RTC * 16][LDS_K];   // Q^T hi, lo
+  __shared__ __attribute__((aligned(16))) uint16_t ldm[2][K1_ROWS][LDS_K];    // M hi, lo
+  __shared__ int s_bad;
 
   // Q^T staging: RTC*16 rank rows x KS k x {hi, lo} in 16-byte units; consecutive threads take
   // consecutive units of a row (coalesced global reads). Threads past the last unit repeat it
   // (same value to the same LDS address), so the code has no branch.
   constexpr int QPR = KS / 8;                   // 16-byte units per rank row
   constexpr int UNITS = RTC * 16 * QPR * 2;
-  constexpr int THREADS = K1_W * kWave;
-  constexpr int UPT = (UNITS + THREADS - 1) / THREADS;
+  constexpr int UPT = (UNITS + K1_THREADS - 1) / K1_THREADS;
   u32x4 stage[UPT];
   auto unit = [&](int j, int& arr, int& rr, int& q) {
-    int u = threadIdx.x + j * THREADS;
+    int u = threadIdx.x + j * K1_THREADS;
     u = u < UNITS ? u : UNITS - 1;
     arr = u / (RTC * 16 * QPR);
     const int rem = u - arr * (RTC * 16 * QPR);
@@ -124,29 +106,46 @@ void k_ef_mq(const DevMat* __restrict__ mats, const Work* __restrict__ work,
       stage[j] = *gcast<u32x4>((arr ? qtl : qth) + (int64_t)(rc0 + rr) * npad + k0 + 8 * q);
     }
   };
-  auto store_stage = [&](int buf) {
+  auto store_stage = [&]() {
 #pragma unroll
     for (int j = 0; j < UPT; ++j) {
       int arr, rr, q;
       unit(j, arr, rr, q);
-      *reinterpret_cast<u32x4*>(&lds[buf][arr][rr][8 * swz1(rr, q)]) = stage[j];
+      *reinterpret_cast<u32x4*>(&ldq[arr][rr][8 * swz1(rr, q)]) = stage[j];
     }
   };
 
-  // A-fragments of one stage: row tile a, k group j -> 8 columns k0 + 32j + 8g of row
-  // row0 + 16a + c. Out-of-range rows/columns read zeros.
-  struct Frag { Raw8<GT> gr[K1_RA][K1_KSUB]; Raw8E er[K1_RA][K1_KSUB]; };
-  auto load_m = [&](int k0, Frag& f) {
+  // M elements of one stage: step st covers rows row0 + lr + LROWS*st, columns k0 + 4*lu + {0..3}.
+  struct Raw { GradVec<GT, 4> gr[NST]; GradVec<G_F32, 4> er[NST]; };
+  auto load_m = [&](int k0, Raw& f) {
+    const int col = k0 + 4 * lu;
 #pragma unroll
-    for (int j = 0; j < K1_KSUB; ++j) {
-      const int col = k0 + 32 * j + 8 * g;
+    for (int st = 0; st < NST; ++st) {
+      const int row = row0 + lr + LROWS * st;
+      const bool ok = row < m && col < n;
+      f.gr[st].load(rg, ok ? (uint32_t)(row * ldg + col) * GB : kOOB);
+      f.er[st].load(re, ok ? (uint32_t)(row * lde + col) * 4u : kOOB);
+    }
+  };
+  bool mbad = false;     // some M element of this lane was not finite
+  auto put_m = [&](const Raw& f) {
+    const int q = lu >> 1, half = lu & 1;
 #pragma unroll
-      for (int a = 0; a < K1_RA; ++a) {
-        const int row = row0 + a * 16 + c;
-        const bool ok = row < m && col < n;
-        f.gr[a][j].load(rg, ok ? (uint32_t)(row * ldg + col) * GB : kOOB);
-        f.er[a][j].load(re, ok ? (uint32_t)(row * lde + col) * 4u : kOOB);
+    for (int st = 0; st < NST; ++st) {
+      const f32x4 gf = f.gr[st].f32();
+      const f32x4 ef = f.er[st].f32();
+      f32x4 mv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        mv[e] = __builtin_fmaf(s, gf[e], ef[e]);
+        mbad |= nonfinite(mv[e]);
       }
+      const bf16x4 hi = __builtin_convertvector(mv, bf16x4);
+      const bf16x4 lo = __builtin_convertvector(mv - __builtin_convertvector(hi, f32x4), bf16x4);
+      const int rr = lr + LROWS * st;
+      const int off = 8 * swz1(rr, q) + 4 * half;
+      *reinterpret_cast<bf16x4*>(&ldm[0][rr][off]) = hi;
+      *reinterpret_cast<bf16x4*>(&ldm[1][rr][off]) = lo;
     }
   };
 
@@ -155,29 +154,23 @@ void k_ef_mq(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   for (int a = 0; a < K1_RA; ++a)
 #pragma unroll
     for (int cc = 0; cc < RTC; ++cc) acc[a][cc] = f32x4{0, 0, 0, 0};
-  bool mbad = false;     // some M element of this lane was not finite
 
-  auto compute = [&](int buf, const Frag& f) {
+  auto compute = [&]() {
 #pragma unroll
     for (int j = 0; j < K1_KSUB; ++j) {
       bf16x8 ah[K1_RA], al[K1_RA];
 #pragma unroll
       for (int a = 0; a < K1_RA; ++a) {
-        const f32x8 gf = f.gr[a][j].f32();
-        const f32x8 ef = f.er[a][j].f32();
-        f32x8 mv;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          mv[e] = __builtin_fmaf(s, gf[e], ef[e]);
-          mbad |= nonfinite(mv[e]);
-        }
-        split_bf16(mv, ah[a], al[a]);
+        const int rp = wv * (K1_RA * 16) + a * 16 + c;
+        const int pq = 8 * swz1(rp, 4 * j + g);
+        ah[a] = *reinterpret_cast<const bf16x8*>(&ldm[0][rp][pq]);
+        al[a] = *reinterpret_cast<const bf16x8*>(&ldm[1][rp][pq]);
       }
 #pragma unroll
       for (int cc = 0; cc < RTC; ++cc) {
         const int pq = 8 * swz1(cc * 16 + c, 4 * j + g);
-        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&lds[buf][0][cc * 16 + c][pq]);
-        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&lds[buf][1][cc * 16 + c][pq]);
+        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&ldq[0][cc * 16 + c][pq]);
+        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&ldq[1][cc * 16 + c][pq]);
 #pragma unroll
         for (int a = 0; a < K1_RA; ++a) {
           acc[a][cc] = mfma_bf16(ah[a], bh, acc[a][cc]);
@@ -188,34 +181,36 @@ void k_ef_mq(const DevMat* __restrict__ mats, const Work* __restrict__ work,
     }
   };
 
-  const int nsteps = (npad + KS - 1) / KS;       // Q^T rows are padded to a whole stage
-  Frag cur;
+  // Per stage: barrier (the previous stage's fragments are read) -> this stage into LDS ->
+  // next stage's loads issued -> barrier -> MFMAs while those loads are in flight.
+  const int nsteps = npad / KS;                 // Q^T rows are padded to a whole stage
+  if (threadIdx.x == 0) s_bad = 0;
+  Raw cur;
   load_stage(0);
   load_m(0, cur);
-  store_stage(0);
-  __syncthreads();
-  int ks = 0;
-  for (; ks + 1 < nsteps; ++ks) {
-    Frag nxt;
-    load_stage((ks + 1) * KS);
-    load_m((ks + 1) * KS, nxt);
-    compute(ks & 1, cur);
-    store_stage((ks & 1) ^ 1);
-    cur = nxt;
+  for (int ks = 0; ks < nsteps; ++ks) {
     __syncthreads();
+    put_m(cur);
+    store_stage();
+    if (ks + 1 < nsteps) {
+      load_stage((ks + 1) * KS);
+      load_m((ks + 1) * KS, cur);
+    }
+    __syncthreads();
+    compute();
   }
-  compute(ks & 1, cur);
 
   // C layout of v_mfma_f32_16x16x32: lane holds rows 4g..4g+3, column c of the 16x16 tile.
   GLOBAL float* __restrict__ praw = gbl(d.p_raw);
-  if (row0 + K1_RA * 16 <= m) {
+  const int wrow0 = row0 + wv * (K1_RA * 16);
+  if (wrow0 + K1_RA * 16 <= m) {
 #pragma unroll
     for (int a = 0; a < K1_RA; ++a)
 #pragma unroll
       for (int cc = 0; cc < RTC; ++cc)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          praw[(int64_t)(row0 + a * 16 + 4 * g + i) * rpad + rc0 + cc * 16 + c] = acc[a][cc][i];
+          praw[(int64_t)(wrow0 + a * 16 + 4 * g + i) * rpad + rc0 + cc * 16 + c] = acc[a][cc][i];
   } else {
 #pragma unroll
     for (int a = 0; a < K1_RA; ++a)
@@ -223,28 +218,30 @@ void k_ef_mq(const DevMat* __restrict__ mats, const Work* __restrict__ work,
       for (int cc = 0; cc < RTC; ++cc)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int row = row0 + a * 16 + 4 * g + i;
+          const int row = wrow0 + a * 16 + 4 * g + i;
           if (row < m) praw[(int64_t)row * rpad + rc0 + cc * 16 + c] = acc[a][cc][i];
         }
   }
 
-  // Flag: M non-finite somewhere in this wave's rows is rare; only then are the inputs G and
-  // E of those rows examined, so the flag is exactly "G or E holds inf/NaN" (M may also be
+  // Flag: M non-finite somewhere in this workgroup's rows is rare; only then are the inputs G
+  // and E of those rows examined, so the flag is exactly "G or E holds inf/NaN" (M may also be
   // non-finite through s or fp32 overflow).
-  if (__builtin_amdgcn_ballot_w64(mbad) != 0) {
+  if (__builtin_amdgcn_ballot_w64(mbad) != 0 && lane == 0) s_bad = 1;
+  __syncthreads();
+  if (s_bad != 0) {
     bool bad = false;
-    for (int col = 8 * g; col < n; col += 32) {
+    for (int col = 4 * lu; col < n; col += KS) {
 #pragma unroll
-      for (int a = 0; a < K1_RA; ++a) {
-        const int row = row0 + a * 16 + c;
+      for (int st = 0; st < NST; ++st) {
+        const int row = row0 + lr + LROWS * st;
         const bool ok = row < m;
-        Raw8<GT> gr;
-        Raw8E er;
+        GradVec<GT, 4> gr;
+        GradVec<G_F32, 4> er;
         gr.load(rg, ok ? (uint32_t)(row * ldg + col) * GB : kOOB);
         er.load(re, ok ? (uint32_t)(row * lde + col) * 4u : kOOB);
-        const f32x8 gf = gr.f32(), ef = er.f32();
+        const f32x4 gf = gr.f32(), ef = er.f32();
 #pragma unroll
-        for (int e = 0; e < 8; ++e) bad |= nonfinite(gf[e]) || nonfinite(ef[e]);
+        for (int e = 0; e < 4; ++e) bad |= nonfinite(gf[e]) || nonfinite(ef[e]);
       }
     }
     if (bad) flags[wi.mat] = 1;
@@ -271,7 +268,7 @@ int ef_mq_k_per_stage() { return KS; }
 hipError_t launch_ef_mq(int gt, int rtc, const DevMat* mats, const Work* work, int n_work,
                         const float* scale, uint8_t* flags, hipStream_t s) {
   if (n_work <= 0) return hipSuccess;
-  const dim3 grid(n_work), block(K1_W * kWave);
+  const dim3 grid(n_work), block(K1_THREADS);
   switch (gt) {
     case G_F16: return launch_gt<G_F16>(rtc, grid, block, s, mats, work, scale, flags);
     case G_BF16: return launch_gt<G_BF16>(rtc, grid, block, s, mats, work, scale, flags);
