@@ -59,7 +59,96 @@ def parse(argv=None):
                     help="only run a plain device copy of 2 GiB (reads 2 GiB, writes 2 GiB) three "
                          "times; under rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE scale the "
                          "traffic counters of the library kernels")
+    ap.add_argument("--pmc-summary", metavar="DIR", default=None,
+                    help="only summarise rocprofv3 --pmc CSV output: DIR holds pmc_FETCH_SIZE/, "
+                         "pmc_WRITE_SIZE/ (bench runs) and pmccopy_FETCH_SIZE/, pmccopy_WRITE_SIZE/ "
+                         "(copy calibration runs); prints per-kernel HBM bytes per launch")
     return ap.parse_args(argv)
+
+
+# ------------------------------------------------------------------------------------------
+# HBM traffic from rocprofv3 counters
+# ------------------------------------------------------------------------------------------
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_64rb_r112.txt")
+COPY_BYTES = 1 << 31          # the calibration copy reads and writes 2 GiB per launch
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the library's HIP sources: traffic counters taken on other sources are stale."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "rank_gradient_compression_powersgd_amd", "csrc", "*"))):
+        if f.endswith((".hip", ".h")):
+            with open(f, "rb") as fh:
+                h.update(os.path.basename(f).encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def _short_kernel(name: str) -> str:
+    import re
+    name = name.replace("psgd::(anonymous namespace)::", "").replace("void ", "")
+    return re.sub(r"\(.*", "", name)
+
+
+def _pmc_means(path: str, counter: str):
+    """Mean counter value (KiB, as rocprofv3 reports these counters) per kernel name."""
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            if row["Counter_Name"] != counter:
+                continue
+            vals.setdefault(_short_kernel(row["Kernel_Name"]), []).append(float(row["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}
+
+
+def pmc_summary(d: str) -> int:
+    fe = _pmc_means(os.path.join(d, "pmc_FETCH_SIZE"), "FETCH_SIZE")
+    wr = _pmc_means(os.path.join(d, "pmc_WRITE_SIZE"), "WRITE_SIZE")
+    cf = _pmc_means(os.path.join(d, "pmccopy_FETCH_SIZE"), "FETCH_SIZE")
+    cw = _pmc_means(os.path.join(d, "pmccopy_WRITE_SIZE"), "WRITE_SIZE")
+    # the calibration copy: the elementwise kernel launched three times on 2 GiB
+    ck = [k for k in cf if "elementwise" in k and cf[k][1] >= 3]
+    if not ck:
+        print("no calibration copy kernel found", file=sys.stderr)
+        return 1
+    f_copy = max(cf[k][0] for k in ck) * 1024.0
+    w_copy = max(cw[k][0] for k in cw if "elementwise" in k) * 1024.0
+    sf, sw = COPY_BYTES / f_copy, COPY_BYTES / w_copy
+    print(f"calibration copy (2 GiB read, 2 GiB written per launch): FETCH_SIZE reads "
+          f"{f_copy / 2**30:.3f} GiB -> scale {sf:.3f}; WRITE_SIZE reads {w_copy / 2**30:.3f} GiB -> "
+          f"scale {sw:.3f}")
+    numel = 1511522304
+    algo = {"k_ef_mq": 6 * numel, "k_mtp": 6 * numel, "k_decomp": 14 * numel}
+    print(f"{'kernel':34s} {'launches':>8s} {'fetch GB':>9s} {'write GB':>9s} {'total GB':>9s} {'algorithmic GB':>15s}")
+    for k in sorted(fe):
+        if not k.startswith("k_"):
+            continue
+        f = fe[k][0] * 1024.0 * sf
+        w = wr.get(k, (0.0, 0))[0] * 1024.0 * sw
+        base = k.split("<")[0]
+        a = algo.get(base)
+        print(f"{k:34s} {fe[k][1]:8d} {f / 1e9:9.3f} {w / 1e9:9.3f} {(f + w) / 1e9:9.3f} "
+              f"{(a / 1e9 if a else float('nan')):15.3f}")
+        if base == "k_decomp":
+            print(f"TRAFFIC decompress {int(f + w)} fetch {int(f)} write {int(w)} source {kernel_source_hash()}")
+    return 0
+
+
+def recorded_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` recorded from the counter runs, or None when absent or
+    taken on other kernel sources."""
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    for ln in lines:
+        f = ln.split()
+        if len(f) >= 9 and f[0] == "TRAFFIC" and f[1] == kernel and f[8] == kernel_source_hash():
+            return int(f[2])
+    return None
 
 
 class Hip:
@@ -142,6 +231,8 @@ def cpu_baseline(seconds: float):
 
 def main(argv=None) -> int:
     a = parse(argv)
+    if a.pmc_summary:
+        return pmc_summary(a.pmc_summary)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (--gpus {a.gpus}, WORLD_SIZE {world}): the "
@@ -213,6 +304,8 @@ def main(argv=None) -> int:
     dom = max(STREAMING, key=lambda n: kern[n])
     roof = dict(rooflines[dom])
     roof["kernel"] = dom
+    if a.workload == 3 and not a.no_out and a.n_blocks in (None, 64):
+        roof["traffic"] = recorded_traffic(dom)
 
     ms_per_step = wall * 1e3 / K
     value = w.grad_bytes * K / wall / 1e9
