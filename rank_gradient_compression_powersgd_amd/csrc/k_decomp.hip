@@ -43,20 +43,23 @@ constexpr int kLdsBytes = kStageBytes > kTileBytes ? kStageBytes : kTileBytes;
 // each) or writing 4 rows (4 units each) hit 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int swz3(int rr, int q) { return q ^ ((rr >> 2) & 3); }
 
+// G, E and out are streamed with the non-temporal policy: they are touched once, and evicting
+// them first keeps the factor tiles, which neighbouring workgroups re-read, in L2.
+constexpr int kPol = kNonTemporal;
 template <int GT> struct Raw4;
 template <> struct Raw4<G_F16> {
   u32x2 v;
-  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { v = bload8(r, off); }
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { v = bload8<kPol>(r, off); }
   __device__ __forceinline__ f32x4 f32() const { return __builtin_convertvector(__builtin_bit_cast(f16x4, v), f32x4); }
 };
 template <> struct Raw4<G_BF16> {
   u32x2 v;
-  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { v = bload8(r, off); }
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { v = bload8<kPol>(r, off); }
   __device__ __forceinline__ f32x4 f32() const { return __builtin_convertvector(__builtin_bit_cast(bf16x4, v), f32x4); }
 };
 template <> struct Raw4<G_F32> {
   u32x4 v;
-  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { v = bload16(r, off); }
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { v = bload16<kPol>(r, off); }
   __device__ __forceinline__ f32x4 f32() const { return __builtin_bit_cast(f32x4, v); }
 };
 
@@ -79,7 +82,7 @@ void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
     for (int idx = threadIdx.x; idx < K3_TM * C4; idx += K3_THREADS) {
       const int row = m0 + idx / C4, col = n0 + 4 * (idx % C4);
       const bool ok = row < m && col < n;
-      bstore16(u32x4{0, 0, 0, 0}, re, ok ? (uint32_t)(row * lde + col) * 4u : kOOB);
+      bstore16<kPol>(u32x4{0, 0, 0, 0}, re, ok ? (uint32_t)(row * lde + col) * 4u : kOOB);
     }
     return;
   }
@@ -207,7 +210,7 @@ void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
     gv[st].load(rg, offset(st, ldg, GB));
-    ev[st] = bload16(re, offset(st, lde, 4u));
+    ev[st] = bload16<kPol>(re, offset(st, lde, 4u));
   }
   {
     int ep[4];
@@ -238,8 +241,8 @@ void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
     f32x4 en;
 #pragma unroll
     for (int i = 0; i < 4; ++i) en[i] = __builtin_fmaf(s, gf[i], ef[i]) - dv[i];
-    bstore16(__builtin_bit_cast(u32x4, en), re, offset(st, lde, 4u));
-    bstore16(__builtin_bit_cast(u32x4, dv), ro, offset(st, ldo, 4u));
+    bstore16<kPol>(__builtin_bit_cast(u32x4, en), re, offset(st, lde, 4u));
+    bstore16<kPol>(__builtin_bit_cast(u32x4, dv), ro, offset(st, ldo, 4u));
   }
 }
 

@@ -36,6 +36,12 @@
 #define K1_OCC 2     // workgroups per CU the register budget is sized for (one converts while the other multiplies)
 #endif
 #define K1_KSUB 2    // 32-column MFMA k groups per pipeline stage
+#ifndef K1_POLG
+#define K1_POLG 0
+#endif
+#ifndef K1_POLE
+#define K1_POLE 0
+#endif
 
 namespace psgd {
 namespace {
@@ -123,8 +129,8 @@ void k_ef_mq(const DevMat* __restrict__ mats, const Work* __restrict__ work,
     for (int st = 0; st < NST; ++st) {
       const int row = row0 + lr + LROWS * st;
       const bool ok = row < m && col < n;
-      f.gr[st].load(rg, ok ? (uint32_t)(row * ldg + col) * GB : kOOB);
-      f.er[st].load(re, ok ? (uint32_t)(row * lde + col) * 4u : kOOB);
+      f.gr[st].template load<K1_POLG>(rg, ok ? (uint32_t)(row * ldg + col) * GB : kOOB);
+      f.er[st].template load<K1_POLE>(re, ok ? (uint32_t)(row * lde + col) * 4u : kOOB);
     }
   };
   bool mbad = false;     // some M element of this lane was not finite

@@ -26,6 +26,12 @@ namespace {
 #ifndef K2_TC
 #define K2_TC 4      // consecutive columns per lane = column tiles per wave (2 or 4)
 #endif
+#ifndef K2_POLG
+#define K2_POLG 0
+#endif
+#ifndef K2_POLE
+#define K2_POLE 0
+#endif
 #ifndef K2_OCC
 #define K2_OCC 1     // workgroups per CU the register budget is sized for
 #endif
@@ -100,8 +106,8 @@ void k_mtp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
     for (int kk = 0; kk < 8; ++kk) {
       const int row = k0 + 8 * g + kk;
       const bool ok = colok && row < m;
-      f.gr[kk].load(rg, ok ? (uint32_t)(row * ldg + colbase) * GB : kOOB);
-      f.er[kk].load(re, ok ? (uint32_t)(row * lde + colbase) * 4u : kOOB);
+      f.gr[kk].template load<K2_POLG>(rg, ok ? (uint32_t)(row * ldg + colbase) * GB : kOOB);
+      f.er[kk].template load<K2_POLE>(re, ok ? (uint32_t)(row * lde + colbase) * 4u : kOOB);
     }
   };
 
