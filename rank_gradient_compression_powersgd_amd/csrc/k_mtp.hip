@@ -35,10 +35,19 @@ namespace {
 #ifndef K2_OCC
 #define K2_OCC 1     // workgroups per CU the register budget is sized for
 #endif
-constexpr int LDS_K = 32;                 // LDS row = 32 bf16 = 4 16-byte units, XOR-swizzled
-// Physical unit of logical unit q in row rr: 16 lanes reading 16 consecutive rows (one unit
-// each) or writing 4 rows (4 units each) hit 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int swz2(int rr, int q) { return q ^ ((rr >> 2) & 3); }
+#ifndef K2_KSUB
+#define K2_KSUB 2    // 32-row MFMA k groups per pipeline stage (rows of M in flight per stage)
+#endif
+constexpr int KR = 32 * K2_KSUB;          // rows of M per stage
+constexpr int LDS_K = KR;                 // LDS row = KR bf16, 16-byte units XOR-swizzled
+constexpr int UPR = KR / 8;               // 16-byte units per LDS row
+// Physical unit of logical unit q in row rr: the 16 lanes of a fragment read (16 consecutive
+// rows, one unit each) hit 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz2(int rr, int q) {
+  if constexpr (UPR == 4) return q ^ ((rr >> 2) & 3);
+  else return q ^ ((rr >> 1) & 7);
+}
+static_assert(UPR == 4 || UPR == 8, "stage of 32 or 64 rows");
 constexpr int TC = K2_TC;
 constexpr int WCOLS = 16 * TC;            // columns per wave
 
@@ -68,8 +77,8 @@ void k_mtp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][RTC * 16][LDS_K];
 
-  // P^T staging: RTC*16 rank rows x 32 m x {hi, lo}; threads past the last unit repeat it.
-  constexpr int UNITS = RTC * 16 * 4 * 2;
+  // P^T staging: RTC*16 rank rows x KR m x {hi, lo}; threads past the last unit repeat it.
+  constexpr int UNITS = RTC * 16 * UPR * 2;
   constexpr int THREADS = K2_W * kWave;
   constexpr int UPT = (UNITS + THREADS - 1) / THREADS;
   u32x4 stage[UPT];
@@ -77,10 +86,10 @@ void k_mtp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   auto unit = [&](int j, int& arr, int& rr, int& q4) {
     int u = threadIdx.x + j * THREADS;
     u = u < UNITS ? u : UNITS - 1;
-    arr = u / (RTC * 64);
-    const int rem = u - arr * (RTC * 64);
-    rr = rem >> 2;
-    q4 = rem & 3;
+    arr = u / (RTC * 16 * UPR);
+    const int rem = u - arr * (RTC * 16 * UPR);
+    rr = rem / UPR;
+    q4 = rem % UPR;
   };
   auto load_stage = [&](int k0) {
 #pragma unroll
@@ -99,16 +108,18 @@ void k_mtp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
     }
   };
 
-  // 8 rows k0 + 8g + kk, TC columns colbase..; out-of-range reads give zeros.
-  struct Frag { GradVec<GT, TC> gr[8]; GradVec<G_F32, TC> er[8]; };
+  // sub-stage j: 8 rows k0 + 32j + 8g + kk, TC columns colbase..; out-of-range reads give zeros.
+  struct Frag { GradVec<GT, TC> gr[K2_KSUB][8]; GradVec<G_F32, TC> er[K2_KSUB][8]; };
   auto load_m = [&](int k0, Frag& f) {
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int row = k0 + 8 * g + kk;
-      const bool ok = colok && row < m;
-      f.gr[kk].template load<K2_POLG>(rg, ok ? (uint32_t)(row * ldg + colbase) * GB : kOOB);
-      f.er[kk].template load<K2_POLE>(re, ok ? (uint32_t)(row * lde + colbase) * 4u : kOOB);
-    }
+    for (int j = 0; j < K2_KSUB; ++j)
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const int row = k0 + 32 * j + 8 * g + kk;
+        const bool ok = colok && row < m;
+        f.gr[j][kk].template load<K2_POLG>(rg, ok ? (uint32_t)(row * ldg + colbase) * GB : kOOB);
+        f.er[j][kk].template load<K2_POLE>(re, ok ? (uint32_t)(row * lde + colbase) * 4u : kOOB);
+      }
   };
 
   f32x4 acc[RTC][TC];
@@ -118,33 +129,36 @@ void k_mtp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
     for (int t = 0; t < TC; ++t) acc[i][t] = f32x4{0, 0, 0, 0};
 
   auto compute = [&](int buf, const Frag& f) {
-    // B-fragments: tile t takes column t of every loaded row (k = 8g + kk).
-    f32x8 mt[TC];
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const auto gf = f.gr[kk].f32();
-      const auto ef = f.er[kk].f32();
+    for (int j = 0; j < K2_KSUB; ++j) {
+      // B-fragments: tile t takes column t of every loaded row (k = 32j + 8g + kk).
+      f32x8 mt[TC];
 #pragma unroll
-      for (int t = 0; t < TC; ++t) mt[t][kk] = __builtin_fmaf(s, gf[t], ef[t]);
-    }
-    bf16x8 bh[TC], bl[TC];
+      for (int kk = 0; kk < 8; ++kk) {
+        const auto gf = f.gr[j][kk].f32();
+        const auto ef = f.er[j][kk].f32();
 #pragma unroll
-    for (int t = 0; t < TC; ++t) split_bf16(mt[t], bh[t], bl[t]);
+        for (int t = 0; t < TC; ++t) mt[t][kk] = __builtin_fmaf(s, gf[t], ef[t]);
+      }
+      bf16x8 bh[TC], bl[TC];
 #pragma unroll
-    for (int i = 0; i < RTC; ++i) {
-      const int pq = 8 * swz2(i * 16 + c, g);
-      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&lds[buf][0][i * 16 + c][pq]);
-      const bf16x8 al = *reinterpret_cast<const bf16x8*>(&lds[buf][1][i * 16 + c][pq]);
+      for (int t = 0; t < TC; ++t) split_bf16(mt[t], bh[t], bl[t]);
 #pragma unroll
-      for (int t = 0; t < TC; ++t) {
-        acc[i][t] = mfma_bf16(ah, bh[t], acc[i][t]);
-        acc[i][t] = mfma_bf16(ah, bl[t], acc[i][t]);
-        acc[i][t] = mfma_bf16(al, bh[t], acc[i][t]);
+      for (int i = 0; i < RTC; ++i) {
+        const int pq = 8 * swz2(i * 16 + c, 4 * j + g);
+        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&lds[buf][0][i * 16 + c][pq]);
+        const bf16x8 al = *reinterpret_cast<const bf16x8*>(&lds[buf][1][i * 16 + c][pq]);
+#pragma unroll
+        for (int t = 0; t < TC; ++t) {
+          acc[i][t] = mfma_bf16(ah, bh[t], acc[i][t]);
+          acc[i][t] = mfma_bf16(ah, bl[t], acc[i][t]);
+          acc[i][t] = mfma_bf16(al, bh[t], acc[i][t]);
+        }
       }
     }
   };
 
-  const int nsteps = mpad / 32;
+  const int nsteps = mpad / KR;                // P^T columns are padded to a whole stage
   Frag cur;
   load_stage(0);
   load_m(0, cur);
@@ -153,8 +167,8 @@ void k_mtp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   int ks = 0;
   for (; ks + 1 < nsteps; ++ks) {
     Frag nxt;
-    load_stage((ks + 1) * 32);
-    load_m((ks + 1) * 32, nxt);
+    load_stage((ks + 1) * KR);
+    load_m((ks + 1) * KR, nxt);
     compute(ks & 1, cur);
     store_stage((ks & 1) ^ 1);
     cur = nxt;
@@ -235,6 +249,7 @@ hipError_t launch_gt(int rtc, dim3 grid, dim3 block, hipStream_t s, const DevMat
 }  // namespace
 
 int mtp_cols_per_block() { return K2_W * WCOLS; }
+int mtp_rows_per_stage() { return KR; }
 
 hipError_t launch_mtp(int gt, int rtc, const DevMat* mats, const Work* work, int n_work,
                       const float* scale, hipStream_t s) {

@@ -125,7 +125,7 @@ struct DevMat {
   int32_t rpad;      // r rounded up to 16 (MFMA tile)
   int32_t kpad3;     // r rounded up to 32 (K of the fp16 decompression MFMA)
   int32_t npad;      // n rounded up to the k extent of one K1 stage
-  int32_t mpad;      // m rounded up to 32
+  int32_t mpad;      // m rounded up to a whole stage of the M^T P kernel
   int32_t gram_parts;
   int32_t gram_rows;   // rows per Gram partial (multiple of 16)
   uint32_t g_bytes, e_bytes, o_bytes;   // byte spans of G, E and out (buffer ranges, < 2^31)

@@ -16,6 +16,7 @@ namespace psgd {
 int ef_mq_rows_per_block();
 int ef_mq_k_per_stage();
 int mtp_cols_per_block();
+int mtp_rows_per_stage();
 int gs_apply_rows_per_block();
 int decomp_tile_m();
 int decomp_tile_n();
@@ -198,7 +199,7 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
     d.m = (int)a.m; d.n = (int)a.n; d.block = a.block; d.r = r;
     d.rpad = rpad; d.kpad3 = kpad3;
     d.npad = (int)rup(a.n, psgd::ef_mq_k_per_stage());   // Q^T covers whole K1 stages
-    d.mpad = (int)rup(a.m, 32);
+    d.mpad = (int)rup(a.m, psgd::mtp_rows_per_stage());   // P^T covers whole K2 stages
     d.gram_rows = big ? psgd::kGramRowsBig : psgd::kGramRows;
     d.gram_parts = (int)((a.m + d.gram_rows - 1) / d.gram_rows);
     const int gsz = gt == psgd::G_F32 ? 4 : 2;
