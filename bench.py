@@ -52,6 +52,10 @@ def parse(argv=None):
     ap.add_argument("--workload", type=int, default=3, choices=(2, 3))
     ap.add_argument("--n-blocks", type=int, default=None, help="resblocks of workload 3 (default 64)")
     ap.add_argument("--no-out", action="store_true", help="do not write the decompressed gradient")
+    ap.add_argument("--inplace", action="store_true",
+                    help="in-place form: backprop has accumulated s_b G into the error buffers, so "
+                         "no gradient is read (value still counts the fp16 gradient bytes the "
+                         "step replaces)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the CPU oracle sample (whole resblocks)")
@@ -180,7 +184,7 @@ class Hip:
         self.lib.hipEventDestroy(ev)
 
 
-def build_workload(config: int, n_blocks, write_out: bool):
+def build_workload(config: int, n_blocks, write_out: bool, inplace: bool = False):
     import torch
     import workloads as wl
     from rank_gradient_compression_powersgd_amd import PowerSGDGroup
@@ -191,7 +195,13 @@ def build_workload(config: int, n_blocks, write_out: bool):
         grads.append(wl.gradient_torch(w, s, 0, dev))
         q0.append(wl.initial_q_torch(w, s, dev))
     scale = torch.tensor(wl.scales_np(w), device=dev)
-    group = PowerSGDGroup(grads, [s.block for s in w.matrices], scale, w.rank, q0, None, write_out)
+    err = None
+    if inplace:
+        # the error buffers hold M = s_b G (zero previous error); no gradient tensors remain
+        err = [g.float().mul_(float(scale[s.block])) for g, s in zip(grads, w.matrices)]
+        grads = [None] * len(grads)
+        torch.cuda.empty_cache()
+    group = PowerSGDGroup(grads, [s.block for s in w.matrices], scale, w.rank, q0, err, write_out)
     passthrough = [torch.from_numpy(wl.passthrough_np(config, w.n_blocks)).to(dev).reshape(-1)]
     torch.cuda.synchronize()
     return w, group, passthrough
@@ -255,7 +265,7 @@ def main(argv=None) -> int:
     psgd.load_library()
     hip = Hip()
     log(f"building workload {a.workload} ...")
-    w, group, passthrough = build_workload(a.workload, a.n_blocks, not a.no_out)
+    w, group, passthrough = build_workload(a.workload, a.n_blocks, not a.no_out, a.inplace)
     stream = int(torch.cuda.current_stream().cuda_stream)
     nslot = len(psgd.PROFILE_SLOTS)
 
@@ -292,6 +302,8 @@ def main(argv=None) -> int:
         hip.destroy(s1)
 
     gsz = 2 if w.dtype in ("f16", "bf16") else 4
+    if a.inplace:
+        gsz = 0                        # no gradient is read
     numel = w.numel
     per_elem = {"ef_mq": gsz + 4, "mtp": gsz + 4, "decompress": gsz + 8 + (0 if a.no_out else 4)}
     rooflines = {}
@@ -304,7 +316,7 @@ def main(argv=None) -> int:
     dom = max(STREAMING, key=lambda n: kern[n])
     roof = dict(rooflines[dom])
     roof["kernel"] = dom
-    if a.workload == 3 and not a.no_out and a.n_blocks in (None, 64):
+    if a.workload == 3 and not a.no_out and not a.inplace and a.n_blocks in (None, 64):
         roof["traffic"] = recorded_traffic(dom)
 
     ms_per_step = wall * 1e3 / K
@@ -328,6 +340,7 @@ def main(argv=None) -> int:
                          f"{w.dtype} matrices (qkv 3968x1488, attn-out 496x3968, mlp-in 3968x1984, "
                          f"mlp-out 1984x3968), {numel} elements, rank {w.rank}"),
             "grad_dtype": w.dtype, "rank": w.rank, "matrices": len(w.matrices),
+            "mode": "in-place (M accumulated in the error buffer)" if a.inplace else "gradient + error buffer",
             "grad_bytes": w.grad_bytes, "decompressed_out": not a.no_out,
             "arithmetic": "M and E fp32; products as split bf16/fp16 MFMA with fp32 accumulation; "
                           "orthonormalisation fp64",

@@ -67,6 +67,10 @@ typedef enum psgd_dtype {
 /*
  * One gradient matrix and its state. Row-major, element (i, j) of G at grad[i * ld_grad + j].
  *  grad    m x n gradient, dtype of the plan (read only). ld_grad >= n, ld_grad % 8 == 0.
+ *          NULL selects the in-place form: the caller has already accumulated s_b * G into
+ *          the error buffer, so err holds M; s_b is not applied to the matrix and no gradient
+ *          is read (4 bytes per element per pass instead of 6 for an fp16 gradient). ld_grad
+ *          is then ignored, and the flag reports a non-finite element of M.
  *  err     m x n fp32 error buffer E (read and written by psgd_decompress_update; read by
  *          psgd_compress). ld_err >= n, ld_err % 4 == 0.
  *  q       n x r fp32 warm start (row-major, leading dimension r). Read by psgd_compress,

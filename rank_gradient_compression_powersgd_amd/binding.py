@@ -135,8 +135,9 @@ def dtype_code(torch_dtype) -> int:
 
 
 def make_matrix(grad, err, q, q_next, p, block: int, out=None) -> psgd_matrix:
-    """psgd_matrix over torch tensors (row-major; leading dimensions from the strides)."""
-    m, n = grad.shape
+    """psgd_matrix over torch tensors (row-major; leading dimensions from the strides).
+    grad=None describes an in-place matrix: err already holds M = s_b G + E."""
+    m, n = (grad if grad is not None else err).shape
     for name, t, shape in (("err", err, (m, n)), ("q", q, None), ("q_next", q_next, None),
                            ("p", p, None), ("out", out, (m, n))):
         if t is None:
@@ -149,7 +150,7 @@ def make_matrix(grad, err, q, q_next, p, block: int, out=None) -> psgd_matrix:
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
     return psgd_matrix(
-        grad=_ptr(grad), ld_grad=grad.stride(0),
+        grad=_ptr(grad), ld_grad=grad.stride(0) if grad is not None else 0,
         err=_ptr(err), ld_err=err.stride(0),
         q=_ptr(q), q_next=_ptr(q_next), p=_ptr(p),
         out=_ptr(out), ld_out=out.stride(0) if out is not None else 0,

@@ -194,7 +194,7 @@ void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   const int ldg = (int)d.ld_grad, ldo = (int)d.ld_out;
   const GLOBAL int32_t* __restrict__ pexp = gbl(d.p3_exp);     // padded to whole tiles
   const GLOBAL int32_t* __restrict__ qexp = gbl(d.q3_exp);
-  const float s = scale[d.block];
+  const float s = d.grad ? scale[d.block] : 0.0f;   // in-place matrices: E already holds M
   constexpr int GB = GradIO<GT>::kBytes;
   constexpr int CQ = K3_TN / 4;                      // 4-column groups per row
   constexpr int RSTEP = K3_THREADS / CQ;             // rows covered by one pass of the workgroup

@@ -75,7 +75,7 @@ void k_ef_mq(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   const rsrc_t re = make_rsrc(d.err, d.e_bytes);
   const GLOBAL uint16_t* __restrict__ qth = gbl(d.qt_hi);
   const GLOBAL uint16_t* __restrict__ qtl = gbl(d.qt_lo);
-  const float s = scale[d.block];
+  const float s = d.grad ? scale[d.block] : 0.0f;   // in-place matrices: E already holds M
   constexpr int GB = GradIO<GT>::kBytes;
 
   const int lane = threadIdx.x & (kWave - 1);

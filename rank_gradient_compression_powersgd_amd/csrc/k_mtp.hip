@@ -65,7 +65,7 @@ void k_mtp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   const rsrc_t re = make_rsrc(d.err, d.e_bytes);
   const GLOBAL uint16_t* __restrict__ pth = gbl(d.pt_hi);
   const GLOBAL uint16_t* __restrict__ ptl = gbl(d.pt_lo);
-  const float s = scale[d.block];
+  const float s = d.grad ? scale[d.block] : 0.0f;   // in-place matrices: E already holds M
   constexpr int GB = GradIO<GT>::kBytes;
 
   const int lane = threadIdx.x & (kWave - 1);

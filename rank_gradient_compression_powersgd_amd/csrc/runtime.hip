@@ -170,14 +170,14 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
   p->mats.resize(n_mats);
   for (int i = 0; i < n_mats; ++i) {
     const psgd_matrix& a = mats[i];
-    if (!a.grad || !a.err || !a.q || !a.q_next || !a.p)
-      return fail(ctx, PSGD_EINVAL, "matrix %d: grad, err, q, q_next and p are required", i);
+    if (!a.err || !a.q || !a.q_next || !a.p)
+      return fail(ctx, PSGD_EINVAL, "matrix %d: err, q, q_next and p are required", i);
     if (a.m < 1 || a.n < 1 || a.m > (1 << 28) || a.n > (1 << 28))
       return fail(ctx, PSGD_EINVAL, "matrix %d: bad shape %lld x %lld", i, (long long)a.m, (long long)a.n);
     if (a.n % 8 != 0) return fail(ctx, PSGD_EINVAL, "matrix %d: n = %lld is not a multiple of 8", i, (long long)a.n);
     if (r > a.m || r > a.n)
       return fail(ctx, PSGD_EINVAL, "matrix %d: rank %d exceeds min(m, n)", i, r);
-    if (a.ld_grad < a.n || a.ld_grad % 8 != 0)
+    if (a.grad && (a.ld_grad < a.n || a.ld_grad % 8 != 0))
       return fail(ctx, PSGD_EINVAL, "matrix %d: ld_grad must be >= n and a multiple of 8", i);
     if (a.ld_err < a.n || a.ld_err % 4 != 0)
       return fail(ctx, PSGD_EINVAL, "matrix %d: ld_err must be >= n and a multiple of 4", i);
@@ -203,7 +203,7 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
     d.gram_rows = big ? psgd::kGramRowsBig : psgd::kGramRows;
     d.gram_parts = (int)((a.m + d.gram_rows - 1) / d.gram_rows);
     const int gsz = gt == psgd::G_F32 ? 4 : 2;
-    const int64_t gb = ((a.m - 1) * a.ld_grad + a.n) * gsz;
+    const int64_t gb = a.grad ? ((a.m - 1) * a.ld_grad + a.n) * gsz : 0;   // no G: every load reads 0
     const int64_t eb = ((a.m - 1) * a.ld_err + a.n) * 4;
     const int64_t ob = a.out ? ((a.m - 1) * a.ld_out + a.n) * 4 : 0;
     if (gb >= (int64_t(1) << 31) || eb >= (int64_t(1) << 31) || ob >= (int64_t(1) << 31))

@@ -13,7 +13,9 @@ from . import binding as B
 class PowerSGDGroup:
     """State of a group: per matrix G (caller-filled each step), E, Q, Q_next, P, optional D.
 
-    grads: list of 2-D device tensors (fp16, bf16 or fp32, all the same dtype, unit row stride)
+    grads: list of 2-D device tensors (fp16, bf16 or fp32, all the same dtype, unit row stride);
+           an entry None makes that matrix in-place (its err tensor, which must then be given,
+           already holds M = s_b G + E)
     blocks: per matrix index into `scale`
     scale: device fp32 tensor of per-resblock multipliers
     q0: list of n x r fp32 initial warm starts (copied)
@@ -30,20 +32,25 @@ class PowerSGDGroup:
         self.grads = list(grads)
         self.blocks = list(blocks)
         self.scale = scale
-        dev = self.grads[0].device
+        if err is None and any(g is None for g in self.grads):
+            raise ValueError("in-place matrices (grad None) need their err tensors")
+        dev = (self.grads[0] if self.grads[0] is not None else err[0]).device
         self.err = ([torch.zeros(g.shape, dtype=torch.float32, device=dev) for g in self.grads]
                     if err is None else list(err))
+        shapes = [tuple(e.shape) for e in self.err]
         self.q = [q.to(device=dev, dtype=torch.float32).contiguous().clone() for q in q0]
         self.q_next = [torch.empty_like(q) for q in self.q]
-        self.p = [torch.empty((g.shape[0], rank), dtype=torch.float32, device=dev) for g in self.grads]
-        self.out = [torch.empty(g.shape, dtype=torch.float32, device=dev) if write_out else None
-                    for g in self.grads]
+        self.p = [torch.empty((sh[0], rank), dtype=torch.float32, device=dev) for sh in shapes]
+        self.out = [torch.empty(sh, dtype=torch.float32, device=dev) if write_out else None
+                    for sh in shapes]
         self.flags = torch.zeros(len(self.grads), dtype=torch.uint8, device=dev)
         self.skip = torch.zeros(1, dtype=torch.int32, device=dev)
         self.ctx = B.psgd_create(device, rank)
         mats = [B.make_matrix(g, e, q, qn, p, b, o) for g, e, q, qn, p, b, o in
                 zip(self.grads, self.err, self.q, self.q_next, self.p, self.blocks, self.out)]
-        self.plan = B.psgd_plan_create(self.ctx, mats, B.dtype_code(self.grads[0].dtype),
+        given = [g for g in self.grads if g is not None]
+        self.plan = B.psgd_plan_create(self.ctx, mats,
+                                       B.dtype_code(given[0].dtype) if given else B.PSGD_F32,
                                        int(scale.numel()))
 
     def compress(self, stream=None):

@@ -342,3 +342,45 @@ def test_rank_deficient_second_pass(rank, true_rank):
     log(f"  |E|/|M| {np.linalg.norm(res['E'][0]) / np.linalg.norm(M):.2e}")
     assert np.linalg.norm(res["E"][0]) / np.linalg.norm(M) <= 1e-4
     case.close()
+
+
+# ------------------------------------------------------------------------------------------
+# in-place matrices: backprop has accumulated s_b G into the error buffer (grad NULL)
+# ------------------------------------------------------------------------------------------
+def test_inplace_matrices_match_oracle_and_skip():
+    """Two of three matrices in-place (err holds M, no gradient read); the third as usual. The
+    oracle sees the in-place matrices as G = 0, E = M. Then a non-finite element planted in an
+    in-place error buffer flags that matrix and skips the step (every error buffer zeroed)."""
+    import torch
+    shapes = [(513, 264), (300, 1048), (640, 512)]
+    rank = 24
+    rng = np.random.default_rng(31)
+    scales = np.array([0.75], np.float32)
+    q0 = [rng.standard_normal((n, rank)).astype(np.float32) for _, n in shapes]
+    Ms = [(rng.standard_normal((m, n)) * 0.3).astype(np.float32) for m, n in shapes]
+    G2 = wl.to_fp16(rng.standard_normal(shapes[2]))
+    E2 = (rng.standard_normal(shapes[2]) * 0.05).astype(np.float32)
+    from rank_gradient_compression_powersgd_amd import PowerSGDGroup
+    dev = torch.device("cuda", 0)
+    err = [torch.from_numpy(x).to(dev) for x in (Ms[0], Ms[1], E2)]
+    grads = [None, None, torch.from_numpy(G2).to(dev)]
+    group = PowerSGDGroup(grads, [0, 0, 0], torch.from_numpy(scales).to(dev), rank,
+                          [torch.from_numpy(q) for q in q0], err, True)
+    skip = group.step([], host=True)
+    torch.cuda.synchronize()
+    assert skip == 0
+    st = oracle.step_group([np.zeros(shapes[0], np.float32), np.zeros(shapes[1], np.float32),
+                            G2.astype(np.float32)], [Ms[0], Ms[1], E2], q0, [0, 0, 0], scales)
+    res = dict(E=[e.cpu().numpy() for e in group.err], Q=[q.cpu().numpy() for q in group.q],
+               P=[p.cpu().numpy() for p in group.p], D=[o.cpu().numpy() for o in group.out],
+               flags=group.flags.cpu().numpy())
+    assert not res["flags"].any()
+    compare_step(res, st, "in-place step")
+    group.err[1][7, 11] = float("nan")
+    skip = group.step([], host=True)
+    torch.cuda.synchronize()
+    assert skip == 1
+    assert list(group.flags.cpu().numpy()) == [0, 1, 0]
+    for e in group.err:
+        assert float(e.abs().max()) == 0.0
+    group.close()
