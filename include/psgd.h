@@ -143,6 +143,39 @@ psgd_status psgd_compress(psgd_ctx* ctx, psgd_plan* plan, const float* scale, ui
                           hipStream_t stream);
 
 /*
+ * The same compression split at the two points where a data-parallel group exchanges factors
+ * (the all-reduce of the low-rank factors instead of the gradients: "Zero-Shot Text-to-Image
+ * Generation — 中文验证版", sections 方法适配 and 证据). psgd_compress is exactly
+ * psgd_compress_p, psgd_orthogonalize and psgd_compress_q in a row. On several GPUs a step is
+ *     psgd_compress_p      -> raw factors M q of every matrix in the plan's factor buffer
+ *     all-reduce (mean) of the factor buffer across the group
+ *     psgd_orthogonalize   -> P (identical on every rank)
+ *     psgd_compress_q      -> q_next = M^T P of the local M
+ *     all-reduce (mean) of every q_next, then psgd_refresh_q
+ *     psgd_check_finite, all-reduce (max) of the skip word
+ *     psgd_decompress_update -> D = P q_next^T (identical on every rank), E = M_local - D
+ * The library issues no collective; on one GPU the exchanges are the identity.
+ *
+ * psgd_compress_p: clears flags, prepares the warm start, computes M q (and the flags).
+ * psgd_orthogonalize: orthonormalises the factor buffer's contents into p.
+ * psgd_compress_q: q_next = M^T p, and the decompression operand built from it.
+ * psgd_refresh_q: rebuilds the decompression operand from q_next (after q_next was reduced).
+ */
+psgd_status psgd_compress_p(psgd_ctx* ctx, psgd_plan* plan, const float* scale, uint8_t* flags,
+                            hipStream_t stream);
+psgd_status psgd_orthogonalize(psgd_ctx* ctx, psgd_plan* plan, hipStream_t stream);
+psgd_status psgd_compress_q(psgd_ctx* ctx, psgd_plan* plan, const float* scale, hipStream_t stream);
+psgd_status psgd_refresh_q(psgd_ctx* ctx, psgd_plan* plan, hipStream_t stream);
+
+/*
+ * The plan's factor buffer: one contiguous fp32 region holding M q of every matrix, matrix i
+ * row-major m_i x rpad at offset sum_{j<i} m_j * rpad (columns at or beyond r are zero).
+ * *count receives the number of floats, *rpad the padded rank. The buffer is owned by the plan
+ * and valid until psgd_plan_destroy.
+ */
+psgd_status psgd_factor_buffer(psgd_plan* plan, void** ptr, int64_t* count, int32_t* rpad);
+
+/*
  * Skip decision ("Zero-Shot Text-to-Image Generation — 中文验证版", section 方法适配: the
  * skip-update rule for non-finite values). *skip_dev = 1 when any flags[i] is set, any element
  * of the pass-through tensors is non-finite, or any of scale[0..n_blocks) is non-finite;

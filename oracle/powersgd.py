@@ -52,6 +52,7 @@ import numpy as np
 __all__ = [
     "as_f64", "gram_schmidt", "modified_gram_schmidt", "nonfinite", "MatrixStep",
     "step_matrix", "GroupStep", "step_group", "subspace_iteration", "truncation_error",
+    "DataParallelStep", "step_data_parallel",
 ]
 
 
@@ -160,6 +161,32 @@ def step_group(grads: Sequence, errs: Sequence, qs: Sequence, blocks: Sequence[i
         D.append(st.D)
         P.append(st.P)
     return GroupStep(flags, pflags, sflag, False, E_next, Q_next, D, P)
+
+
+@dataclasses.dataclass
+class DataParallelStep:
+    P: np.ndarray              # orthonormal factor, the same on every rank
+    Q_next: np.ndarray         # mean over ranks of M_i^T P
+    D: np.ndarray              # P @ Q_next.T, the same on every rank
+    E_next: List[np.ndarray]   # per rank: M_i - D
+
+
+def step_data_parallel(grads: Sequence, errs: Sequence, Q, s: float = 1.0) -> DataParallelStep:
+    """One step of one matrix across a data-parallel group of k ranks (float64).
+
+    The pages replace the all-reduce of the gradients by an all-reduce of the low-rank factors
+    ([card] 方法适配, 证据). They do not say where the mean is taken; the plainest order that
+    keeps P identical on every rank is read here: the raw factors M_i Q are averaged before
+    orthonormalisation, the products M_i^T P after it, and each rank keeps its own error
+    buffer E_i = M_i - P Q_next^T.
+    """
+    Ms = [float(s) * as_f64(g) + as_f64(e) for g, e in zip(grads, errs)]
+    Q = as_f64(Q)
+    k = len(Ms)
+    P = gram_schmidt(sum(M @ Q for M in Ms) / k)
+    Qn = sum(M.T @ P for M in Ms) / k
+    D = P @ Qn.T
+    return DataParallelStep(P, Qn, D, [M - D for M in Ms])
 
 
 def subspace_iteration(M, Q0, iters: int):

@@ -81,9 +81,15 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.psgd_debug_buffer.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp),
                                       ctypes.POINTER(i64), ctypes.POINTER(i32)]
     lib.psgd_profile_events.argtypes = [vp, ctypes.POINTER(vp), ctypes.c_int]
+    lib.psgd_compress_p.argtypes = [vp, vp, vp, vp, vp]
+    lib.psgd_orthogonalize.argtypes = [vp, vp, vp]
+    lib.psgd_compress_q.argtypes = [vp, vp, vp, vp]
+    lib.psgd_refresh_q.argtypes = [vp, vp, vp]
+    lib.psgd_factor_buffer.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.POINTER(i32)]
     for name in ("psgd_create", "psgd_destroy", "psgd_plan_create", "psgd_plan_destroy",
                  "psgd_compress", "psgd_check_finite", "psgd_decompress_update",
-                 "psgd_debug_buffer", "psgd_profile_events"):
+                 "psgd_debug_buffer", "psgd_profile_events", "psgd_compress_p", "psgd_orthogonalize",
+                 "psgd_compress_q", "psgd_refresh_q", "psgd_factor_buffer"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -172,6 +178,33 @@ def psgd_plan_destroy(plan: int) -> None:
 def psgd_compress(ctx: int, plan: int, scale, flags, stream=None) -> None:
     _check(ctx, "psgd_compress",
            load_library().psgd_compress(ctx, plan, _ptr(scale), _ptr(flags), _stream(stream)))
+
+
+def psgd_compress_p(ctx: int, plan: int, scale, flags, stream=None) -> None:
+    _check(ctx, "psgd_compress_p",
+           load_library().psgd_compress_p(ctx, plan, _ptr(scale), _ptr(flags), _stream(stream)))
+
+
+def psgd_orthogonalize(ctx: int, plan: int, stream=None) -> None:
+    _check(ctx, "psgd_orthogonalize", load_library().psgd_orthogonalize(ctx, plan, _stream(stream)))
+
+
+def psgd_compress_q(ctx: int, plan: int, scale, stream=None) -> None:
+    _check(ctx, "psgd_compress_q",
+           load_library().psgd_compress_q(ctx, plan, _ptr(scale), _stream(stream)))
+
+
+def psgd_refresh_q(ctx: int, plan: int, stream=None) -> None:
+    _check(ctx, "psgd_refresh_q", load_library().psgd_refresh_q(ctx, plan, _stream(stream)))
+
+
+def psgd_factor_buffer(plan: int):
+    """(device address, float count, rpad) of the plan's contiguous raw-factor buffer."""
+    ptr, count, rpad = ctypes.c_void_p(), ctypes.c_int64(), ctypes.c_int32()
+    _check(None, "psgd_factor_buffer",
+           load_library().psgd_factor_buffer(plan, ctypes.byref(ptr), ctypes.byref(count),
+                                             ctypes.byref(rpad)))
+    return ptr.value, count.value, rpad.value
 
 
 def psgd_check_finite(ctx: int, plan: int, flags, passthrough: Iterable, scale, skip_dev,

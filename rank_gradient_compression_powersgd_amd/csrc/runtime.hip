@@ -34,13 +34,14 @@ struct psgd_ctx {
 
 namespace {
 
-enum WorkKind { W_PREP, W_K1, W_GRAM, W_REDUCE, W_FACTOR, W_APPLY, W_K2, W_SPLIT3, W_K3, W_COMMIT,
-                W_KINDS };
+enum WorkKind { W_PREP, W_K1, W_GRAM, W_REDUCE, W_FACTOR, W_APPLY, W_K2, W_SPLIT3, W_SPLITQ, W_K3,
+                W_COMMIT, W_KINDS };
 
 }  // namespace
 
 struct psgd_plan {
   psgd_ctx* ctx = nullptr;
+  size_t praw_bytes = 0;   // the contiguous raw-factor region at the start of the workspace
   int n_mats = 0, n_blocks = 0, gt = 0, rt = 0, rtc = 0, chunks = 0;
   bool big = false;   // rank above one 128-column block: blocked orthonormalisation
   std::vector<DevMat> mats;
@@ -163,7 +164,13 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
   p->big = big;
 
   // ---- validate and lay out the workspace ---------------------------------------------
-  size_t ws = 0;
+  // The raw factors M q of all matrices come first, as one contiguous region (the buffer a
+  // data-parallel caller all-reduces between psgd_compress_p and psgd_orthogonalize).
+  size_t praw_total = 0;
+  for (int i = 0; i < n_mats; ++i)
+    if (mats[i].m >= 1 && mats[i].m <= (1 << 28)) praw_total += (size_t)mats[i].m * rpad * 4;
+  size_t praw_cursor = 0;
+  size_t ws = (size_t)rup((int64_t)praw_total, 256);
   auto take = [&](size_t bytes) { size_t o = ws; ws += (size_t)rup((int64_t)bytes, 256); return o; };
   struct Off { size_t p_raw, qth, qtl, pth, ptl, p3h, p3l, p3e, q3h, q3l, q3e, gram, tmat, wsum, p2, reorth; };
   std::vector<Off> offs(n_mats);
@@ -212,7 +219,8 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
     d.e_bytes = (uint32_t)eb;
     d.o_bytes = (uint32_t)ob;
     Off& o = offs[i];
-    o.p_raw = take((size_t)a.m * rpad * 4);
+    o.p_raw = praw_cursor;
+    praw_cursor += (size_t)a.m * rpad * 4;
     o.qth = take((size_t)rpad * d.npad * 2);
     o.qtl = take((size_t)rpad * d.npad * 2);
     o.pth = take((size_t)rpad * d.mpad * 2);
@@ -311,6 +319,10 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
       for (int r0 = 0; r0 < p->mats[i].n; r0 += 64) all.push_back(Work{i, r0, 1, 0});
     }
   end_kind(W_SPLIT3, false);
+  begin_kind(W_SPLITQ);
+  for (int i = 0; i < n_mats; ++i)
+    for (int r0 = 0; r0 < p->mats[i].n; r0 += 64) all.push_back(Work{i, r0, 1, 0});
+  end_kind(W_SPLITQ, false);
   begin_kind(W_K3);
   for (int i = 0; i < n_mats; ++i)
     for (int m0 = 0; m0 < p->mats[i].m; m0 += tm)
@@ -330,6 +342,7 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
   hipError_t e = hipMalloc(&p->workspace, ws ? ws : 256);
   if (e != hipSuccess) return fail(ctx, PSGD_ENOMEM, "workspace of %zu bytes: %s", ws, hipGetErrorString(e));
   p->ws_bytes = ws;
+  p->praw_bytes = praw_total;
   auto cleanup = [&]() {
     if (p->workspace) (void)hipFree(p->workspace);
     if (p->d_mats) (void)hipFree(p->d_mats);
@@ -380,18 +393,32 @@ psgd_status psgd_plan_destroy(psgd_plan* plan) {
   return PSGD_OK;
 }
 
-psgd_status psgd_compress(psgd_ctx* ctx, psgd_plan* plan, const float* scale, uint8_t* flags,
-                          hipStream_t stream) {
+namespace {
+psgd_status check_call(psgd_ctx* ctx, psgd_plan* plan) {
   if (!ctx) return PSGD_EINVAL;
   ctx->err.clear();
   if (!plan || plan->ctx != ctx) return fail(ctx, PSGD_EINVAL, "plan does not belong to this context");
-  if (!scale || !flags) return fail(ctx, PSGD_EINVAL, "scale and flags are required");
   HIPCHK(ctx, hipSetDevice(ctx->device), "hipSetDevice");
+  return PSGD_OK;
+}
+}  // namespace
+
+psgd_status psgd_compress_p(psgd_ctx* ctx, psgd_plan* plan, const float* scale, uint8_t* flags,
+                            hipStream_t stream) {
+  if (psgd_status st = check_call(ctx, plan); st != PSGD_OK) return st;
+  if (!scale || !flags) return fail(ctx, PSGD_EINVAL, "scale and flags are required");
   const DevMat* dm = plan->d_mats;
   auto W = [&](int k) { return plan->d_work + plan->off[k]; };
   HIPCHK(ctx, traced(ctx, S_ZERO_FLAGS, stream, [&] { return psgd::launch_zero_u8(flags, plan->n_mats, stream); }), "flag clear");
   HIPCHK(ctx, traced(ctx, S_PREP, stream, [&] { return psgd::launch_prep_qt(dm, W(W_PREP), plan->cnt[W_PREP], 0, stream); }), "warm-start operand");
   HIPCHK(ctx, traced(ctx, S_K1, stream, [&] { return psgd::launch_ef_mq(plan->gt, plan->rtc, dm, W(W_K1), plan->cnt[W_K1], scale, flags, stream); }), "M Q");
+  return PSGD_OK;
+}
+
+psgd_status psgd_orthogonalize(psgd_ctx* ctx, psgd_plan* plan, hipStream_t stream) {
+  if (psgd_status st = check_call(ctx, plan); st != PSGD_OK) return st;
+  const DevMat* dm = plan->d_mats;
+  auto W = [&](int k) { return plan->d_work + plan->off[k]; };
   const bool big = plan->big;
   HIPCHK(ctx, traced(ctx, S_GRAM, stream, [&] { return psgd::launch_gs_gram(plan->rt, big, 0, dm, W(W_GRAM), plan->cnt[W_GRAM], stream); }), "Gram");
   if (big)
@@ -405,9 +432,40 @@ psgd_status psgd_compress(psgd_ctx* ctx, psgd_plan* plan, const float* scale, ui
     if (e == hipSuccess) e = psgd::launch_gs_factor(big, 1, dm, W(W_FACTOR), plan->cnt[W_FACTOR], stream);
     if (e == hipSuccess) e = psgd::launch_gs_apply(plan->rt, big, 1, dm, W(W_APPLY), plan->cnt[W_APPLY], stream);
     return e; }), "second orthonormalisation pass");
+  return PSGD_OK;
+}
+
+psgd_status psgd_compress_q(psgd_ctx* ctx, psgd_plan* plan, const float* scale, hipStream_t stream) {
+  if (psgd_status st = check_call(ctx, plan); st != PSGD_OK) return st;
+  if (!scale) return fail(ctx, PSGD_EINVAL, "scale is required");
+  const DevMat* dm = plan->d_mats;
+  auto W = [&](int k) { return plan->d_work + plan->off[k]; };
   HIPCHK(ctx, traced(ctx, S_K2, stream, [&] { return psgd::launch_mtp(plan->gt, plan->rtc, dm, W(W_K2), plan->cnt[W_K2], scale, stream); }), "M^T P");
-  if (big)
+  if (plan->big)
     HIPCHK(ctx, traced(ctx, S_SPLIT3, stream, [&] { return psgd::launch_split3(dm, W(W_SPLIT3), plan->cnt[W_SPLIT3], stream); }), "decompression operands");
+  return PSGD_OK;
+}
+
+psgd_status psgd_refresh_q(psgd_ctx* ctx, psgd_plan* plan, hipStream_t stream) {
+  if (psgd_status st = check_call(ctx, plan); st != PSGD_OK) return st;
+  const DevMat* dm = plan->d_mats;
+  auto W = [&](int k) { return plan->d_work + plan->off[k]; };
+  HIPCHK(ctx, traced(ctx, S_SPLIT3, stream, [&] { return psgd::launch_split3(dm, W(W_SPLITQ), plan->cnt[W_SPLITQ], stream); }), "decompression operand of q_next");
+  return PSGD_OK;
+}
+
+psgd_status psgd_compress(psgd_ctx* ctx, psgd_plan* plan, const float* scale, uint8_t* flags,
+                          hipStream_t stream) {
+  if (psgd_status st = psgd_compress_p(ctx, plan, scale, flags, stream); st != PSGD_OK) return st;
+  if (psgd_status st = psgd_orthogonalize(ctx, plan, stream); st != PSGD_OK) return st;
+  return psgd_compress_q(ctx, plan, scale, stream);
+}
+
+psgd_status psgd_factor_buffer(psgd_plan* plan, void** ptr, int64_t* count, int32_t* rpad) {
+  if (!plan || !ptr || !count) return PSGD_EINVAL;
+  *ptr = plan->workspace;
+  *count = (int64_t)(plan->praw_bytes / 4);
+  if (rpad) *rpad = plan->mats.empty() ? 0 : plan->mats[0].rpad;
   return PSGD_OK;
 }
 

@@ -21,7 +21,9 @@ def _declared():
 def test_header_declares_the_step_calls():
     names = _declared()
     for n in ("psgd_compress", "psgd_check_finite", "psgd_decompress_update", "psgd_create",
-              "psgd_destroy", "psgd_plan_create", "psgd_plan_destroy", "psgd_last_error"):
+              "psgd_destroy", "psgd_plan_create", "psgd_plan_destroy", "psgd_last_error",
+              "psgd_compress_p", "psgd_orthogonalize", "psgd_compress_q", "psgd_refresh_q",
+              "psgd_factor_buffer"):
         assert n in names
 
 

@@ -384,3 +384,105 @@ def test_inplace_matrices_match_oracle_and_skip():
     for e in group.err:
         assert float(e.abs().max()) == 0.0
     group.close()
+
+
+# ------------------------------------------------------------------------------------------
+# data-parallel split calls: two ranks simulated on one GPU, factors averaged between calls
+# ------------------------------------------------------------------------------------------
+def _dev_copy(dst: int, src: int, nbytes: int):
+    import ctypes
+    lib = ctypes.CDLL("libamdhip64.so.7")
+    lib.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    assert lib.hipMemcpy(dst, src, nbytes, 3) == 0       # device to device
+
+
+def test_split_calls_two_simulated_ranks():
+    """psgd_compress_p -> mean of the factor buffers -> psgd_orthogonalize -> psgd_compress_q ->
+    mean of q_next -> psgd_refresh_q -> check -> decompress, for two ranks holding different
+    gradients of the same matrices (two plans on one GPU, torch doing the means), against the
+    oracle's data-parallel step: P and D identical on both ranks, each rank's own E."""
+    import torch
+    from rank_gradient_compression_powersgd_amd import PowerSGDGroup
+    from rank_gradient_compression_powersgd_amd import binding as B
+    shapes = [(520, 264), (300, 512)]
+    rank = 16
+    rng = np.random.default_rng(77)
+    q0 = [rng.standard_normal((n, rank)).astype(np.float32) for _, n in shapes]
+    scale = torch.tensor([0.5], device="cuda")
+    ranks = []
+    for k in range(2):
+        gs = [wl.to_fp16(rng.standard_normal(sh)) for sh in shapes]
+        es = [(rng.standard_normal(sh) * 0.05).astype(np.float32) for sh in shapes]
+        grp = PowerSGDGroup([torch.from_numpy(g).cuda() for g in gs], [0, 0], scale, rank,
+                            [torch.from_numpy(q) for q in q0],
+                            [torch.from_numpy(e).cuda() for e in es], True)
+        ranks.append((grp, gs, es))
+    for grp, _, _ in ranks:
+        B.psgd_compress_p(grp.ctx, grp.plan, grp.scale, grp.flags)
+    bufs = [B.psgd_factor_buffer(grp.plan) for grp, _, _ in ranks]
+    count = bufs[0][1]
+    torch.cuda.synchronize()
+    f = [torch.empty(count, device="cuda") for _ in ranks]
+    for t, (ptr, cnt, _) in zip(f, bufs):
+        assert cnt == count
+        _dev_copy(t.data_ptr(), ptr, 4 * count)
+    mean = (f[0] + f[1]) / 2
+    torch.cuda.synchronize()
+    for ptr, _, _ in bufs:
+        _dev_copy(ptr, mean.data_ptr(), 4 * count)
+    for grp, _, _ in ranks:
+        B.psgd_orthogonalize(grp.ctx, grp.plan)
+        B.psgd_compress_q(grp.ctx, grp.plan, grp.scale)
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        qm = (ranks[0][0].q_next[i] + ranks[1][0].q_next[i]) / 2
+        for grp, _, _ in ranks:
+            grp.q_next[i].copy_(qm)
+    torch.cuda.synchronize()
+    for grp, _, _ in ranks:
+        B.psgd_refresh_q(grp.ctx, grp.plan)
+        assert grp.check_finite([], host=True) == 0
+        grp.decompress_update()
+    torch.cuda.synchronize()
+    for i, sh in enumerate(shapes):
+        st = oracle.step_data_parallel([ranks[k][1][i].astype(np.float32) for k in range(2)],
+                                       [ranks[k][2][i] for k in range(2)], q0[i], 0.5)
+        P = [grp.p[i].cpu().numpy() for grp, _, _ in ranks]
+        D = [grp.out[i].cpu().numpy() for grp, _, _ in ranks]
+        assert np.array_equal(P[0], P[1]) and np.array_equal(D[0], D[1])
+        r = dict(P=rel(P[0], st.P), D=rel(D[0], st.D), Q=rel(ranks[0][0].q[i].cpu().numpy(), st.Q_next),
+                 E0=rel(ranks[0][0].err[i].cpu().numpy(), st.E_next[0]),
+                 E1=rel(ranks[1][0].err[i].cpu().numpy(), st.E_next[1]), orth=orth_err(P[0]))
+        log(f"  matrix {i} {sh}: " + " ".join(f"{k}={v:.2e}" for k, v in r.items()))
+        for k in ("P", "D", "Q", "E0", "E1"):
+            assert r[k] <= REL_TOL, (i, k, r[k])
+        assert r["orth"] <= ORTH_TOL
+    for grp, _, _ in ranks:
+        grp.close()
+
+
+def test_split_calls_equal_the_fused_call():
+    """On one GPU the exchanges are the identity: the split calls must give bit-identical
+    results to psgd_compress."""
+    import torch
+    from rank_gradient_compression_powersgd_amd import binding as B
+    outs = []
+    for split in (False, True):
+        w, specs, case = _shard_case(2, None, err_warm=True)
+        case.set_grads([wl.gradient_np(w, s, 2) for s in specs])
+        g = case.group
+        if split:
+            B.psgd_compress_p(g.ctx, g.plan, g.scale, g.flags)
+            B.psgd_orthogonalize(g.ctx, g.plan)
+            B.psgd_compress_q(g.ctx, g.plan, g.scale)
+            B.psgd_refresh_q(g.ctx, g.plan)
+        else:
+            g.compress()
+        g.check_finite([], host=True)
+        g.decompress_update()
+        torch.cuda.synchronize()
+        outs.append(case.fetch())
+        case.close()
+    for k in ("E", "Q", "P", "D"):
+        for a, b in zip(outs[0][k], outs[1][k]):
+            assert np.array_equal(a, b), k

@@ -205,3 +205,39 @@ def test_unmodified_mutant_passes():
     impl = _mutant()
     for check in pins.ALL_CHECKS:
         check(impl)
+
+
+# ------------------------------------------------------------------------------------------
+# data-parallel step (factor all-reduces), pinned to the single-GPU step it must reduce to
+# ------------------------------------------------------------------------------------------
+def test_data_parallel_identical_ranks_is_the_single_step():
+    """k ranks holding the same gradient and error buffer: the averaged factors equal each
+    rank's own, so the group step must be exactly the single-GPU step."""
+    rng = np.random.default_rng(901)
+    G = rng.standard_normal((40, 24))
+    E = rng.standard_normal((40, 24)) * 0.1
+    Q = rng.standard_normal((24, 5))
+    one = oracle.step_matrix(G, 0.5, E, Q)
+    dp = oracle.step_data_parallel([G] * 3, [E] * 3, Q, 0.5)
+    for a, b in ((dp.P, one.P), (dp.Q_next, one.Q_next), (dp.D, one.D)):
+        assert np.abs(a - b).max() <= 1e-12 * max(1.0, np.abs(b).max())
+    for e in dp.E_next:
+        assert np.abs(e - one.E_next).max() <= 1e-12 * max(1.0, np.abs(one.E_next).max())
+
+
+def test_data_parallel_mean_error_is_the_step_of_the_mean():
+    """Every product in the step is linear in M, so with the factors averaged across ranks the
+    decompressed gradient is the single step of the mean M, and the ranks' error buffers
+    average to that step's error buffer. Averaging P after orthonormalisation, or D instead of
+    Q, breaks this."""
+    rng = np.random.default_rng(902)
+    Gs = [rng.standard_normal((36, 20)) for _ in range(3)]
+    Es = [rng.standard_normal((36, 20)) * 0.2 for _ in range(3)]
+    Q = rng.standard_normal((20, 4))
+    dp = oracle.step_data_parallel(Gs, Es, Q, 1.0)
+    Mbar = sum(G + E for G, E in zip(Gs, Es)) / 3
+    one = oracle.step_matrix(Mbar, 1.0, np.zeros_like(Mbar), Q)
+    assert np.abs(dp.D - one.D).max() <= 1e-12 * np.abs(one.D).max()
+    assert np.abs(sum(dp.E_next) / 3 - one.E_next).max() <= 1e-12 * np.abs(one.E_next).max()
+    for G, E, En in zip(Gs, Es, dp.E_next):
+        assert np.abs(G + E - dp.D - En).max() == 0.0
