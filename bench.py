@@ -49,7 +49,7 @@ def parse(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=3, choices=(2, 3))
+    ap.add_argument("--workload", type=int, default=3, choices=(2, 3, 5))
     ap.add_argument("--n-blocks", type=int, default=None, help="resblocks of workload 3 (default 64)")
     ap.add_argument("--no-out", action="store_true", help="do not write the decompressed gradient")
     ap.add_argument("--inplace", action="store_true",
@@ -182,6 +182,19 @@ class Hip:
 
     def destroy(self, ev: int):
         self.lib.hipEventDestroy(ev)
+
+
+def workload_name(config: int, w, numel: int) -> str:
+    shapes = []
+    for s in w.matrices:
+        kind = s.name.split(".")[-1]
+        if all(k != kind for k, _ in shapes):
+            shapes.append((kind, f"{s.m}x{s.n}"))
+    what = ", ".join(f"{k} {mn}" for k, mn in shapes)
+    share = ("unsharded d_model=3968 resblock" if config == 5
+             else f"{w.n_blocks}-resblock d_model=3968 per-GPU shard")
+    return (f"{share}: {len(w.matrices)} {w.dtype} matrices ({what}), {numel} elements, "
+            f"rank {w.rank}")
 
 
 def build_workload(config: int, n_blocks, write_out: bool, inplace: bool = False):
@@ -336,9 +349,7 @@ def main(argv=None) -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": (f"{w.n_blocks}-resblock d_model=3968 per-GPU shard: {len(w.matrices)} "
-                         f"{w.dtype} matrices (qkv 3968x1488, attn-out 496x3968, mlp-in 3968x1984, "
-                         f"mlp-out 1984x3968), {numel} elements, rank {w.rank}"),
+            "workload": workload_name(a.workload, w, numel),
             "grad_dtype": w.dtype, "rank": w.rank, "matrices": len(w.matrices),
             "mode": "in-place (M accumulated in the error buffer)" if a.inplace else "gradient + error buffer",
             "grad_bytes": w.grad_bytes, "decompressed_out": not a.no_out,

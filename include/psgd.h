@@ -82,7 +82,8 @@ typedef enum psgd_dtype {
  *  m, n    shape; n % 8 == 0; 1 <= r <= min(m, n).
  *  block   index into the per-resblock scale array (0 <= block < n_blocks).
  * Every pointer must be 16-byte aligned. Buffers of different matrices must not overlap. The
- * byte span of each of G, E and out ((m - 1) * ld + n elements) must be below 2 GiB.
+ * byte span of each of G, E and out ((m - 1) * ld + n elements), and of q (n * r elements),
+ * must be below 2 GiB.
  */
 typedef struct psgd_matrix {
   const void* grad;   int64_t ld_grad;
@@ -205,12 +206,12 @@ psgd_status psgd_decompress_update(psgd_ctx* ctx, psgd_plan* plan, const float* 
  * Tracing hook. Install an array of n HIP events created by the caller with timing enabled.
  * While installed, the launch of each kernel in slot k is bracketed by hipEventRecord of
  * events[2k] (before) and events[2k+1] (after) on the call's stream; elapsed times between the
- * pair give that kernel's duration. Slots: 0 flag clear, 1 warm-start operand, 2 M Q with
- * error feedback, 3 Gram partials, 4 Gram-Schmidt, 5 orthonormal P, 6 M^T P, 7 skip clear,
- * 8 finite check, 9 decompression + error update, 10 q commit, 11 Gram sum (rank > 128 only),
- * 12 decompression operands (rank > 128 only), 13 second orthonormalisation pass (all four of
- * its launches; they return at once for matrices whose first pass was well conditioned).
- * Slots a call does not launch keep their events unrecorded. n must be at least 28.
+ * pair give that kernel's duration. Slots: 0 flag clear, 1 M Q with error feedback, 2 Gram
+ * partials, 3 Gram-Schmidt, 4 orthonormal P, 5 M^T P, 6 skip clear, 7 finite check,
+ * 8 decompression + error update, 9 q commit, 10 Gram sum (rank > 128 only), 11 decompression
+ * operands (rank > 128 only), 12 second orthonormalisation pass (all four of its launches;
+ * they return at once for matrices whose first pass was well conditioned).
+ * Slots a call does not launch keep their events unrecorded. n must be at least 26.
  * events == NULL (n ignored) removes the hook. The events stay owned by the caller.
  */
 psgd_status psgd_profile_events(psgd_ctx* ctx, hipEvent_t* events, int n);

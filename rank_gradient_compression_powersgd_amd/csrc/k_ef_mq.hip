@@ -19,8 +19,8 @@
 //   * each lane forms M for its elements, tests them, splits them into bf16 hi/lo and writes
 //     them to an LDS tile (rows x 64 columns, 16-byte units XOR-swizzled by row); the MFMA
 //     A-fragments are read from there;
-//   * the shared operand, Q^T split into bf16 hi/lo (prepared once per step), is staged in LDS
-//     beside it;
+//   * the shared operand, 64 rows of q, is read in fp32, split into bf16 hi/lo and staged in
+//     LDS beside it, transposed;
 //   * the flag test runs on M (one class test per element); only when the workgroup met a
 //     non-finite M are the inputs G and E of its rows examined, after the main loop, so the
 //     flag is exactly "G or E holds inf/NaN".
@@ -69,12 +69,11 @@ void k_ef_mq(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   const Work wi = work[xcd_remap(blockIdx.x, gridDim.x)];
   if (wi.mat < 0) return;
   const DevMat& d = mats[wi.mat];
-  const int m = d.m, n = d.n, npad = d.npad, rpad = d.rpad;
+  const int m = d.m, n = d.n, r = d.r, rpad = d.rpad;
   const int ldg = (int)d.ld_grad, lde = (int)d.ld_err;
   const rsrc_t rg = make_rsrc(d.grad, d.g_bytes);
   const rsrc_t re = make_rsrc(d.err, d.e_bytes);
-  const GLOBAL uint16_t* __restrict__ qth = gbl(d.qt_hi);
-  const GLOBAL uint16_t* __restrict__ qtl = gbl(d.qt_lo);
+  const rsrc_t rq = make_rsrc(d.q, (uint32_t)n * (uint32_t)r * 4u);
   const float s = d.grad ? scale[d.block] : 0.0f;   // in-place matrices: E already holds M
   constexpr int GB = GradIO<GT>::kBytes;
 
@@ -85,39 +84,71 @@ void k_ef_mq(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   const int rc0 = wi.b * RTC * 16;
   const int lu = threadIdx.x % LCOL, lr = threadIdx.x / LCOL;
 
-  __shared__ __attribute__((aligned(16))) uint16_t ldq[2][RTC * 16][LDS_K];   // Q^T hi, lo
-  __shared__ __attribute__((aligned(16))) uint16_t ldm[2][K1_ROWS][LDS_K];    // M hi, lo
+  // One LDS arena: the staged operands during the main loop, the output tile afterwards.
+  constexpr int RC = RTC * 16;                      // rank columns of this chunk
+  constexpr int PT_LD = RC + 4;                     // output tile row (padded against bank conflicts)
+  constexpr int kQBytes = 2 * RC * LDS_K * 2;
+  constexpr int kMBytes = 2 * K1_ROWS * LDS_K * 2;
+  constexpr int kPBytes = K1_ROWS * PT_LD * 4;
+  constexpr int kArena = kQBytes + kMBytes > kPBytes ? kQBytes + kMBytes : kPBytes;
+  __shared__ __attribute__((aligned(16))) unsigned char lds_raw[kArena];
+  auto& ldq = *reinterpret_cast<uint16_t (*)[2][RC][LDS_K]>(lds_raw);             // Q^T hi, lo
+  auto& ldm = *reinterpret_cast<uint16_t (*)[2][K1_ROWS][LDS_K]>(lds_raw + kQBytes);  // M hi, lo
   __shared__ int s_bad;
 
-  // Q^T staging: RTC*16 rank rows x KS k x {hi, lo} in 16-byte units; consecutive threads take
-  // consecutive units of a row (coalesced global reads). Threads past the last unit repeat it
-  // (same value to the same LDS address), so the code has no branch.
-  constexpr int QPR = KS / 8;                   // 16-byte units per rank row
-  constexpr int UNITS = RTC * 16 * QPR * 2;
-  constexpr int UPT = (UNITS + K1_THREADS - 1) / K1_THREADS;
-  u32x4 stage[UPT];
-  auto unit = [&](int j, int& arr, int& rr, int& q) {
+  // Warm-start staging: rows k0 .. k0 + KS - 1 of q (n x r fp32, row-major), ranks rc0 ..
+  // rc0 + RC - 1, split into bf16 hi + lo and transposed into ldq[hi/lo][rank][k]. A unit is 4
+  // consecutive ranks of the two rows k, k + 1: consecutive threads take consecutive rank
+  // groups of a row pair (coalesced reads of q), and every rank's (k, k + 1) pair becomes one
+  // 4-byte LDS store. Rows past n and ranks past r read zeros. Threads past the last unit
+  // repeat it (same values to the same LDS addresses), so the code has no branch.
+  constexpr int RG = RC / 4;                    // rank groups per row
+  constexpr int QUNITS = (KS / 2) * RG;
+  constexpr int UPT = (QUNITS + K1_THREADS - 1) / K1_THREADS;
+  const bool qvec = (r & 3) == 0;               // rows of q are whole 16-byte units
+  f32x4 stq[UPT][2];
+  auto qunit = [&](int j, int& kp, int& rg) {
     int u = threadIdx.x + j * K1_THREADS;
-    u = u < UNITS ? u : UNITS - 1;
-    arr = u / (RTC * 16 * QPR);
-    const int rem = u - arr * (RTC * 16 * QPR);
-    rr = rem / QPR;
-    q = rem % QPR;
+    u = u < QUNITS ? u : QUNITS - 1;
+    kp = u / RG;
+    rg = u - kp * RG;
   };
   auto load_stage = [&](int k0) {
 #pragma unroll
     for (int j = 0; j < UPT; ++j) {
-      int arr, rr, q;
-      unit(j, arr, rr, q);
-      stage[j] = *gcast<u32x4>((arr ? qtl : qth) + (int64_t)(rc0 + rr) * npad + k0 + 8 * q);
+      int kp, rg;
+      qunit(j, kp, rg);
+      const int rank = rc0 + 4 * rg;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = k0 + 2 * kp + h;
+        const bool ok = row < n;
+        if (qvec) {
+          stq[j][h] = __builtin_bit_cast(f32x4, bload16(rq, ok && rank < r ? (uint32_t)(row * r + rank) * 4u : kOOB));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            stq[j][h][e] = __builtin_bit_cast(float, bload4(rq, ok && rank + e < r ? (uint32_t)(row * r + rank + e) * 4u : kOOB));
+        }
+      }
     }
   };
   auto store_stage = [&]() {
 #pragma unroll
     for (int j = 0; j < UPT; ++j) {
-      int arr, rr, q;
-      unit(j, arr, rr, q);
-      *reinterpret_cast<u32x4*>(&ldq[arr][rr][8 * swz1(rr, q)]) = stage[j];
+      int kp, rg;
+      qunit(j, kp, rg);
+      const int qq = kp >> 2, w = (2 * kp) & 7;   // 16-byte unit of k = 2 kp, bf16 offset in it
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rr = 4 * rg + e;
+        const f32x2 x = {stq[j][0][e], stq[j][1][e]};
+        const bf16x2 hi = __builtin_convertvector(x, bf16x2);
+        const bf16x2 lo = __builtin_convertvector(x - __builtin_convertvector(hi, f32x2), bf16x2);
+        const int off = 8 * swz1(rr, qq) + w;
+        *reinterpret_cast<bf16x2*>(&ldq[0][rr][off]) = hi;
+        *reinterpret_cast<bf16x2*>(&ldq[1][rr][off]) = lo;
+      }
     }
   };
 
@@ -189,7 +220,7 @@ void k_ef_mq(const DevMat* __restrict__ mats, const Work* __restrict__ work,
 
   // Per stage: barrier (the previous stage's fragments are read) -> this stage into LDS ->
   // next stage's loads issued -> barrier -> MFMAs while those loads are in flight.
-  const int nsteps = npad / KS;                 // Q^T rows are padded to a whole stage
+  const int nsteps = (n + KS - 1) / KS;
   if (threadIdx.x == 0) s_bad = 0;
   Raw cur;
   load_stage(0);
@@ -207,26 +238,26 @@ void k_ef_mq(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   }
 
   // C layout of v_mfma_f32_16x16x32: lane holds rows 4g..4g+3, column c of the 16x16 tile.
+  // The tile goes through LDS so that the stores to P are whole 16-byte units on consecutive
+  // addresses (written straight from the C layout they would be 64-byte pieces of 4 rows).
+  // They are non-temporal: scattered among the reads of G and E, writes slow the read stream
+  // down well beyond their own size, and keeping them out of the caches costs it the least.
+  float* pt = reinterpret_cast<float*>(lds_raw);
+  __syncthreads();                              // the last stage's fragments have been read
+#pragma unroll
+  for (int a = 0; a < K1_RA; ++a)
+#pragma unroll
+    for (int cc = 0; cc < RTC; ++cc)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        pt[(wv * (K1_RA * 16) + a * 16 + 4 * g + i) * PT_LD + cc * 16 + c] = acc[a][cc][i];
+  __syncthreads();
   GLOBAL float* __restrict__ praw = gbl(d.p_raw);
-  const int wrow0 = row0 + wv * (K1_RA * 16);
-  if (wrow0 + K1_RA * 16 <= m) {
-#pragma unroll
-    for (int a = 0; a < K1_RA; ++a)
-#pragma unroll
-      for (int cc = 0; cc < RTC; ++cc)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          praw[(int64_t)(wrow0 + a * 16 + 4 * g + i) * rpad + rc0 + cc * 16 + c] = acc[a][cc][i];
-  } else {
-#pragma unroll
-    for (int a = 0; a < K1_RA; ++a)
-#pragma unroll
-      for (int cc = 0; cc < RTC; ++cc)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = wrow0 + a * 16 + 4 * g + i;
-          if (row < m) praw[(int64_t)row * rpad + rc0 + cc * 16 + c] = acc[a][cc][i];
-        }
+  const int rows = min(K1_ROWS, m - row0);
+  constexpr int U4 = RC / 4;                    // 16-byte units per row of the tile
+  for (int u = threadIdx.x; u < rows * U4; u += K1_THREADS) {
+    const int rr = u / U4, q = u - rr * U4;
+    __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(&pt[rr * PT_LD + 4 * q]), gcast<f32x4>(praw + (int64_t)(row0 + rr) * rpad + rc0 + 4 * q));
   }
 
   // Flag: M non-finite somewhere in this workgroup's rows is rare; only then are the inputs G
@@ -269,7 +300,6 @@ hipError_t launch_gt(int rtc, dim3 grid, dim3 block, hipStream_t s, const DevMat
 }  // namespace
 
 int ef_mq_rows_per_block() { return K1_ROWS; }
-int ef_mq_k_per_stage() { return KS; }
 
 hipError_t launch_ef_mq(int gt, int rtc, const DevMat* mats, const Work* work, int n_work,
                         const float* scale, uint8_t* flags, hipStream_t s) {

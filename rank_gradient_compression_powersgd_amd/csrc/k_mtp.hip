@@ -75,7 +75,14 @@ void k_mtp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   const bool colok = colbase < n;              // n % 8 == 0: TC-column groups are all in or out
   const int rc0 = wi.b * RTC * 16;
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][RTC * 16][LDS_K];
+  // One LDS arena: the staged P^T during the main loop, the output tile afterwards.
+  constexpr int RC = RTC * 16;                  // rank columns of this chunk
+  constexpr int QT_LD = RC + 4;                 // output tile row (padded against bank conflicts)
+  constexpr int kSBytes = 2 * 2 * RC * LDS_K * 2;
+  constexpr int kTBytes = K2_W * WCOLS * QT_LD * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char lds_raw[kSBytes > kTBytes ? kSBytes : kTBytes];
+  __shared__ int s_ex[K2_W * WCOLS];
+  auto& lds = *reinterpret_cast<uint16_t (*)[2][2][RC][LDS_K]>(lds_raw);
 
   // P^T staging: RTC*16 rank rows x KR m x {hi, lo}; threads past the last unit repeat it.
   constexpr int UNITS = RTC * 16 * UPR * 2;
@@ -177,61 +184,75 @@ void k_mtp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   compute(ks & 1, cur);
 
   // Output tile (i, t): lane holds Q'^T rows rc0 + 16i + 4g + {0..3}, i.e. Q'[colbase + t][..].
-  GLOBAL float* __restrict__ qn = gbl(d.q_next);
-  const bool full = (wi.a + wv * WCOLS + WCOLS <= n) && (r & 3) == 0 && rc0 + RTC * 16 <= r;
-  if (full) {
+  // The tile goes through LDS so that the stores to Q' and to the decompression operand are
+  // whole 16-byte units on consecutive addresses (from the C layout they would be 32- and
+  // 64-byte pieces of 16 rows), stored non-temporally as in the M Q kernel.
+  float* qt = reinterpret_cast<float*>(lds_raw);          // [K2_W * WCOLS][QT_LD]
+  const bool whole = RC == rpad;                // this chunk covers the whole padded rank
+  __syncthreads();                              // the staged P^T has been read
 #pragma unroll
-    for (int t = 0; t < TC; ++t)
+  for (int t = 0; t < TC; ++t) {
+    const int lc = wv * WCOLS + TC * c + t;     // column of the workgroup's block
+#pragma unroll
+    for (int i = 0; i < RTC; ++i)
+      *reinterpret_cast<f32x4*>(&qt[lc * QT_LD + i * 16 + 4 * g]) = acc[i][t];
+    if (whole) {
+      // Decompression operand: each row of Q' scaled by a power of two (its largest entry in
+      // [2^13, 2^14)) and split into fp16 hi + lo.
+      float amax = 0.0f;
 #pragma unroll
       for (int i = 0; i < RTC; ++i)
-        *gcast<f32x4>(qn + (int64_t)(colbase + t) * r + rc0 + i * 16 + 4 * g) = acc[i][t];
-  } else if (colok) {
 #pragma unroll
-    for (int t = 0; t < TC; ++t)
-#pragma unroll
-      for (int i = 0; i < RTC; ++i) {
-        const int rr = rc0 + i * 16 + 4 * g;
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-          if (rr + ii < r) qn[(int64_t)(colbase + t) * r + rr + ii] = acc[i][t][ii];
-      }
+        for (int ii = 0; ii < 4; ++ii) amax = fmaxf(amax, fabsf(acc[i][t][ii]));
+      amax = fmaxf(amax, __shfl_xor(amax, 16));
+      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      if (g == 0) s_ex[lc] = fp16_row_exponent(amax);
+    }
   }
+  __syncthreads();
 
-  // Decompression operand (only when this chunk covers the whole padded rank): each row of Q'
-  // scaled by a power of two and split into fp16 hi + lo.
-  if (RTC * 16 != rpad) return;
+  constexpr int THREADS_ = K2_W * kWave;
+  const int ncols = min(K2_W * WCOLS, n - wi.a);          // rows of Q' this workgroup owns
+  const int rend = min(r, rc0 + RC);
+  GLOBAL float* __restrict__ qn = gbl(d.q_next);
+  if ((r & 3) == 0) {
+    const int U4 = (rend - rc0) / 4;            // 16-byte units per row
+    for (int u = threadIdx.x; u < ncols * U4; u += THREADS_) {
+      const int j = u / U4, q = u - j * U4;
+      __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(&qt[j * QT_LD + 4 * q]), gcast<f32x4>(qn + (int64_t)(wi.a + j) * r + rc0 + 4 * q));
+    }
+  } else {
+    const int w = rend - rc0;
+    for (int u = threadIdx.x; u < ncols * w; u += THREADS_) {
+      const int j = u / w, q = u - j * w;
+      qn[(int64_t)(wi.a + j) * r + rc0 + q] = qt[j * QT_LD + q];
+    }
+  }
+  if (!whole) return;
+
   const int kpad3 = d.kpad3;
   GLOBAL uint16_t* __restrict__ q3h = gbl(d.q3_hi);
   GLOBAL uint16_t* __restrict__ q3l = gbl(d.q3_lo);
   GLOBAL int32_t* __restrict__ q3e = gbl(d.q3_exp);
+  constexpr int U8 = RC / 8;                    // 16-byte units of fp16 per row
+  for (int u = threadIdx.x; u < ncols * U8; u += THREADS_) {
+    const int j = u / U8, q = u - j * U8;
+    const int ex = s_ex[j];
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(&qt[j * QT_LD + 8 * q]);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(&qt[j * QT_LD + 8 * q + 4]);
+    uint32_t hw[4], lw[4];
 #pragma unroll
-  for (int t = 0; t < TC; ++t) {
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < RTC; ++i)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) amax = fmaxf(amax, fabsf(acc[i][t][ii]));
-    amax = fmaxf(amax, __shfl_xor(amax, 16));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
-    const int ex = fp16_row_exponent(amax);
-    const int ncol = colbase + t;
-    if (!colok) continue;
-#pragma unroll
-    for (int i = 0; i < RTC; ++i) {
-      const int rr = i * 16 + 4 * g;
-      uint16_t h4[4], l4[4];
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const float x = ldexpf(acc[i][t][ii], ex);
-        const _Float16 h = (_Float16)x;
-        h4[ii] = f16_bits(h);
-        l4[ii] = f16_bits((_Float16)(x - (float)h));
-      }
-      *gcast<u32x2>(q3h + (int64_t)ncol * kpad3 + rr) = u32x2{h4[0] | ((uint32_t)h4[1] << 16), h4[2] | ((uint32_t)h4[3] << 16)};
-      *gcast<u32x2>(q3l + (int64_t)ncol * kpad3 + rr) = u32x2{l4[0] | ((uint32_t)l4[1] << 16), l4[2] | ((uint32_t)l4[3] << 16)};
+    for (int e = 0; e < 4; ++e) {
+      const float a0 = ldexpf(e < 2 ? x0[2 * e] : x1[2 * e - 4], ex);
+      const float a1 = ldexpf(e < 2 ? x0[2 * e + 1] : x1[2 * e - 3], ex);
+      const _Float16 h0 = (_Float16)a0, h1 = (_Float16)a1;
+      hw[e] = f16_bits(h0) | ((uint32_t)f16_bits(h1) << 16);
+      lw[e] = f16_bits((_Float16)(a0 - (float)h0)) | ((uint32_t)f16_bits((_Float16)(a1 - (float)h1)) << 16);
     }
-    if (g == 0) q3e[ncol] = ex;
+    __builtin_nontemporal_store(u32x4{hw[0], hw[1], hw[2], hw[3]}, gcast<u32x4>(q3h + (int64_t)(wi.a + j) * kpad3 + 8 * q));
+    __builtin_nontemporal_store(u32x4{lw[0], lw[1], lw[2], lw[3]}, gcast<u32x4>(q3l + (int64_t)(wi.a + j) * kpad3 + 8 * q));
   }
+  for (int j = threadIdx.x; j < ncols; j += THREADS_) q3e[wi.a + j] = s_ex[j];
 }
 
 template <int GT>

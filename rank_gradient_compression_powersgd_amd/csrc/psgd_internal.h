@@ -13,6 +13,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
@@ -124,7 +126,7 @@ struct DevMat {
   int32_t m, n, block, r;
   int32_t rpad;      // r rounded up to 16 (MFMA tile)
   int32_t kpad3;     // r rounded up to 32 (K of the fp16 decompression MFMA)
-  int32_t npad;      // n rounded up to the k extent of one K1 stage
+  int32_t pad1_;
   int32_t mpad;      // m rounded up to a whole stage of the M^T P kernel
   int32_t gram_parts;
   int32_t gram_rows;   // rows per Gram partial (multiple of 16)
@@ -132,7 +134,6 @@ struct DevMat {
   uint32_t pad2_;
   // workspace (library owned)
   float* p_raw;                        // m x rpad fp32: M q before orthonormalisation
-  uint16_t* qt_hi; uint16_t* qt_lo;    // rpad x npad bf16: q^T split into hi + lo
   uint16_t* pt_hi; uint16_t* pt_lo;    // rpad x mpad bf16: P^T split into hi + lo
   uint16_t* p3_hi; uint16_t* p3_lo;    // m3 x kpad3 fp16: P * 2^p3_exp[row], split hi + lo
   int32_t* p3_exp;                     // m3 (m rounded up to a decompression tile; zero rows)
@@ -249,7 +250,6 @@ __device__ __forceinline__ f32x8 load_f32x8(const GLOBAL float* p) {
 namespace psgd {
 hipError_t launch_zero_u8(uint8_t* p, int n, hipStream_t s);
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
-hipError_t launch_prep_qt(const DevMat* mats, const Work* work, int n_work, int rpad_max, hipStream_t s);
 hipError_t launch_ef_mq(int gt, int rtc, const DevMat* mats, const Work* work, int n_work,
                         const float* scale, uint8_t* flags, hipStream_t s);
 hipError_t launch_gs_gram(int rt, bool big, int pass, const DevMat* mats, const Work* work, int n_work, hipStream_t s);

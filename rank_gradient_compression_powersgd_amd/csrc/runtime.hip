@@ -14,7 +14,6 @@
 
 namespace psgd {
 int ef_mq_rows_per_block();
-int ef_mq_k_per_stage();
 int mtp_cols_per_block();
 int mtp_rows_per_stage();
 int gs_apply_rows_per_block();
@@ -34,7 +33,7 @@ struct psgd_ctx {
 
 namespace {
 
-enum WorkKind { W_PREP, W_K1, W_GRAM, W_REDUCE, W_FACTOR, W_APPLY, W_K2, W_SPLIT3, W_SPLITQ, W_K3,
+enum WorkKind { W_K1, W_GRAM, W_REDUCE, W_FACTOR, W_APPLY, W_K2, W_SPLIT3, W_SPLITQ, W_K3,
                 W_COMMIT, W_KINDS };
 
 }  // namespace
@@ -72,7 +71,7 @@ psgd_status hip_fail(psgd_ctx* ctx, hipError_t e, const char* what) {
   return fail(ctx, PSGD_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-enum Slot { S_ZERO_FLAGS, S_PREP, S_K1, S_GRAM, S_FACTOR, S_APPLY, S_K2, S_ZERO_SKIP, S_CHECK,
+enum Slot { S_ZERO_FLAGS, S_K1, S_GRAM, S_FACTOR, S_APPLY, S_K2, S_ZERO_SKIP, S_CHECK,
             S_K3, S_COMMIT, S_REDUCE, S_SPLIT3, S_REORTH, S_SLOTS };
 
 // Launch `expr` in tracing slot `slot`, bracketed by the hook's events when installed.
@@ -172,7 +171,7 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
   size_t praw_cursor = 0;
   size_t ws = (size_t)rup((int64_t)praw_total, 256);
   auto take = [&](size_t bytes) { size_t o = ws; ws += (size_t)rup((int64_t)bytes, 256); return o; };
-  struct Off { size_t p_raw, qth, qtl, pth, ptl, p3h, p3l, p3e, q3h, q3l, q3e, gram, tmat, wsum, p2, reorth; };
+  struct Off { size_t p_raw, pth, ptl, p3h, p3l, p3e, q3h, q3l, q3e, gram, tmat, wsum, p2, reorth; };
   std::vector<Off> offs(n_mats);
   p->mats.resize(n_mats);
   for (int i = 0; i < n_mats; ++i) {
@@ -205,7 +204,6 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
     d.out = a.out; d.ld_out = a.ld_out;
     d.m = (int)a.m; d.n = (int)a.n; d.block = a.block; d.r = r;
     d.rpad = rpad; d.kpad3 = kpad3;
-    d.npad = (int)rup(a.n, psgd::ef_mq_k_per_stage());   // Q^T covers whole K1 stages
     d.mpad = (int)rup(a.m, psgd::mtp_rows_per_stage());   // P^T covers whole K2 stages
     d.gram_rows = big ? psgd::kGramRowsBig : psgd::kGramRows;
     d.gram_parts = (int)((a.m + d.gram_rows - 1) / d.gram_rows);
@@ -213,16 +211,15 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
     const int64_t gb = a.grad ? ((a.m - 1) * a.ld_grad + a.n) * gsz : 0;   // no G: every load reads 0
     const int64_t eb = ((a.m - 1) * a.ld_err + a.n) * 4;
     const int64_t ob = a.out ? ((a.m - 1) * a.ld_out + a.n) * 4 : 0;
-    if (gb >= (int64_t(1) << 31) || eb >= (int64_t(1) << 31) || ob >= (int64_t(1) << 31))
-      return fail(ctx, PSGD_EINVAL, "matrix %d: G, E and out must each span less than 2 GiB", i);
+    if (gb >= (int64_t(1) << 31) || eb >= (int64_t(1) << 31) || ob >= (int64_t(1) << 31) ||
+        a.n * r * 4 >= (int64_t(1) << 31))
+      return fail(ctx, PSGD_EINVAL, "matrix %d: G, E, out and q must each span less than 2 GiB", i);
     d.g_bytes = (uint32_t)gb;
     d.e_bytes = (uint32_t)eb;
     d.o_bytes = (uint32_t)ob;
     Off& o = offs[i];
     o.p_raw = praw_cursor;
     praw_cursor += (size_t)a.m * rpad * 4;
-    o.qth = take((size_t)rpad * d.npad * 2);
-    o.qtl = take((size_t)rpad * d.npad * 2);
     o.pth = take((size_t)rpad * d.mpad * 2);
     o.ptl = take((size_t)rpad * d.mpad * 2);
     const int64_t m3 = rup(a.m, psgd::decomp_tile_m()), n3 = rup(a.n, psgd::decomp_tile_n());
@@ -273,10 +270,6 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
   const int k2cols = psgd::mtp_cols_per_block();
   const int aprows = psgd::gs_apply_rows_per_block();
   const int tm = psgd::decomp_tile_m(), tn = psgd::decomp_tile_n();
-  begin_kind(W_PREP);
-  for (int i = 0; i < n_mats; ++i)
-    for (int n0 = 0; n0 < p->mats[i].n; n0 += 64) all.push_back(Work{i, n0, 0, 0});
-  end_kind(W_PREP, false);
   begin_kind(W_K1);
   for (int i = 0; i < n_mats; ++i)
     for (int ch = 0; ch < p->chunks; ++ch)
@@ -356,8 +349,6 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
     DevMat& d = p->mats[i];
     const Off& o = offs[i];
     d.p_raw = reinterpret_cast<float*>(base + o.p_raw);
-    d.qt_hi = reinterpret_cast<uint16_t*>(base + o.qth);
-    d.qt_lo = reinterpret_cast<uint16_t*>(base + o.qtl);
     d.pt_hi = reinterpret_cast<uint16_t*>(base + o.pth);
     d.pt_lo = reinterpret_cast<uint16_t*>(base + o.ptl);
     d.p3_hi = reinterpret_cast<uint16_t*>(base + o.p3h);
@@ -410,7 +401,6 @@ psgd_status psgd_compress_p(psgd_ctx* ctx, psgd_plan* plan, const float* scale, 
   const DevMat* dm = plan->d_mats;
   auto W = [&](int k) { return plan->d_work + plan->off[k]; };
   HIPCHK(ctx, traced(ctx, S_ZERO_FLAGS, stream, [&] { return psgd::launch_zero_u8(flags, plan->n_mats, stream); }), "flag clear");
-  HIPCHK(ctx, traced(ctx, S_PREP, stream, [&] { return psgd::launch_prep_qt(dm, W(W_PREP), plan->cnt[W_PREP], 0, stream); }), "warm-start operand");
   HIPCHK(ctx, traced(ctx, S_K1, stream, [&] { return psgd::launch_ef_mq(plan->gt, plan->rtc, dm, W(W_K1), plan->cnt[W_K1], scale, flags, stream); }), "M Q");
   return PSGD_OK;
 }
