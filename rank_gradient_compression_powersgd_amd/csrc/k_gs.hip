@@ -372,9 +372,180 @@ void k_gs_factor_blk(const DevMat* __restrict__ mats, const Work* __restrict__ w
 constexpr int GSA_RA = 2;                          // 16-row tiles per wave
 constexpr int GSA_ROWS = GSA_RA * 16 * (GS_THREADS / kWave);   // 128 rows per workgroup
 
-// Small ranks (BIG = false): all RT column tiles of P_hat for rows [a, a + 128). Large ranks
-// (BIG = true, RT = 8): the 128-column block b of P_hat; its fp16 decompression operand is
-// built afterwards by split3 (its row scale needs every column).
+// Small ranks (RT tiles of 16 columns, rpad <= 128): all columns of P_hat for rows
+// [a, a + 128). The P tile (128 rows x rpad, one contiguous block of the factor buffer) is
+// read into LDS with 16-byte loads, all in flight at once. Each wave then owns output column
+// tiles {t, RT - 1 - t} (T is upper triangular, so tile t costs t + 1 k tiles and every pair
+// costs RT + 1) for all 8 row tiles, or a share of the row tiles when there are fewer pairs
+// than waves: each fragment of T, read from L2, feeds every row tile of the wave. The k index
+// of an MFMA step is permuted within a 16-k tile (k = 16 kt + 4 g + ks), so that a lane takes
+// its 4 A values of a k tile from one 16-byte LDS read. Products and sums are fp64; P_hat is
+// rounded to fp32 once.
+template <int RT>
+__global__ __launch_bounds__(GS_THREADS, 2)
+void k_gs_apply_s(const DevMat* __restrict__ mats, const Work* __restrict__ work, int pass)
+{
+  const Work wi = work[xcd_remap(blockIdx.x, gridDim.x)];
+  if (wi.mat < 0) return;
+  const DevMat& d = mats[wi.mat];
+  const bool again = *d.reorth != 0;      // a second pass follows (pass 0) / runs (pass 1)
+  if (pass && !again) return;
+  const int m = d.m, r = d.r, rpad = d.rpad, mpad = d.mpad, kpad3 = d.kpad3;
+  const GLOBAL float* __restrict__ P = gbl(pass ? d.p2 : d.p_raw);
+  const GLOBAL double* __restrict__ Tm = gbl(d.tmat);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  const int c = lane & 15, g = lane >> 4;
+  const int row0 = wi.a;
+  const int rows = min(GSA_ROWS, m - row0);
+  constexpr int RC = RT * 16;
+  constexpr int LD = RC + 4;               // LDS row pitch (floats): rows stay 16-byte aligned
+  constexpr int NW = GS_THREADS / kWave;
+  constexpr int NRT = GSA_ROWS / 16;       // row tiles (8)
+
+  __shared__ __attribute__((aligned(16))) float S[GSA_ROWS * LD];
+  __shared__ int sexp[GSA_ROWS];
+
+  // (1) the P tile into LDS; rows past m are zero
+  constexpr int U4 = RT * 4;               // 16-byte units per row
+  constexpr int NL = GSA_ROWS * U4 / GS_THREADS;
+  static_assert(NL * GS_THREADS == GSA_ROWS * U4, "load units");
+  {
+    f32x4 v[NL];
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int u = threadIdx.x + j * GS_THREADS, rr = u / U4, q = u - rr * U4;
+      v[j] = rr < rows ? *gcast<f32x4>(P + (int64_t)(row0 + rr) * rpad + 4 * q) : f32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int u = threadIdx.x + j * GS_THREADS, rr = u / U4, q = u - rr * U4;
+      *reinterpret_cast<f32x4*>(&S[rr * LD + 4 * q]) = v[j];
+    }
+  }
+  __syncthreads();
+
+  // (2) this wave's column-tile pair and row tiles
+  constexpr int NG = (RT + 1) / 2;         // column-tile pairs
+  constexpr int WPG = NG >= NW ? 1 : NW / NG;   // waves per pair
+  constexpr int RPW = NRT / WPG;           // row tiles per wave
+  const int gi = wv % NG, rs = wv / NG;    // pair, row share
+  const bool active = wv < NG * WPG;
+  const int tA = gi, tB = RT - 1 - gi;     // tB == tA for the middle tile of odd RT
+  f64x4 acc[2][RPW];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int a = 0; a < RPW; ++a) acc[h][a] = f64x4{0, 0, 0, 0};
+  if (active) {
+#pragma unroll 1
+    for (int kt = 0; kt <= tB; ++kt) {
+      f32x4 av[RPW];
+#pragma unroll
+      for (int a = 0; a < RPW; ++a)
+        av[a] = *reinterpret_cast<const f32x4*>(&S[((rs + a * WPG) * 16 + c) * LD + 16 * kt + 4 * g]);
+      const bool useA = kt <= tA && tA != tB;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int64_t krow = (int64_t)(16 * kt + 4 * g + ks) * rpad;
+        const double bB = Tm[krow + 16 * tB + c];
+        const double bA = useA ? Tm[krow + 16 * tA + c] : 0.0;
+#pragma unroll
+        for (int a = 0; a < RPW; ++a) {
+          acc[1][a] = mfma_f64((double)av[a][ks], bB, acc[1][a]);
+          if (useA) acc[0][a] = mfma_f64((double)av[a][ks], bA, acc[0][a]);
+        }
+      }
+    }
+  }
+  __syncthreads();                         // every wave has read its A values
+  // C layout of v_mfma_f64_16x16x4f64: lane 16g + c, register i holds C[g + 4i][c].
+  if (active) {
+#pragma unroll
+    for (int a = 0; a < RPW; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = (rs + a * WPG) * 16 + g + 4 * i;
+        S[rr * LD + 16 * tB + c] = (float)acc[1][a][i];
+        if (tA != tB) S[rr * LD + 16 * tA + c] = (float)acc[0][a][i];
+      }
+  }
+  __syncthreads();
+
+  if (pass == 0 && again) {
+    // first pass of a matrix that needs two: the result is the second pass's input
+    GLOBAL float* __restrict__ p2 = gbl(d.p2);
+    for (int u = threadIdx.x; u < rows * U4; u += GS_THREADS) {
+      const int rr = u / U4, q = u - rr * U4;
+      *gcast<f32x4>(p2 + (int64_t)(row0 + rr) * rpad + 4 * q) = *reinterpret_cast<const f32x4*>(&S[rr * LD + 4 * q]);
+    }
+    return;
+  }
+
+  // (a) fp32 P_hat, m x r row-major
+  GLOBAL float* __restrict__ pout = gbl(d.p);
+  if ((r & 3) == 0) {
+    const int ur = r / 4;
+    for (int u = threadIdx.x; u < rows * ur; u += GS_THREADS) {
+      const int rr = u / ur, q = u - rr * ur;
+      *gcast<f32x4>(pout + (int64_t)(row0 + rr) * r + 4 * q) = *reinterpret_cast<const f32x4*>(&S[rr * LD + 4 * q]);
+    }
+  } else {
+    for (int u = threadIdx.x; u < rows * r; u += GS_THREADS) {
+      const int rr = u / r, cc = u - rr * r;
+      pout[(int64_t)(row0 + rr) * r + cc] = S[rr * LD + cc];
+    }
+  }
+  // (b) P_hat^T split bf16 hi/lo, rpad x mpad: 8 consecutive rows of one column per store
+  GLOBAL uint16_t* __restrict__ pth = gbl(d.pt_hi);
+  GLOBAL uint16_t* __restrict__ ptl = gbl(d.pt_lo);
+  for (int idx = threadIdx.x; idx < RC * (GSA_ROWS / 8); idx += GS_THREADS) {
+    const int col = idx / (GSA_ROWS / 8), r8 = (idx % (GSA_ROWS / 8)) * 8;
+    if (row0 + r8 >= mpad) continue;
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x0 = S[(r8 + 2 * e) * LD + col], x1 = S[(r8 + 2 * e + 1) * LD + col];
+      const __bf16 h0 = (__bf16)x0, h1 = (__bf16)x1;
+      h[e] = bf16_bits(h0) | ((uint32_t)bf16_bits(h1) << 16);
+      l[e] = bf16_bits((__bf16)(x0 - (float)h0)) | ((uint32_t)bf16_bits((__bf16)(x1 - (float)h1)) << 16);
+    }
+    *gcast<u32x4>(pth + (int64_t)col * mpad + row0 + r8) = u32x4{h[0], h[1], h[2], h[3]};
+    *gcast<u32x4>(ptl + (int64_t)col * mpad + row0 + r8) = u32x4{l[0], l[1], l[2], l[3]};
+  }
+  // (c) rows scaled by 2^e (largest entry in [2^13, 2^14)) and split fp16 hi/lo, m x kpad3
+  if (threadIdx.x < GSA_ROWS) {
+    float amax = 0.0f;
+    for (int cc = 0; cc < RC; ++cc) amax = fmaxf(amax, fabsf(S[threadIdx.x * LD + cc]));
+    sexp[threadIdx.x] = fp16_row_exponent(amax);
+  }
+  __syncthreads();
+  GLOBAL uint16_t* __restrict__ p3h = gbl(d.p3_hi);
+  GLOBAL uint16_t* __restrict__ p3l = gbl(d.p3_lo);
+  GLOBAL int32_t* __restrict__ p3e = gbl(d.p3_exp);
+  constexpr int U8 = RT * 2;               // 8-column units per row (rpad / 8)
+  for (int idx = threadIdx.x; idx < rows * U8; idx += GS_THREADS) {
+    const int rr = idx / U8, c8 = (idx % U8) * 8;
+    const int ex = sexp[rr];
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(&S[rr * LD + c8]);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(&S[rr * LD + c8 + 4]);
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float y0 = ldexpf(e < 2 ? x0[2 * e] : x1[2 * e - 4], ex);
+      const float y1 = ldexpf(e < 2 ? x0[2 * e + 1] : x1[2 * e - 3], ex);
+      const _Float16 h0 = (_Float16)y0, h1 = (_Float16)y1;
+      h[e] = f16_bits(h0) | ((uint32_t)f16_bits(h1) << 16);
+      l[e] = f16_bits((_Float16)(y0 - (float)h0)) | ((uint32_t)f16_bits((_Float16)(y1 - (float)h1)) << 16);
+    }
+    *gcast<u32x4>(p3h + (int64_t)(row0 + rr) * kpad3 + c8) = u32x4{h[0], h[1], h[2], h[3]};
+    *gcast<u32x4>(p3l + (int64_t)(row0 + rr) * kpad3 + c8) = u32x4{l[0], l[1], l[2], l[3]};
+  }
+  if ((int)threadIdx.x < rows) p3e[row0 + threadIdx.x] = sexp[threadIdx.x];
+}
+
+// Large ranks (rpad > 128, RT = 8): the 128-column block b of P_hat for rows [a, a + 128); its
+// fp16 decompression operand is built afterwards by split3 (its row scale needs every column).
 template <int RT, bool BIG>
 __global__ __launch_bounds__(GS_THREADS)
 void k_gs_apply(const DevMat* __restrict__ mats, const Work* __restrict__ work, int pass)
@@ -584,7 +755,7 @@ hipError_t launch_gs_apply(int rt, bool big, int pass, const DevMat* mats, const
     return hipGetLastError();
   }
   switch (rt) {
-#define CASE(R) case R: k_gs_apply<R, false><<<grid, block, 0, s>>>(mats, work, pass); break;
+#define CASE(R) case R: k_gs_apply_s<R><<<grid, block, 0, s>>>(mats, work, pass); break;
     CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
 #undef CASE
     default: return hipErrorInvalidValue;
