@@ -10,7 +10,11 @@ device synchronisation, inputs resident in HBM. Per-kernel durations come from H
 library records around each launch on the step's stream (psgd_profile_events), over the same
 timed steps. The `roofline` object is for the streaming kernel with the longest average
 duration. `cpu_baseline` times the float64 oracle on a bounded sample of the same workload
-(whole resblocks, on this host's cores).
+(whole resblocks, on this host's cores). `traffic` (HBM bytes per launch) and `mfma` (per
+multiplying kernel: MFMA flops per launch and the fraction of cycles its MFMA units were busy)
+come from the rocprofv3 counter runs summarised under profiles/; they are reported only while
+the library's HIP sources hash to the value recorded there. `mfma.achieved_tflops` divides
+the counted flops by the live kernel duration.
 
 One GPU only: --gpus above 1 exits with an error (the path has no multi-GPU leg here; the factor
 all-reduces are the identity on one GPU).
@@ -74,6 +78,11 @@ def parse(argv=None):
 # HBM traffic from rocprofv3 counters
 # ------------------------------------------------------------------------------------------
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_64rb_r112.txt")
+MFMA_FILE = os.path.join(ROOT, "profiles", "pmc_mfma_64rb_r112.txt")
+# library kernel (name before any template arguments) -> profiling slot
+KERNEL_SLOT = {"k_ef_mq": "ef_mq", "k_mtp": "mtp", "k_decomp": "decompress", "k_gs_gram": "gs_gram",
+               "k_gs_factor": "gs_factor", "k_gs_apply_s": "gs_apply", "k_gs_apply": "gs_apply"}
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f64": 78.6}
 COPY_BYTES = 1 << 31          # the calibration copy reads and writes 2 GiB per launch
 
 
@@ -95,8 +104,8 @@ def _short_kernel(name: str) -> str:
     return re.sub(r"\(.*", "", name)
 
 
-def _pmc_means(path: str, counter: str):
-    """Mean counter value (KiB, as rocprofv3 reports these counters) per kernel name."""
+def _pmc_values(path: str, counter: str):
+    """{kernel name: {dispatch id: counter value}} of one counter run."""
     import csv
     import glob
     vals = {}
@@ -104,8 +113,14 @@ def _pmc_means(path: str, counter: str):
         for row in csv.DictReader(open(f)):
             if row["Counter_Name"] != counter:
                 continue
-            vals.setdefault(_short_kernel(row["Kernel_Name"]), []).append(float(row["Counter_Value"]))
-    return {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}
+            k = _short_kernel(row["Kernel_Name"])
+            vals.setdefault(k, {})[row["Dispatch_Id"]] = float(row["Counter_Value"])
+    return vals
+
+
+def _pmc_means(path: str, counter: str):
+    """Mean counter value (KiB, as rocprofv3 reports these counters) per kernel name."""
+    return {k: (sum(v.values()) / len(v), len(v)) for k, v in _pmc_values(path, counter).items()}
 
 
 def pmc_summary(d: str) -> int:
@@ -136,9 +151,48 @@ def pmc_summary(d: str) -> int:
         a = algo.get(base)
         print(f"{k:34s} {fe[k][1]:8d} {f / 1e9:9.3f} {w / 1e9:9.3f} {(f + w) / 1e9:9.3f} "
               f"{(a / 1e9 if a else float('nan')):15.3f}")
-        if base == "k_decomp":
-            print(f"TRAFFIC decompress {int(f + w)} fetch {int(f)} write {int(w)} source {kernel_source_hash()}")
+        if base in ("k_ef_mq", "k_mtp", "k_decomp"):
+            print(f"TRAFFIC {KERNEL_SLOT[base]} {int(f + w)} fetch {int(f)} write {int(w)} source {kernel_source_hash()}")
+    mf = os.path.join(d, "pmc_MFMA")
+    if os.path.isdir(mf):
+        busy = _pmc_values(mf, "SQ_VALU_MFMA_BUSY_CYCLES")
+        gui = _pmc_values(mf, "GRBM_GUI_ACTIVE")
+        mops = {t: _pmc_values(mf, f"SQ_INSTS_VALU_MFMA_MOPS_{t.upper()}") for t in ("bf16", "f16", "f64")}
+        print()
+        print("MFMA counters, mean over the launches that multiply (a second-pass launch that returns at")
+        print("once is left out): busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs);")
+        print("flops = 512 x SQ_INSTS_VALU_MFMA_MOPS_<type>")
+        print(f"{'kernel':34s} {'launches':>8s} {'busy':>6s} {'bf16 GFLOP':>11s} {'f16 GFLOP':>10s} {'f64 GFLOP':>10s}")
+        for k in sorted(busy):
+            if not k.startswith("k_") or k not in gui:
+                continue
+            ids = [i for i in busy[k] if sum(mops[t].get(k, {}).get(i, 0.0) for t in mops) > 0]
+            if not ids:
+                continue
+            cyc = sum(gui[k][i] for i in ids) / 8.0
+            frac = sum(busy[k][i] for i in ids) / (cyc * 1024.0) if cyc > 0 else 0.0
+            fl = {t: sum(mops[t].get(k, {}).get(i, 0.0) for i in ids) / len(ids) * 512.0 for t in mops}
+            print(f"{k:34s} {len(ids):8d} {frac:6.3f} {fl['bf16'] / 1e9:11.1f} {fl['f16'] / 1e9:10.1f} "
+                  f"{fl['f64'] / 1e9:10.1f}")
+            base = k.split("<")[0]
+            if base in KERNEL_SLOT and any(fl.values()):
+                print(f"MFMA {KERNEL_SLOT[base]} busy {frac:.4f} bf16 {int(fl['bf16'])} f16 {int(fl['f16'])} "
+                      f"f64 {int(fl['f64'])} source {kernel_source_hash()}")
     return 0
+
+
+def recorded_mfma(slot: str):
+    """{"busy": fraction, dtype: flops per launch} of a kernel from the MFMA counter run, or None
+    when absent or taken on other kernel sources."""
+    try:
+        lines = open(MFMA_FILE).read().splitlines()
+    except OSError:
+        return None
+    for ln in lines:
+        f = ln.split()
+        if len(f) == 12 and f[0] == "MFMA" and f[1] == slot and f[11] == kernel_source_hash():
+            return {"busy": float(f[3]), "bf16": int(f[5]), "f16": int(f[7]), "f64": int(f[9])}
+    return None
 
 
 def recorded_traffic(kernel: str):
@@ -327,10 +381,23 @@ def main(argv=None) -> int:
                            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                            "bytes_per_launch": nbytes, "avg_ms": round(kern[name], 4)}
     dom = max(STREAMING, key=lambda n: kern[n])
+    counted = a.workload == 3 and not a.no_out and not a.inplace and a.n_blocks in (None, 64)
+    mfma = {}
+    if counted:
+        for name in STREAMING:
+            rooflines[name]["traffic"] = recorded_traffic(name)
+        # MFMA use of the kernels that multiply, from the counter run on the same sources
+        for name in ("ef_mq", "gs_gram", "gs_apply", "mtp", "decompress"):
+            rec = recorded_mfma(name)
+            if rec is None or name not in kern:
+                continue
+            dt = max(("bf16", "f16", "f64"), key=lambda t: rec[t])
+            tf = rec[dt] / (kern[name] * 1e-3) / 1e12
+            mfma[name] = {"dtype": dt, "flops_per_launch": rec[dt], "achieved_tflops": round(tf, 1),
+                          "peak_tflops": MFMA_PEAK_TFLOPS[dt], "frac": round(tf / MFMA_PEAK_TFLOPS[dt], 4),
+                          "busy": round(rec["busy"], 4)}
     roof = dict(rooflines[dom])
     roof["kernel"] = dom
-    if a.workload == 3 and not a.no_out and not a.inplace and a.n_blocks in (None, 64):
-        roof["traffic"] = recorded_traffic(dom)
 
     ms_per_step = wall * 1e3 / K
     value = w.grad_bytes * K / wall / 1e9
@@ -361,6 +428,7 @@ def main(argv=None) -> int:
         "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
         "streaming": rooflines,
         "mfma_equivalent_tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 1),
+        "mfma": mfma or None,
         "roofline": roof,
         "cpu_baseline": None,
     }
