@@ -193,7 +193,46 @@ __device__ double factor_block(double* W, double* T, const double* diag0, double
   return minratio;
 }
 
-// Ranks up to 128: W summed from the partials straight into LDS.
+// Ranks up to 128: the same recurrence in 16-column panels. W is summed from the partials
+// straight into LDS as full 16 x 16 blocks of its upper block triangle, beside the coefficient
+// matrix U (initially I; block column p of U becomes block column p of T). For each panel p:
+//   (A) one wave takes the diagonal block W_pp into registers and runs the column recurrence on
+//       it with lane shuffles (no barriers), giving the panel's local factor L (T_pp = L);
+//   (B) T_ip = U_ip L for i <= p, and the panel row of R, R_pj = L^T W_pj for j > p;
+//   (C) U_ij -= T_ip R_pj (i <= p < j) and W_ij -= R_pi^T R_pj (p < i <= j).
+// (B) and (C) are 16 x 16 x 16 block products on v_mfma_f64_16x16x4f64, one block per wave.
+// This is the right-looking blocked form of the column recurrence: every column still sees
+// the residual Gram entries of its own step, so dependent columns are dropped by the same test.
+constexpr int FB = 16;                 // panel width
+constexpr int FBP = FB + 1;            // LDS block row pitch (doubles): column reads spread over banks
+constexpr int FBS = FB * FBP;          // doubles per stored block
+constexpr int FNB = kBlk / FB;         // panels at most (8)
+constexpr int FNBLK = FNB * (FNB + 1) / 2;
+
+__device__ __forceinline__ int fblk(int i, int j, int nb) {   // upper block (i <= j), packed
+  return i * nb - (i * (i - 1)) / 2 + (j - i);
+}
+
+// C (+)= op(A) B for 16 x 16 blocks in LDS (pitch FBP). transA: op(A) = A^T. sub: C -= product,
+// else C = product. One wave; lane 16g + c.
+__device__ __forceinline__ void fblock_mm(double* C, const double* A, bool transA, const double* B,
+                                          bool sub, int c, int g)
+{
+  f64x4 acc = {0, 0, 0, 0};
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    const int k = 4 * st + g;
+    const double a = transA ? A[k * FBP + c] : A[c * FBP + k];
+    acc = mfma_f64(a, B[k * FBP + c], acc);
+  }
+  // C layout of v_mfma_f64_16x16x4f64: lane 16g + c, register i holds C[g + 4i][c].
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    double& cv = C[(g + 4 * i) * FBP + c];
+    cv = sub ? cv - acc[i] : acc[i];
+  }
+}
+
 __global__ __launch_bounds__(GSF_THREADS)
 void k_gs_factor(const DevMat* __restrict__ mats, const Work* __restrict__ work, int pass)
 {
@@ -201,37 +240,113 @@ void k_gs_factor(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   if (wi.mat < 0) return;
   const DevMat& d = mats[wi.mat];
   if (pass && *d.reorth == 0) return;
-  const int rp = d.rpad;
+  const int rp = d.rpad, nb = rp / FB;
   const int parts = d.gram_parts;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   const GLOBAL double* __restrict__ gram = gbl(d.gram);
   GLOBAL double* __restrict__ tmat = gbl(d.tmat);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  constexpr int NWV = GSF_THREADS / kWave;
+  const int c = lane & 15, g = lane >> 4;
 
-  __shared__ double W[kPackMax];
-  __shared__ double T[kPackMax];
+  __shared__ double Wb[FNBLK * FBS];
+  __shared__ double Ub[FNBLK * FBS];
+  __shared__ double Lsh[FBS];
   __shared__ double diag0[kBlk];
-  __shared__ double rrow[kBlk];
 
-  // W = sum of the partial Gram matrices in part order; T = I.
-  for (int i = ty; i < rp; i += 32) {
-    const int base = i * rp - (i * (i - 1)) / 2 - i;
-    for (int j = i + tx; j < rp; j += 32) {
-      double sum = 0.0;
-      for (int pt = 0; pt < parts; ++pt) sum += gram[((int64_t)pt * rp + i) * rp + j];
-      W[base + j] = sum;
-      T[base + j] = (i == j) ? 1.0 : 0.0;
-    }
+  // W = sum of the partial Gram matrices in part order (upper block triangle); U = I.
+  const int nblk = nb * (nb + 1) / 2;
+  for (int e = threadIdx.x; e < nblk * FB * FB; e += GSF_THREADS) {
+    const int b = e / (FB * FB), rc = e - b * FB * FB, rr = rc / FB, cc = rc - rr * FB;
+    int bi = 0;
+    while (fblk(bi + 1, bi + 1, nb) <= b && bi + 1 < nb) ++bi;
+    const int bj = bi + (b - fblk(bi, bi, nb));
+    const int row = bi * FB + rr, col = bj * FB + cc;
+    double sum = 0.0;
+    for (int pt = 0; pt < parts; ++pt) sum += gram[((int64_t)pt * rp + row) * rp + col];
+    Wb[b * FBS + rr * FBP + cc] = sum;
+    Ub[b * FBS + rr * FBP + cc] = (bi == bj && rr == cc) ? 1.0 : 0.0;
+    if (bi == bj && rr == cc) diag0[row] = sum;
   }
   __syncthreads();
-  if (threadIdx.x < rp) diag0[threadIdx.x] = W[pidx(threadIdx.x, threadIdx.x, rp)];
-  __syncthreads();
 
-  const double minratio = factor_block(W, T, diag0, rrow, rp);
+  double minratio = 1.0;               // wave 0, every lane
+  for (int p = 0; p < nb; ++p) {
+    // (A) diagonal block: lane 16g + c holds rows g + 4i, column c, of the residual Gram block
+    // (a) and of the local factor (l).
+    if (wv == 0) {
+      const double* Wpp = &Wb[fblk(p, p, nb) * FBS];
+      double a[4], l[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = Wpp[(g + 4 * i) * FBP + c];
+        l[i] = (g + 4 * i == c) ? 1.0 : 0.0;
+      }
+#pragma unroll
+      for (int jj = 0; jj < FB; ++jj) {
+        const int gj = jj & 3, ij = jj >> 2;       // holder of row jj: lanes 16 gj + x, register ij
+        const double dj = __shfl(a[ij], 16 * gj + jj);
+        const double d0 = diag0[p * FB + jj];
+        const bool ok = (d0 > 0.0) && (dj > kDegenerate * d0) && (dj <= 1.0e300);
+        const double inv = ok ? 1.0 / sqrt(dj) : 0.0;
+        if (ok) minratio = fmin(minratio, dj / d0);
+        // row jj of the residual block, scaled: r[x] = a[jj][x] / ||v_jj||
+        const double rc = __shfl(a[ij], 16 * gj + c) * inv;
+        double rrow[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rrow[i] = __shfl(a[ij], 16 * gj + g + 4 * i) * inv;
+        // local factor: column jj scaled, then removed from the later columns
+        if (c == jj) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) l[i] *= inv;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const double lj = __shfl(l[i], 16 * g + jj);
+          if (c > jj) l[i] -= rc * lj;
+          if (c > jj && g + 4 * i > jj) a[i] -= rrow[i] * rc;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Lsh[(g + 4 * i) * FBP + c] = l[i];
+    }
+    __syncthreads();
+    // (B) T_ip = U_ip L (in place, i <= p) and R_pj = L^T W_pj (in place, j > p)
+    for (int t = wv; t < nb; t += NWV) {
+      if (t <= p) {
+        double* U = &Ub[fblk(t, p, nb) * FBS];
+        fblock_mm(U, U, false, Lsh, false, c, g);
+      } else {
+        double* Wj = &Wb[fblk(p, t, nb) * FBS];
+        fblock_mm(Wj, Lsh, true, Wj, false, c, g);
+      }
+    }
+    __syncthreads();
+    // (C) U_ij -= T_ip R_pj (i <= p < j); W_ij -= R_pi^T R_pj (p < i <= j)
+    const int nr = nb - p - 1;                     // block columns right of the panel
+    const int nu = (p + 1) * nr, nw = nr * (nr + 1) / 2;
+    for (int t = wv; t < nu + nw; t += NWV) {
+      if (t < nu) {
+        const int i = t / nr, j = p + 1 + t % nr;
+        fblock_mm(&Ub[fblk(i, j, nb) * FBS], &Ub[fblk(i, p, nb) * FBS], false,
+                  &Wb[fblk(p, j, nb) * FBS], true, c, g);
+      } else {
+        int u = t - nu, i = p + 1;
+        while (u >= nb - i) { u -= nb - i; ++i; }
+        const int j = i + u;
+        fblock_mm(&Wb[fblk(i, j, nb) * FBS], &Wb[fblk(p, i, nb) * FBS], true,
+                  &Wb[fblk(p, j, nb) * FBS], true, c, g);
+      }
+    }
+    __syncthreads();
+  }
   if (pass == 0 && threadIdx.x == 0) *gbl(d.reorth) = minratio < kReorth ? 1 : 0;
 
-  for (int i = ty; i < rp; i += 32) {
-    const int base = i * rp - (i * (i - 1)) / 2 - i;
-    for (int j = tx; j < rp; j += 32) tmat[(int64_t)i * rp + j] = (j >= i) ? T[base + j] : 0.0;
+  // T (row-major rpad x rpad; zero below the block diagonal)
+  for (int e = threadIdx.x; e < rp * rp; e += GSF_THREADS) {
+    const int row = e / rp, col = e - row * rp;
+    const int bi = row / FB, bj = col / FB;
+    tmat[e] = bj >= bi ? Ub[fblk(bi, bj, nb) * FBS + (row % FB) * FBP + col % FB] : 0.0;
   }
 }
 
