@@ -263,6 +263,7 @@ void k_gs_factor(const DevMat* __restrict__ mats, const Work* __restrict__ work,
     const int bj = bi + (b - fblk(bi, bi, nb));
     const int row = bi * FB + rr, col = bj * FB + cc;
     double sum = 0.0;
+#pragma unroll 8
     for (int pt = 0; pt < parts; ++pt) sum += gram[((int64_t)pt * rp + row) * rp + col];
     Wb[b * FBS + rr * FBP + cc] = sum;
     Ub[b * FBS + rr * FBP + cc] = (bi == bj && rr == cc) ? 1.0 : 0.0;
