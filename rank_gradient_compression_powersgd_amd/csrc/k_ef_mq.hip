@@ -21,9 +21,11 @@
 //     A-fragments are read from there;
 //   * the shared operand, 64 rows of q, is read in fp32, split into bf16 hi/lo and staged in
 //     LDS beside it, transposed;
-//   * the flag test runs on M (one class test per element); only when the workgroup met a
-//     non-finite M are the inputs G and E of its rows examined, after the main loop, so the
-//     flag is exactly "G or E holds inf/NaN".
+//   * the flag test runs on the finished P rows: a non-finite element of M makes its row of
+//     P non-finite (inf times a nonzero factor entry is inf, times zero is NaN, and NaN
+//     propagates; the split of inf has a NaN low half). Only when the workgroup's P is
+//     non-finite are the inputs G and E of its rows examined, after the main loop, so the
+//     flag is exactly "G or E holds inf/NaN" (P may also overflow from finite inputs).
 #include "psgd_internal.h"
 
 #ifndef K1_RA
@@ -164,7 +166,6 @@ void k_ef_mq(const DevMat* __restrict__ mats, const Work* __restrict__ work,
       f.er[st].template load<K1_POLE>(re, ok ? (uint32_t)(row * lde + col) * 4u : kOOB);
     }
   };
-  bool mbad = false;     // some M element of this lane was not finite
   auto put_m = [&](const Raw& f) {
     const int q = lu >> 1, half = lu & 1;
 #pragma unroll
@@ -175,7 +176,6 @@ void k_ef_mq(const DevMat* __restrict__ mats, const Work* __restrict__ work,
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         mv[e] = __builtin_fmaf(s, gf[e], ef[e]);
-        mbad |= nonfinite(mv[e]);
       }
       const bf16x4 hi = __builtin_convertvector(mv, bf16x4);
       const bf16x4 lo = __builtin_convertvector(mv - __builtin_convertvector(hi, f32x4), bf16x4);
@@ -260,9 +260,16 @@ void k_ef_mq(const DevMat* __restrict__ mats, const Work* __restrict__ work,
     __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(&pt[rr * PT_LD + 4 * q]), gcast<f32x4>(praw + (int64_t)(row0 + rr) * rpad + rc0 + 4 * q));
   }
 
-  // Flag: M non-finite somewhere in this workgroup's rows is rare; only then are the inputs G
-  // and E of those rows examined, so the flag is exactly "G or E holds inf/NaN" (M may also be
+  // Flag: a non-finite P row in this workgroup is rare; only then are the inputs G and E of
+  // its rows examined, so the flag is exactly "G or E holds inf/NaN" (P may also be
   // non-finite through s or fp32 overflow).
+  bool mbad = false;
+#pragma unroll
+  for (int a = 0; a < K1_RA; ++a)
+#pragma unroll
+    for (int cc = 0; cc < RTC; ++cc)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mbad |= nonfinite(acc[a][cc][i]);
   if (__builtin_amdgcn_ballot_w64(mbad) != 0 && lane == 0) s_bad = 1;
   __syncthreads();
   if (s_bad != 0) {

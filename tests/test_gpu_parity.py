@@ -157,6 +157,28 @@ def test_ragged_shapes(dtype, rank):
 
 
 # ------------------------------------------------------------------------------------------
+# the flag reports non-finite G or E only: a finite M whose product overflows sets none
+# ------------------------------------------------------------------------------------------
+def test_product_overflow_is_not_a_flag():
+    import torch
+    log("flag: overflowing product of a finite M")
+    m, n, rank = 128, 64, 4
+    q0 = [np.full((n, rank), 2.0, np.float32)]
+    err0 = [np.zeros((m, n), np.float32)]
+    err0[0][5, :] = 3.0e38             # finite; the row's product with q exceeds fp32
+    case = Case([(m, n)], [0], "f32", rank, np.ones(1, np.float32), q0, err0)
+    case.set_grads([np.zeros((m, n), np.float32)])
+    case.group.compress()
+    torch.cuda.synchronize()
+    assert case.group.flags.cpu().numpy().tolist() == [0]
+    case.group.err[0][7, 3] = float("nan")
+    case.group.compress()
+    torch.cuda.synchronize()
+    assert case.group.flags.cpu().numpy().tolist() == [1]
+    case.close()
+
+
+# ------------------------------------------------------------------------------------------
 # non-finite values: flags and skip bit-exact, error buffers zeroed, q kept
 # ------------------------------------------------------------------------------------------
 def test_nonfinite_flags_skip_and_zeroing():
@@ -179,6 +201,8 @@ def test_nonfinite_flags_skip_and_zeroing():
         ("grad +inf", dict(grad=(1, 5, 7, np.inf))),
         ("grad nan", dict(grad=(2, 199, 103, np.nan))),
         ("grad -inf", dict(grad=(0, 0, 0, -np.inf))),
+        # the only nonzero factor of this column is gone: inf * 0 in the product must still flag
+        ("grad +inf on a zero row of q", dict(grad=(0, 9, 17, np.inf), zero_q_row=(0, 17))),
         ("err nan", dict(err=(1, 63, 511, np.nan))),
         ("pass nan", dict(passthrough=np.array([0.0, np.nan, 1.0]))),
         ("scale inf", dict(scale=(1, np.inf))),
@@ -196,6 +220,11 @@ def test_nonfinite_flags_skip_and_zeroing():
         if "scale" in ev:
             b, v = ev["scale"]
             case.group.scale[b] = float(v)
+        if "zero_q_row" in ev:
+            i, qr = ev["zero_q_row"]
+            case.group.q[i][qr, :] = 0.0
+            case.Q_or[i] = case.Q_or[i].copy()
+            case.Q_or[i][qr, :] = 0.0
         q_before = [q.clone() for q in case.group.q]
         out_before = [o.clone() for o in case.group.out]
         pt = [ev["passthrough"]] if "passthrough" in ev else [np.ones(10)]
