@@ -82,8 +82,8 @@ typedef enum psgd_dtype {
  *  m, n    shape; n % 8 == 0; 1 <= r <= min(m, n).
  *  block   index into the per-resblock scale array (0 <= block < n_blocks).
  * Every pointer must be 16-byte aligned. Buffers of different matrices must not overlap. The
- * byte span of each of G, E and out ((m - 1) * ld + n elements), and of q (n * r elements),
- * must be below 2 GiB.
+ * byte span of each of G, E and out ((m - 1) * ld + n elements), and of q and p (n * r and
+ * m * r elements), must be below 2 GiB.
  */
 typedef struct psgd_matrix {
   const void* grad;   int64_t ld_grad;
@@ -157,10 +157,10 @@ psgd_status psgd_compress(psgd_ctx* ctx, psgd_plan* plan, const float* scale, ui
  *     psgd_decompress_update -> D = P q_next^T (identical on every rank), E = M_local - D
  * The library issues no collective; on one GPU the exchanges are the identity.
  *
- * psgd_compress_p: clears flags, prepares the warm start, computes M q (and the flags).
+ * psgd_compress_p: clears flags, computes M q (and the flags).
  * psgd_orthogonalize: orthonormalises the factor buffer's contents into p.
- * psgd_compress_q: q_next = M^T p, and the decompression operand built from it.
- * psgd_refresh_q: rebuilds the decompression operand from q_next (after q_next was reduced).
+ * psgd_compress_q: q_next = M^T p, and the row scales the decompression applies to it.
+ * psgd_refresh_q: recomputes those row scales from q_next (after q_next was reduced).
  */
 psgd_status psgd_compress_p(psgd_ctx* ctx, psgd_plan* plan, const float* scale, uint8_t* flags,
                             hipStream_t stream);

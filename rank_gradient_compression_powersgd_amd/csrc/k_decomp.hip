@@ -2,10 +2,11 @@
 // E = M - D with M = s_b G + E recomputed; optional D output.
 //
 // "Zero-Shot Text-to-Image Generation — 中文验证版" (section 证据) asks for 32-bit products in
-// the decompressed gradient. Both factors were stored as fp16 hi + lo pairs of rows scaled by
-// powers of two (|x - hi - lo| <= 2^-22 |x|), and three fp16 MFMA products (hi*hi + hi*lo +
-// lo*hi) with fp32 accumulation reproduce fp32 products to about 2^-21. The power-of-two row
-// scales are removed exactly with ldexp.
+// the decompressed gradient. Both factors are read in fp32 (p and q_next), each row scaled by
+// a power of two (computed with the factor, one exponent per row) and split into fp16 hi + lo
+// (|x - hi - lo| <= 2^-22 |x|) while staged; three fp16 MFMA products (hi*hi + hi*lo + lo*hi)
+// with fp32 accumulation reproduce fp32 products to about 2^-21. The power-of-two row scales
+// are removed exactly with ldexp.
 //
 // The tile is computed transposed, D^T = Q' P^T, so the MFMA C layout gives every lane 4
 // consecutive columns of one row of D. The finished tile is passed through LDS so that the
@@ -98,49 +99,71 @@ void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   auto ldq = reinterpret_cast<uint16_t(*)[2][K3_TN][LDS_K]>(lds_raw);
   auto ldp = reinterpret_cast<uint16_t(*)[2][K3_TM][LDS_K]>(lds_raw + kStageQBytes);
 
-  // staging: K3_TN rows of Q' and K3_TM rows of P x 32 k x {hi, lo}, in 16-byte units. The
-  // operand arrays are padded with zero rows to whole tiles, so no staging load is masked.
-  constexpr int QU = K3_TN * 8 / K3_THREADS, PU = K3_TM * 8 / K3_THREADS;
-  static_assert(QU * K3_THREADS == K3_TN * 8 && PU * K3_THREADS == K3_TM * 8, "staging units");
-  const GLOBAL uint16_t* __restrict__ q3h = gbl(d.q3_hi) + (int64_t)n0 * kpad3;
-  const GLOBAL uint16_t* __restrict__ q3l = gbl(d.q3_lo) + (int64_t)n0 * kpad3;
-  const GLOBAL uint16_t* __restrict__ p3h = gbl(d.p3_hi) + (int64_t)m0 * kpad3;
-  const GLOBAL uint16_t* __restrict__ p3l = gbl(d.p3_lo) + (int64_t)m0 * kpad3;
-  u32x4 sq[QU], sp[PU];
-  // unit u of a `rows`-row operand: array (hi/lo), row, 16-byte unit; consecutive threads take
-  // consecutive units of a row (coalesced global reads).
-  auto unit = [](int u, int rows, int& arr, int& rr, int& q4) {
-    arr = u / (rows * 4);
-    const int v = u - arr * rows * 4;
-    rr = v >> 2;
-    q4 = v & 3;
+  // staging: K3_TN rows of Q' (q_next) and K3_TM rows of P (p), both fp32 with row pitch r, 32
+  // ranks per stage. A group is 4 consecutive ranks of one row (one 16-byte load); 8 threads
+  // cover a row's 32 ranks (one 128-byte line). Each value is scaled by its row's power of two
+  // (largest entry of the row in [2^13, 2^14)) and split into fp16 hi + lo on its way into LDS.
+  // Rows past n (m) and ranks past r read zeros.
+  constexpr int QG = K3_TN * 8 / K3_THREADS, PG = K3_TM * 8 / K3_THREADS;
+  static_assert(QG * K3_THREADS == K3_TN * 8 && PG * K3_THREADS == K3_TM * 8, "staging groups");
+  const int r = d.r;
+  const bool rvec = (r & 3) == 0;               // rows are whole 16-byte groups
+  const rsrc_t rsq = make_rsrc(d.q_next, (uint32_t)n * (uint32_t)r * 4u);
+  const rsrc_t rsp = make_rsrc(d.p, (uint32_t)m * (uint32_t)r * 4u);
+  const int hq = threadIdx.x & 7, rq0 = threadIdx.x >> 3;   // group within the row, first row
+  constexpr int RSTEP3 = K3_THREADS / 8;        // rows between a thread's groups
+  f32x4 sq[QG], sp[PG];
+  int eq[QG], epx[PG];
+  uint32_t qrow[QG], prow[PG];                  // byte offsets of the thread's rows (kOOB past the end)
+#pragma unroll
+  for (int j = 0; j < QG; ++j) {
+    const int row = n0 + rq0 + RSTEP3 * j;
+    eq[j] = gbl(d.q3_exp)[row];                 // padded to whole tiles
+    qrow[j] = row < n ? (uint32_t)row * (uint32_t)r * 4u : kOOB;
+  }
+#pragma unroll
+  for (int j = 0; j < PG; ++j) {
+    const int row = m0 + rq0 + RSTEP3 * j;
+    epx[j] = gbl(d.p3_exp)[row];
+    prow[j] = row < m ? (uint32_t)row * (uint32_t)r * 4u : kOOB;
+  }
+  // a row offset of kOOB stays past the buffer range (< 2 GiB) with any rank added
+  auto load_group = [&](rsrc_t rs_, uint32_t rowoff, int k) -> f32x4 {
+    if (rvec) return __builtin_bit_cast(f32x4, bload16(rs_, k < r ? rowoff + 4u * k : kOOB));
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = __builtin_bit_cast(float, bload4(rs_, k + e < r ? rowoff + 4u * (k + e) : kOOB));
+    return v;
   };
   auto load_stage = [&](int k0) {
+    const int k = k0 + 4 * hq;
 #pragma unroll
-    for (int j = 0; j < QU; ++j) {
-      int arr, rr, q4;
-      unit(threadIdx.x + j * K3_THREADS, K3_TN, arr, rr, q4);
-      sq[j] = *gcast<u32x4>((arr ? q3l : q3h) + (int64_t)rr * kpad3 + k0 + 8 * q4);
-    }
+    for (int j = 0; j < QG; ++j) sq[j] = load_group(rsq, qrow[j], k);
 #pragma unroll
-    for (int j = 0; j < PU; ++j) {
-      int arr, rr, q4;
-      unit(threadIdx.x + j * K3_THREADS, K3_TM, arr, rr, q4);
-      sp[j] = *gcast<u32x4>((arr ? p3l : p3h) + (int64_t)rr * kpad3 + k0 + 8 * q4);
-    }
+    for (int j = 0; j < PG; ++j) sp[j] = load_group(rsp, prow[j], k);
+  };
+  // 4 values -> 4 fp16 hi and 4 fp16 lo at the group's place in its swizzled LDS row
+  auto put_group = [&](uint16_t* hi_row, uint16_t* lo_row, int rr, f32x4 v, int ex) {
+    f32x4 x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = ldexpf(v[e], ex);
+    const f16x4 h = __builtin_convertvector(x, f16x4);
+    const f16x4 l = __builtin_convertvector(x - __builtin_convertvector(h, f32x4), f16x4);
+    const int off = 8 * swz3(rr, hq >> 1) + 4 * (hq & 1);
+    *reinterpret_cast<f16x4*>(hi_row + off) = h;
+    *reinterpret_cast<f16x4*>(lo_row + off) = l;
   };
   auto store_stage = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < QU; ++j) {
-      int arr, rr, q4;
-      unit(threadIdx.x + j * K3_THREADS, K3_TN, arr, rr, q4);
-      *reinterpret_cast<u32x4*>(&ldq[buf][arr][rr][8 * swz3(rr, q4)]) = sq[j];
+    for (int j = 0; j < QG; ++j) {
+      const int rr = rq0 + RSTEP3 * j;
+      put_group(ldq[buf][0][rr], ldq[buf][1][rr], rr, sq[j], eq[j]);
     }
 #pragma unroll
-    for (int j = 0; j < PU; ++j) {
-      int arr, rr, q4;
-      unit(threadIdx.x + j * K3_THREADS, K3_TM, arr, rr, q4);
-      *reinterpret_cast<u32x4*>(&ldp[buf][arr][rr][8 * swz3(rr, q4)]) = sp[j];
+    for (int j = 0; j < PG; ++j) {
+      const int rr = rq0 + RSTEP3 * j;
+      put_group(ldp[buf][0][rr], ldp[buf][1][rr], rr, sp[j], epx[j]);
     }
   };
 
@@ -201,9 +224,13 @@ void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   constexpr int NS = K3_TM / RSTEP;                  // passes over the tile
   static_assert(RSTEP * CQ == K3_THREADS && NS * RSTEP == K3_TM, "epilogue mapping");
   const int cq = threadIdx.x % CQ, rs = threadIdx.x / CQ;
+  const int erow = m0 + rs, ecol = n0 + 4 * cq;
+  const bool ecolok = ecol < n;
+  // byte offset of pass st in an array with leading dimension ld: a base plus st row steps
   auto offset = [&](int st, int ld, uint32_t bytes) -> uint32_t {
-    const int row = m0 + rs + RSTEP * st, col = n0 + 4 * cq;
-    return (row < m && col < n) ? (uint32_t)(row * ld + col) * bytes : kOOB;
+    const uint32_t base = ((uint32_t)erow * (uint32_t)ld + (uint32_t)ecol) * bytes;
+    const uint32_t step = (uint32_t)(RSTEP * ld) * bytes;
+    return (erow + RSTEP * st < m && ecolok) ? base + step * (uint32_t)st : kOOB;
   };
   Raw4<GT> gv[NS];
   u32x4 ev[NS];

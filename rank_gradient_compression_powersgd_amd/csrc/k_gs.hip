@@ -506,7 +506,7 @@ void k_gs_apply_s(const DevMat* __restrict__ mats, const Work* __restrict__ work
   const DevMat& d = mats[wi.mat];
   const bool again = *d.reorth != 0;      // a second pass follows (pass 0) / runs (pass 1)
   if (pass && !again) return;
-  const int m = d.m, r = d.r, rpad = d.rpad, mpad = d.mpad, kpad3 = d.kpad3;
+  const int m = d.m, r = d.r, rpad = d.rpad, mpad = d.mpad;
   const GLOBAL float* __restrict__ P = gbl(pass ? d.p2 : d.p_raw);
   const GLOBAL double* __restrict__ Tm = gbl(d.tmat);
   const int lane = threadIdx.x & (kWave - 1);
@@ -520,7 +520,6 @@ void k_gs_apply_s(const DevMat* __restrict__ mats, const Work* __restrict__ work
   constexpr int NRT = GSA_ROWS / 16;       // row tiles (8)
 
   __shared__ __attribute__((aligned(16))) float S[GSA_ROWS * LD];
-  __shared__ int sexp[GSA_ROWS];
 
   // (1) the P tile into LDS; rows past m are zero
   constexpr int U4 = RT * 4;               // 16-byte units per row
@@ -629,39 +628,19 @@ void k_gs_apply_s(const DevMat* __restrict__ mats, const Work* __restrict__ work
     *gcast<u32x4>(pth + (int64_t)col * mpad + row0 + r8) = u32x4{h[0], h[1], h[2], h[3]};
     *gcast<u32x4>(ptl + (int64_t)col * mpad + row0 + r8) = u32x4{l[0], l[1], l[2], l[3]};
   }
-  // (c) rows scaled by 2^e (largest entry in [2^13, 2^14)) and split fp16 hi/lo, m x kpad3
-  if (threadIdx.x < GSA_ROWS) {
+  // (c) row exponents of the decompression operand: the power of two that brings the row's
+  // largest entry into [2^13, 2^14) before the decompression splits it into fp16 hi + lo
+  GLOBAL int32_t* __restrict__ p3e = gbl(d.p3_exp);
+  if ((int)threadIdx.x < rows) {
     float amax = 0.0f;
     for (int cc = 0; cc < RC; ++cc) amax = fmaxf(amax, fabsf(S[threadIdx.x * LD + cc]));
-    sexp[threadIdx.x] = fp16_row_exponent(amax);
+    p3e[row0 + threadIdx.x] = fp16_row_exponent(amax);
   }
-  __syncthreads();
-  GLOBAL uint16_t* __restrict__ p3h = gbl(d.p3_hi);
-  GLOBAL uint16_t* __restrict__ p3l = gbl(d.p3_lo);
-  GLOBAL int32_t* __restrict__ p3e = gbl(d.p3_exp);
-  constexpr int U8 = RT * 2;               // 8-column units per row (rpad / 8)
-  for (int idx = threadIdx.x; idx < rows * U8; idx += GS_THREADS) {
-    const int rr = idx / U8, c8 = (idx % U8) * 8;
-    const int ex = sexp[rr];
-    const f32x4 x0 = *reinterpret_cast<const f32x4*>(&S[rr * LD + c8]);
-    const f32x4 x1 = *reinterpret_cast<const f32x4*>(&S[rr * LD + c8 + 4]);
-    uint32_t h[4], l[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float y0 = ldexpf(e < 2 ? x0[2 * e] : x1[2 * e - 4], ex);
-      const float y1 = ldexpf(e < 2 ? x0[2 * e + 1] : x1[2 * e - 3], ex);
-      const _Float16 h0 = (_Float16)y0, h1 = (_Float16)y1;
-      h[e] = f16_bits(h0) | ((uint32_t)f16_bits(h1) << 16);
-      l[e] = f16_bits((_Float16)(y0 - (float)h0)) | ((uint32_t)f16_bits((_Float16)(y1 - (float)h1)) << 16);
-    }
-    *gcast<u32x4>(p3h + (int64_t)(row0 + rr) * kpad3 + c8) = u32x4{h[0], h[1], h[2], h[3]};
-    *gcast<u32x4>(p3l + (int64_t)(row0 + rr) * kpad3 + c8) = u32x4{l[0], l[1], l[2], l[3]};
-  }
-  if ((int)threadIdx.x < rows) p3e[row0 + threadIdx.x] = sexp[threadIdx.x];
 }
 
-// Large ranks (rpad > 128, RT = 8): the 128-column block b of P_hat for rows [a, a + 128); its
-// fp16 decompression operand is built afterwards by split3 (its row scale needs every column).
+// Large ranks (rpad > 128, RT = 8): the 128-column block b of P_hat for rows [a, a + 128); the
+// row exponents of its decompression operand are found afterwards by split3 (they need every
+// column).
 template <int RT, bool BIG>
 __global__ __launch_bounds__(GS_THREADS)
 void k_gs_apply(const DevMat* __restrict__ mats, const Work* __restrict__ work, int pass)
@@ -671,7 +650,7 @@ void k_gs_apply(const DevMat* __restrict__ mats, const Work* __restrict__ work, 
   const DevMat& d = mats[wi.mat];
   const bool again = *d.reorth != 0;      // a second pass follows (pass 0) / runs (pass 1)
   if (pass && !again) return;
-  const int m = d.m, r = d.r, rpad = d.rpad, mpad = d.mpad, kpad3 = d.kpad3;
+  const int m = d.m, r = d.r, rpad = d.rpad, mpad = d.mpad;
   const GLOBAL float* __restrict__ P = gbl(pass ? d.p2 : d.p_raw);
   const GLOBAL double* __restrict__ Tm = gbl(d.tmat);
   const int lane = threadIdx.x & (kWave - 1);
@@ -684,7 +663,6 @@ void k_gs_apply(const DevMat* __restrict__ mats, const Work* __restrict__ work, 
   constexpr int SP = RT * 16 + 1;          // LDS row pitch (floats); odd, so column reads spread over banks
 
   __shared__ float S[GSA_ROWS * SP];
-  __shared__ int sexp[GSA_ROWS];
 
   f64x4 acc[GSA_RA][RT];
 #pragma unroll
@@ -766,53 +744,22 @@ void k_gs_apply(const DevMat* __restrict__ mats, const Work* __restrict__ work, 
     *gcast<u32x4>(pth + (int64_t)(c0 + col) * mpad + row0 + r8) = u32x4{h[0], h[1], h[2], h[3]};
     *gcast<u32x4>(ptl + (int64_t)(c0 + col) * mpad + row0 + r8) = u32x4{l[0], l[1], l[2], l[3]};
   }
-  if constexpr (BIG) return;
-  // (c) rows scaled by 2^e (largest entry in [2^13, 2^14)) and split fp16 hi/lo, m x kpad3
-  if (threadIdx.x < GSA_ROWS) {
-    float amax = 0.0f;
-    for (int cc = 0; cc < RT * 16; ++cc) amax = fmaxf(amax, fabsf(S[threadIdx.x * SP + cc]));
-    sexp[threadIdx.x] = fp16_row_exponent(amax);
-  }
-  __syncthreads();
-  GLOBAL uint16_t* __restrict__ p3h = gbl(d.p3_hi);
-  GLOBAL uint16_t* __restrict__ p3l = gbl(d.p3_lo);
-  GLOBAL int32_t* __restrict__ p3e = gbl(d.p3_exp);
-  constexpr int U8 = RT * 2;                         // 8-column units per row (rpad / 8)
-  for (int idx = threadIdx.x; idx < GSA_ROWS * U8; idx += GS_THREADS) {
-    const int rr = idx / U8, c8 = (idx % U8) * 8;
-    if (row0 + rr >= m || c8 >= kpad3) continue;
-    const int ex = sexp[rr];
-    uint32_t h[4], l[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float x0 = ldexpf(S[rr * SP + c8 + 2 * e], ex), x1 = ldexpf(S[rr * SP + c8 + 2 * e + 1], ex);
-      const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
-      h[e] = f16_bits(h0) | ((uint32_t)f16_bits(h1) << 16);
-      l[e] = f16_bits((_Float16)(x0 - (float)h0)) | ((uint32_t)f16_bits((_Float16)(x1 - (float)h1)) << 16);
-    }
-    *gcast<u32x4>(p3h + (int64_t)(row0 + rr) * kpad3 + c8) = u32x4{h[0], h[1], h[2], h[3]};
-    *gcast<u32x4>(p3l + (int64_t)(row0 + rr) * kpad3 + c8) = u32x4{l[0], l[1], l[2], l[3]};
-  }
-  if (threadIdx.x < GSA_ROWS && row0 + (int)threadIdx.x < m) p3e[row0 + threadIdx.x] = sexp[threadIdx.x];
 }
 
-// Decompression operands from the fp32 factors (large ranks): each row of P_hat (which = 0,
-// from p) or of Q' (which = 1, from q_next) scaled by a power of two so that its largest entry
-// lies in [2^13, 2^14), split into fp16 hi + lo over kpad3 columns (zero beyond r), and the
-// exponent stored. One work item: 64 rows [a, a + 64) of matrix `mat`, which = b; one wave per
-// row at a time.
+// Row exponents of the decompression operands (ranks above one chunk, or q_next after the
+// caller changed it): for each row of P_hat (which = 0, from p) or of Q' (which = 1, from
+// q_next), the power of two that brings its largest entry into [2^13, 2^14). One work item:
+// 64 rows [a, a + 64) of matrix `mat`, which = b; one wave per row at a time.
 __global__ __launch_bounds__(256)
 void k_split3(const DevMat* __restrict__ mats, const Work* __restrict__ work)
 {
   const Work wi = work[blockIdx.x];
   if (wi.mat < 0) return;
   const DevMat& d = mats[wi.mat];
-  const int r = d.r, kpad3 = d.kpad3;
+  const int r = d.r;
   const bool isq = wi.b != 0;
   const int rows = isq ? d.n : d.m;
   const GLOBAL float* __restrict__ src = gbl(isq ? d.q_next : d.p);
-  GLOBAL uint16_t* __restrict__ hi = gbl(isq ? d.q3_hi : d.p3_hi);
-  GLOBAL uint16_t* __restrict__ lo = gbl(isq ? d.q3_lo : d.p3_lo);
   GLOBAL int32_t* __restrict__ ex = gbl(isq ? d.q3_exp : d.p3_exp);
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
@@ -821,14 +768,7 @@ void k_split3(const DevMat* __restrict__ mats, const Work* __restrict__ work)
     for (int col = lane; col < r; col += kWave) amax = fmaxf(amax, fabsf(src[(int64_t)row * r + col]));
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-    const int e = fp16_row_exponent(amax);
-    for (int col = lane; col < kpad3; col += kWave) {
-      const float x = col < r ? ldexpf(src[(int64_t)row * r + col], e) : 0.0f;
-      const _Float16 h = (_Float16)x;
-      hi[(int64_t)row * kpad3 + col] = f16_bits(h);
-      lo[(int64_t)row * kpad3 + col] = f16_bits((_Float16)(x - (float)h));
-    }
-    if (lane == 0) ex[row] = e;
+    if (lane == 0) ex[row] = fp16_row_exponent(amax);
   }
 }
 

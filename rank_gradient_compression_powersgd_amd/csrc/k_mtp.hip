@@ -13,8 +13,8 @@
 // so the loop body has no branches and the next rows' loads overlap the current MFMAs.
 //
 // Epilogue: Q' is written in fp32 (the caller's q_next). When the whole rank fits one chunk
-// the kernel also writes the decompression operand: each row of Q' scaled by a power of two
-// (so its largest entry lies in [2^13, 2^14)) and split into fp16 hi + lo.
+// the kernel also writes each row's exponent for the decompression: the power of two that
+// brings the row's largest entry into [2^13, 2^14) before the decompression splits it.
 #include "psgd_internal.h"
 
 namespace psgd {
@@ -197,8 +197,8 @@ void k_mtp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
     for (int i = 0; i < RTC; ++i)
       *reinterpret_cast<f32x4*>(&qt[lc * QT_LD + i * 16 + 4 * g]) = acc[i][t];
     if (whole) {
-      // Decompression operand: each row of Q' scaled by a power of two (its largest entry in
-      // [2^13, 2^14)) and split into fp16 hi + lo.
+      // Row exponent of the decompression operand: the power of two that brings the row's
+      // largest entry into [2^13, 2^14) before its fp16 split.
       float amax = 0.0f;
 #pragma unroll
       for (int i = 0; i < RTC; ++i)
@@ -230,28 +230,7 @@ void k_mtp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   }
   if (!whole) return;
 
-  const int kpad3 = d.kpad3;
-  GLOBAL uint16_t* __restrict__ q3h = gbl(d.q3_hi);
-  GLOBAL uint16_t* __restrict__ q3l = gbl(d.q3_lo);
   GLOBAL int32_t* __restrict__ q3e = gbl(d.q3_exp);
-  constexpr int U8 = RC / 8;                    // 16-byte units of fp16 per row
-  for (int u = threadIdx.x; u < ncols * U8; u += THREADS_) {
-    const int j = u / U8, q = u - j * U8;
-    const int ex = s_ex[j];
-    const f32x4 x0 = *reinterpret_cast<const f32x4*>(&qt[j * QT_LD + 8 * q]);
-    const f32x4 x1 = *reinterpret_cast<const f32x4*>(&qt[j * QT_LD + 8 * q + 4]);
-    uint32_t hw[4], lw[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float a0 = ldexpf(e < 2 ? x0[2 * e] : x1[2 * e - 4], ex);
-      const float a1 = ldexpf(e < 2 ? x0[2 * e + 1] : x1[2 * e - 3], ex);
-      const _Float16 h0 = (_Float16)a0, h1 = (_Float16)a1;
-      hw[e] = f16_bits(h0) | ((uint32_t)f16_bits(h1) << 16);
-      lw[e] = f16_bits((_Float16)(a0 - (float)h0)) | ((uint32_t)f16_bits((_Float16)(a1 - (float)h1)) << 16);
-    }
-    __builtin_nontemporal_store(u32x4{hw[0], hw[1], hw[2], hw[3]}, gcast<u32x4>(q3h + (int64_t)(wi.a + j) * kpad3 + 8 * q));
-    __builtin_nontemporal_store(u32x4{lw[0], lw[1], lw[2], lw[3]}, gcast<u32x4>(q3l + (int64_t)(wi.a + j) * kpad3 + 8 * q));
-  }
   for (int j = threadIdx.x; j < ncols; j += THREADS_) q3e[wi.a + j] = s_ex[j];
 }
 

@@ -135,10 +135,9 @@ struct DevMat {
   // workspace (library owned)
   float* p_raw;                        // m x rpad fp32: M q before orthonormalisation
   uint16_t* pt_hi; uint16_t* pt_lo;    // rpad x mpad bf16: P^T split into hi + lo
-  uint16_t* p3_hi; uint16_t* p3_lo;    // m3 x kpad3 fp16: P * 2^p3_exp[row], split hi + lo
-  int32_t* p3_exp;                     // m3 (m rounded up to a decompression tile; zero rows)
-  uint16_t* q3_hi; uint16_t* q3_lo;    // n3 x kpad3 fp16: q_next * 2^q3_exp[row], split hi + lo
-  int32_t* q3_exp;                     // n3 (n rounded up to a decompression tile; zero rows)
+  int32_t* p3_exp;                     // m3 (m rounded up to a decompression tile; zero rows):
+                                       // row exponent of P for the decompression's fp16 split
+  int32_t* q3_exp;                     // n3 likewise for q_next
   double* gram;                        // gram_parts x rpad x rpad fp64 partial Gram matrices
   double* tmat;                        // rpad x rpad fp64 upper-triangular T, P = (M q) T
   double* wsum;                        // rpad x rpad fp64 summed Gram matrix, overwritten by the

@@ -171,7 +171,7 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
   size_t praw_cursor = 0;
   size_t ws = (size_t)rup((int64_t)praw_total, 256);
   auto take = [&](size_t bytes) { size_t o = ws; ws += (size_t)rup((int64_t)bytes, 256); return o; };
-  struct Off { size_t p_raw, pth, ptl, p3h, p3l, p3e, q3h, q3l, q3e, gram, tmat, wsum, p2, reorth; };
+  struct Off { size_t p_raw, pth, ptl, p3e, q3e, gram, tmat, wsum, p2, reorth; };
   std::vector<Off> offs(n_mats);
   p->mats.resize(n_mats);
   for (int i = 0; i < n_mats; ++i) {
@@ -212,8 +212,8 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
     const int64_t eb = ((a.m - 1) * a.ld_err + a.n) * 4;
     const int64_t ob = a.out ? ((a.m - 1) * a.ld_out + a.n) * 4 : 0;
     if (gb >= (int64_t(1) << 31) || eb >= (int64_t(1) << 31) || ob >= (int64_t(1) << 31) ||
-        a.n * r * 4 >= (int64_t(1) << 31))
-      return fail(ctx, PSGD_EINVAL, "matrix %d: G, E, out and q must each span less than 2 GiB", i);
+        a.n * r * 4 >= (int64_t(1) << 31) || a.m * r * 4 >= (int64_t(1) << 31))
+      return fail(ctx, PSGD_EINVAL, "matrix %d: G, E, out, q and p must each span less than 2 GiB", i);
     d.g_bytes = (uint32_t)gb;
     d.e_bytes = (uint32_t)eb;
     d.o_bytes = (uint32_t)ob;
@@ -223,11 +223,7 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
     o.pth = take((size_t)rpad * d.mpad * 2);
     o.ptl = take((size_t)rpad * d.mpad * 2);
     const int64_t m3 = rup(a.m, psgd::decomp_tile_m()), n3 = rup(a.n, psgd::decomp_tile_n());
-    o.p3h = take((size_t)m3 * kpad3 * 2);      // zero rows up to a whole decompression tile
-    o.p3l = take((size_t)m3 * kpad3 * 2);
-    o.p3e = take((size_t)m3 * 4);
-    o.q3h = take((size_t)n3 * kpad3 * 2);
-    o.q3l = take((size_t)n3 * kpad3 * 2);
+    o.p3e = take((size_t)m3 * 4);              // zero rows up to a whole decompression tile
     o.q3e = take((size_t)n3 * 4);
     o.gram = take((size_t)d.gram_parts * rpad * rpad * 8);
     o.tmat = take((size_t)rpad * rpad * 8);
@@ -351,11 +347,7 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
     d.p_raw = reinterpret_cast<float*>(base + o.p_raw);
     d.pt_hi = reinterpret_cast<uint16_t*>(base + o.pth);
     d.pt_lo = reinterpret_cast<uint16_t*>(base + o.ptl);
-    d.p3_hi = reinterpret_cast<uint16_t*>(base + o.p3h);
-    d.p3_lo = reinterpret_cast<uint16_t*>(base + o.p3l);
     d.p3_exp = reinterpret_cast<int32_t*>(base + o.p3e);
-    d.q3_hi = reinterpret_cast<uint16_t*>(base + o.q3h);
-    d.q3_lo = reinterpret_cast<uint16_t*>(base + o.q3l);
     d.q3_exp = reinterpret_cast<int32_t*>(base + o.q3e);
     d.gram = reinterpret_cast<double*>(base + o.gram);
     d.tmat = reinterpret_cast<double*>(base + o.tmat);
@@ -432,7 +424,7 @@ psgd_status psgd_compress_q(psgd_ctx* ctx, psgd_plan* plan, const float* scale, 
   auto W = [&](int k) { return plan->d_work + plan->off[k]; };
   HIPCHK(ctx, traced(ctx, S_K2, stream, [&] { return psgd::launch_mtp(plan->gt, plan->rtc, dm, W(W_K2), plan->cnt[W_K2], scale, stream); }), "M^T P");
   if (plan->big)
-    HIPCHK(ctx, traced(ctx, S_SPLIT3, stream, [&] { return psgd::launch_split3(dm, W(W_SPLIT3), plan->cnt[W_SPLIT3], stream); }), "decompression operands");
+    HIPCHK(ctx, traced(ctx, S_SPLIT3, stream, [&] { return psgd::launch_split3(dm, W(W_SPLIT3), plan->cnt[W_SPLIT3], stream); }), "decompression row scales");
   return PSGD_OK;
 }
 
@@ -440,7 +432,7 @@ psgd_status psgd_refresh_q(psgd_ctx* ctx, psgd_plan* plan, hipStream_t stream) {
   if (psgd_status st = check_call(ctx, plan); st != PSGD_OK) return st;
   const DevMat* dm = plan->d_mats;
   auto W = [&](int k) { return plan->d_work + plan->off[k]; };
-  HIPCHK(ctx, traced(ctx, S_SPLIT3, stream, [&] { return psgd::launch_split3(dm, W(W_SPLITQ), plan->cnt[W_SPLITQ], stream); }), "decompression operand of q_next");
+  HIPCHK(ctx, traced(ctx, S_SPLIT3, stream, [&] { return psgd::launch_split3(dm, W(W_SPLITQ), plan->cnt[W_SPLITQ], stream); }), "decompression row scales of q_next");
   return PSGD_OK;
 }
 
