@@ -40,7 +40,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # algorithmic bytes per gradient element of each streaming kernel (gradient dtype size g):
 #   ef_mq       reads G and E                         g + 4
 #   mtp         reads G and E again                   g + 4
-#   decompress  reads G and E, writes E (and D)       g + 8 (+ 4)
+#   decompress  reads G and E, writes E (and D)       g + 8 (+ 4), plus the q commit (4 n r
+#               bytes per matrix: q <- q_next)
 STREAMING = ("ef_mq", "mtp", "decompress")
 
 
@@ -140,7 +141,8 @@ def pmc_summary(d: str) -> int:
           f"{f_copy / 2**30:.3f} GiB -> scale {sf:.3f}; WRITE_SIZE reads {w_copy / 2**30:.3f} GiB -> "
           f"scale {sw:.3f}")
     numel = 1511522304
-    algo = {"k_ef_mq": 6 * numel, "k_mtp": 6 * numel, "k_decomp": 14 * numel}
+    qcommit = 4 * 81772544             # the decompression also writes q <- q_next (sum of n x r fp32)
+    algo = {"k_ef_mq": 6 * numel, "k_mtp": 6 * numel, "k_decomp": 14 * numel + qcommit}
     print(f"{'kernel':34s} {'launches':>8s} {'fetch GB':>9s} {'write GB':>9s} {'total GB':>9s} {'algorithmic GB':>15s}")
     for k in sorted(fe):
         if not k.startswith("k_"):
@@ -376,6 +378,8 @@ def main(argv=None) -> int:
     rooflines = {}
     for name in STREAMING:
         nbytes = per_elem[name] * numel
+        if name == "decompress":       # and commits q <- q_next: n x r fp32 written per matrix
+            nbytes += 4 * w.rank * sum(spec.n for spec in w.matrices)
         gbs = nbytes / (kern[name] * 1e-3) / 1e9
         rooflines[name] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,

@@ -208,10 +208,11 @@ psgd_status psgd_decompress_update(psgd_ctx* ctx, psgd_plan* plan, const float* 
  * events[2k] (before) and events[2k+1] (after) on the call's stream; elapsed times between the
  * pair give that kernel's duration. Slots: 0 flag clear, 1 M Q with error feedback, 2 Gram
  * partials, 3 Gram-Schmidt, 4 orthonormal P, 5 M^T P, 6 skip clear, 7 finite check,
- * 8 decompression + error update, 9 q commit, 10 Gram sum (rank > 128 only), 11 decompression
- * operands (rank > 128 only), 12 second orthonormalisation pass (all four of its launches;
- * they return at once for matrices whose first pass was well conditioned).
- * Slots a call does not launch keep their events unrecorded. n must be at least 26.
+ * 8 decompression + error update + q commit, 9 Gram sum (rank > 128 only), 10 decompression
+ * row scales (rank > 128 only, and psgd_refresh_q), 11 second orthonormalisation pass (all
+ * four of its launches; they return at once for matrices whose first pass was well
+ * conditioned). Slots a call does not launch keep their events unrecorded. n must be at
+ * least 24.
  * events == NULL (n ignored) removes the hook. The events stay owned by the caller.
  */
 psgd_status psgd_profile_events(psgd_ctx* ctx, hipEvent_t* events, int n);

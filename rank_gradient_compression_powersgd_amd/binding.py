@@ -20,7 +20,7 @@ STATUS_NAMES = {0: "PSGD_OK", 1: "PSGD_EINVAL", 2: "PSGD_EDTYPE", 3: "PSGD_ENOME
 
 # Names of the profiling slots (order of psgd_profile_events).
 PROFILE_SLOTS = ("zero_flags", "ef_mq", "gs_gram", "gs_factor", "gs_apply", "mtp",
-                 "zero_skip", "check_finite", "decompress", "commit_q", "gs_reduce", "split3",
+                 "zero_skip", "check_finite", "decompress", "gs_reduce", "split3",
                  "gs_second_pass")
 
 

@@ -15,6 +15,9 @@
 // out go through buffer descriptors: ragged edges read zeros and drop their stores in
 // hardware, so the epilogue issues the loads of all its rows at once and has no branches.
 //
+// The workgroups of the first row of tiles also copy the q_next rows they stage into q (the
+// warm start of the next step), so a non-skipped step commits q without a pass of its own.
+//
 // Skip: the device-side skip word is read first. A skipped step zeroes the error buffer over
 // the tile and writes nothing else (the error buffer is zeroed on non-finite values: Korean
 // summary of the paper, section "Distributed Optimization").
@@ -154,11 +157,27 @@ void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
     *reinterpret_cast<f16x4*>(hi_row + off) = h;
     *reinterpret_cast<f16x4*>(lo_row + off) = l;
   };
-  auto store_stage = [&](int buf) {
+  // The first row of tiles also commits q <- q_next (the step is not skipped here): it writes
+  // the fp32 groups of q_next it has just read to the same place in q.
+  const bool commit = m0 == 0;
+  const rsrc_t rqc = make_rsrc(d.q, commit ? (uint32_t)n * (uint32_t)r * 4u : 0u);
+  auto store_stage = [&](int buf, int k0) {
+    const int k = k0 + 4 * hq;
 #pragma unroll
     for (int j = 0; j < QG; ++j) {
       const int rr = rq0 + RSTEP3 * j;
       put_group(ldq[buf][0][rr], ldq[buf][1][rr], rr, sq[j], eq[j]);
+      if (commit) {
+        if (rvec) {
+          bstore16(__builtin_bit_cast(u32x4, sq[j]), rqc, k < r ? qrow[j] + 4u * k : kOOB);
+        } else {
+          const u32x4 bits = __builtin_bit_cast(u32x4, sq[j]);
+          __builtin_amdgcn_raw_buffer_store_b32(bits[0], rqc, k < r ? qrow[j] + 4u * k : kOOB, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(bits[1], rqc, k + 1 < r ? qrow[j] + 4u * (k + 1) : kOOB, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(bits[2], rqc, k + 2 < r ? qrow[j] + 4u * (k + 2) : kOOB, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(bits[3], rqc, k + 3 < r ? qrow[j] + 4u * (k + 3) : kOOB, 0, 0);
+        }
+      }
     }
 #pragma unroll
     for (int j = 0; j < PG; ++j) {
@@ -197,13 +216,13 @@ void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
 
   const int nsteps = kpad3 / 32;
   load_stage(0);
-  store_stage(0);
+  store_stage(0, 0);
   __syncthreads();
   int ks = 0;
   for (; ks + 1 < nsteps; ++ks) {
     load_stage((ks + 1) * 32);
     compute(ks & 1);
-    store_stage((ks & 1) ^ 1);
+    store_stage((ks & 1) ^ 1, (ks + 1) * 32);
     __syncthreads();
   }
   compute(ks & 1);
@@ -273,36 +292,6 @@ void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   }
 }
 
-// q <- q_next when the step is not skipped. One work item: 4096 consecutive floats of q (a
-// 16-byte aligned range: q is n x r contiguous); each thread moves four 16-byte vectors, all
-// loads issued before the stores.
-__global__ __launch_bounds__(256)
-void k_commit_q(const DevMat* __restrict__ mats, const Work* __restrict__ work,
-                const int32_t* __restrict__ skip)
-{
-  const Work wi = work[blockIdx.x];
-  if (wi.mat < 0 || *skip != 0) return;
-  const DevMat& d = mats[wi.mat];
-  const int64_t total = (int64_t)d.n * d.r;
-  const int64_t beg = (int64_t)wi.a * 4096;
-  const int64_t end = beg + 4096 < total ? beg + 4096 : total;
-  const int64_t vend = beg + ((end - beg) & ~int64_t(3));
-  GLOBAL float* __restrict__ q = gbl(d.q);
-  const GLOBAL float* __restrict__ qn = gbl(d.q_next);
-  f32x4 v[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int64_t i = beg + 4 * ((int64_t)threadIdx.x + 256 * b);
-    if (i < vend) v[b] = *gcast<f32x4>(qn + i);
-  }
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int64_t i = beg + 4 * ((int64_t)threadIdx.x + 256 * b);
-    if (i < vend) *gcast<f32x4>(q + i) = v[b];
-  }
-  if ((int)threadIdx.x < end - vend) q[vend + threadIdx.x] = qn[vend + threadIdx.x];
-}
-
 template <int GT>
 hipError_t launch_gt(dim3 grid, hipStream_t s, const DevMat* mats, const Work* work,
                      const float* scale, const int32_t* skip) {
@@ -325,13 +314,6 @@ hipError_t launch_decompress(int gt, const DevMat* mats, const Work* work, int n
     case G_F32: return launch_gt<G_F32>(grid, s, mats, work, scale, skip);
   }
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_commit_q(const DevMat* mats, const Work* work, int n_work, const int32_t* skip,
-                           hipStream_t s) {
-  if (n_work <= 0) return hipSuccess;
-  k_commit_q<<<dim3(n_work), dim3(256), 0, s>>>(mats, work, skip);
-  return hipGetLastError();
 }
 
 }  // namespace psgd

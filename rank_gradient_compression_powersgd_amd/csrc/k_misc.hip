@@ -1,4 +1,4 @@
-// Small kernels: fills, the q commit and the skip decision.
+// Small kernels: fills and the skip decision.
 #include "psgd_internal.h"
 
 namespace psgd {

@@ -260,8 +260,6 @@ hipError_t launch_mtp(int gt, int rtc, const DevMat* mats, const Work* work, int
                       const float* scale, hipStream_t s);
 hipError_t launch_decompress(int gt, const DevMat* mats, const Work* work, int n_work,
                              const float* scale, const int32_t* skip, hipStream_t s);
-hipError_t launch_commit_q(const DevMat* mats, const Work* work, int n_work, const int32_t* skip,
-                           hipStream_t s);
 struct PassList;
 hipError_t launch_check_finite(const uint8_t* flags, int n_flags, const float* scale, int n_scale,
                                const float* const* pass_ptr, const int64_t* pass_n, int n_pass,

@@ -34,7 +34,7 @@ struct psgd_ctx {
 namespace {
 
 enum WorkKind { W_K1, W_GRAM, W_REDUCE, W_FACTOR, W_APPLY, W_K2, W_SPLIT3, W_SPLITQ, W_K3,
-                W_COMMIT, W_KINDS };
+                W_KINDS };
 
 }  // namespace
 
@@ -72,7 +72,7 @@ psgd_status hip_fail(psgd_ctx* ctx, hipError_t e, const char* what) {
 }
 
 enum Slot { S_ZERO_FLAGS, S_K1, S_GRAM, S_FACTOR, S_APPLY, S_K2, S_ZERO_SKIP, S_CHECK,
-            S_K3, S_COMMIT, S_REDUCE, S_SPLIT3, S_REORTH, S_SLOTS };
+            S_K3, S_REDUCE, S_SPLIT3, S_REORTH, S_SLOTS };
 
 // Launch `expr` in tracing slot `slot`, bracketed by the hook's events when installed.
 template <typename F>
@@ -318,12 +318,6 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
       for (int n0 = 0; n0 < p->mats[i].n; n0 += tn)
         push(Work{i, m0, n0, 0}, (int64_t)std::min(tm, p->mats[i].m - m0) * std::min(tn, p->mats[i].n - n0));
   end_kind(W_K3, true);
-  begin_kind(W_COMMIT);
-  for (int i = 0; i < n_mats; ++i) {
-    const int64_t tot = (int64_t)p->mats[i].n * r;
-    for (int64_t c0 = 0; c0 * 4096 < tot; ++c0) all.push_back(Work{i, (int)c0, 0, 0});
-  }
-  end_kind(W_COMMIT, false);
   for (int k = 0; k < W_KINDS; ++k)
     if (p->cnt[k] > 0x7fffffff / 2) return fail(ctx, PSGD_EINVAL, "work list too long");
 
@@ -490,7 +484,6 @@ psgd_status psgd_decompress_update(psgd_ctx* ctx, psgd_plan* plan, const float* 
   const DevMat* dm = plan->d_mats;
   auto W = [&](int k) { return plan->d_work + plan->off[k]; };
   HIPCHK(ctx, traced(ctx, S_K3, stream, [&] { return psgd::launch_decompress(plan->gt, dm, W(W_K3), plan->cnt[W_K3], scale, skip_dev, stream); }), "decompress");
-  HIPCHK(ctx, traced(ctx, S_COMMIT, stream, [&] { return psgd::launch_commit_q(dm, W(W_COMMIT), plan->cnt[W_COMMIT], skip_dev, stream); }), "commit q");
   return PSGD_OK;
 }
 
