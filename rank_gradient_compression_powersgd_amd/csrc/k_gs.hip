@@ -127,9 +127,10 @@ void k_gs_gram(const DevMat* __restrict__ mats, const Work* __restrict__ work, i
       }
 }
 
-// W = sum of the Gram partials in part order (large ranks). One work item: 4096 consecutive
-// elements of the rpad x rpad matrix starting at a * 4096. Elements of blocks below the
-// diagonal were never written and sum to zero.
+// W = sum of the Gram partials in part order (large ranks); also U = I (tmat) and the
+// diagonal of W saved in wdiag for the factorisation's dependence test. One work item: 4096
+// consecutive elements of the rpad x rpad matrix starting at a * 4096. Elements of blocks below
+// the diagonal were never written and sum to zero.
 __global__ __launch_bounds__(256)
 void k_gs_reduce(const DevMat* __restrict__ mats, const Work* __restrict__ work, int pass)
 {
@@ -137,65 +138,36 @@ void k_gs_reduce(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   if (wi.mat < 0) return;
   const DevMat& d = mats[wi.mat];
   if (pass && *d.reorth == 0) return;
-  const int64_t tot = (int64_t)d.rpad * d.rpad;
+  const int rp = d.rpad;
+  const int64_t tot = (int64_t)rp * rp;
   const int parts = d.gram_parts;
   const GLOBAL double* __restrict__ gram = gbl(d.gram);
   GLOBAL double* __restrict__ wsum = gbl(d.wsum);
+  GLOBAL double* __restrict__ tmat = gbl(d.tmat);
+  GLOBAL double* __restrict__ wdiag = gbl(d.wdiag);
   for (int64_t e = (int64_t)wi.a * 4096 + threadIdx.x; e < tot && e < (int64_t)(wi.a + 1) * 4096; e += 256) {
     double sum = 0.0;
+#pragma unroll 8
     for (int pt = 0; pt < parts; ++pt) sum += gram[(int64_t)pt * tot + e];
     wsum[e] = sum;
+    const bool diag = e / rp == e % rp;
+    tmat[e] = diag ? 1.0 : 0.0;
+    if (diag) wdiag[e / rp] = sum;
   }
 }
 
 // ------------------------------------------------------------------------------------------
-// Gram-Schmidt on a Gram matrix block resident in LDS (block size <= 128)
+// Gram-Schmidt on the Gram matrix (Cholesky form, T = R^-1)
 // ------------------------------------------------------------------------------------------
-constexpr int kPackMax = kBlk * (kBlk + 1) / 2;
-constexpr int GSF_THREADS = 1024;     // 32 x 32 thread grid over the r x r problem
+constexpr int GSF_THREADS = 1024;
 
-__device__ __forceinline__ int pidx(int i, int j, int rp) {   // packed upper, i <= j
-  return i * rp - (i * (i - 1)) / 2 + (j - i);
-}
-
-// Column recurrence on packed W (bs x bs, updated in place) and T (packed, initialised to I):
-// on return P T has orthonormal columns when W = P^T P; dependent columns of T are zero.
-// diag0[j] is column j's squared norm before any projection. All GSF_THREADS threads call it
-// and all return the smallest squared residual ratio of a kept column (1 if none is kept).
-__device__ double factor_block(double* W, double* T, const double* diag0, double* rrow, int bs)
-{
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  double minratio = 1.0;
-  for (int j = 0; j < bs; ++j) {
-    const double dj = W[pidx(j, j, bs)];
-    const double d0 = diag0[j];
-    const bool ok = (d0 > 0.0) && (dj > kDegenerate * d0) && (dj <= 1.0e300);
-    const double inv = ok ? 1.0 / sqrt(dj) : 0.0;
-    if (ok) minratio = fmin(minratio, dj / d0);
-    // r_jk = <q_j, v_k> = W[j][k] / ||v_j||; t_j = u_j / ||v_j||
-    const int k1 = j + 1 + (int)threadIdx.x;
-    if (k1 < bs) rrow[k1] = W[pidx(j, k1, bs)] * inv;
-    if ((int)threadIdx.x <= j) T[pidx(threadIdx.x, j, bs)] *= inv;
-    __syncthreads();
-    // v_k -= r_jk q_j for k > j: Gram update and coefficient update
-    for (int k = j + 1 + ty; k < bs; k += 32) {
-      const int base = k * bs - (k * (k - 1)) / 2 - k;
-      const double rk = rrow[k];
-      for (int l = k + ((tx - (k - j - 1)) & 31); l < bs; l += 32) W[base + l] -= rk * rrow[l];
-    }
-    for (int i = ty; i <= j; i += 32) {
-      const int base = i * bs - (i * (i - 1)) / 2 - i;
-      const double tij = T[base + j];
-      for (int k = j + 1 + tx; k < bs; k += 32) T[base + k] -= rrow[k] * tij;
-    }
-    __syncthreads();
-  }
-  return minratio;
-}
-
-// Ranks up to 128: the same recurrence in 16-column panels. W is summed from the partials
-// straight into LDS as full 16 x 16 blocks of its upper block triangle, beside the coefficient
-// matrix U (initially I; block column p of U becomes block column p of T). For each panel p:
+// The column recurrence: for column j, with W the Gram matrix of the residual columns, v_j is
+// kept when W_jj > 2^-40 x (its squared norm before any projection) and is normalised by
+// 1 / sqrt(W_jj); the later columns lose their component along it, in W and in the
+// coefficient matrix T (P T has orthonormal columns; a dropped column's T column is zero).
+// It runs in 16-column panels. W is held as full 16 x 16 blocks of its upper block triangle,
+// beside the coefficient matrix U (initially I; block column p of U becomes block column p of
+// T). For each panel p:
 //   (A) one wave takes the diagonal block W_pp into registers and runs the column recurrence on
 //       it with lane shuffles (no barriers), giving the panel's local factor L (T_pp = L);
 //   (B) T_ip = U_ip L for i <= p, and the panel row of R, R_pj = L^T W_pj for j > p;
@@ -233,45 +205,17 @@ __device__ __forceinline__ void fblock_mm(double* C, const double* A, bool trans
   }
 }
 
-__global__ __launch_bounds__(GSF_THREADS)
-void k_gs_factor(const DevMat* __restrict__ mats, const Work* __restrict__ work, int pass)
+// The panel recurrence on nb panels held in LDS: Wb (upper block triangle of the residual
+// Gram matrix), Ub (I on entry; T on return), d0 (each column's squared norm before any
+// projection). All GSF_THREADS threads call it; wave 0 returns the smallest squared residual
+// ratio of a kept column (1 if none is kept), the other waves 1.
+__device__ __forceinline__ double factor_panels(double* Wb, double* Ub, double* Lsh, const double* d0, int nb)
 {
-  const Work wi = work[blockIdx.x];
-  if (wi.mat < 0) return;
-  const DevMat& d = mats[wi.mat];
-  if (pass && *d.reorth == 0) return;
-  const int rp = d.rpad, nb = rp / FB;
-  const int parts = d.gram_parts;
-  const GLOBAL double* __restrict__ gram = gbl(d.gram);
-  GLOBAL double* __restrict__ tmat = gbl(d.tmat);
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
   constexpr int NWV = GSF_THREADS / kWave;
   const int c = lane & 15, g = lane >> 4;
-
-  __shared__ double Wb[FNBLK * FBS];
-  __shared__ double Ub[FNBLK * FBS];
-  __shared__ double Lsh[FBS];
-  __shared__ double diag0[kBlk];
-
-  // W = sum of the partial Gram matrices in part order (upper block triangle); U = I.
-  const int nblk = nb * (nb + 1) / 2;
-  for (int e = threadIdx.x; e < nblk * FB * FB; e += GSF_THREADS) {
-    const int b = e / (FB * FB), rc = e - b * FB * FB, rr = rc / FB, cc = rc - rr * FB;
-    int bi = 0;
-    while (fblk(bi + 1, bi + 1, nb) <= b && bi + 1 < nb) ++bi;
-    const int bj = bi + (b - fblk(bi, bi, nb));
-    const int row = bi * FB + rr, col = bj * FB + cc;
-    double sum = 0.0;
-#pragma unroll 8
-    for (int pt = 0; pt < parts; ++pt) sum += gram[((int64_t)pt * rp + row) * rp + col];
-    Wb[b * FBS + rr * FBP + cc] = sum;
-    Ub[b * FBS + rr * FBP + cc] = (bi == bj && rr == cc) ? 1.0 : 0.0;
-    if (bi == bj && rr == cc) diag0[row] = sum;
-  }
-  __syncthreads();
-
-  double minratio = 1.0;               // wave 0, every lane
+  double minratio = 1.0;
   for (int p = 0; p < nb; ++p) {
     // (A) diagonal block: lane 16g + c holds rows g + 4i, column c, of the residual Gram block
     // (a) and of the local factor (l).
@@ -287,10 +231,10 @@ void k_gs_factor(const DevMat* __restrict__ mats, const Work* __restrict__ work,
       for (int jj = 0; jj < FB; ++jj) {
         const int gj = jj & 3, ij = jj >> 2;       // holder of row jj: lanes 16 gj + x, register ij
         const double dj = __shfl(a[ij], 16 * gj + jj);
-        const double d0 = diag0[p * FB + jj];
-        const bool ok = (d0 > 0.0) && (dj > kDegenerate * d0) && (dj <= 1.0e300);
+        const double dz = d0[p * FB + jj];
+        const bool ok = (dz > 0.0) && (dj > kDegenerate * dz) && (dj <= 1.0e300);
         const double inv = ok ? 1.0 / sqrt(dj) : 0.0;
-        if (ok) minratio = fmin(minratio, dj / d0);
+        if (ok) minratio = fmin(minratio, dj / dz);
         // row jj of the residual block, scaled: r[x] = a[jj][x] / ||v_jj||
         const double rc = __shfl(a[ij], 16 * gj + c) * inv;
         double rrow[4];
@@ -341,145 +285,222 @@ void k_gs_factor(const DevMat* __restrict__ mats, const Work* __restrict__ work,
     }
     __syncthreads();
   }
+  return minratio;
+}
+
+// row-major element (row, col) of the block layout (upper block triangle only)
+__device__ __forceinline__ double& fel(double* B, int row, int col, int nb) {
+  return B[fblk(row / FB, col / FB, nb) * FBS + (row % FB) * FBP + col % FB];
+}
+
+// Ranks up to 128: W summed from the partials straight into LDS.
+__global__ __launch_bounds__(GSF_THREADS)
+void k_gs_factor(const DevMat* __restrict__ mats, const Work* __restrict__ work, int pass)
+{
+  const Work wi = work[blockIdx.x];
+  if (wi.mat < 0) return;
+  const DevMat& d = mats[wi.mat];
+  if (pass && *d.reorth == 0) return;
+  const int rp = d.rpad, nb = rp / FB;
+  const int parts = d.gram_parts;
+  const GLOBAL double* __restrict__ gram = gbl(d.gram);
+  GLOBAL double* __restrict__ tmat = gbl(d.tmat);
+
+  __shared__ double Wb[FNBLK * FBS];
+  __shared__ double Ub[FNBLK * FBS];
+  __shared__ double Lsh[FBS];
+  __shared__ double diag0[kBlk];
+
+  // W = sum of the partial Gram matrices in part order (upper block triangle); U = I.
+  const int nblk = nb * (nb + 1) / 2;
+  for (int e = threadIdx.x; e < nblk * FB * FB; e += GSF_THREADS) {
+    const int b = e / (FB * FB), rc = e - b * FB * FB, rr = rc / FB, cc = rc - rr * FB;
+    int bi = 0;
+    while (fblk(bi + 1, bi + 1, nb) <= b && bi + 1 < nb) ++bi;
+    const int bj = bi + (b - fblk(bi, bi, nb));
+    const int row = bi * FB + rr, col = bj * FB + cc;
+    double sum = 0.0;
+#pragma unroll 8
+    for (int pt = 0; pt < parts; ++pt) sum += gram[((int64_t)pt * rp + row) * rp + col];
+    Wb[b * FBS + rr * FBP + cc] = sum;
+    Ub[b * FBS + rr * FBP + cc] = (bi == bj && rr == cc) ? 1.0 : 0.0;
+    if (bi == bj && rr == cc) diag0[row] = sum;
+  }
+  __syncthreads();
+
+  const double minratio = factor_panels(Wb, Ub, Lsh, diag0, nb);
   if (pass == 0 && threadIdx.x == 0) *gbl(d.reorth) = minratio < kReorth ? 1 : 0;
 
   // T (row-major rpad x rpad; zero below the block diagonal)
   for (int e = threadIdx.x; e < rp * rp; e += GSF_THREADS) {
     const int row = e / rp, col = e - row * rp;
-    const int bi = row / FB, bj = col / FB;
-    tmat[e] = bj >= bi ? Ub[fblk(bi, bj, nb) * FBS + (row % FB) * FBP + col % FB] : 0.0;
+    tmat[e] = col / FB >= row / FB ? fel(Ub, row, col, nb) : 0.0;
   }
 }
 
-// C (bi x bj, ld) = alpha * op(A) op(B) (+ C when accumulate), with op(A) bi x bk and op(B)
-// bk x bj, all fp64 in global memory (leading dimension ld). transA: A is stored bk x bi and
-// op(A) = A^T. transB likewise. Blocks are at most 128 x 128; GSF_THREADS threads, each
-// owning a 4 x 4 piece of C; 16-deep k slices staged in LDS (As, Bs: 16 x 128 each). Every
-// thread reads all of A and B before any thread writes C, so C may alias A or B.
-__device__ void block_gemm(GLOBAL double* C, const GLOBAL double* A, bool transA,
-                           const GLOBAL double* B, bool transB, int ld, int bi, int bj, int bk,
-                           double alpha, bool accumulate, double* As, double* Bs)
+// ------------------------------------------------------------------------------------------
+// Ranks above 128: the same blocked recurrence on 128-column blocks, one launch per phase.
+// W (wsum, rpad x rpad, summed by k_gs_reduce, which also saves its diagonal in wdiag and sets
+// tmat = I) and U (tmat) live in global memory. For each block k:
+//   k_gs_fdiag(k):  the diagonal block W_kk is factored in LDS by factor_panels; its local
+//                   factor L is T_kk (written into tmat);
+//   k_gs_bgemm(k, 0): T_ik = U_ik L (i < k) and R_kj = L^T W_kj (j > k), in place;
+//   k_gs_bgemm(k, 1): U_ij -= T_ik R_kj (i <= k < j) and W_ij -= R_ki^T R_kj (k < i <= j).
+// Every product is one 128 x 128 x 128 block (ragged last block) per workgroup, so the work of
+// each phase spreads over many CUs.
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(GSF_THREADS)
+void k_gs_fdiag(const DevMat* __restrict__ mats, const Work* __restrict__ work, int pass, int kb)
 {
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  double acc[4][4];
+  const Work wi = work[blockIdx.x];
+  if (wi.mat < 0) return;
+  const DevMat& d = mats[wi.mat];
+  if (pass && *d.reorth == 0) return;
+  const int rp = d.rpad, k0 = kb * kBlk, bs = min(kBlk, rp - k0), nb = bs / FB;
+  GLOBAL double* __restrict__ W = gbl(d.wsum);
+  GLOBAL double* __restrict__ Tg = gbl(d.tmat);
+  const GLOBAL double* __restrict__ wd = gbl(d.wdiag);
+
+  __shared__ double Wb[FNBLK * FBS];
+  __shared__ double Ub[FNBLK * FBS];
+  __shared__ double Lsh[FBS];
+  __shared__ double diag0[kBlk];
+
+  const int nblk = nb * (nb + 1) / 2;
+  for (int e = threadIdx.x; e < nblk * FB * FB; e += GSF_THREADS) {
+    const int b = e / (FB * FB), rc = e - b * FB * FB, rr = rc / FB, cc = rc - rr * FB;
+    int bi = 0;
+    while (fblk(bi + 1, bi + 1, nb) <= b && bi + 1 < nb) ++bi;
+    const int bj = bi + (b - fblk(bi, bi, nb));
+    const int row = bi * FB + rr, col = bj * FB + cc;
+    Wb[b * FBS + rr * FBP + cc] = W[(int64_t)(k0 + row) * rp + k0 + col];
+    Ub[b * FBS + rr * FBP + cc] = (bi == bj && rr == cc) ? 1.0 : 0.0;
+  }
+  for (int i = threadIdx.x; i < bs; i += GSF_THREADS) diag0[i] = wd[k0 + i];
+  __syncthreads();
+
+  const double minratio = factor_panels(Wb, Ub, Lsh, diag0, nb);
+  if (pass == 0 && threadIdx.x == 0) {
+    const int again = minratio < kReorth ? 1 : 0;
+    if (kb == 0) *gbl(d.reorth) = again;
+    else if (again) *gbl(d.reorth) = 1;
+  }
+  for (int e = threadIdx.x; e < bs * bs; e += GSF_THREADS) {
+    const int row = e / bs, col = e - row * bs;
+    Tg[(int64_t)(k0 + row) * rp + k0 + col] = col / FB >= row / FB ? fel(Ub, row, col, nb) : 0.0;
+  }
+}
+
+// C (bi x bj) = / -= op(A) (bi x bk) B (bk x bj), fp64, row-major with leading dimension ld.
+// 256 threads: waves 2 x 2, each a 64 x 64 quarter of C as 4 x 4 MFMA tiles; k slices of 16
+// staged in LDS (op(A) as [row][k], B as [k][col]), the next slice loaded while this one is
+// multiplied. Every read of A and B happens before C is written, so C may alias A or B.
+constexpr int BG_THREADS = 256;
+__device__ void bgemm_block(GLOBAL double* C, const GLOBAL double* A, bool transA,
+                            const GLOBAL double* B, bool sub, int ld, int bi, int bj, int bk)
+{
+  constexpr int KS = 16;
+  constexpr int AP = KS + 1;               // op(A) slice pitch: column reads spread over banks
+  __shared__ double As[kBlk * AP];
+  __shared__ double Bs[KS * kBlk];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  const int wm = wv & 1, wn = wv >> 1;
+  const int c = lane & 15, g = lane >> 4;
+  // staging: 2048 elements of each slice, 8 per thread
+  double ra[8], rb[8];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int u = threadIdx.x + e * BG_THREADS;
+      // op(A)[row][k]: transA reads A[k][row] along rows of A (row index fastest)
+      int row, kk;
+      if (transA) { kk = u / kBlk; row = u % kBlk; } else { row = u / KS; kk = u % KS; }
+      const int k = k0 + kk;
+      ra[e] = (row < bi && k < bk) ? (transA ? A[(int64_t)k * ld + row] : A[(int64_t)row * ld + k]) : 0.0;
+      const int bkk = u / kBlk, col = u % kBlk;
+      rb[e] = (col < bj && k0 + bkk < bk) ? B[(int64_t)(k0 + bkk) * ld + col] : 0.0;
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int u = threadIdx.x + e * BG_THREADS;
+      int row, kk;
+      if (transA) { kk = u / kBlk; row = u % kBlk; } else { row = u / KS; kk = u % KS; }
+      As[row * AP + kk] = ra[e];
+      Bs[u] = rb[e];                       // [k][col]
+    }
+  };
+  f64x4 acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
-  for (int k0 = 0; k0 < bk; k0 += 16) {
-    for (int e = threadIdx.x; e < 16 * kBlk; e += GSF_THREADS) {
-      const int kk = e / kBlk, ii = e % kBlk, k = k0 + kk;
-      double av = 0.0, bv = 0.0;
-      if (k < bk && ii < bi) av = transA ? A[(int64_t)k * ld + ii] : A[(int64_t)ii * ld + k];
-      if (k < bk && ii < bj) bv = transB ? B[(int64_t)ii * ld + k] : B[(int64_t)k * ld + ii];
-      As[kk * kBlk + ii] = av;
-      Bs[kk * kBlk + ii] = bv;
-    }
+    for (int b = 0; b < 4; ++b) acc[a][b] = f64x4{0, 0, 0, 0};
+  load(0);
+  for (int k0 = 0; k0 < bk; k0 += KS) {
     __syncthreads();
-#pragma unroll 4
-    for (int kk = 0; kk < 16; ++kk) {
+    store();
+    if (k0 + KS < bk) load(k0 + KS);
+    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < KS / 4; ++st) {
+      const int k = 4 * st + g;
       double av[4], bv[4];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) av[a] = As[kk * kBlk + 4 * ty + a];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) bv[b] = Bs[kk * kBlk + 4 * tx + b];
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = fma(av[a], bv[b], acc[a][b]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int i = 4 * ty + a, j = 4 * tx + b;
-      if (i < bi && j < bj) {
-        GLOBAL double* cp = C + (int64_t)i * ld + j;
-        *cp = alpha * acc[a][b] + (accumulate ? *cp : 0.0);
+      for (int t = 0; t < 4; ++t) {
+        av[t] = As[(wm * 64 + t * 16 + c) * AP + k];
+        bv[t] = Bs[k * kBlk + wn * 64 + t * 16 + c];
       }
+#pragma unroll
+      for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = mfma_f64(av[tm], bv[tn], acc[tm][tn]);
     }
-  __syncthreads();
+  }
+  // C layout of v_mfma_f64_16x16x4f64: lane 16g + c, register i holds C[g + 4i][c].
+#pragma unroll
+  for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = wm * 64 + tm * 16 + g + 4 * i, col = wn * 64 + tn * 16 + c;
+        if (row < bi && col < bj) {
+          GLOBAL double* cp = C + (int64_t)row * ld + col;
+          *cp = sub ? *cp - acc[tm][tn][i] : acc[tm][tn][i];
+        }
+      }
 }
 
-// Ranks above 128: blocked factorisation of the summed Gram matrix (see the file comment).
-// One workgroup per matrix. wsum's upper blocks are overwritten by R's off-diagonal blocks; the
-// first 128 x 128 doubles of the (no longer needed) partial buffer serve as scratch.
-__global__ __launch_bounds__(GSF_THREADS)
-void k_gs_factor_blk(const DevMat* __restrict__ mats, const Work* __restrict__ work, int pass)
+// One work item: matrix `mat`, blocks (i = a, j = b); phase 0 items with j == kb form
+// T_ik = U_ik L, the others R_kj = L^T W_kj; phase 1 items with i <= kb update U, the others W.
+__global__ __launch_bounds__(BG_THREADS)
+void k_gs_bgemm(const DevMat* __restrict__ mats, const Work* __restrict__ work, int pass, int kb,
+                int phase)
 {
   const Work wi = work[blockIdx.x];
   if (wi.mat < 0) return;
   const DevMat& d = mats[wi.mat];
   if (pass && *d.reorth == 0) return;
   const int rp = d.rpad;
-  const int nb = (rp + kBlk - 1) / kBlk;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   GLOBAL double* __restrict__ W = gbl(d.wsum);
   GLOBAL double* __restrict__ Tg = gbl(d.tmat);
-  GLOBAL double* __restrict__ S = gbl(d.gram);
-
-  __shared__ double lW[kPackMax];          // packed diagonal block; staging of block_gemm
-  __shared__ double lT[kPackMax];
-  __shared__ double diag0[kMaxRank];
-  __shared__ double rrow[kBlk];
-
-  for (int i = threadIdx.x; i < rp; i += GSF_THREADS) diag0[i] = W[(int64_t)i * rp + i];
-  __syncthreads();
-
-  double minratio = 1.0;
-  for (int kb = 0; kb < nb; ++kb) {
-    const int k0 = kb * kBlk, bs = min(kBlk, rp - k0);
-    // diagonal block in LDS
-    for (int i = ty; i < bs; i += 32) {
-      const int base = i * bs - (i * (i - 1)) / 2 - i;
-      for (int j = i + tx; j < bs; j += 32) {
-        lW[base + j] = W[(int64_t)(k0 + i) * rp + k0 + j];
-        lT[base + j] = (i == j) ? 1.0 : 0.0;
-      }
-    }
-    __syncthreads();
-    minratio = fmin(minratio, factor_block(lW, lT, diag0 + k0, rrow, bs));
-    for (int i = ty; i < bs; i += 32) {
-      const int base = i * bs - (i * (i - 1)) / 2 - i;
-      for (int j = tx; j < bs; j += 32) Tg[(int64_t)(k0 + i) * rp + k0 + j] = (j >= i) ? lT[base + j] : 0.0;
-    }
-    __syncthreads();
-    // block row of R: R_kj = T_kk^T W_kj (in place)
-    for (int jb = kb + 1; jb < nb; ++jb) {
-      const int j0 = jb * kBlk, bj = min(kBlk, rp - j0);
-      block_gemm(W + (int64_t)k0 * rp + j0, Tg + (int64_t)k0 * rp + k0, true,
-                 W + (int64_t)k0 * rp + j0, false, rp, bs, bj, bs, 1.0, false, lW, lT);
-    }
-    // trailing Gram blocks: W_ij -= R_ki^T R_kj
-    for (int ib = kb + 1; ib < nb; ++ib)
-      for (int jb = ib; jb < nb; ++jb) {
-        const int i0 = ib * kBlk, j0 = jb * kBlk;
-        block_gemm(W + (int64_t)i0 * rp + j0, W + (int64_t)k0 * rp + i0, true,
-                   W + (int64_t)k0 * rp + j0, false, rp, min(kBlk, rp - i0), min(kBlk, rp - j0), bs,
-                   -1.0, true, lW, lT);
-      }
+  const int ib = wi.a, jb = wi.b;
+  const int k0 = kb * kBlk, i0 = ib * kBlk, j0 = jb * kBlk;
+  const int bsk = min(kBlk, rp - k0), bsi = min(kBlk, rp - i0), bsj = min(kBlk, rp - j0);
+  auto blk = [&](GLOBAL double* X, int r0, int c0) { return X + (int64_t)r0 * rp + c0; };
+  if (phase == 0) {
+    if (jb == kb)   // T_ik = U_ik L
+      bgemm_block(blk(Tg, i0, k0), blk(Tg, i0, k0), false, blk(Tg, k0, k0), false, rp, bsi, bsk, bsk);
+    else            // R_kj = L^T W_kj
+      bgemm_block(blk(W, k0, j0), blk(Tg, k0, k0), true, blk(W, k0, j0), false, rp, bsk, bsj, bsk);
+  } else {
+    if (ib <= kb)   // U_ij -= T_ik R_kj
+      bgemm_block(blk(Tg, i0, j0), blk(Tg, i0, k0), false, blk(W, k0, j0), true, rp, bsi, bsj, bsk);
+    else            // W_ij -= R_ki^T R_kj
+      bgemm_block(blk(W, i0, j0), blk(W, k0, i0), true, blk(W, k0, j0), true, rp, bsi, bsj, bsk);
   }
-  if (pass == 0 && threadIdx.x == 0) *gbl(d.reorth) = minratio < kReorth ? 1 : 0;
-  // T = R^-1, block column by block column: T_ij = -T_ii sum_{i<k<=j} R_ik T_kj
-  for (int jb = 1; jb < nb; ++jb) {
-    const int j0 = jb * kBlk, bj = min(kBlk, rp - j0);
-    for (int ib = jb - 1; ib >= 0; --ib) {
-      const int i0 = ib * kBlk, bi = min(kBlk, rp - i0);
-      for (int kb = ib + 1; kb <= jb; ++kb) {
-        const int q0 = kb * kBlk, bq = min(kBlk, rp - q0);
-        block_gemm(S, W + (int64_t)i0 * rp + q0, false, Tg + (int64_t)q0 * rp + j0, false, rp,
-                   bi, bj, bq, 1.0, kb > ib + 1, lW, lT);
-      }
-      block_gemm(Tg + (int64_t)i0 * rp + j0, Tg + (int64_t)i0 * rp + i0, false, S, false, rp,
-                 bi, bj, bi, -1.0, false, lW, lT);
-    }
-  }
-  // blocks below the diagonal of T
-  for (int i = ty; i < rp; i += 32)
-    for (int j = tx; j < rp; j += 32)
-      if (j / kBlk < i / kBlk) Tg[(int64_t)i * rp + j] = 0.0;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -796,10 +817,22 @@ hipError_t launch_gs_reduce(int pass, const DevMat* mats, const Work* work, int 
   return hipGetLastError();
 }
 
-hipError_t launch_gs_factor(bool big, int pass, const DevMat* mats, const Work* work, int n_work, hipStream_t s) {
+hipError_t launch_gs_factor(int pass, const DevMat* mats, const Work* work, int n_work, hipStream_t s) {
   if (n_work <= 0) return hipSuccess;
-  if (big) k_gs_factor_blk<<<dim3(n_work), dim3(GSF_THREADS), 0, s>>>(mats, work, pass);
-  else k_gs_factor<<<dim3(n_work), dim3(GSF_THREADS), 0, s>>>(mats, work, pass);
+  k_gs_factor<<<dim3(n_work), dim3(GSF_THREADS), 0, s>>>(mats, work, pass);
+  return hipGetLastError();
+}
+
+hipError_t launch_gs_fdiag(int pass, int kb, const DevMat* mats, const Work* work, int n_work, hipStream_t s) {
+  if (n_work <= 0) return hipSuccess;
+  k_gs_fdiag<<<dim3(n_work), dim3(GSF_THREADS), 0, s>>>(mats, work, pass, kb);
+  return hipGetLastError();
+}
+
+hipError_t launch_gs_bgemm(int pass, int kb, int phase, const DevMat* mats, const Work* work, int n_work,
+                           hipStream_t s) {
+  if (n_work <= 0) return hipSuccess;
+  k_gs_bgemm<<<dim3(n_work), dim3(BG_THREADS), 0, s>>>(mats, work, pass, kb, phase);
   return hipGetLastError();
 }
 

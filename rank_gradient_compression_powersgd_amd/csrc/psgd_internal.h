@@ -140,8 +140,9 @@ struct DevMat {
   int32_t* q3_exp;                     // n3 likewise for q_next
   double* gram;                        // gram_parts x rpad x rpad fp64 partial Gram matrices
   double* tmat;                        // rpad x rpad fp64 upper-triangular T, P = (M q) T
-  double* wsum;                        // rpad x rpad fp64 summed Gram matrix, overwritten by the
-                                       // off-diagonal blocks of R (r > 128 only; else unused)
+  double* wsum;                        // rpad x rpad fp64 summed Gram matrix, updated in place by
+                                       // the blocked factorisation (r > 128 only; else unused)
+  double* wdiag;                       // rpad fp64: its diagonal before the factorisation (r > 128)
   float* p2;                           // m x rpad fp32: first-pass orthonormal factor, the input
                                        // of the second pass when one is needed
   int32_t* reorth;                     // 1: this step's factor needs a second pass
@@ -253,7 +254,10 @@ hipError_t launch_ef_mq(int gt, int rtc, const DevMat* mats, const Work* work, i
                         const float* scale, uint8_t* flags, hipStream_t s);
 hipError_t launch_gs_gram(int rt, bool big, int pass, const DevMat* mats, const Work* work, int n_work, hipStream_t s);
 hipError_t launch_gs_reduce(int pass, const DevMat* mats, const Work* work, int n_work, hipStream_t s);
-hipError_t launch_gs_factor(bool big, int pass, const DevMat* mats, const Work* work, int n_work, hipStream_t s);
+hipError_t launch_gs_factor(int pass, const DevMat* mats, const Work* work, int n_work, hipStream_t s);
+hipError_t launch_gs_fdiag(int pass, int kb, const DevMat* mats, const Work* work, int n_work, hipStream_t s);
+hipError_t launch_gs_bgemm(int pass, int kb, int phase, const DevMat* mats, const Work* work, int n_work,
+                           hipStream_t s);
 hipError_t launch_gs_apply(int rt, bool big, int pass, const DevMat* mats, const Work* work, int n_work, hipStream_t s);
 hipError_t launch_split3(const DevMat* mats, const Work* work, int n_work, hipStream_t s);
 hipError_t launch_mtp(int gt, int rtc, const DevMat* mats, const Work* work, int n_work,

@@ -33,8 +33,9 @@ struct psgd_ctx {
 
 namespace {
 
-enum WorkKind { W_K1, W_GRAM, W_REDUCE, W_FACTOR, W_APPLY, W_K2, W_SPLIT3, W_SPLITQ, W_K3,
+enum WorkKind { W_K1, W_GRAM, W_REDUCE, W_FACTOR, W_BGEMM, W_APPLY, W_K2, W_SPLIT3, W_SPLITQ, W_K3,
                 W_KINDS };
+constexpr int kMaxBlocks = psgd::kMaxRank / psgd::kBlk;   // 128-column blocks of the largest rank
 
 }  // namespace
 
@@ -50,6 +51,9 @@ struct psgd_plan {
   Work* d_work = nullptr;
   int off[W_KINDS] = {0};
   int cnt[W_KINDS] = {0};
+  int nblk = 1;                          // 128-column blocks of rpad
+  int bg_off[kMaxBlocks][2] = {{0}};     // block products of step k, phase 0/1 (within W_BGEMM)
+  int bg_cnt[kMaxBlocks][2] = {{0}};
 };
 
 namespace {
@@ -171,7 +175,7 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
   size_t praw_cursor = 0;
   size_t ws = (size_t)rup((int64_t)praw_total, 256);
   auto take = [&](size_t bytes) { size_t o = ws; ws += (size_t)rup((int64_t)bytes, 256); return o; };
-  struct Off { size_t p_raw, pth, ptl, p3e, q3e, gram, tmat, wsum, p2, reorth; };
+  struct Off { size_t p_raw, pth, ptl, p3e, q3e, gram, tmat, wsum, wdiag, p2, reorth; };
   std::vector<Off> offs(n_mats);
   p->mats.resize(n_mats);
   for (int i = 0; i < n_mats; ++i) {
@@ -228,6 +232,7 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
     o.gram = take((size_t)d.gram_parts * rpad * rpad * 8);
     o.tmat = take((size_t)rpad * rpad * 8);
     o.wsum = big ? take((size_t)rpad * rpad * 8) : 0;
+    o.wdiag = big ? take((size_t)rpad * 8) : 0;
     o.p2 = take((size_t)a.m * rpad * 4);
     o.reorth = take(4);
   }
@@ -290,6 +295,27 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
   begin_kind(W_FACTOR);
   for (int i = 0; i < n_mats; ++i) all.push_back(Work{i, 0, 0, 0});
   end_kind(W_FACTOR, false);
+  // block products of the large-rank factorisation, grouped by step k and phase
+  begin_kind(W_BGEMM);
+  p->nblk = nblk;
+  if (big)
+    for (int kb = 0; kb < nblk; ++kb)
+      for (int ph = 0; ph < 2; ++ph) {
+        p->bg_off[kb][ph] = (int)all.size() - p->off[W_BGEMM];
+        for (int i = 0; i < n_mats; ++i) {
+          if (ph == 0) {
+            for (int ib = 0; ib < kb; ++ib) all.push_back(Work{i, ib, kb, 0});        // T_ik
+            for (int jb = kb + 1; jb < nblk; ++jb) all.push_back(Work{i, kb, jb, 0}); // R_kj
+          } else {
+            for (int ib = 0; ib <= kb; ++ib)
+              for (int jb = kb + 1; jb < nblk; ++jb) all.push_back(Work{i, ib, jb, 0});  // U_ij
+            for (int ib = kb + 1; ib < nblk; ++ib)
+              for (int jb = ib; jb < nblk; ++jb) all.push_back(Work{i, ib, jb, 0});      // W_ij
+          }
+        }
+        p->bg_cnt[kb][ph] = (int)all.size() - p->off[W_BGEMM] - p->bg_off[kb][ph];
+      }
+  end_kind(W_BGEMM, false);
   begin_kind(W_APPLY);
   for (int i = 0; i < n_mats; ++i)
     for (int r0 = 0; r0 < p->mats[i].m; r0 += aprows)
@@ -346,6 +372,7 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
     d.gram = reinterpret_cast<double*>(base + o.gram);
     d.tmat = reinterpret_cast<double*>(base + o.tmat);
     d.wsum = big ? reinterpret_cast<double*>(base + o.wsum) : nullptr;
+    d.wdiag = big ? reinterpret_cast<double*>(base + o.wdiag) : nullptr;
     d.p2 = reinterpret_cast<float*>(base + o.p2);
     d.reorth = reinterpret_cast<int32_t*>(base + o.reorth);
   }
@@ -391,23 +418,41 @@ psgd_status psgd_compress_p(psgd_ctx* ctx, psgd_plan* plan, const float* scale, 
   return PSGD_OK;
 }
 
-psgd_status psgd_orthogonalize(psgd_ctx* ctx, psgd_plan* plan, hipStream_t stream) {
-  if (psgd_status st = check_call(ctx, plan); st != PSGD_OK) return st;
+namespace {
+// One orthonormalisation pass: Gram partials, T, P_hat = P T. Large ranks sum the partials and
+// factor W by 128-column blocks (diagonal block, then the block products of that step).
+hipError_t orth_pass(psgd_plan* plan, int pass, hipStream_t stream, psgd_ctx* ctx, bool trace) {
   const DevMat* dm = plan->d_mats;
   auto W = [&](int k) { return plan->d_work + plan->off[k]; };
   const bool big = plan->big;
-  HIPCHK(ctx, traced(ctx, S_GRAM, stream, [&] { return psgd::launch_gs_gram(plan->rt, big, 0, dm, W(W_GRAM), plan->cnt[W_GRAM], stream); }), "Gram");
-  if (big)
-    HIPCHK(ctx, traced(ctx, S_REDUCE, stream, [&] { return psgd::launch_gs_reduce(0, dm, W(W_REDUCE), plan->cnt[W_REDUCE], stream); }), "Gram sum");
-  HIPCHK(ctx, traced(ctx, S_FACTOR, stream, [&] { return psgd::launch_gs_factor(big, 0, dm, W(W_FACTOR), plan->cnt[W_FACTOR], stream); }), "Gram-Schmidt");
-  HIPCHK(ctx, traced(ctx, S_APPLY, stream, [&] { return psgd::launch_gs_apply(plan->rt, big, 0, dm, W(W_APPLY), plan->cnt[W_APPLY], stream); }), "orthonormal P");
+  auto run = [&](int slot, auto&& f) { return trace ? traced(ctx, slot, stream, f) : f(); };
+  hipError_t e = run(S_GRAM, [&] { return psgd::launch_gs_gram(plan->rt, big, pass, dm, W(W_GRAM), plan->cnt[W_GRAM], stream); });
+  if (e != hipSuccess) return e;
+  if (big) {
+    e = run(S_REDUCE, [&] { return psgd::launch_gs_reduce(pass, dm, W(W_REDUCE), plan->cnt[W_REDUCE], stream); });
+    if (e != hipSuccess) return e;
+    e = run(S_FACTOR, [&] {
+      hipError_t r = hipSuccess;
+      for (int kb = 0; kb < plan->nblk && r == hipSuccess; ++kb) {
+        r = psgd::launch_gs_fdiag(pass, kb, dm, W(W_FACTOR), plan->cnt[W_FACTOR], stream);
+        for (int ph = 0; ph < 2 && r == hipSuccess; ++ph)
+          r = psgd::launch_gs_bgemm(pass, kb, ph, dm, W(W_BGEMM) + plan->bg_off[kb][ph], plan->bg_cnt[kb][ph], stream);
+      }
+      return r; });
+  } else {
+    e = run(S_FACTOR, [&] { return psgd::launch_gs_factor(pass, dm, W(W_FACTOR), plan->cnt[W_FACTOR], stream); });
+  }
+  if (e != hipSuccess) return e;
+  return run(S_APPLY, [&] { return psgd::launch_gs_apply(plan->rt, big, pass, dm, W(W_APPLY), plan->cnt[W_APPLY], stream); });
+}
+}  // namespace
+
+psgd_status psgd_orthogonalize(psgd_ctx* ctx, psgd_plan* plan, hipStream_t stream) {
+  if (psgd_status st = check_call(ctx, plan); st != PSGD_OK) return st;
+  HIPCHK(ctx, orth_pass(plan, 0, stream, ctx, true), "orthonormalisation");
   // second pass, for the matrices whose first pass flagged it (the others return at once)
-  HIPCHK(ctx, traced(ctx, S_REORTH, stream, [&] {
-    hipError_t e = psgd::launch_gs_gram(plan->rt, big, 1, dm, W(W_GRAM), plan->cnt[W_GRAM], stream);
-    if (e == hipSuccess && big) e = psgd::launch_gs_reduce(1, dm, W(W_REDUCE), plan->cnt[W_REDUCE], stream);
-    if (e == hipSuccess) e = psgd::launch_gs_factor(big, 1, dm, W(W_FACTOR), plan->cnt[W_FACTOR], stream);
-    if (e == hipSuccess) e = psgd::launch_gs_apply(plan->rt, big, 1, dm, W(W_APPLY), plan->cnt[W_APPLY], stream);
-    return e; }), "second orthonormalisation pass");
+  HIPCHK(ctx, traced(ctx, S_REORTH, stream, [&] { return orth_pass(plan, 1, stream, ctx, false); }),
+         "second orthonormalisation pass");
   return PSGD_OK;
 }
 
