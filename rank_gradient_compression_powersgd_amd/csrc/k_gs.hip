@@ -574,8 +574,25 @@ void k_gs_apply_s(const DevMat* __restrict__ mats, const Work* __restrict__ work
 #pragma unroll
     for (int a = 0; a < RPW; ++a) acc[h][a] = f64x4{0, 0, 0, 0};
   if (active) {
+    // T fragments of k tile kt for both output tiles; the next k tile's are loaded (from L2)
+    // while this one's MFMAs run
+    double nB[4], nA[4];
+    auto fetch = [&](int kt) {
+      const bool useA = kt <= tA && tA != tB;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int64_t krow = (int64_t)(16 * kt + 4 * g + ks) * rpad;
+        nB[ks] = Tm[krow + 16 * tB + c];
+        nA[ks] = useA ? Tm[krow + 16 * tA + c] : 0.0;
+      }
+    };
+    fetch(0);
 #pragma unroll 1
     for (int kt = 0; kt <= tB; ++kt) {
+      double bB[4], bA[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) { bB[ks] = nB[ks]; bA[ks] = nA[ks]; }
+      if (kt < tB) fetch(kt + 1);
       f32x4 av[RPW];
 #pragma unroll
       for (int a = 0; a < RPW; ++a)
@@ -583,13 +600,10 @@ void k_gs_apply_s(const DevMat* __restrict__ mats, const Work* __restrict__ work
       const bool useA = kt <= tA && tA != tB;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const int64_t krow = (int64_t)(16 * kt + 4 * g + ks) * rpad;
-        const double bB = Tm[krow + 16 * tB + c];
-        const double bA = useA ? Tm[krow + 16 * tA + c] : 0.0;
 #pragma unroll
         for (int a = 0; a < RPW; ++a) {
-          acc[1][a] = mfma_f64((double)av[a][ks], bB, acc[1][a]);
-          if (useA) acc[0][a] = mfma_f64((double)av[a][ks], bA, acc[0][a]);
+          acc[1][a] = mfma_f64((double)av[a][ks], bB[ks], acc[1][a]);
+          if (useA) acc[0][a] = mfma_f64((double)av[a][ks], bA[ks], acc[0][a]);
         }
       }
     }
