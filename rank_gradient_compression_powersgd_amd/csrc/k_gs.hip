@@ -509,18 +509,21 @@ void k_gs_bgemm(const DevMat* __restrict__ mats, const Work* __restrict__ work, 
 constexpr int GSA_RA = 2;                          // 16-row tiles per wave
 constexpr int GSA_ROWS = GSA_RA * 16 * (GS_THREADS / kWave);   // 128 rows per workgroup
 
-// Small ranks (RT tiles of 16 columns, rpad <= 128): all columns of P_hat for rows
-// [a, a + 128). The P tile (128 rows x rpad, one contiguous block of the factor buffer) is
-// read into LDS with 16-byte loads, all in flight at once. Each wave then owns output column
-// tiles {t, RT - 1 - t} (T is upper triangular, so tile t costs t + 1 k tiles and every pair
-// costs RT + 1) for all 8 row tiles, or a share of the row tiles when there are fewer pairs
-// than waves: each fragment of T, read from L2, feeds every row tile of the wave. The k index
-// of an MFMA step is permuted within a 16-k tile (k = 16 kt + 4 g + ks), so that a lane takes
-// its 4 A values of a k tile from one 16-byte LDS read. Products and sums are fp64; P_hat is
-// rounded to fp32 once.
-template <int RT>
-__global__ __launch_bounds__(GS_THREADS, 2)
-void k_gs_apply_s(const DevMat* __restrict__ mats, const Work* __restrict__ work, int pass)
+// One work item: rows [a, a + 128) of P_hat and, for large ranks (BIG: RT = 8, rpad > 128),
+// its 128-column block b; small ranks (rpad <= 128) take all RT column tiles at once. P is read
+// into LDS by column blocks of RT tiles (one block for small ranks; blocks 0..b for large ones),
+// each with all its 16-byte loads in flight at once. Each wave owns output column tiles
+// {t, RT - 1 - t}: within the diagonal block of T (upper triangular) tile t costs t + 1 k tiles,
+// so every pair costs RT + 1; off-diagonal blocks are dense. A wave computes its pair for all
+// 8 row tiles (or a share of them when there are fewer pairs than waves), so each fragment of
+// T, read from L2 one k tile ahead, feeds every row tile of the wave. The k index of an MFMA
+// step is permuted within a 16-k tile (k = 16 kt + 4 g + ks), so that a lane takes its 4 A
+// values of a k tile from one 16-byte LDS read. Products and sums are fp64; P_hat is rounded
+// to fp32 once. Large ranks leave the row exponents of the decompression to split3 (they need
+// every column block).
+template <int RT, bool BIG>
+__global__ __launch_bounds__(GS_THREADS, BIG ? 1 : 2)
+void k_gs_apply(const DevMat* __restrict__ mats, const Work* __restrict__ work, int pass)
 {
   const Work wi = work[xcd_remap(blockIdx.x, gridDim.x)];
   if (wi.mat < 0) return;
@@ -539,117 +542,130 @@ void k_gs_apply_s(const DevMat* __restrict__ mats, const Work* __restrict__ work
   constexpr int LD = RC + 4;               // LDS row pitch (floats): rows stay 16-byte aligned
   constexpr int NW = GS_THREADS / kWave;
   constexpr int NRT = GSA_ROWS / 16;       // row tiles (8)
+  const int cb = BIG ? wi.b : 0;           // output column block
+  const int c0 = cb * RC;
+  const int ncols = BIG ? min(RC, rpad - c0) : RC;   // output columns present (whole tiles)
+  const int nto = ncols / 16;
 
   __shared__ __attribute__((aligned(16))) float S[GSA_ROWS * LD];
 
-  // (1) the P tile into LDS; rows past m are zero
-  constexpr int U4 = RT * 4;               // 16-byte units per row
-  constexpr int NL = GSA_ROWS * U4 / GS_THREADS;
-  static_assert(NL * GS_THREADS == GSA_ROWS * U4, "load units");
-  {
-    f32x4 v[NL];
-#pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      const int u = threadIdx.x + j * GS_THREADS, rr = u / U4, q = u - rr * U4;
-      v[j] = rr < rows ? *gcast<f32x4>(P + (int64_t)(row0 + rr) * rpad + 4 * q) : f32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      const int u = threadIdx.x + j * GS_THREADS, rr = u / U4, q = u - rr * U4;
-      *reinterpret_cast<f32x4*>(&S[rr * LD + 4 * q]) = v[j];
-    }
-  }
-  __syncthreads();
-
-  // (2) this wave's column-tile pair and row tiles
+  // this wave's column-tile pair and row tiles
   constexpr int NG = (RT + 1) / 2;         // column-tile pairs
   constexpr int WPG = NG >= NW ? 1 : NW / NG;   // waves per pair
   constexpr int RPW = NRT / WPG;           // row tiles per wave
   const int gi = wv % NG, rs = wv / NG;    // pair, row share
   const bool active = wv < NG * WPG;
   const int tA = gi, tB = RT - 1 - gi;     // tB == tA for the middle tile of odd RT
+  const bool haveB = active && tB < nto, haveA = active && tA < nto && tA != tB;
   f64x4 acc[2][RPW];
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int a = 0; a < RPW; ++a) acc[h][a] = f64x4{0, 0, 0, 0};
-  if (active) {
-    // T fragments of k tile kt for both output tiles; the next k tile's are loaded (from L2)
-    // while this one's MFMAs run
-    double nB[4], nA[4];
-    auto fetch = [&](int kt) {
-      const bool useA = kt <= tA && tA != tB;
+
+  constexpr int U4 = RT * 4;               // 16-byte units per row of a column block
+  constexpr int NL = GSA_ROWS * U4 / GS_THREADS;
+  static_assert(NL * GS_THREADS == GSA_ROWS * U4, "load units");
+  for (int kb = 0; kb <= cb; ++kb) {
+    const int k0 = kb * RC;
+    const int nkt = BIG ? min(RT, (rpad - k0) / 16) : RT;   // k tiles present
+    // (1) columns [k0, k0 + 16 nkt) of the P tile into LDS; rows past m and missing columns zero
+    if (kb > 0) __syncthreads();           // the previous block's A values have been read
+    {
+      f32x4 v[NL];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int64_t krow = (int64_t)(16 * kt + 4 * g + ks) * rpad;
-        nB[ks] = Tm[krow + 16 * tB + c];
-        nA[ks] = useA ? Tm[krow + 16 * tA + c] : 0.0;
+      for (int j = 0; j < NL; ++j) {
+        const int u = threadIdx.x + j * GS_THREADS, rr = u / U4, q = u - rr * U4;
+        const bool ok = rr < rows && (!BIG || 4 * q < 16 * nkt);
+        v[j] = ok ? *gcast<f32x4>(P + (int64_t)(row0 + rr) * rpad + k0 + 4 * q) : f32x4{0, 0, 0, 0};
       }
-    };
-    fetch(0);
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        const int u = threadIdx.x + j * GS_THREADS, rr = u / U4, q = u - rr * U4;
+        *reinterpret_cast<f32x4*>(&S[rr * LD + 4 * q]) = v[j];
+      }
+    }
+    __syncthreads();
+    // (2) the pair's products with this block of T: triangular on the diagonal, else dense
+    const bool diag = kb == cb;
+    const int endB = haveB ? (diag ? tB : nkt - 1) : -1;
+    const int endA = haveA ? (diag ? tA : nkt - 1) : -1;
+    const int kend = endB > endA ? endB : endA;
+    if (kend >= 0) {
+      double nB[4], nA[4];
+      auto fetch = [&](int kt) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int64_t krow = (int64_t)(k0 + 16 * kt + 4 * g + ks) * rpad + c0;
+          nB[ks] = (!BIG || kt <= endB) ? Tm[krow + 16 * tB + c] : 0.0;
+          nA[ks] = kt <= endA ? Tm[krow + 16 * tA + c] : 0.0;
+        }
+      };
+      fetch(0);
 #pragma unroll 1
-    for (int kt = 0; kt <= tB; ++kt) {
-      double bB[4], bA[4];
+      for (int kt = 0; kt <= kend; ++kt) {
+        double bB[4], bA[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) { bB[ks] = nB[ks]; bA[ks] = nA[ks]; }
-      if (kt < tB) fetch(kt + 1);
-      f32x4 av[RPW];
+        for (int ks = 0; ks < 4; ++ks) { bB[ks] = nB[ks]; bA[ks] = nA[ks]; }
+        if (kt < kend) fetch(kt + 1);
+        f32x4 av[RPW];
 #pragma unroll
-      for (int a = 0; a < RPW; ++a)
-        av[a] = *reinterpret_cast<const f32x4*>(&S[((rs + a * WPG) * 16 + c) * LD + 16 * kt + 4 * g]);
-      const bool useA = kt <= tA && tA != tB;
+        for (int a = 0; a < RPW; ++a)
+          av[a] = *reinterpret_cast<const f32x4*>(&S[((rs + a * WPG) * 16 + c) * LD + 16 * kt + 4 * g]);
+        const bool useB = !BIG || kt <= endB, useA = kt <= endA;   // small ranks: kend == endB
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+        for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-        for (int a = 0; a < RPW; ++a) {
-          acc[1][a] = mfma_f64((double)av[a][ks], bB[ks], acc[1][a]);
-          if (useA) acc[0][a] = mfma_f64((double)av[a][ks], bA[ks], acc[0][a]);
+          for (int a = 0; a < RPW; ++a) {
+            if (useB) acc[1][a] = mfma_f64((double)av[a][ks], bB[ks], acc[1][a]);
+            if (useA) acc[0][a] = mfma_f64((double)av[a][ks], bA[ks], acc[0][a]);
+          }
         }
       }
     }
   }
   __syncthreads();                         // every wave has read its A values
   // C layout of v_mfma_f64_16x16x4f64: lane 16g + c, register i holds C[g + 4i][c].
-  if (active) {
 #pragma unroll
-    for (int a = 0; a < RPW; ++a)
+  for (int a = 0; a < RPW; ++a)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = (rs + a * WPG) * 16 + g + 4 * i;
-        S[rr * LD + 16 * tB + c] = (float)acc[1][a][i];
-        if (tA != tB) S[rr * LD + 16 * tA + c] = (float)acc[0][a][i];
-      }
-  }
+    for (int i = 0; i < 4; ++i) {
+      const int rr = (rs + a * WPG) * 16 + g + 4 * i;
+      if (haveB) S[rr * LD + 16 * tB + c] = (float)acc[1][a][i];
+      if (haveA) S[rr * LD + 16 * tA + c] = (float)acc[0][a][i];
+    }
   __syncthreads();
 
+  const int u4c = ncols / 4;               // 16-byte units of a row present
   if (pass == 0 && again) {
     // first pass of a matrix that needs two: the result is the second pass's input
     GLOBAL float* __restrict__ p2 = gbl(d.p2);
-    for (int u = threadIdx.x; u < rows * U4; u += GS_THREADS) {
-      const int rr = u / U4, q = u - rr * U4;
-      *gcast<f32x4>(p2 + (int64_t)(row0 + rr) * rpad + 4 * q) = *reinterpret_cast<const f32x4*>(&S[rr * LD + 4 * q]);
+    for (int u = threadIdx.x; u < rows * u4c; u += GS_THREADS) {
+      const int rr = u / u4c, q = u - rr * u4c;
+      *gcast<f32x4>(p2 + (int64_t)(row0 + rr) * rpad + c0 + 4 * q) = *reinterpret_cast<const f32x4*>(&S[rr * LD + 4 * q]);
     }
     return;
   }
 
-  // (a) fp32 P_hat, m x r row-major
+  // (a) fp32 P_hat, m x r row-major (this block's columns below r)
   GLOBAL float* __restrict__ pout = gbl(d.p);
+  const int pc = max(0, min(ncols, r - c0));
   if ((r & 3) == 0) {
-    const int ur = r / 4;
+    const int ur = pc / 4;
     for (int u = threadIdx.x; u < rows * ur; u += GS_THREADS) {
       const int rr = u / ur, q = u - rr * ur;
-      *gcast<f32x4>(pout + (int64_t)(row0 + rr) * r + 4 * q) = *reinterpret_cast<const f32x4*>(&S[rr * LD + 4 * q]);
+      *gcast<f32x4>(pout + (int64_t)(row0 + rr) * r + c0 + 4 * q) = *reinterpret_cast<const f32x4*>(&S[rr * LD + 4 * q]);
     }
   } else {
-    for (int u = threadIdx.x; u < rows * r; u += GS_THREADS) {
-      const int rr = u / r, cc = u - rr * r;
-      pout[(int64_t)(row0 + rr) * r + cc] = S[rr * LD + cc];
+    for (int u = threadIdx.x; u < rows * pc; u += GS_THREADS) {
+      const int rr = u / pc, cc = u - rr * pc;
+      pout[(int64_t)(row0 + rr) * r + c0 + cc] = S[rr * LD + cc];
     }
   }
   // (b) P_hat^T split bf16 hi/lo, rpad x mpad: 8 consecutive rows of one column per store
   GLOBAL uint16_t* __restrict__ pth = gbl(d.pt_hi);
   GLOBAL uint16_t* __restrict__ ptl = gbl(d.pt_lo);
-  for (int idx = threadIdx.x; idx < RC * (GSA_ROWS / 8); idx += GS_THREADS) {
+  for (int idx = threadIdx.x; idx < ncols * (GSA_ROWS / 8); idx += GS_THREADS) {
     const int col = idx / (GSA_ROWS / 8), r8 = (idx % (GSA_ROWS / 8)) * 8;
     if (row0 + r8 >= mpad) continue;
     uint32_t h[4], l[4];
@@ -660,9 +676,10 @@ void k_gs_apply_s(const DevMat* __restrict__ mats, const Work* __restrict__ work
       h[e] = bf16_bits(h0) | ((uint32_t)bf16_bits(h1) << 16);
       l[e] = bf16_bits((__bf16)(x0 - (float)h0)) | ((uint32_t)bf16_bits((__bf16)(x1 - (float)h1)) << 16);
     }
-    *gcast<u32x4>(pth + (int64_t)col * mpad + row0 + r8) = u32x4{h[0], h[1], h[2], h[3]};
-    *gcast<u32x4>(ptl + (int64_t)col * mpad + row0 + r8) = u32x4{l[0], l[1], l[2], l[3]};
+    *gcast<u32x4>(pth + (int64_t)(c0 + col) * mpad + row0 + r8) = u32x4{h[0], h[1], h[2], h[3]};
+    *gcast<u32x4>(ptl + (int64_t)(c0 + col) * mpad + row0 + r8) = u32x4{l[0], l[1], l[2], l[3]};
   }
+  if constexpr (BIG) return;
   // (c) row exponents of the decompression operand: the power of two that brings the row's
   // largest entry into [2^13, 2^14) before the decompression splits it into fp16 hi + lo
   GLOBAL int32_t* __restrict__ p3e = gbl(d.p3_exp);
@@ -670,114 +687,6 @@ void k_gs_apply_s(const DevMat* __restrict__ mats, const Work* __restrict__ work
     float amax = 0.0f;
     for (int cc = 0; cc < RC; ++cc) amax = fmaxf(amax, fabsf(S[threadIdx.x * LD + cc]));
     p3e[row0 + threadIdx.x] = fp16_row_exponent(amax);
-  }
-}
-
-// Large ranks (rpad > 128, RT = 8): the 128-column block b of P_hat for rows [a, a + 128); the
-// row exponents of its decompression operand are found afterwards by split3 (they need every
-// column).
-template <int RT, bool BIG>
-__global__ __launch_bounds__(GS_THREADS)
-void k_gs_apply(const DevMat* __restrict__ mats, const Work* __restrict__ work, int pass)
-{
-  const Work wi = work[xcd_remap(blockIdx.x, gridDim.x)];
-  if (wi.mat < 0) return;
-  const DevMat& d = mats[wi.mat];
-  const bool again = *d.reorth != 0;      // a second pass follows (pass 0) / runs (pass 1)
-  if (pass && !again) return;
-  const int m = d.m, r = d.r, rpad = d.rpad, mpad = d.mpad;
-  const GLOBAL float* __restrict__ P = gbl(pass ? d.p2 : d.p_raw);
-  const GLOBAL double* __restrict__ Tm = gbl(d.tmat);
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wv = threadIdx.x / kWave;
-  const int c = lane & 15, g = lane >> 4;
-  const int row0 = wi.a;                   // this workgroup's GSA_ROWS rows
-  const int t0 = BIG ? wi.b * RT : 0;      // first output column tile
-  const int nto = BIG ? min(RT, rpad / 16 - t0) : RT;   // output tiles present
-  const int c0 = t0 * 16;
-  constexpr int SP = RT * 16 + 1;          // LDS row pitch (floats); odd, so column reads spread over banks
-
-  __shared__ float S[GSA_ROWS * SP];
-
-  f64x4 acc[GSA_RA][RT];
-#pragma unroll
-  for (int a = 0; a < GSA_RA; ++a)
-#pragma unroll
-    for (int t = 0; t < RT; ++t) acc[a][t] = f64x4{0, 0, 0, 0};
-
-  auto kstep = [&](int k, int tfirst) {
-    double av[GSA_RA];
-#pragma unroll
-    for (int a = 0; a < GSA_RA; ++a) {
-      const int rowA = row0 + (wv * GSA_RA + a) * 16 + c;     // A-fragment row of this lane
-      av[a] = rowA < m ? (double)P[(int64_t)rowA * rpad + k] : 0.0;
-    }
-#pragma unroll
-    for (int tj = 0; tj < RT; ++tj) {
-      if (tj < tfirst || tj >= nto) continue;
-      const double b = Tm[(int64_t)k * rpad + c0 + tj * 16 + c];
-#pragma unroll
-      for (int a = 0; a < GSA_RA; ++a) acc[a][tj] = mfma_f64(av[a], b, acc[a][tj]);
-    }
-  };
-  if constexpr (BIG) {
-    // k tiles left of the block feed every output tile
-    for (int kt = 0; kt < t0; ++kt)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kstep(kt * 16 + ks * 4 + g, 0);
-  }
-  // P_hat = P T with T upper triangular: k tile t0 + kt only feeds column tiles tj >= kt.
-#pragma unroll
-  for (int kt = 0; kt < RT; ++kt) {
-    if (kt >= nto) break;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) kstep((t0 + kt) * 16 + ks * 4 + g, kt);
-  }
-
-  // C layout of v_mfma_f64_16x16x4f64: lane 16g + c, register i holds C[g + 4i][c].
-#pragma unroll
-  for (int a = 0; a < GSA_RA; ++a)
-#pragma unroll
-    for (int t = 0; t < RT; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        S[((wv * GSA_RA + a) * 16 + g + 4 * i) * SP + t * 16 + c] = (float)acc[a][t][i];
-  __syncthreads();
-
-  if (pass == 0 && again) {
-    // first pass of a matrix that needs two: the result is the second pass's input
-    GLOBAL float* __restrict__ p2 = gbl(d.p2);
-    const int nc = nto * 16;
-    for (int idx = threadIdx.x; idx < GSA_ROWS * nc; idx += GS_THREADS) {
-      const int rr = idx / nc, cc = idx - rr * nc;
-      if (row0 + rr < m) p2[(int64_t)(row0 + rr) * rpad + c0 + cc] = S[rr * SP + cc];
-    }
-    return;
-  }
-
-  // (a) fp32 P_hat, m x r row-major (this block's columns)
-  GLOBAL float* __restrict__ pout = gbl(d.p);
-  const int ncol = max(0, min(nto * 16, r - c0));
-  for (int idx = threadIdx.x; idx < GSA_ROWS * ncol; idx += GS_THREADS) {
-    const int rr = idx / ncol, cc = idx - rr * ncol;
-    if (row0 + rr < m) pout[(int64_t)(row0 + rr) * r + c0 + cc] = S[rr * SP + cc];
-  }
-  // (b) P_hat^T split bf16 hi/lo, rpad x mpad: 8 consecutive rows of one column per store
-  GLOBAL uint16_t* __restrict__ pth = gbl(d.pt_hi);
-  GLOBAL uint16_t* __restrict__ ptl = gbl(d.pt_lo);
-  for (int idx = threadIdx.x; idx < nto * 16 * (GSA_ROWS / 8); idx += GS_THREADS) {
-    const int col = idx / (GSA_ROWS / 8), r8 = (idx % (GSA_ROWS / 8)) * 8;
-    if (row0 + r8 >= mpad) continue;
-    uint32_t h[4], l[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float x0 = S[(r8 + 2 * e) * SP + col], x1 = S[(r8 + 2 * e + 1) * SP + col];
-      const __bf16 h0 = (__bf16)x0, h1 = (__bf16)x1;
-      h[e] = bf16_bits(h0) | ((uint32_t)bf16_bits(h1) << 16);
-      l[e] = bf16_bits((__bf16)(x0 - (float)h0)) | ((uint32_t)bf16_bits((__bf16)(x1 - (float)h1)) << 16);
-    }
-    *gcast<u32x4>(pth + (int64_t)(c0 + col) * mpad + row0 + r8) = u32x4{h[0], h[1], h[2], h[3]};
-    *gcast<u32x4>(ptl + (int64_t)(c0 + col) * mpad + row0 + r8) = u32x4{l[0], l[1], l[2], l[3]};
   }
 }
 
@@ -858,7 +767,7 @@ hipError_t launch_gs_apply(int rt, bool big, int pass, const DevMat* mats, const
     return hipGetLastError();
   }
   switch (rt) {
-#define CASE(R) case R: k_gs_apply_s<R><<<grid, block, 0, s>>>(mats, work, pass); break;
+#define CASE(R) case R: k_gs_apply<R, false><<<grid, block, 0, s>>>(mats, work, pass); break;
     CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
 #undef CASE
     default: return hipErrorInvalidValue;
