@@ -14,7 +14,8 @@
 //              result is P t_j. The inner products <q_i, v_j> and the norms ||v_j|| are read
 //              from the running Gram matrix, which is updated as columns are projected out.
 //              This gives the upper-triangular T with P T orthonormal, T = R^-1 of the thin
-//              QR. fp64, one workgroup per matrix, W and T resident in LDS.
+//              QR. fp64, one workgroup per matrix, W and T resident in LDS, in 16-column
+//              panels (one wave per diagonal panel, fp64 MFMA block updates).
 //              A column whose remaining squared norm is at most 2^-40 of its original squared
 //              norm (or zero, or not finite) is dependent: its column of T is set to zero.
 //   second pass The Gram form loses orthogonality as eps_64 times the squared condition
@@ -24,17 +25,15 @@
 //              of the two triangular factors is again the thin-QR factor, so the result is the
 //              same P). Matrices that need no second pass leave those launches at once.
 //   gs_apply   P_hat = P T with fp64 MFMA accumulation, then the stores the products need:
-//              P_hat in fp32 (caller's p), P_hat^T split bf16 hi/lo for K2, and P_hat rows
-//              scaled by a power of two and split fp16 hi/lo for the decompression kernel.
+//              P_hat in fp32 (caller's p), P_hat^T split bf16 hi/lo for K2, and each row's
+//              power-of-two exponent for the decompression's fp16 split.
 //
-// Ranks above 128 (r x r no longer fits in LDS) take the blocked form of the same recurrence,
-// on 128-column blocks: the Gram matrix is formed block pair by block pair and summed
-// (gs_reduce); gs_factor_blk then walks the diagonal blocks. Each diagonal block is factored
-// in LDS by the same column recurrence (giving T_kk = R_kk^-1), the block row of R to its right
-// is R_kj = T_kk^T W_kj, and the trailing Gram blocks lose R_ki^T R_kj (a right-looking blocked
-// Cholesky factorisation W = R^T R). The off-diagonal blocks of T = R^-1 follow from
-// T_ij = -T_ii (sum_{i<k<=j} R_ik T_kj). gs_apply forms P_hat by 128-column blocks and
-// split3 builds the scaled fp16 operands of the decompression from the fp32 factors.
+// Ranks above 128 (r x r no longer fits in LDS) run the same blocked recurrence on 128-column
+// blocks, with W and T in global memory: the Gram matrix is formed block pair by block pair
+// and summed (gs_reduce); then, per block k, gs_fdiag factors the diagonal block in LDS with
+// the panel routine and gs_bgemm applies the block products of that step as fp64 MFMA GEMMs
+// spread over many workgroups. gs_apply forms P_hat by 128-column blocks, and split3 finds the
+// row exponents of the decompression from the fp32 factors.
 #include "psgd_internal.h"
 
 namespace psgd {

@@ -184,9 +184,9 @@ void k_mtp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   compute(ks & 1, cur);
 
   // Output tile (i, t): lane holds Q'^T rows rc0 + 16i + 4g + {0..3}, i.e. Q'[colbase + t][..].
-  // The tile goes through LDS so that the stores to Q' and to the decompression operand are
-  // whole 16-byte units on consecutive addresses (from the C layout they would be 32- and
-  // 64-byte pieces of 16 rows), stored non-temporally as in the M Q kernel.
+  // The tile goes through LDS so that the stores to Q' are whole 16-byte units on consecutive
+  // addresses (from the C layout they would be 64-byte pieces of 16 rows), stored
+  // non-temporally as in the M Q kernel.
   float* qt = reinterpret_cast<float*>(lds_raw);          // [K2_W * WCOLS][QT_LD]
   const bool whole = RC == rpad;                // this chunk covers the whole padded rank
   __syncthreads();                              // the staged P^T has been read
