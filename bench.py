@@ -88,14 +88,17 @@ COPY_BYTES = 1 << 31          # the calibration copy reads and writes 2 GiB per 
 
 
 def kernel_source_hash() -> str:
-    """sha256 over the library's HIP sources: traffic counters taken on other sources are stale."""
+    """sha256 over the code of the library's HIP sources (line comments and blank lines left
+    out, so that comment edits keep recorded counters valid): counters taken on other code are
+    stale."""
     import glob
     import hashlib
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(ROOT, "rank_gradient_compression_powersgd_amd", "csrc", "*"))):
         if f.endswith((".hip", ".h")):
-            with open(f, "rb") as fh:
-                h.update(os.path.basename(f).encode() + b"\0" + fh.read())
+            with open(f, encoding="utf-8") as fh:
+                code = [ln.split("//", 1)[0].rstrip() for ln in fh]
+            h.update(os.path.basename(f).encode() + b"\0" + "\n".join(c for c in code if c).encode())
     return h.hexdigest()[:16]
 
 
