@@ -1,6 +1,7 @@
 // C ABI of libpsgd.so: contexts, plans (validated descriptor tables + workspace) and the three
 // step calls, each enqueuing grouped kernels on the caller's stream.
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <memory>
@@ -242,25 +243,47 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
   std::vector<int64_t> cost;   // bytes one item streams (same index as `all`)
   auto begin_kind = [&](int k) { p->off[k] = (int)all.size(); };
   // Padded lists are launched with xcd_remap: XCD x walks the x-th eighth of the list in order.
-  // For the two long-running product kernels, whose items differ in length by up to 2.7x, the
-  // items within each eighth are sorted by decreasing cost (stable, so the blocks of one
-  // matrix stay together and share its factor in that XCD's L2): the longest items start first
-  // and the short ones fill the tail (longest-processing-time-first list scheduling).
+  // For the two long-running product kernels, whose items differ in length (2.7x within the
+  // sharded resblock, 4x across the unsharded one), the list is cut into eight contiguous
+  // ranges of about equal total cost rather than equal item count (each range then padded
+  // with empty items to the longest), and each range is sorted by decreasing cost (stable, so
+  // the blocks of one matrix stay together and share its factor in that XCD's L2): every XCD
+  // gets the same work, its longest items start first and the short ones fill the tail
+  // (longest-processing-time-first list scheduling).
   auto end_kind = [&](int k, bool pad8, bool sort = false) {
-    if (pad8) while ((all.size() - p->off[k]) % psgd::kXcds) all.push_back(Work{-1, 0, 0, 0});
-    p->cnt[k] = (int)all.size() - p->off[k];
     cost.resize(all.size(), 0);
-    if (!sort) return;
-    const int per = p->cnt[k] / psgd::kXcds;
-    std::vector<int> idx(per);
-    std::vector<Work> tmp(per);
-    for (int x = 0; x < psgd::kXcds; ++x) {
-      const int b = p->off[k] + x * per;
-      for (int j = 0; j < per; ++j) idx[j] = b + j;
-      std::stable_sort(idx.begin(), idx.end(), [&](int u, int v) { return cost[u] > cost[v]; });
-      for (int j = 0; j < per; ++j) tmp[j] = all[idx[j]];
-      for (int j = 0; j < per; ++j) all[b + j] = tmp[j];
+    if (sort) {
+      const int beg = p->off[k], n = (int)all.size() - beg;
+      int64_t total = 0;
+      for (int j = 0; j < n; ++j) total += cost[beg + j];
+      int cut[psgd::kXcds + 1];
+      cut[0] = 0;
+      int64_t run = 0;
+      for (int x = 1, j = 0; x <= psgd::kXcds; ++x) {
+        const int64_t goal = x == psgd::kXcds ? INT64_MAX : (total * x + psgd::kXcds / 2) / psgd::kXcds;
+        while (j < n && run + cost[beg + j] / 2 < goal) run += cost[beg + j++];
+        cut[x] = x == psgd::kXcds ? n : j;
+      }
+      int per = 0;
+      for (int x = 0; x < psgd::kXcds; ++x) per = std::max(per, cut[x + 1] - cut[x]);
+      std::vector<Work> out;
+      std::vector<int64_t> oc;
+      for (int x = 0; x < psgd::kXcds; ++x) {
+        std::vector<int> idx;
+        for (int j = cut[x]; j < cut[x + 1]; ++j) idx.push_back(beg + j);
+        std::stable_sort(idx.begin(), idx.end(), [&](int u, int v) { return cost[u] > cost[v]; });
+        for (int u : idx) { out.push_back(all[u]); oc.push_back(cost[u]); }
+        for (int j = (int)idx.size(); j < per; ++j) { out.push_back(Work{-1, 0, 0, 0}); oc.push_back(0); }
+      }
+      all.resize(beg);
+      cost.resize(beg);
+      all.insert(all.end(), out.begin(), out.end());
+      cost.insert(cost.end(), oc.begin(), oc.end());
+    } else if (pad8) {
+      while ((all.size() - p->off[k]) % psgd::kXcds) all.push_back(Work{-1, 0, 0, 0});
+      cost.resize(all.size(), 0);
     }
+    p->cnt[k] = (int)all.size() - p->off[k];
   };
   auto push = [&](Work w, int64_t c) {
     all.push_back(w);
