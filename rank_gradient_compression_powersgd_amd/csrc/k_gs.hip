@@ -390,13 +390,15 @@ void k_gs_fdiag(const DevMat* __restrict__ mats, const Work* __restrict__ work, 
   }
 }
 
-// C (bi x bj) = / -= op(A) (bi x bk) B (bk x bj), fp64, row-major with leading dimension ld.
+// C (bi x bj) = / -= op(A) (bi x bk) B (bk x bj), row-major with leading dimension ld; C fp64,
+// A and B fp64 or fp32 (T: widened exactly on load), products and sums fp64.
 // 256 threads: waves 2 x 2, each a 64 x 64 quarter of C as 4 x 4 MFMA tiles; k slices of 16
 // staged in LDS (op(A) as [row][k], B as [k][col]), the next slice loaded while this one is
 // multiplied. Every read of A and B happens before C is written, so C may alias A or B.
 constexpr int BG_THREADS = 256;
-__device__ void bgemm_block(GLOBAL double* C, const GLOBAL double* A, bool transA,
-                            const GLOBAL double* B, bool sub, int ld, int bi, int bj, int bk)
+template <typename T>
+__device__ void bgemm_block(GLOBAL double* C, rsrc_t rA, uint32_t aoff, bool transA, rsrc_t rB,
+                            uint32_t boff, bool sub, int ld, int bi, int bj, int bk)
 {
   constexpr int KS = 16;
   constexpr int AP = KS + 1;               // op(A) slice pitch: column reads spread over banks
@@ -406,19 +408,37 @@ __device__ void bgemm_block(GLOBAL double* C, const GLOBAL double* A, bool trans
   const int wv = threadIdx.x / kWave;
   const int wm = wv & 1, wn = wv >> 1;
   const int c = lane & 15, g = lane >> 4;
-  // staging: 2048 elements of each slice, 8 per thread
+  // staging: 2048 elements of each slice, 8 per thread, loaded through buffer descriptors
+  // (element offsets relative to the block's first element; masked elements read zero). op(A)
+  // with transA reads A[k][row] along rows of A (row index fastest).
+  uint32_t oa[8], ob[8];
+  int ka[8], kbb[8];
+  bool va[8], vb[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int u = threadIdx.x + e * BG_THREADS;
+    int row, kk;
+    if (transA) { kk = u / kBlk; row = u % kBlk; } else { row = u / KS; kk = u % KS; }
+    oa[e] = aoff + (transA ? (uint32_t)kk * ld + row : (uint32_t)row * ld + kk);
+    ka[e] = kk;
+    va[e] = row < bi;
+    const int bkk = u / kBlk, col = u % kBlk;
+    ob[e] = boff + (uint32_t)bkk * ld + col;
+    kbb[e] = bkk;
+    vb[e] = col < bj;
+  }
+  constexpr uint32_t ES = sizeof(T);
+  auto ld1 = [&](rsrc_t r, uint32_t off) -> double {
+    if constexpr (ES == 8) return __builtin_bit_cast(double, bload8(r, off));
+    else return (double)__builtin_bit_cast(float, bload4(r, off));
+  };
   double ra[8], rb[8];
   auto load = [&](int k0) {
+    const uint32_t astep = transA ? (uint32_t)k0 * ld : (uint32_t)k0, bstep = (uint32_t)k0 * ld;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int u = threadIdx.x + e * BG_THREADS;
-      // op(A)[row][k]: transA reads A[k][row] along rows of A (row index fastest)
-      int row, kk;
-      if (transA) { kk = u / kBlk; row = u % kBlk; } else { row = u / KS; kk = u % KS; }
-      const int k = k0 + kk;
-      ra[e] = (row < bi && k < bk) ? (transA ? A[(int64_t)k * ld + row] : A[(int64_t)row * ld + k]) : 0.0;
-      const int bkk = u / kBlk, col = u % kBlk;
-      rb[e] = (col < bj && k0 + bkk < bk) ? B[(int64_t)(k0 + bkk) * ld + col] : 0.0;
+      ra[e] = ld1(rA, va[e] && k0 + ka[e] < bk ? (oa[e] + astep) * ES : kOOB);
+      rb[e] = ld1(rB, vb[e] && k0 + kbb[e] < bk ? (ob[e] + bstep) * ES : kOOB);
     }
   };
   auto store = [&]() {
@@ -489,17 +509,39 @@ void k_gs_bgemm(const DevMat* __restrict__ mats, const Work* __restrict__ work, 
   const int k0 = kb * kBlk, i0 = ib * kBlk, j0 = jb * kBlk;
   const int bsk = min(kBlk, rp - k0), bsi = min(kBlk, rp - i0), bsj = min(kBlk, rp - j0);
   auto blk = [&](GLOBAL double* X, int r0, int c0) { return X + (int64_t)r0 * rp + c0; };
+  auto at = [&](int r0, int c0) { return (uint32_t)(r0 * rp + c0); };   // element offset
+  const uint32_t bytes = (uint32_t)rp * (uint32_t)rp * 8u;
+  const rsrc_t rW = make_rsrc(d.wsum, bytes), rT = make_rsrc(d.tmat, bytes);
   if (phase == 0) {
     if (jb == kb)   // T_ik = U_ik L
-      bgemm_block(blk(Tg, i0, k0), blk(Tg, i0, k0), false, blk(Tg, k0, k0), false, rp, bsi, bsk, bsk);
+      bgemm_block<double>(blk(Tg, i0, k0), rT, at(i0, k0), false, rT, at(k0, k0), false, rp, bsi, bsk, bsk);
     else            // R_kj = L^T W_kj
-      bgemm_block(blk(W, k0, j0), blk(Tg, k0, k0), true, blk(W, k0, j0), false, rp, bsk, bsj, bsk);
+      bgemm_block<double>(blk(W, k0, j0), rT, at(k0, k0), true, rW, at(k0, j0), false, rp, bsk, bsj, bsk);
   } else {
     if (ib <= kb)   // U_ij -= T_ik R_kj
-      bgemm_block(blk(Tg, i0, j0), blk(Tg, i0, k0), false, blk(W, k0, j0), true, rp, bsi, bsj, bsk);
+      bgemm_block<double>(blk(Tg, i0, j0), rT, at(i0, k0), false, rW, at(k0, j0), true, rp, bsi, bsj, bsk);
     else            // W_ij -= R_ki^T R_kj
-      bgemm_block(blk(W, i0, j0), blk(W, k0, i0), true, blk(W, k0, j0), true, rp, bsi, bsj, bsk);
+      bgemm_block<double>(blk(W, i0, j0), rW, at(k0, i0), true, rW, at(k0, j0), true, rp, bsi, bsj, bsk);
   }
+}
+
+// Gram partial of large ranks through the same block product: one work item is rows
+// [a, a + gram_rows) of one matrix, partial index b, block pair c = bi | bj << 16 (bi <= bj):
+// W_part(bi, bj) = P_rows(:, bi)^T P_rows(:, bj).
+__global__ __launch_bounds__(BG_THREADS)
+void k_gs_gram_big(const DevMat* __restrict__ mats, const Work* __restrict__ work, int pass)
+{
+  const Work wi = work[xcd_remap(blockIdx.x, gridDim.x)];
+  if (wi.mat < 0) return;
+  const DevMat& d = mats[wi.mat];
+  if (pass && *d.reorth == 0) return;
+  const int rp = d.rpad;
+  const int ci0 = (wi.c & 0xffff) * kBlk, cj0 = (wi.c >> 16) * kBlk;
+  const rsrc_t rP = make_rsrc(pass ? d.p2 : d.p_raw, (uint32_t)d.m * (uint32_t)rp * 4u);
+  GLOBAL double* __restrict__ out = gbl(d.gram) + (int64_t)wi.b * rp * rp;
+  bgemm_block<float>(out + (int64_t)ci0 * rp + cj0, rP, (uint32_t)(wi.a * rp + ci0), true, rP,
+                     (uint32_t)(wi.a * rp + cj0), false, rp, min(kBlk, rp - ci0), min(kBlk, rp - cj0),
+                     min(d.gram_rows, d.m - wi.a));
 }
 
 // ------------------------------------------------------------------------------------------
@@ -721,7 +763,7 @@ hipError_t launch_gs_gram(int rt, bool big, int pass, const DevMat* mats, const 
   if (n_work <= 0) return hipSuccess;
   const dim3 grid(n_work), block(GS_THREADS);
   if (big) {
-    k_gs_gram<kMaxRankTiles, true><<<grid, block, 0, s>>>(mats, work, pass);
+    k_gs_gram_big<<<grid, dim3(BG_THREADS), 0, s>>>(mats, work, pass);
     return hipGetLastError();
   }
   switch (rt) {
