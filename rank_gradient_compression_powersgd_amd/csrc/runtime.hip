@@ -294,10 +294,13 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
   const int k2cols = psgd::mtp_cols_per_block();
   const int aprows = psgd::gs_apply_rows_per_block();
   const int tm = psgd::decomp_tile_m(), tn = psgd::decomp_tile_n();
+  // The rank chunks of one row (column) block are adjacent in the product lists: they land on
+  // one XCD at about the same time and walk the same G and E lines in step, so one chunk's
+  // reads bring the lines into that XCD's L2 for the others.
   begin_kind(W_K1);
   for (int i = 0; i < n_mats; ++i)
-    for (int ch = 0; ch < p->chunks; ++ch)
-      for (int r0 = 0; r0 < p->mats[i].m; r0 += k1rows)
+    for (int r0 = 0; r0 < p->mats[i].m; r0 += k1rows)
+      for (int ch = 0; ch < p->chunks; ++ch)
         push(Work{i, r0, ch, 0}, (int64_t)std::min(k1rows, p->mats[i].m - r0) * p->mats[i].n);
   end_kind(W_K1, true, true);
   begin_kind(W_GRAM);
@@ -346,8 +349,8 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
   end_kind(W_APPLY, true);
   begin_kind(W_K2);
   for (int i = 0; i < n_mats; ++i)
-    for (int ch = 0; ch < p->chunks; ++ch)
-      for (int c0 = 0; c0 < p->mats[i].n; c0 += k2cols)
+    for (int c0 = 0; c0 < p->mats[i].n; c0 += k2cols)
+      for (int ch = 0; ch < p->chunks; ++ch)
         push(Work{i, c0, ch, 0}, (int64_t)std::min(k2cols, p->mats[i].n - c0) * p->mats[i].m);
   end_kind(W_K2, true, true);
   begin_kind(W_SPLIT3);
