@@ -203,6 +203,18 @@ psgd_status psgd_decompress_update(psgd_ctx* ctx, psgd_plan* plan, const float* 
                                    const int32_t* skip_dev, hipStream_t stream);
 
 /*
+ * Zero the error buffer of every matrix of the plan: the restart case of the rule that the
+ * error buffer is zeroed as rarely as possible, on non-finite values from mixed-precision
+ * backprop and when training restarts from a checkpoint (Korean summary of the paper, section
+ * "Distributed Optimization"). Error buffers are not checkpointed; a caller resuming a run
+ * calls this once before the first step and restores q (the warm starts) itself.
+ * It is the skipped form of psgd_decompress_update with no skip word: E = 0 over m x n of
+ * every matrix (in-place matrices included), nothing else is written, q and out are untouched.
+ * Asynchronous on stream; PSGD_EINVAL for a plan of another context. Traced in slot 8.
+ */
+psgd_status psgd_reset_errors(psgd_ctx* ctx, psgd_plan* plan, hipStream_t stream);
+
+/*
  * Tracing hook. Install an array of n HIP events created by the caller with timing enabled.
  * While installed, the launch of each kernel in slot k is bracketed by hipEventRecord of
  * events[2k] (before) and events[2k+1] (after) on the call's stream; elapsed times between the

@@ -86,10 +86,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.psgd_compress_q.argtypes = [vp, vp, vp, vp]
     lib.psgd_refresh_q.argtypes = [vp, vp, vp]
     lib.psgd_factor_buffer.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.POINTER(i32)]
+    lib.psgd_reset_errors.argtypes = [vp, vp, vp]
     for name in ("psgd_create", "psgd_destroy", "psgd_plan_create", "psgd_plan_destroy",
                  "psgd_compress", "psgd_check_finite", "psgd_decompress_update",
                  "psgd_debug_buffer", "psgd_profile_events", "psgd_compress_p", "psgd_orthogonalize",
-                 "psgd_compress_q", "psgd_refresh_q", "psgd_factor_buffer"):
+                 "psgd_compress_q", "psgd_refresh_q", "psgd_factor_buffer", "psgd_reset_errors"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -222,6 +223,11 @@ def psgd_check_finite(ctx: int, plan: int, flags, passthrough: Iterable, scale, 
 def psgd_decompress_update(ctx: int, plan: int, scale, skip_dev, stream=None) -> None:
     _check(ctx, "psgd_decompress_update",
            load_library().psgd_decompress_update(ctx, plan, _ptr(scale), _ptr(skip_dev), _stream(stream)))
+
+
+def psgd_reset_errors(ctx: int, plan: int, stream=None) -> None:
+    """Zero every error buffer of the plan (restart from a checkpoint)."""
+    _check(ctx, "psgd_reset_errors", load_library().psgd_reset_errors(ctx, plan, _stream(stream)))
 
 
 def psgd_last_error(ctx: int) -> str:

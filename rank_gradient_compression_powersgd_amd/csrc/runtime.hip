@@ -55,6 +55,8 @@ struct psgd_plan {
   int nblk = 1;                          // 128-column blocks of rpad
   int bg_off[kMaxBlocks][2] = {{0}};     // block products of step k, phase 0/1 (within W_BGEMM)
   int bg_cnt[kMaxBlocks][2] = {{0}};
+  int32_t* d_one = nullptr;              // a device word holding 1: the decompression's skip
+                                         // word for psgd_reset_errors
 };
 
 namespace {
@@ -238,6 +240,8 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
     o.reorth = take(4);
   }
 
+  const size_t one_off = take(4);
+
   // ---- work lists -------------------------------------------------------------------------
   std::vector<Work> all;
   std::vector<int64_t> cost;   // bytes one item streams (same index as `all`)
@@ -403,6 +407,9 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
     d.reorth = reinterpret_cast<int32_t*>(base + o.reorth);
   }
   if ((e = hipMemset(p->workspace, 0, ws ? ws : 256)) != hipSuccess) { cleanup(); return hip_fail(ctx, e, "workspace clear"); }
+  p->d_one = reinterpret_cast<int32_t*>(base + one_off);
+  const int32_t one = 1;
+  if ((e = hipMemcpy(p->d_one, &one, sizeof one, hipMemcpyHostToDevice)) != hipSuccess) { cleanup(); return hip_fail(ctx, e, "constant upload"); }
   if ((e = hipMalloc(&p->d_mats, sizeof(DevMat) * n_mats)) != hipSuccess) { cleanup(); return fail(ctx, PSGD_ENOMEM, "descriptor table"); }
   if ((e = hipMemcpy(p->d_mats, p->mats.data(), sizeof(DevMat) * n_mats, hipMemcpyHostToDevice)) != hipSuccess) { cleanup(); return hip_fail(ctx, e, "descriptor upload"); }
   if ((e = hipMalloc(&p->d_work, sizeof(Work) * all.size())) != hipSuccess) { cleanup(); return fail(ctx, PSGD_ENOMEM, "work lists"); }
@@ -555,6 +562,18 @@ psgd_status psgd_decompress_update(psgd_ctx* ctx, psgd_plan* plan, const float* 
   const DevMat* dm = plan->d_mats;
   auto W = [&](int k) { return plan->d_work + plan->off[k]; };
   HIPCHK(ctx, traced(ctx, S_K3, stream, [&] { return psgd::launch_decompress(plan->gt, dm, W(W_K3), plan->cnt[W_K3], scale, skip_dev, stream); }), "decompress");
+  return PSGD_OK;
+}
+
+psgd_status psgd_reset_errors(psgd_ctx* ctx, psgd_plan* plan, hipStream_t stream) {
+  if (!ctx) return PSGD_EINVAL;
+  ctx->err.clear();
+  if (!plan || plan->ctx != ctx) return fail(ctx, PSGD_EINVAL, "plan does not belong to this context");
+  HIPCHK(ctx, hipSetDevice(ctx->device), "hipSetDevice");
+  // the decompression's skipped form zeroes every error buffer and touches nothing else (no
+  // scale is read on that path; the pointer only has to be valid)
+  const float* any_scale = reinterpret_cast<const float*>(plan->d_one);
+  HIPCHK(ctx, traced(ctx, S_K3, stream, [&] { return psgd::launch_decompress(plan->gt, plan->d_mats, plan->d_work + plan->off[W_K3], plan->cnt[W_K3], any_scale, plan->d_one, stream); }), "error buffer reset");
   return PSGD_OK;
 }
 

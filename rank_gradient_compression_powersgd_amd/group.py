@@ -63,6 +63,10 @@ class PowerSGDGroup:
     def decompress_update(self, stream=None):
         B.psgd_decompress_update(self.ctx, self.plan, self.scale, self.skip, stream)
 
+    def reset_errors(self, stream=None):
+        """E = 0 for every matrix: resuming from a checkpoint, which holds no error buffers."""
+        B.psgd_reset_errors(self.ctx, self.plan, stream)
+
     def step(self, passthrough: Sequence = (), host: bool = False, stream=None):
         self.compress(stream)
         s = self.check_finite(passthrough, host, stream)

@@ -415,6 +415,60 @@ def test_inplace_matrices_match_oracle_and_skip():
     group.close()
 
 
+def test_reset_errors_restart_from_checkpoint():
+    """psgd_reset_errors after two steps: every error buffer becomes exactly zero over m x n
+    (the padding columns of a strided buffer, q and the D buffers are untouched), and the next
+    step matches the oracle started from E = 0 with the warm starts the run had reached."""
+    import torch
+    shapes = [(640, 264), (300, 1048), (1029, 512)]
+    rank = 40
+    rng = np.random.default_rng(47)
+    scales = np.array([1.0, 0.5], np.float32)
+    blocks = [0, 1, 1]
+    q0 = [rng.standard_normal((n, rank)).astype(np.float32) for _, n in shapes]
+    from rank_gradient_compression_powersgd_amd import PowerSGDGroup
+    dev = torch.device("cuda", 0)
+    # the second error buffer is a view into a wider allocation (8 padding columns per row)
+    wide = torch.full((shapes[1][0], shapes[1][1] + 8), 7.0, dtype=torch.float32, device=dev)
+    err = [torch.zeros(shapes[0], dtype=torch.float32, device=dev), wide[:, :shapes[1][1]],
+           torch.zeros(shapes[2], dtype=torch.float32, device=dev)]
+    err[1].zero_()
+    Gs = [[wl.to_fp16(rng.standard_normal(sh)) for sh in shapes] for _ in range(3)]
+    grads = [torch.from_numpy(g).to(dev) for g in Gs[0]]
+    group = PowerSGDGroup(grads, blocks, torch.from_numpy(scales).to(dev), rank,
+                          [torch.from_numpy(q) for q in q0], err, True)
+    for t in range(2):
+        for i in range(3):
+            group.grads[i].copy_(torch.from_numpy(Gs[t][i]))
+        assert group.step([], host=True) == 0
+    torch.cuda.synchronize()
+    assert all(float(e.abs().max()) > 0 for e in group.err)
+    q_before = [q.clone() for q in group.q]
+    out_before = [o.clone() for o in group.out]
+    group.reset_errors()
+    torch.cuda.synchronize()
+    for e in group.err:
+        assert float(e.abs().max()) == 0.0
+    assert float(wide[:, shapes[1][1]:].sub(7.0).abs().max()) == 0.0
+    for a, b in zip(group.q, q_before):
+        assert torch.equal(a, b)
+    for a, b in zip(group.out, out_before):
+        assert torch.equal(a, b)
+    for i in range(3):
+        group.grads[i].copy_(torch.from_numpy(Gs[2][i]))
+    assert group.step([], host=True) == 0
+    torch.cuda.synchronize()
+    st = oracle.step_group([g.astype(np.float32) for g in Gs[2]],
+                           [np.zeros(sh, np.float32) for sh in shapes],
+                           [q.cpu().numpy() for q in q_before], blocks, scales)
+    res = dict(E=[e.cpu().numpy() for e in group.err], Q=[q.cpu().numpy() for q in group.q],
+               P=[p.cpu().numpy() for p in group.p], D=[o.cpu().numpy() for o in group.out],
+               flags=group.flags.cpu().numpy())
+    compare_step(res, st, "step after reset")
+    assert float(wide[:, shapes[1][1]:].sub(7.0).abs().max()) == 0.0
+    group.close()
+
+
 # ------------------------------------------------------------------------------------------
 # data-parallel split calls: two ranks simulated on one GPU, factors averaged between calls
 # ------------------------------------------------------------------------------------------
