@@ -54,7 +54,7 @@ def parse(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=3, choices=(2, 3, 5))
+    ap.add_argument("--workload", type=int, default=3, choices=(2, 3, 4, 5))
     ap.add_argument("--n-blocks", type=int, default=None, help="resblocks of workload 3 (default 64)")
     ap.add_argument("--no-out", action="store_true", help="do not write the decompressed gradient")
     ap.add_argument("--inplace", action="store_true",
