@@ -215,6 +215,36 @@ psgd_status psgd_decompress_update(psgd_ctx* ctx, psgd_plan* plan, const float* 
 psgd_status psgd_reset_errors(psgd_ctx* ctx, psgd_plan* plan, hipStream_t stream);
 
 /*
+ * Per-resblock gradient scaling at the boundaries of backprop, the step that produces a
+ * block's gradients and its multiplier s_b = 1 / S_b for the calls above. Every resblock has
+ * its own scale factor S_b ("Zero-Shot Text-to-Image Generation — 中文验证版", section
+ * 方法适配); the gradient is multiplied by S_b when backprop enters the block and divided by
+ * it when backprop leaves, where Inf/NaN values become 0 so that they do not reach other
+ * blocks (Korean summary, section "Mixed-Precision Training"). The gradient between blocks
+ * (the residual stream) is fp32 in true units; inside the block it is fp16 or bf16.
+ *
+ * psgd_block_grad_enter: out[i] = to16(fp32(S_b * dx[i])), round to nearest even (fp16 keeps
+ *   subnormals, overflow gives inf).
+ *     dx     n fp32 (device, read), 16-byte aligned
+ *     scale  one fp32 on the device: S_b, finite and > 0 (not checked: it stays on the device)
+ *     out    n 16-bit values of out_dtype (device, written), 16-byte aligned
+ * psgd_block_grad_exit: dx[i] += fp32(g[i] / S_b) for each finite g[i] (IEEE division and
+ *   addition, each rounded once); a g[i] that is inf or NaN adds 0. *flag is set to 1 when any
+ *   g[i] was inf or NaN and left as it is otherwise, so one flag can gather several calls (the
+ *   caller clears it). flag may be NULL.
+ *     dx     n fp32 (device, read and written), 16-byte aligned
+ *     g      n 16-bit values of g_dtype (device, read): the block's output gradient, scaled
+ * Both: n >= 0 (0 is a no-op), dtype PSGD_F16 or PSGD_BF16 (else PSGD_EDTYPE), asynchronous on
+ * stream, PSGD_EINVAL for NULL or misaligned pointers. The ctx gives the device and the
+ * error message; no plan is involved.
+ */
+psgd_status psgd_block_grad_enter(psgd_ctx* ctx, const float* dx, int64_t n, const float* scale,
+                                  void* out, psgd_dtype out_dtype, hipStream_t stream);
+psgd_status psgd_block_grad_exit(psgd_ctx* ctx, float* dx, const void* g, int64_t n,
+                                 const float* scale, psgd_dtype g_dtype, uint8_t* flag,
+                                 hipStream_t stream);
+
+/*
  * Tracing hook. Install an array of n HIP events created by the caller with timing enabled.
  * While installed, the launch of each kernel in slot k is bracketed by hipEventRecord of
  * events[2k] (before) and events[2k+1] (after) on the call's stream; elapsed times between the

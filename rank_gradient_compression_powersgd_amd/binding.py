@@ -87,10 +87,13 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.psgd_refresh_q.argtypes = [vp, vp, vp]
     lib.psgd_factor_buffer.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.POINTER(i32)]
     lib.psgd_reset_errors.argtypes = [vp, vp, vp]
+    lib.psgd_block_grad_enter.argtypes = [vp, vp, i64, vp, vp, ctypes.c_int, vp]
+    lib.psgd_block_grad_exit.argtypes = [vp, vp, vp, i64, vp, ctypes.c_int, vp, vp]
     for name in ("psgd_create", "psgd_destroy", "psgd_plan_create", "psgd_plan_destroy",
                  "psgd_compress", "psgd_check_finite", "psgd_decompress_update",
                  "psgd_debug_buffer", "psgd_profile_events", "psgd_compress_p", "psgd_orthogonalize",
-                 "psgd_compress_q", "psgd_refresh_q", "psgd_factor_buffer", "psgd_reset_errors"):
+                 "psgd_compress_q", "psgd_refresh_q", "psgd_factor_buffer", "psgd_reset_errors", "psgd_block_grad_enter",
+                 "psgd_block_grad_exit"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -228,6 +231,36 @@ def psgd_decompress_update(ctx: int, plan: int, scale, skip_dev, stream=None) ->
 def psgd_reset_errors(ctx: int, plan: int, stream=None) -> None:
     """Zero every error buffer of the plan (restart from a checkpoint)."""
     _check(ctx, "psgd_reset_errors", load_library().psgd_reset_errors(ctx, plan, _stream(stream)))
+
+
+def _block_dtype(t) -> int:
+    import torch
+    if t.dtype == torch.float16:
+        return PSGD_F16
+    if t.dtype == torch.bfloat16:
+        return PSGD_BF16
+    raise PsgdError(f"block gradients must be float16 or bfloat16, got {t.dtype}")
+
+
+def psgd_block_grad_enter(ctx: int, dx, scale, out, stream=None) -> None:
+    """out = to16(S_b * dx): a contiguous fp32 gradient entering a resblock, scaled by the
+    block's factor (scale: one-element fp32 device tensor) into the 16-bit tensor out."""
+    if dx.numel() != out.numel() or not dx.is_contiguous() or not out.is_contiguous():
+        raise PsgdError("dx and out must be contiguous with the same number of elements")
+    _check(ctx, "psgd_block_grad_enter",
+           load_library().psgd_block_grad_enter(ctx, _ptr(dx), dx.numel(), _ptr(scale), _ptr(out),
+                                                _block_dtype(out), _stream(stream)))
+
+
+def psgd_block_grad_exit(ctx: int, dx, g, scale, flag=None, stream=None) -> None:
+    """dx += g / S_b over the finite elements of the 16-bit block output g (Inf/NaN add 0);
+    flag (one-element uint8 device tensor, or None) is set to 1 if g held Inf/NaN."""
+    if dx.numel() != g.numel() or not dx.is_contiguous() or not g.is_contiguous():
+        raise PsgdError("dx and g must be contiguous with the same number of elements")
+    _check(ctx, "psgd_block_grad_exit",
+           load_library().psgd_block_grad_exit(ctx, _ptr(dx), _ptr(g), dx.numel(), _ptr(scale),
+                                               _block_dtype(g), None if flag is None else _ptr(flag),
+                                               _stream(stream)))
 
 
 def psgd_last_error(ctx: int) -> str:

@@ -265,6 +265,10 @@ hipError_t launch_mtp(int gt, int rtc, const DevMat* mats, const Work* work, int
 hipError_t launch_decompress(int gt, const DevMat* mats, const Work* work, int n_work,
                              const float* scale, const int32_t* skip, hipStream_t s);
 struct PassList;
+hipError_t launch_block_enter(int dt, const float* dx, int64_t n, const float* scale, uint16_t* out,
+                              hipStream_t s);
+hipError_t launch_block_exit(int dt, float* dx, const uint16_t* g, int64_t n, const float* scale,
+                             uint8_t* flag, hipStream_t s);
 hipError_t launch_check_finite(const uint8_t* flags, int n_flags, const float* scale, int n_scale,
                                const float* const* pass_ptr, const int64_t* pass_n, int n_pass,
                                int32_t* skip, hipStream_t s);

@@ -577,6 +577,39 @@ psgd_status psgd_reset_errors(psgd_ctx* ctx, psgd_plan* plan, hipStream_t stream
   return PSGD_OK;
 }
 
+namespace {
+psgd_status check_block_args(psgd_ctx* ctx, const void* a, const void* b, int64_t n, const float* scale,
+                             psgd_dtype dt) {
+  if (!ctx) return PSGD_EINVAL;
+  ctx->err.clear();
+  if (n < 0) return fail(ctx, PSGD_EINVAL, "negative element count");
+  if (dt != PSGD_F16 && dt != PSGD_BF16) return fail(ctx, PSGD_EDTYPE, "the block's gradient type must be fp16 or bf16");
+  if (n == 0) return PSGD_OK;
+  if (!a || !b || !scale) return fail(ctx, PSGD_EINVAL, "NULL tensor or scale pointer");
+  if ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b)) & 15)
+    return fail(ctx, PSGD_EINVAL, "tensor base addresses must be 16-byte aligned");
+  return PSGD_OK;
+}
+}  // namespace
+
+psgd_status psgd_block_grad_enter(psgd_ctx* ctx, const float* dx, int64_t n, const float* scale,
+                                  void* out, psgd_dtype out_dtype, hipStream_t stream) {
+  if (psgd_status st = check_block_args(ctx, dx, out, n, scale, out_dtype); st != PSGD_OK || n == 0) return st;
+  HIPCHK(ctx, hipSetDevice(ctx->device), "hipSetDevice");
+  HIPCHK(ctx, psgd::launch_block_enter(out_dtype == PSGD_F16 ? psgd::G_F16 : psgd::G_BF16, dx, n, scale,
+                                       static_cast<uint16_t*>(out), stream), "block entry scaling");
+  return PSGD_OK;
+}
+
+psgd_status psgd_block_grad_exit(psgd_ctx* ctx, float* dx, const void* g, int64_t n, const float* scale,
+                                 psgd_dtype g_dtype, uint8_t* flag, hipStream_t stream) {
+  if (psgd_status st = check_block_args(ctx, dx, g, n, scale, g_dtype); st != PSGD_OK || n == 0) return st;
+  HIPCHK(ctx, hipSetDevice(ctx->device), "hipSetDevice");
+  HIPCHK(ctx, psgd::launch_block_exit(g_dtype == PSGD_F16 ? psgd::G_F16 : psgd::G_BF16, dx,
+                                      static_cast<const uint16_t*>(g), n, scale, flag, stream), "block exit unscaling");
+  return PSGD_OK;
+}
+
 psgd_status psgd_profile_events(psgd_ctx* ctx, hipEvent_t* events, int n) {
   if (!ctx) return PSGD_EINVAL;
   ctx->err.clear();
