@@ -56,6 +56,7 @@ def parse(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3, choices=(2, 3, 4, 5))
     ap.add_argument("--n-blocks", type=int, default=None, help="resblocks of workload 3 (default 64)")
+    ap.add_argument("--rank", type=int, default=None, help="override the workload's rank")
     ap.add_argument("--no-out", action="store_true", help="do not write the decompressed gradient")
     ap.add_argument("--inplace", action="store_true",
                     help="in-place form: backprop has accumulated s_b G into the error buffers, so "
@@ -68,6 +69,10 @@ def parse(argv=None):
                     help="only run a plain device copy of 2 GiB (reads 2 GiB, writes 2 GiB) three "
                          "times; under rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE scale the "
                          "traffic counters of the library kernels")
+    ap.add_argument("--block-scaling", action="store_true",
+                    help="only measure the block-boundary gradient scaling calls "
+                         "(psgd_block_grad_enter / _exit) on residual-stream gradients of one and "
+                         "of 16 sequences (1280 tokens x d_model 3968 each); one JSON line")
     ap.add_argument("--pmc-summary", metavar="DIR", default=None,
                     help="only summarise rocprofv3 --pmc CSV output: DIR holds pmc_FETCH_SIZE/, "
                          "pmc_WRITE_SIZE/ (bench runs) and pmccopy_FETCH_SIZE/, pmccopy_WRITE_SIZE/ "
@@ -256,16 +261,19 @@ def workload_name(config: int, w, numel: int) -> str:
             f"rank {w.rank}")
 
 
-def build_workload(config: int, n_blocks, write_out: bool, inplace: bool = False):
+def build_workload(config: int, n_blocks, write_out: bool, inplace: bool = False, rank=None):
+    import dataclasses
     import torch
     import workloads as wl
     from rank_gradient_compression_powersgd_amd import PowerSGDGroup
     w = wl.workload(config, n_blocks) if config == 3 else wl.workload(config)
+    if rank is not None:
+        w = dataclasses.replace(w, rank=rank)
     dev = torch.device("cuda", 0)
     grads, q0 = [], []
     for s in w.matrices:
         grads.append(wl.gradient_torch(w, s, 0, dev))
-        q0.append(wl.initial_q_torch(w, s, dev))
+        q0.append(wl.initial_q_torch(w, s, dev, w.rank))
     scale = torch.tensor(wl.scales_np(w), device=dev)
     err = None
     if inplace:
@@ -311,6 +319,74 @@ def cpu_baseline(seconds: float):
                       f"{t_total:.1f} s"}
 
 
+def block_scaling_bench(a) -> int:
+    """Per-launch time of the block-boundary scaling calls, HIP events on the launch stream.
+    Algorithmic bytes per element: entry reads 4 (fp32) and writes 2 (fp16); exit reads 2 + 4
+    and writes 4. The per-backward figure is 64 resblocks x (entry + exit) at one sequence."""
+    import numpy as np
+    import torch
+    import rank_gradient_compression_powersgd_amd as psgd
+    dev = torch.device("cuda", 0)
+    ctx = psgd.psgd_create(0, 1)
+    d_model, tokens = 3968, 1280
+    scale = torch.tensor([np.float32(2.0 ** 12)], device=dev)
+    flag = torch.zeros(1, dtype=torch.uint8, device=dev)
+    res = {}
+    for seqs in (1, 16):
+        n = seqs * tokens * d_model
+        g = torch.Generator(device=dev)
+        g.manual_seed(7000 + seqs)
+        dx = torch.randn(n, generator=g, device=dev).mul_(1e-6)
+        out = torch.empty(n, dtype=torch.float16, device=dev)
+        acc = torch.zeros(n, dtype=torch.float32, device=dev)
+        for name, call, bpe in (("enter", lambda: psgd.psgd_block_grad_enter(ctx, dx, scale, out), 6),
+                                ("exit", lambda: psgd.psgd_block_grad_exit(ctx, acc, out, scale, flag), 10)):
+            for _ in range(a.warmup):
+                call()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(a.steps):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / a.steps
+            gbs = bpe * n / (us * 1e-6) / 1e9
+            res[f"{name}_{seqs}seq"] = {"elements": n, "us": round(us, 2), "GB/s": round(gbs, 1),
+                                        "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_element": bpe}
+    psgd.psgd_destroy(ctx)
+    # the oracle on one sequence (entry + exit), on this host's cores
+    import oracle
+    rng = np.random.default_rng(7001)
+    x = (rng.standard_normal(tokens * d_model) * 1e-6).astype(np.float32)
+    t0 = time.perf_counter()
+    reps = 0
+    while time.perf_counter() - t0 < 5.0:
+        h = oracle.block_grad_enter(x, 4096.0, "f16")
+        oracle.block_grad_exit(np.zeros_like(x), h, 4096.0, "f16")
+        reps += 1
+    cpu_s = (time.perf_counter() - t0) / reps
+    big = res["exit_16seq"]
+    line = {
+        "metric": "block-boundary gradient scaling GB/s (algorithmic bytes), 1 MI355X",
+        "value": big["GB/s"], "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "higher_is_better": True, "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "residual-stream gradient at resblock boundaries: 1280 tokens x "
+                               "d_model 3968 per sequence, 1 and 16 sequences, S_b = 2^12"},
+        "ops": res,
+        "backward_pass_us_1seq": round(64 * (res["enter_1seq"]["us"] + res["exit_1seq"]["us"]), 1),
+        "roofline": {"bound": "hbm", "achieved": big["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": big["frac"], "traffic": None, "kernel": "k_block_exit, 16 sequences"},
+        "cpu_baseline": {"value": round(10 * tokens * d_model / cpu_s / 1e9, 3), "unit": "GB/s",
+                         "cores": 1, "kind": "oracle",
+                         "sample": f"entry + exit of one sequence ({tokens * d_model} elements), "
+                                   f"numpy float64, {reps} repetitions in {reps * cpu_s:.1f} s; "
+                                   "GB/s of the exit's 10 bytes per element"},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     a = parse(argv)
     if a.pmc_summary:
@@ -335,9 +411,11 @@ def main(argv=None) -> int:
                                                "bytes_written": y.numel() * 4, "launches": 3}}))
         return 0
     psgd.load_library()
+    if a.block_scaling:
+        return block_scaling_bench(a)
     hip = Hip()
     log(f"building workload {a.workload} ...")
-    w, group, passthrough = build_workload(a.workload, a.n_blocks, not a.no_out, a.inplace)
+    w, group, passthrough = build_workload(a.workload, a.n_blocks, not a.no_out, a.inplace, a.rank)
     stream = int(torch.cuda.current_stream().cuda_stream)
     nslot = len(psgd.PROFILE_SLOTS)
 
@@ -388,7 +466,8 @@ def main(argv=None) -> int:
                            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                            "bytes_per_launch": nbytes, "avg_ms": round(kern[name], 4)}
     dom = max(STREAMING, key=lambda n: kern[n])
-    counted = a.workload == 3 and not a.no_out and not a.inplace and a.n_blocks in (None, 64)
+    counted = (a.workload == 3 and not a.no_out and not a.inplace and a.n_blocks in (None, 64)
+               and a.rank in (None, 112))
     mfma = {}
     if counted:
         for name in STREAMING:
@@ -410,7 +489,7 @@ def main(argv=None) -> int:
     value = w.grad_bytes * K / wall / 1e9
     flops = 6 * w.rank * numel * 3       # three bf16/fp16 products per GEMM, three GEMMs
     line = {
-        "metric": METRIC,
+        "metric": METRIC if w.rank == 112 else METRIC.replace("rank 112", f"rank {w.rank}"),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
