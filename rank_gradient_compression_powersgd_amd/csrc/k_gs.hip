@@ -508,17 +508,23 @@ void k_gs_bgemm(const DevMat* __restrict__ mats, const Work* __restrict__ work, 
   auto at = [&](int r0, int c0) { return (uint32_t)(r0 * rp + c0); };   // element offset
   const uint32_t bytes = (uint32_t)rp * (uint32_t)rp * 8u;
   const rsrc_t rW = make_rsrc(d.wsum, bytes), rT = make_rsrc(d.tmat, bytes);
-  if (phase == 0) {
-    if (jb == kb)   // T_ik = U_ik L
-      bgemm_block<double>(blk(Tg, i0, k0), rT, at(i0, k0), false, rT, at(k0, k0), false, rp, bsi, bsk, bsk);
-    else            // R_kj = L^T W_kj
-      bgemm_block<double>(blk(W, k0, j0), rT, at(k0, k0), true, rW, at(k0, j0), false, rp, bsk, bsj, bsk);
-  } else {
-    if (ib <= kb)   // U_ij -= T_ik R_kj
-      bgemm_block<double>(blk(Tg, i0, j0), rT, at(i0, k0), false, rW, at(k0, j0), true, rp, bsi, bsj, bsk);
-    else            // W_ij -= R_ki^T R_kj
-      bgemm_block<double>(blk(W, i0, j0), rW, at(k0, i0), true, rW, at(k0, j0), true, rp, bsi, bsj, bsk);
+  // The four products differ only in their operands, chosen here, so that the block product
+  // is inlined once (four inlined copies took 380 VGPRs and spilled 808 bytes per lane).
+  GLOBAL double* C;
+  rsrc_t rA = rT, rB = rW;
+  uint32_t ao, bo = at(k0, j0);
+  bool transA, sub = phase != 0;
+  int bi = bsi, bj = bsj;
+  if (phase == 0 && jb == kb) {          // T_ik = U_ik L
+    C = blk(Tg, i0, k0); ao = at(i0, k0); transA = false; rB = rT; bo = at(k0, k0); bj = bsk;
+  } else if (phase == 0) {               // R_kj = L^T W_kj
+    C = blk(W, k0, j0); ao = at(k0, k0); transA = true; bi = bsk;
+  } else if (ib <= kb) {                 // U_ij -= T_ik R_kj
+    C = blk(Tg, i0, j0); ao = at(i0, k0); transA = false;
+  } else {                               // W_ij -= R_ki^T R_kj
+    C = blk(W, i0, j0); rA = rW; ao = at(k0, i0); transA = true;
   }
+  bgemm_block<double>(C, rA, ao, transA, rB, bo, sub, rp, bi, bj, bsk);
 }
 
 // Gram partial of large ranks through the same block product: one work item is rows
