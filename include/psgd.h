@@ -55,7 +55,7 @@ typedef enum psgd_status {
   PSGD_EDTYPE = 2,        /* unknown gradient dtype */
   PSGD_ENOMEM = 3,        /* workspace allocation failed */
   PSGD_EHIP = 4,          /* a HIP runtime call or kernel launch failed */
-  PSGD_EUNSUPPORTED = 5   /* valid request this build does not implement (rank above 1024) */
+  PSGD_EUNSUPPORTED = 5   /* valid request the library does not implement (rank above 1024) */
 } psgd_status;
 
 typedef enum psgd_dtype {
