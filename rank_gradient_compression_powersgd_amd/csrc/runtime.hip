@@ -35,7 +35,7 @@ struct psgd_ctx {
 namespace {
 
 enum WorkKind { W_K1, W_GRAM, W_REDUCE, W_FACTOR, W_BGEMM, W_APPLY, W_K2, W_SPLIT3, W_SPLITQ, W_K3,
-                W_KINDS };
+                W_SPLITM, W_SPLITQT, W_G1, W_G2, W_KINDS };
 constexpr int kMaxBlocks = psgd::kMaxRank / psgd::kBlk;   // 128-column blocks of the largest rank
 
 }  // namespace
@@ -178,7 +178,7 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
   size_t praw_cursor = 0;
   size_t ws = (size_t)rup((int64_t)praw_total, 256);
   auto take = [&](size_t bytes) { size_t o = ws; ws += (size_t)rup((int64_t)bytes, 256); return o; };
-  struct Off { size_t p_raw, pth, ptl, p3e, q3e, gram, tmat, wsum, wdiag, p2, reorth; };
+  struct Off { size_t p_raw, pth, ptl, p3e, q3e, gram, tmat, wsum, wdiag, p2, reorth, mh, ml, mth, mtl, qth, qtl; };
   std::vector<Off> offs(n_mats);
   p->mats.resize(n_mats);
   for (int i = 0; i < n_mats; ++i) {
@@ -211,7 +211,8 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
     d.out = a.out; d.ld_out = a.ld_out;
     d.m = (int)a.m; d.n = (int)a.n; d.block = a.block; d.r = r;
     d.rpad = rpad; d.kpad3 = kpad3;
-    d.mpad = (int)rup(a.m, psgd::mtp_rows_per_stage());   // P^T covers whole K2 stages
+    // P^T covers whole M^T P stages and, for ranks above 128, whole split tiles (powers of two)
+    d.mpad = (int)rup(a.m, std::max(psgd::mtp_rows_per_stage(), psgd::big_split_tile()));
     d.gram_rows = big ? psgd::kGramRowsBig : psgd::kGramRows;
     d.gram_parts = (int)((a.m + d.gram_rows - 1) / d.gram_rows);
     const int gsz = gt == psgd::G_F32 ? 4 : 2;
@@ -238,6 +239,17 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
     o.wdiag = big ? take((size_t)rpad * 8) : 0;
     o.p2 = take((size_t)a.m * rpad * 4);
     o.reorth = take(4);
+    d.npad_b = (int)rup(a.n, psgd::big_split_tile());
+    d.rpad_b = (int)rup(rpad, psgd::big_gemm_tile());
+    if (big) {
+      // the split operands of the two factor GEMMs: M and M^T (2 x 4 bytes per element of the
+      // padded matrix) and q^T; each half addressed through a buffer range below 2 GiB
+      const size_t mb = (size_t)d.mpad * d.npad_b * 2, qb = (size_t)d.rpad_b * d.npad_b * 2;
+      if (mb >= (size_t(1) << 31))
+        return fail(ctx, PSGD_EINVAL, "matrix %d: %d x %d is too large for ranks above 128 (each bf16 half of M must span less than 2 GiB)", i, (int)a.m, (int)a.n);
+      o.mh = take(mb); o.ml = take(mb); o.mth = take(mb); o.mtl = take(mb);
+      o.qth = take(qb); o.qtl = take(qb);
+    }
   }
 
   const size_t one_off = take(4);
@@ -302,11 +314,39 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
   // one XCD at about the same time and walk the same G and E lines in step, so one chunk's
   // reads bring the lines into that XCD's L2 for the others.
   begin_kind(W_K1);
-  for (int i = 0; i < n_mats; ++i)
-    for (int r0 = 0; r0 < p->mats[i].m; r0 += k1rows)
-      for (int ch = 0; ch < p->chunks; ++ch)
-        push(Work{i, r0, ch, 0}, (int64_t)std::min(k1rows, p->mats[i].m - r0) * p->mats[i].n);
+  if (!big)
+    for (int i = 0; i < n_mats; ++i)
+      for (int r0 = 0; r0 < p->mats[i].m; r0 += k1rows)
+        for (int ch = 0; ch < p->chunks; ++ch)
+          push(Work{i, r0, ch, 0}, (int64_t)std::min(k1rows, p->mats[i].m - r0) * p->mats[i].n);
   end_kind(W_K1, true, true);
+  // r > 128: split tiles of M (the padded range) and of q, then the two GEMMs' C tiles (rank
+  // tiles of one row tile adjacent, so they share the A tile in their XCD's L2)
+  const int stile = psgd::big_split_tile(), gtile = psgd::big_gemm_tile();
+  begin_kind(W_SPLITM);
+  if (big)
+    for (int i = 0; i < n_mats; ++i)
+      for (int i0 = 0; i0 < p->mats[i].mpad; i0 += stile)
+        for (int j0 = 0; j0 < p->mats[i].npad_b; j0 += stile) push(Work{i, i0, j0, 0}, 1);
+  end_kind(W_SPLITM, true);
+  begin_kind(W_SPLITQT);
+  if (big)
+    for (int i = 0; i < n_mats; ++i)
+      for (int i0 = 0; i0 < p->mats[i].npad_b; i0 += stile)
+        for (int j0 = 0; j0 < p->mats[i].rpad_b; j0 += stile) push(Work{i, i0, j0, 0}, 1);
+  end_kind(W_SPLITQT, true);
+  begin_kind(W_G1);
+  if (big)
+    for (int i = 0; i < n_mats; ++i)
+      for (int i0 = 0; i0 < p->mats[i].m; i0 += gtile)
+        for (int j0 = 0; j0 < rpad; j0 += gtile) push(Work{i, i0, j0, 0}, (int64_t)p->mats[i].n);
+  end_kind(W_G1, true, true);
+  begin_kind(W_G2);
+  if (big)
+    for (int i = 0; i < n_mats; ++i)
+      for (int i0 = 0; i0 < p->mats[i].n; i0 += gtile)
+        for (int j0 = 0; j0 < rpad; j0 += gtile) push(Work{i, i0, j0, 1}, (int64_t)p->mats[i].mpad);
+  end_kind(W_G2, true, true);
   begin_kind(W_GRAM);
   const int nblk = (rpad + psgd::kBlk - 1) / psgd::kBlk;
   for (int i = 0; i < n_mats; ++i) {
@@ -352,10 +392,11 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
       for (int cb = 0; cb < (big ? nblk : 1); ++cb) push(Work{i, r0, cb, 0}, std::min(aprows, p->mats[i].m - r0));
   end_kind(W_APPLY, true);
   begin_kind(W_K2);
-  for (int i = 0; i < n_mats; ++i)
-    for (int c0 = 0; c0 < p->mats[i].n; c0 += k2cols)
-      for (int ch = 0; ch < p->chunks; ++ch)
-        push(Work{i, c0, ch, 0}, (int64_t)std::min(k2cols, p->mats[i].n - c0) * p->mats[i].m);
+  if (!big)
+    for (int i = 0; i < n_mats; ++i)
+      for (int c0 = 0; c0 < p->mats[i].n; c0 += k2cols)
+        for (int ch = 0; ch < p->chunks; ++ch)
+          push(Work{i, c0, ch, 0}, (int64_t)std::min(k2cols, p->mats[i].n - c0) * p->mats[i].m);
   end_kind(W_K2, true, true);
   begin_kind(W_SPLIT3);
   if (big)
@@ -405,6 +446,14 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
     d.wdiag = big ? reinterpret_cast<double*>(base + o.wdiag) : nullptr;
     d.p2 = reinterpret_cast<float*>(base + o.p2);
     d.reorth = reinterpret_cast<int32_t*>(base + o.reorth);
+    if (big) {
+      d.mh = reinterpret_cast<uint16_t*>(base + o.mh);
+      d.ml = reinterpret_cast<uint16_t*>(base + o.ml);
+      d.mth = reinterpret_cast<uint16_t*>(base + o.mth);
+      d.mtl = reinterpret_cast<uint16_t*>(base + o.mtl);
+      d.qth = reinterpret_cast<uint16_t*>(base + o.qth);
+      d.qtl = reinterpret_cast<uint16_t*>(base + o.qtl);
+    }
   }
   if ((e = hipMemset(p->workspace, 0, ws ? ws : 256)) != hipSuccess) { cleanup(); return hip_fail(ctx, e, "workspace clear"); }
   p->d_one = reinterpret_cast<int32_t*>(base + one_off);
@@ -447,6 +496,14 @@ psgd_status psgd_compress_p(psgd_ctx* ctx, psgd_plan* plan, const float* scale, 
   const DevMat* dm = plan->d_mats;
   auto W = [&](int k) { return plan->d_work + plan->off[k]; };
   HIPCHK(ctx, traced(ctx, S_ZERO_FLAGS, stream, [&] { return psgd::launch_zero_u8(flags, plan->n_mats, stream); }), "flag clear");
+  if (plan->big) {
+    HIPCHK(ctx, traced(ctx, S_K1, stream, [&] {
+      hipError_t e = psgd::launch_split_m(plan->gt, dm, W(W_SPLITM), plan->cnt[W_SPLITM], scale, flags, stream);
+      if (e == hipSuccess) e = psgd::launch_split_qt(dm, W(W_SPLITQT), plan->cnt[W_SPLITQT], stream);
+      if (e == hipSuccess) e = psgd::launch_gemm_nt(dm, W(W_G1), plan->cnt[W_G1], stream);
+      return e; }), "M Q");
+    return PSGD_OK;
+  }
   HIPCHK(ctx, traced(ctx, S_K1, stream, [&] { return psgd::launch_ef_mq(plan->gt, plan->rtc, dm, W(W_K1), plan->cnt[W_K1], scale, flags, stream); }), "M Q");
   return PSGD_OK;
 }
@@ -494,7 +551,10 @@ psgd_status psgd_compress_q(psgd_ctx* ctx, psgd_plan* plan, const float* scale, 
   if (!scale) return fail(ctx, PSGD_EINVAL, "scale is required");
   const DevMat* dm = plan->d_mats;
   auto W = [&](int k) { return plan->d_work + plan->off[k]; };
-  HIPCHK(ctx, traced(ctx, S_K2, stream, [&] { return psgd::launch_mtp(plan->gt, plan->rtc, dm, W(W_K2), plan->cnt[W_K2], scale, stream); }), "M^T P");
+  if (plan->big)
+    HIPCHK(ctx, traced(ctx, S_K2, stream, [&] { return psgd::launch_gemm_nt(dm, W(W_G2), plan->cnt[W_G2], stream); }), "M^T P");
+  else
+    HIPCHK(ctx, traced(ctx, S_K2, stream, [&] { return psgd::launch_mtp(plan->gt, plan->rtc, dm, W(W_K2), plan->cnt[W_K2], scale, stream); }), "M^T P");
   if (plan->big)
     HIPCHK(ctx, traced(ctx, S_SPLIT3, stream, [&] { return psgd::launch_split3(dm, W(W_SPLIT3), plan->cnt[W_SPLIT3], stream); }), "decompression row scales");
   return PSGD_OK;

@@ -376,13 +376,13 @@ def test_rank_deficient_second_pass(rank, true_rank):
 # ------------------------------------------------------------------------------------------
 # in-place matrices: backprop has accumulated s_b G into the error buffer (grad NULL)
 # ------------------------------------------------------------------------------------------
-def test_inplace_matrices_match_oracle_and_skip():
+@pytest.mark.parametrize("rank", [24, 200])
+def test_inplace_matrices_match_oracle_and_skip(rank):
     """Two of three matrices in-place (err holds M, no gradient read); the third as usual. The
     oracle sees the in-place matrices as G = 0, E = M. Then a non-finite element planted in an
     in-place error buffer flags that matrix and skips the step (every error buffer zeroed)."""
     import torch
     shapes = [(513, 264), (300, 1048), (640, 512)]
-    rank = 24
     rng = np.random.default_rng(31)
     scales = np.array([0.75], np.float32)
     q0 = [rng.standard_normal((n, rank)).astype(np.float32) for _, n in shapes]
@@ -479,7 +479,8 @@ def _dev_copy(dst: int, src: int, nbytes: int):
     assert lib.hipMemcpy(dst, src, nbytes, 3) == 0       # device to device
 
 
-def test_split_calls_two_simulated_ranks():
+@pytest.mark.parametrize("rank", [16, 160])
+def test_split_calls_two_simulated_ranks(rank):
     """psgd_compress_p -> mean of the factor buffers -> psgd_orthogonalize -> psgd_compress_q ->
     mean of q_next -> psgd_refresh_q -> check -> decompress, for two ranks holding different
     gradients of the same matrices (two plans on one GPU, torch doing the means), against the
@@ -488,7 +489,6 @@ def test_split_calls_two_simulated_ranks():
     from rank_gradient_compression_powersgd_amd import PowerSGDGroup
     from rank_gradient_compression_powersgd_amd import binding as B
     shapes = [(520, 264), (300, 512)]
-    rank = 16
     rng = np.random.default_rng(77)
     q0 = [rng.standard_normal((n, rank)).astype(np.float32) for _, n in shapes]
     scale = torch.tensor([0.5], device="cuda")
