@@ -136,9 +136,9 @@ void k_split_qt(const DevMat* __restrict__ mats, const Work* __restrict__ work)
 constexpr int GT_M = 128, GT_N = 128;          // C tile; 4 waves of 64 x 64
 constexpr int GM_THREADS = 256;
 constexpr int GK = 32;                         // K per stage: LDS row = 32 bf16 = 4 16-byte units
-// physical 16-byte unit of logical unit q in LDS row rr (16 consecutive rows of a fragment
-// read spread over the banks)
-__device__ __forceinline__ int swzg(int rr, int q) { return q ^ ((rr >> 2) & 3); }
+// physical 16-byte unit of logical unit q in LDS row rr (64-byte rows): the 8 lanes of one LDS
+// pass read 8 consecutive rows and hit the 8 distinct 16-byte groups of the 32 banks
+__device__ __forceinline__ int swzg(int rr, int q) { return q ^ ((rr >> 1) & 3); }
 
 struct GemmArgs {
   rsrc_t ah, al, bh, bl;        // operand halves: A rows x K, B rows x K, K-contiguous
@@ -244,8 +244,8 @@ void k_gemm_nt(const DevMat* __restrict__ mats, const Work* __restrict__ work)
     }
   };
 
-  // stage s lives in LDS buffer s & 1 and arrives in register set s & 1
   const int nsteps = ga.K / GK;
+  // stage s lives in LDS buffer s & 1 and arrives in register set s & 1
   load_stage(R0, 0);
   if (nsteps > 1) load_stage(R1, GK);
   store_stage(R0, 0);

@@ -43,9 +43,10 @@ constexpr int kStageQBytes = 2 * 2 * K3_TN * LDS_K * 2;
 constexpr int kStageBytes = kStageQBytes + 2 * 2 * K3_TM * LDS_K * 2;
 constexpr int kTileBytes = K3_TM * K3_DTP * 4;
 constexpr int kLdsBytes = kStageBytes > kTileBytes ? kStageBytes : kTileBytes;
-// Physical unit of logical unit q in row rr: 16 lanes reading 16 consecutive rows (one unit
-// each) or writing 4 rows (4 units each) hit 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int swz3(int rr, int q) { return q ^ ((rr >> 2) & 3); }
+// Physical unit of logical unit q in row rr (64-byte rows, 4 units): the 8 lanes an LDS pass
+// serves read 8 consecutive rows, whose units land on the 8 distinct 16-byte groups of the 32
+// banks (two rows per 128 bytes, four swizzle values per row parity).
+__device__ __forceinline__ int swz3(int rr, int q) { return q ^ ((rr >> 1) & 3); }
 
 // G, E and out are streamed with the non-temporal policy: they are touched once, and evicting
 // them first keeps the factor tiles, which neighbouring workgroups re-read, in L2.
