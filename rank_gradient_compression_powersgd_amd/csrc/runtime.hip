@@ -147,9 +147,10 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
   }
   HIPCHK(ctx, hipSetDevice(ctx->device), "hipSetDevice");
 
-  // Rank layout. The two product kernels carry at most kMaxRankTiles 16-column tiles per pass,
-  // so larger ranks are split into `chunks` equal chunks of `rtc` tiles (each chunk re-reads M);
-  // rpad = chunks * rtc * 16 >= r, the extra columns of the factors stay zero.
+  // Rank layout. The streaming product kernels carry at most kMaxRankTiles 16-column tiles, so
+  // ranks above 128 (which take the split-once GEMM path instead) are laid out as `chunks`
+  // equal chunks of `rtc` tiles; rpad = chunks * rtc * 16 >= r, the extra factor columns stay
+  // zero. The 128-column blocks of the orthonormalisation follow the same padding.
   const int r = ctx->rank;
   const int rt0 = (int)(rup(r, 16) / 16);
   const int chunks = (rt0 + psgd::kMaxRankTiles - 1) / psgd::kMaxRankTiles;
@@ -310,9 +311,7 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
   const int k2cols = psgd::mtp_cols_per_block();
   const int aprows = psgd::gs_apply_rows_per_block();
   const int tm = psgd::decomp_tile_m(), tn = psgd::decomp_tile_n();
-  // The rank chunks of one row (column) block are adjacent in the product lists: they land on
-  // one XCD at about the same time and walk the same G and E lines in step, so one chunk's
-  // reads bring the lines into that XCD's L2 for the others.
+  // streaming products (r <= 128: a single rank chunk)
   begin_kind(W_K1);
   if (!big)
     for (int i = 0; i < n_mats; ++i)
