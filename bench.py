@@ -322,7 +322,9 @@ def cpu_baseline(seconds: float):
 def block_scaling_bench(a) -> int:
     """Per-launch time of the block-boundary scaling calls, HIP events on the launch stream.
     Algorithmic bytes per element: entry reads 4 (fp32) and writes 2 (fp16); exit reads 2 + 4
-    and writes 4. The per-backward figure is 64 resblocks x (entry + exit) at one sequence."""
+    and writes 4; the fused boundary (exit of block b, entry of block b - 1) reads 4 + 2 and
+    writes 4 + 2. The per-backward figures are 64 resblocks x (entry + exit) at one sequence,
+    and the same with the 63 inner boundaries fused."""
     import numpy as np
     import torch
     import rank_gradient_compression_powersgd_amd as psgd
@@ -339,8 +341,10 @@ def block_scaling_bench(a) -> int:
         dx = torch.randn(n, generator=g, device=dev).mul_(1e-6)
         out = torch.empty(n, dtype=torch.float16, device=dev)
         acc = torch.zeros(n, dtype=torch.float32, device=dev)
+        out2 = torch.empty(n, dtype=torch.float16, device=dev)
         for name, call, bpe in (("enter", lambda: psgd.psgd_block_grad_enter(ctx, dx, scale, out), 6),
-                                ("exit", lambda: psgd.psgd_block_grad_exit(ctx, acc, out, scale, flag), 10)):
+                                ("exit", lambda: psgd.psgd_block_grad_exit(ctx, acc, out, scale, flag), 10),
+                                ("exit_enter", lambda: psgd.psgd_block_grad_exit_enter(ctx, acc, out, scale, scale, out2, flag), 12)):
             for _ in range(a.warmup):
                 call()
             torch.cuda.synchronize()
@@ -375,6 +379,8 @@ def block_scaling_bench(a) -> int:
                                "d_model 3968 per sequence, 1 and 16 sequences, S_b = 2^12"},
         "ops": res,
         "backward_pass_us_1seq": round(64 * (res["enter_1seq"]["us"] + res["exit_1seq"]["us"]), 1),
+        "backward_pass_us_1seq_fused": round(res["enter_1seq"]["us"] + 63 * res["exit_enter_1seq"]["us"]
+                                             + res["exit_1seq"]["us"], 1),
         "roofline": {"bound": "hbm", "achieved": big["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": big["frac"], "traffic": None, "kernel": "k_block_exit, 16 sequences"},
         "cpu_baseline": {"value": round(10 * tokens * d_model / cpu_s / 1e9, 3), "unit": "GB/s",

@@ -243,6 +243,16 @@ psgd_status psgd_block_grad_enter(psgd_ctx* ctx, const float* dx, int64_t n, con
 psgd_status psgd_block_grad_exit(psgd_ctx* ctx, float* dx, const void* g, int64_t n,
                                  const float* scale, psgd_dtype g_dtype, uint8_t* flag,
                                  hipStream_t stream);
+/*
+ * The boundary between block b and block b - 1 in one pass: psgd_block_grad_exit with S_b
+ * (scale_exit) on dx and g, then psgd_block_grad_enter with S_{b-1} (scale_enter) from the
+ * updated dx into out (same 16-bit dtype as g). Results equal the two calls in sequence; dx,
+ * g and out are read or written once (12 bytes per element instead of 16). dx, g and out
+ * 16-byte aligned; out must not overlap g. Errors as for the two calls.
+ */
+psgd_status psgd_block_grad_exit_enter(psgd_ctx* ctx, float* dx, const void* g, int64_t n,
+                                       const float* scale_exit, const float* scale_enter, void* out,
+                                       psgd_dtype dtype, uint8_t* flag, hipStream_t stream);
 
 /*
  * Tracing hook. Install an array of n HIP events created by the caller with timing enabled.

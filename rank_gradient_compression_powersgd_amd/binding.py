@@ -89,11 +89,12 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.psgd_reset_errors.argtypes = [vp, vp, vp]
     lib.psgd_block_grad_enter.argtypes = [vp, vp, i64, vp, vp, ctypes.c_int, vp]
     lib.psgd_block_grad_exit.argtypes = [vp, vp, vp, i64, vp, ctypes.c_int, vp, vp]
+    lib.psgd_block_grad_exit_enter.argtypes = [vp, vp, vp, i64, vp, vp, vp, ctypes.c_int, vp, vp]
     for name in ("psgd_create", "psgd_destroy", "psgd_plan_create", "psgd_plan_destroy",
                  "psgd_compress", "psgd_check_finite", "psgd_decompress_update",
                  "psgd_debug_buffer", "psgd_profile_events", "psgd_compress_p", "psgd_orthogonalize",
                  "psgd_compress_q", "psgd_refresh_q", "psgd_factor_buffer", "psgd_reset_errors", "psgd_block_grad_enter",
-                 "psgd_block_grad_exit"):
+                 "psgd_block_grad_exit", "psgd_block_grad_exit_enter"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -261,6 +262,19 @@ def psgd_block_grad_exit(ctx: int, dx, g, scale, flag=None, stream=None) -> None
            load_library().psgd_block_grad_exit(ctx, _ptr(dx), _ptr(g), dx.numel(), _ptr(scale),
                                                _block_dtype(g), None if flag is None else _ptr(flag),
                                                _stream(stream)))
+
+
+def psgd_block_grad_exit_enter(ctx: int, dx, g, scale_exit, scale_enter, out, flag=None, stream=None) -> None:
+    """Leave block b (dx += g / S_b over finite g) and enter block b - 1 (out = to16(S_{b-1} dx))
+    in one pass; g and out are 16-bit tensors of the same dtype."""
+    if not (dx.numel() == g.numel() == out.numel()) or not (dx.is_contiguous() and g.is_contiguous() and out.is_contiguous()):
+        raise PsgdError("dx, g and out must be contiguous with the same number of elements")
+    if g.dtype != out.dtype:
+        raise PsgdError("g and out must have the same 16-bit dtype")
+    _check(ctx, "psgd_block_grad_exit_enter",
+           load_library().psgd_block_grad_exit_enter(ctx, _ptr(dx), _ptr(g), dx.numel(), _ptr(scale_exit),
+                                                     _ptr(scale_enter), _ptr(out), _block_dtype(g),
+                                                     _ptr(flag), _stream(stream)))
 
 
 def psgd_last_error(ctx: int) -> str:

@@ -129,6 +129,53 @@ void k_block_exit(float* __restrict__ dx_, const uint16_t* __restrict__ g_, int6
   if (flag && __builtin_amdgcn_ballot_w64(bad) != 0 && (threadIdx.x & (kWave - 1)) == 0) gbl(flag)[0] = 1;
 }
 
+// Leaving block b and entering block b - 1 at the same boundary: dx = dx + g / S_b (as
+// k_block_exit), then out = to16(S_{b-1} * dx) (as k_block_enter) from the new dx while it is
+// in registers: 12 bytes per element instead of 10 + 6, one launch instead of two.
+template <int DT>
+__global__ __launch_bounds__(BS_THREADS)
+void k_block_exit_enter(float* __restrict__ dx_, const uint16_t* __restrict__ g_, int64_t n,
+                        const float* __restrict__ scale_exit, const float* __restrict__ scale_enter,
+                        uint16_t* __restrict__ out_, uint8_t* __restrict__ flag)
+{
+  GLOBAL float* dx = gbl(dx_);
+  const GLOBAL uint16_t* g = gbl(g_);
+  GLOBAL uint16_t* out = gbl(out_);
+  const float s = *gbl(scale_exit), s2 = *gbl(scale_enter);
+  const int64_t n8 = n >> 3;
+  const int64_t stride = (int64_t)gridDim.x * BS_THREADS;
+  bool bad = false;
+  for (int64_t i = (int64_t)blockIdx.x * BS_THREADS + threadIdx.x; i < n8; i += stride) {
+    const u32x4 w = ld<BS_EXIT_POL>(gcast<u32x4>(g + 8 * i));
+    f32x4 a = ld<BS_EXIT_POL>(gcast<f32x4>(dx + 8 * i));
+    f32x4 b = ld<BS_EXIT_POL>(gcast<f32x4>(dx + 8 * i + 4));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bool nf0, nf1;
+      const float v0 = from16<DT>(w, e, nf0), v1 = from16<DT>(w, e + 4, nf1);
+      a[e] = a[e] + (nf0 ? 0.0f : v0 / s);
+      b[e] = b[e] + (nf1 ? 0.0f : v1 / s);
+      bad |= nf0 | nf1;
+    }
+    st<BS_EXIT_POL>(a, gcast<f32x4>(dx + 8 * i));
+    st<BS_EXIT_POL>(b, gcast<f32x4>(dx + 8 * i + 4));
+    st<BS_EXIT_POL>(to16x8<DT>(s2 * a, s2 * b), gcast<u32x4>(out + 8 * i));
+  }
+  if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
+    const int64_t j = 8 * n8 + threadIdx.x;
+    const u32x4 w = {(uint32_t)g[j], 0u, 0u, 0u};
+    bool nf;
+    const float v = from16<DT>(w, 0, nf);
+    const float x = dx[j] + (nf ? 0.0f : v / s);
+    dx[j] = x;
+    const float p = s2 * x;
+    if constexpr (DT == G_F16) out[j] = __builtin_bit_cast(uint16_t, (_Float16)p);
+    else out[j] = __builtin_bit_cast(uint16_t, (__bf16)p);
+    bad |= nf;
+  }
+  if (flag && __builtin_amdgcn_ballot_w64(bad) != 0 && (threadIdx.x & (kWave - 1)) == 0) gbl(flag)[0] = 1;
+}
+
 int grid_for(int64_t n) {
   const int64_t groups = (n >> 3) > 0 ? (n >> 3) : 1;
   const int64_t blocks = (groups + BS_THREADS - 1) / BS_THREADS;
@@ -153,6 +200,16 @@ hipError_t launch_block_exit(int dt, float* dx, const uint16_t* g, int64_t n, co
   const dim3 grid(grid_for(n)), block(BS_THREADS);
   if (dt == G_F16) k_block_exit<G_F16><<<grid, block, 0, s>>>(dx, g, n, scale, flag);
   else if (dt == G_BF16) k_block_exit<G_BF16><<<grid, block, 0, s>>>(dx, g, n, scale, flag);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_block_exit_enter(int dt, float* dx, const uint16_t* g, int64_t n, const float* scale_exit,
+                                   const float* scale_enter, uint16_t* out, uint8_t* flag, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const dim3 grid(grid_for(n)), block(BS_THREADS);
+  if (dt == G_F16) k_block_exit_enter<G_F16><<<grid, block, 0, s>>>(dx, g, n, scale_exit, scale_enter, out, flag);
+  else if (dt == G_BF16) k_block_exit_enter<G_BF16><<<grid, block, 0, s>>>(dx, g, n, scale_exit, scale_enter, out, flag);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

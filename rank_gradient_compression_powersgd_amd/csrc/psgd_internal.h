@@ -281,6 +281,8 @@ hipError_t launch_block_enter(int dt, const float* dx, int64_t n, const float* s
                               hipStream_t s);
 hipError_t launch_block_exit(int dt, float* dx, const uint16_t* g, int64_t n, const float* scale,
                              uint8_t* flag, hipStream_t s);
+hipError_t launch_block_exit_enter(int dt, float* dx, const uint16_t* g, int64_t n, const float* scale_exit,
+                                   const float* scale_enter, uint16_t* out, uint8_t* flag, hipStream_t s);
 hipError_t launch_check_finite(const uint8_t* flags, int n_flags, const float* scale, int n_scale,
                                const float* const* pass_ptr, const int64_t* pass_n, int n_pass,
                                int32_t* skip, hipStream_t s);

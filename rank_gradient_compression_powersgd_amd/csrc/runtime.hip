@@ -669,6 +669,19 @@ psgd_status psgd_block_grad_exit(psgd_ctx* ctx, float* dx, const void* g, int64_
   return PSGD_OK;
 }
 
+psgd_status psgd_block_grad_exit_enter(psgd_ctx* ctx, float* dx, const void* g, int64_t n,
+                                       const float* scale_exit, const float* scale_enter, void* out,
+                                       psgd_dtype dtype, uint8_t* flag, hipStream_t stream) {
+  if (psgd_status st = check_block_args(ctx, dx, g, n, scale_exit, dtype); st != PSGD_OK || n == 0) return st;
+  if (!scale_enter || !out) return fail(ctx, PSGD_EINVAL, "NULL tensor or scale pointer");
+  if (reinterpret_cast<uintptr_t>(out) & 15) return fail(ctx, PSGD_EINVAL, "tensor base addresses must be 16-byte aligned");
+  HIPCHK(ctx, hipSetDevice(ctx->device), "hipSetDevice");
+  HIPCHK(ctx, psgd::launch_block_exit_enter(dtype == PSGD_F16 ? psgd::G_F16 : psgd::G_BF16, dx,
+                                            static_cast<const uint16_t*>(g), n, scale_exit, scale_enter,
+                                            static_cast<uint16_t*>(out), flag, stream), "block boundary rescaling");
+  return PSGD_OK;
+}
+
 psgd_status psgd_profile_events(psgd_ctx* ctx, hipEvent_t* events, int n) {
   if (!ctx) return PSGD_EINVAL;
   ctx->err.clear();

@@ -23,7 +23,8 @@ def test_header_declares_the_step_calls():
     for n in ("psgd_compress", "psgd_check_finite", "psgd_decompress_update", "psgd_create",
               "psgd_destroy", "psgd_plan_create", "psgd_plan_destroy", "psgd_last_error",
               "psgd_compress_p", "psgd_orthogonalize", "psgd_compress_q", "psgd_refresh_q",
-              "psgd_factor_buffer", "psgd_reset_errors", "psgd_block_grad_enter", "psgd_block_grad_exit"):
+              "psgd_factor_buffer", "psgd_reset_errors", "psgd_block_grad_enter", "psgd_block_grad_exit",
+              "psgd_block_grad_exit_enter"):
         assert n in names
 
 

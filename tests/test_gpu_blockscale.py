@@ -167,3 +167,48 @@ def test_block_arguments_rejected():
     assert lib.psgd_block_grad_exit(ctx, None, None, 0, None, psgd.PSGD_BF16, None, vp(s)) == 0
     torch.cuda.synchronize()
     psgd.psgd_destroy(ctx)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("n", [1, 7, 1000003, TOKENS_X_DMODEL])
+def test_exit_enter_fused(dt, n):
+    """The boundary between block b and block b - 1 in one pass equals leaving block b and
+    entering block b - 1 as two calls: against the oracle (bit for bit, NaN positions as NaN)
+    and against the two library calls."""
+    import torch
+    psgd, ctx = _ctx()
+    dev = torch.device("cuda", 0)
+    tdt = torch.float16 if dt == "f16" else torch.bfloat16
+    seed = 900 + n % 1000
+    log(f"block boundary fused {dt} n={n} seed={seed}")
+    rng = np.random.default_rng(seed)
+    s_exit, s_enter = np.float32(4096.0), np.float32(2896.309)
+    dx0 = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    g_src = _inputs(n, seed + 1) * np.float32(1e4)
+    g_codes = oracle.block_grad_enter(g_src, 1.0, dt)      # the block's 16-bit output (Inf/NaN kept)
+    g_t = torch.from_numpy(g_codes.view(np.int16) if dt == "f16" else g_codes.view(np.int16)).to(dev).view(tdt)
+    se, sn = torch.tensor([s_exit], device=dev), torch.tensor([s_enter], device=dev)
+    dx = torch.from_numpy(dx0).to(dev)
+    out = torch.empty(n, dtype=tdt, device=dev)
+    flag = torch.zeros(1, dtype=torch.uint8, device=dev)
+    psgd.psgd_block_grad_exit_enter(ctx, dx, g_t, se, sn, out, flag)
+    # the same through the two calls
+    dx2 = torch.from_numpy(dx0).to(dev)
+    out2 = torch.empty(n, dtype=tdt, device=dev)
+    flag2 = torch.zeros(1, dtype=torch.uint8, device=dev)
+    psgd.psgd_block_grad_exit(ctx, dx2, g_t, se, flag2)
+    psgd.psgd_block_grad_enter(ctx, dx2, sn, out2)
+    torch.cuda.synchronize()
+    want_dx, want_flag = oracle.block_grad_exit(dx0, g_codes, float(s_exit), dt)
+    want_out = _oracle_codes(oracle.block_grad_enter(want_dx, float(s_enter), dt), dt)
+    got_dx, got_out = dx.cpu().numpy(), _codes16(out)
+    _same_bits_or_nan(got_dx.view(np.uint32), want_dx.view(np.uint32), np.isnan(got_dx), np.isnan(want_dx), "dx")
+    if dt == "f16":
+        nan_g, nan_w = np.isnan(got_out.view(np.float16)), np.isnan(want_out.view(np.float16))
+    else:
+        nan_g, nan_w = np.isnan(oracle.bf16_bits_to_f64(got_out)), np.isnan(oracle.bf16_bits_to_f64(want_out))
+    _same_bits_or_nan(got_out, want_out, nan_g, nan_w, "out")
+    assert bool(flag.item()) == want_flag == bool(flag2.item())
+    assert np.array_equal(got_dx.view(np.uint32), dx2.cpu().numpy().view(np.uint32))
+    assert np.array_equal(got_out, _codes16(out2))
+    psgd.psgd_destroy(ctx)
