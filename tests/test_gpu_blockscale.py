@@ -163,8 +163,16 @@ def test_block_arguments_rejected():
                                     psgd.PSGD_F16, None, vp(s)) == 1
     assert lib.psgd_block_grad_exit(ctx, vp(dx.data_ptr()), vp(out.data_ptr()), -1, vp(scale.data_ptr()),
                                     psgd.PSGD_F16, None, vp(s)) == 1
+    # the fused boundary: misaligned out, missing second scale, fp32
+    assert lib.psgd_block_grad_exit_enter(ctx, vp(dx.data_ptr()), vp(out.data_ptr()), 8, vp(scale.data_ptr()),
+                                          vp(scale.data_ptr()), vp(out.data_ptr() + 2), psgd.PSGD_F16, None, vp(s)) == 1
+    assert lib.psgd_block_grad_exit_enter(ctx, vp(dx.data_ptr()), vp(out.data_ptr()), 8, vp(scale.data_ptr()),
+                                          None, vp(out.data_ptr()), psgd.PSGD_F16, None, vp(s)) == 1
+    assert lib.psgd_block_grad_exit_enter(ctx, vp(dx.data_ptr()), vp(out.data_ptr()), 8, vp(scale.data_ptr()),
+                                          vp(scale.data_ptr()), vp(out.data_ptr()), psgd.PSGD_F32, None, vp(s)) == 2
     # n = 0 is a no-op even with NULL pointers
     assert lib.psgd_block_grad_exit(ctx, None, None, 0, None, psgd.PSGD_BF16, None, vp(s)) == 0
+    assert lib.psgd_block_grad_exit_enter(ctx, None, None, 0, None, None, None, psgd.PSGD_F16, None, vp(s)) == 0
     torch.cuda.synchronize()
     psgd.psgd_destroy(ctx)
 
