@@ -111,8 +111,9 @@ typedef struct psgd_plan psgd_plan;
 int psgd_version(void);
 
 /* Create a context on HIP device `device` for compression rank `rank` (1..1024). Ranks above
- * 128 are processed in rank chunks of at most 128 columns by the two products (each chunk
- * re-reads the gradient and error buffer) and orthonormalised blockwise.
+ * 128 form M once per step as bf16 halves in the plan workspace (8 bytes per element of each
+ * matrix, row-major and transposed) for the two factor products, which then run as GEMMs,
+ * and are orthonormalised by 128-column blocks.
  * Writes *ctx; on failure *ctx is NULL (rank above 1024: PSGD_EUNSUPPORTED). */
 psgd_status psgd_create(psgd_ctx** ctx, int device, int rank);
 
@@ -122,8 +123,9 @@ psgd_status psgd_destroy(psgd_ctx* ctx);
 /*
  * Describe a group of gradient matrices that are compressed together in grouped launches
  * (the grouped all-reduce of "Zero-Shot Text-to-Image Generation — 中文验证版", section 证据).
- * Validates every matrix, allocates and zeroes the plan workspace, and uploads the descriptor
- * tables once (synchronously, on the null stream). The pointers in `mats` are captured: the
+ * Validates every matrix, allocates and zeroes the plan workspace (about 8 bytes per factor
+ * element, plus 8 bytes per gradient element when the rank is above 128), and uploads the
+ * descriptor tables once (synchronously, on the null stream). The pointers in `mats` are captured: the
  * same buffers are used by every later call on the plan. n_blocks is the length of the scale
  * array later calls pass.
  */
