@@ -123,8 +123,8 @@ psgd_status psgd_destroy(psgd_ctx* ctx);
 /*
  * Describe a group of gradient matrices that are compressed together in grouped launches
  * (the grouped all-reduce of "Zero-Shot Text-to-Image Generation — 中文验证版", section 证据).
- * Validates every matrix, allocates and zeroes the plan workspace (about 8 bytes per factor
- * element, plus 8 bytes per gradient element when the rank is above 128), and uploads the
+ * Validates every matrix, allocates and zeroes the plan workspace (about 16 bytes per element
+ * of the m x r factors, plus 8 per gradient element when the rank is above 128), uploads the
  * descriptor tables once (synchronously, on the null stream). The pointers in `mats` are captured: the
  * same buffers are used by every later call on the plan. n_blocks is the length of the scale
  * array later calls pass.
