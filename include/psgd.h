@@ -124,10 +124,10 @@ psgd_status psgd_destroy(psgd_ctx* ctx);
  * Describe a group of gradient matrices that are compressed together in grouped launches
  * (the grouped all-reduce of "Zero-Shot Text-to-Image Generation — 中文验证版", section 证据).
  * Validates every matrix, allocates and zeroes the plan workspace (about 16 bytes per element
- * of the m x r factors, plus 8 per gradient element when the rank is above 128), uploads the
- * descriptor tables once (synchronously, on the null stream). The pointers in `mats` are captured: the
- * same buffers are used by every later call on the plan. n_blocks is the length of the scale
- * array later calls pass.
+ * of the m x r factors, plus 8 per gradient element when the rank is above 128), and uploads
+ * the descriptor tables once (synchronously, on the null stream). The pointers in `mats` are
+ * captured: the same buffers are used by every later call on the plan. n_blocks is the length
+ * of the scale array later calls pass.
  */
 psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
                              psgd_dtype grad_dtype, int n_blocks, psgd_plan** plan);
