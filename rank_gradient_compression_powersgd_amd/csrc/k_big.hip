@@ -133,7 +133,12 @@ void k_split_qt(const DevMat* __restrict__ mats, const Work* __restrict__ work)
 }
 
 // ---- C = A B^T on split bf16 operands -----------------------------------------------------
-constexpr int GT_M = 128, GT_N = 128;          // C tile; 4 waves of 64 x 64
+#ifndef GEMM_WRT
+#define GEMM_WRT 4
+#endif
+constexpr int WRT = GEMM_WRT;                  // 16-row A tiles per wave
+constexpr int GT_M = 2 * WRT * 16, GT_N = 128; // C tile; 2 x 2 waves of (16 WRT) x 64
+constexpr int UA = GT_M / 64, UB = GT_N / 64;  // 16-byte staging units per thread and operand half
 constexpr int GM_THREADS = 256;
 constexpr int GK = 32;                         // K per stage: LDS row = 32 bf16 = 4 16-byte units
 // physical 16-byte unit of logical unit q in LDS row rr (64-byte rows): the 8 lanes of one LDS
@@ -165,7 +170,7 @@ __device__ __forceinline__ GemmArgs gemm_args(const DevMat& d, int which) {
 }
 
 // One work item: matrix `mat`, C tile rows a.., columns b.., product c (0: M q, 1: M^T P).
-__global__ __launch_bounds__(GM_THREADS, 2)
+__global__ __launch_bounds__(GM_THREADS, WRT == 4 ? 2 : 1)
 void k_gemm_nt(const DevMat* __restrict__ mats, const Work* __restrict__ work)
 {
   const Work wi = work[xcd_remap(blockIdx.x, gridDim.x)];
@@ -177,49 +182,59 @@ void k_gemm_nt(const DevMat* __restrict__ mats, const Work* __restrict__ work)
   const int wm = wv & 1, wn = wv >> 1;
   const int c = lane & 15, g = lane >> 4;
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][2][GT_M][GK];   // [buf][A/B][hi/lo][row][k]
-  static_assert(GT_M == GT_N, "square tile");
+  __shared__ __attribute__((aligned(16))) uint16_t ldsA[2][2][GT_M][GK];   // [buf][hi/lo][row][k]
+  __shared__ __attribute__((aligned(16))) uint16_t ldsB[2][2][GT_N][GK];
 
-  // staging: a 16-byte unit is 8 consecutive k of one row; 4 units per row, 512 units per
-  // operand half, 2 per thread. Rows past the operand's padded extent read zeros. Two register
+  // staging: a 16-byte unit is 8 consecutive k of one row; 4 units per row, UA (UB) per
+  // thread and operand half. Rows past the operand's padded extent read zeros. Two register
   // sets hold the next two stages, so a stage's loads have two stages of products to arrive.
-  struct Regs { u32x4 a[2][2], b[2][2]; };     // [unit][hi/lo]
+  struct Regs { u32x4 a[UA][2], b[UB][2]; };     // [unit][hi/lo]
   Regs R0, R1;
-  uint32_t aoff[2], boff[2];
-  int srow[2], sq[2];
+  uint32_t aoff[UA], boff[UB];
+  int arow[UA], aq[UA], brow[UB], bq[UB];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < UA; ++j) {
     const int u = threadIdx.x + GM_THREADS * j;
-    srow[j] = u >> 2;
-    sq[j] = u & 3;
-    aoff[j] = ((uint32_t)(i0 + srow[j]) * (uint32_t)ga.lda + 8u * sq[j]) * 2u;
-    boff[j] = ((uint32_t)(j0 + srow[j]) * (uint32_t)ga.ldb + 8u * sq[j]) * 2u;
+    arow[j] = u >> 2;
+    aq[j] = u & 3;
+    aoff[j] = ((uint32_t)(i0 + arow[j]) * (uint32_t)ga.lda + 8u * aq[j]) * 2u;
+  }
+#pragma unroll
+  for (int j = 0; j < UB; ++j) {
+    const int u = threadIdx.x + GM_THREADS * j;
+    brow[j] = u >> 2;
+    bq[j] = u & 3;
+    boff[j] = ((uint32_t)(j0 + brow[j]) * (uint32_t)ga.ldb + 8u * bq[j]) * 2u;
   }
   auto load_stage = [&](Regs& R, int k0) {
     const uint32_t kb = (uint32_t)k0 * 2u;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < UA; ++j) {
       R.a[j][0] = bload16(ga.ah, aoff[j] + kb);
       R.a[j][1] = bload16(ga.al, aoff[j] + kb);
+    }
+#pragma unroll
+    for (int j = 0; j < UB; ++j) {
       R.b[j][0] = bload16(ga.bh, boff[j] + kb);
       R.b[j][1] = bload16(ga.bl, boff[j] + kb);
     }
   };
   auto store_stage = [&](const Regs& R, int buf) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int off = 8 * swzg(srow[j], sq[j]);
+    for (int j = 0; j < UA; ++j)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        *reinterpret_cast<u32x4*>(&lds[buf][0][h][srow[j]][off]) = R.a[j][h];
-        *reinterpret_cast<u32x4*>(&lds[buf][1][h][srow[j]][off]) = R.b[j][h];
-      }
-    }
+      for (int h = 0; h < 2; ++h)
+        *reinterpret_cast<u32x4*>(&ldsA[buf][h][arow[j]][8 * swzg(arow[j], aq[j])]) = R.a[j][h];
+#pragma unroll
+    for (int j = 0; j < UB; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        *reinterpret_cast<u32x4*>(&ldsB[buf][h][brow[j]][8 * swzg(brow[j], bq[j])]) = R.b[j][h];
   };
 
-  f32x4 acc[4][4];   // [A tile][B tile]
+  f32x4 acc[WRT][4];   // [A tile][B tile]
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < WRT; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0, 0, 0, 0};
   auto compute = [&](int buf) {
@@ -227,14 +242,14 @@ void k_gemm_nt(const DevMat* __restrict__ mats, const Work* __restrict__ work)
 #pragma unroll
     for (int jn = 0; jn < 4; ++jn) {
       const int rb = wn * 64 + jn * 16 + c;
-      bh[jn] = *reinterpret_cast<const bf16x8*>(&lds[buf][1][0][rb][8 * swzg(rb, g)]);
-      bl[jn] = *reinterpret_cast<const bf16x8*>(&lds[buf][1][1][rb][8 * swzg(rb, g)]);
+      bh[jn] = *reinterpret_cast<const bf16x8*>(&ldsB[buf][0][rb][8 * swzg(rb, g)]);
+      bl[jn] = *reinterpret_cast<const bf16x8*>(&ldsB[buf][1][rb][8 * swzg(rb, g)]);
     }
 #pragma unroll
-    for (int im = 0; im < 4; ++im) {
-      const int ra = wm * 64 + im * 16 + c;
-      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&lds[buf][0][0][ra][8 * swzg(ra, g)]);
-      const bf16x8 al = *reinterpret_cast<const bf16x8*>(&lds[buf][0][1][ra][8 * swzg(ra, g)]);
+    for (int im = 0; im < WRT; ++im) {
+      const int ra = wm * (WRT * 16) + im * 16 + c;
+      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&ldsA[buf][0][ra][8 * swzg(ra, g)]);
+      const bf16x8 al = *reinterpret_cast<const bf16x8*>(&ldsA[buf][1][ra][8 * swzg(ra, g)]);
 #pragma unroll
       for (int jn = 0; jn < 4; ++jn) {
         acc[im][jn] = mfma_bf16(ah, bh[jn], acc[im][jn]);
@@ -265,13 +280,13 @@ void k_gemm_nt(const DevMat* __restrict__ mats, const Work* __restrict__ work)
 
   // C layout of v_mfma_f32_16x16x32_bf16: lane holds rows 4g..4g+3 (of A), column c (of B).
 #pragma unroll
-  for (int im = 0; im < 4; ++im)
+  for (int im = 0; im < WRT; ++im)
 #pragma unroll
     for (int jn = 0; jn < 4; ++jn) {
       const int col = j0 + wn * 64 + jn * 16 + c;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = i0 + wm * 64 + im * 16 + 4 * g + i;
+        const int row = i0 + wm * (WRT * 16) + im * 16 + 4 * g + i;
         if (row < ga.crows && col < ga.ccols) ga.c[(int64_t)row * ga.ldc + col] = acc[im][jn][i];
       }
     }
@@ -280,7 +295,8 @@ void k_gemm_nt(const DevMat* __restrict__ mats, const Work* __restrict__ work)
 }  // namespace
 
 int big_split_tile() { return ST; }
-int big_gemm_tile() { return GT_M; }
+int big_gemm_tile_m() { return GT_M; }
+int big_gemm_tile_n() { return GT_N; }
 
 hipError_t launch_split_m(int gt, const DevMat* mats, const Work* work, int n_work, const float* scale,
                           uint8_t* flags, hipStream_t s) {

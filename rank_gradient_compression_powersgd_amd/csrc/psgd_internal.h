@@ -272,7 +272,8 @@ hipError_t launch_decompress(int gt, const DevMat* mats, const Work* work, int n
                              const float* scale, const int32_t* skip, hipStream_t s);
 struct PassList;
 int big_split_tile();
-int big_gemm_tile();
+int big_gemm_tile_m();
+int big_gemm_tile_n();
 hipError_t launch_split_m(int gt, const DevMat* mats, const Work* work, int n_work, const float* scale,
                           uint8_t* flags, hipStream_t s);
 hipError_t launch_split_qt(const DevMat* mats, const Work* work, int n_work, hipStream_t s);

@@ -241,7 +241,7 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
     o.p2 = take((size_t)a.m * rpad * 4);
     o.reorth = take(4);
     d.npad_b = (int)rup(a.n, psgd::big_split_tile());
-    d.rpad_b = (int)rup(rpad, psgd::big_gemm_tile());
+    d.rpad_b = (int)rup(rpad, psgd::big_gemm_tile_n());
     if (big) {
       // the split operands of the two factor GEMMs: M and M^T (2 x 4 bytes per element of the
       // padded matrix) and q^T; each half addressed through a buffer range below 2 GiB
@@ -321,7 +321,7 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
   end_kind(W_K1, true, true);
   // r > 128: split tiles of M (the padded range) and of q, then the two GEMMs' C tiles (rank
   // tiles of one row tile adjacent, so they share the A tile in their XCD's L2)
-  const int stile = psgd::big_split_tile(), gtile = psgd::big_gemm_tile();
+  const int stile = psgd::big_split_tile(), gtm = psgd::big_gemm_tile_m(), gtn = psgd::big_gemm_tile_n();
   begin_kind(W_SPLITM);
   if (big)
     for (int i = 0; i < n_mats; ++i)
@@ -337,14 +337,14 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
   begin_kind(W_G1);
   if (big)
     for (int i = 0; i < n_mats; ++i)
-      for (int i0 = 0; i0 < p->mats[i].m; i0 += gtile)
-        for (int j0 = 0; j0 < rpad; j0 += gtile) push(Work{i, i0, j0, 0}, (int64_t)p->mats[i].n);
+      for (int i0 = 0; i0 < p->mats[i].m; i0 += gtm)
+        for (int j0 = 0; j0 < rpad; j0 += gtn) push(Work{i, i0, j0, 0}, (int64_t)p->mats[i].n);
   end_kind(W_G1, true, true);
   begin_kind(W_G2);
   if (big)
     for (int i = 0; i < n_mats; ++i)
-      for (int i0 = 0; i0 < p->mats[i].n; i0 += gtile)
-        for (int j0 = 0; j0 < rpad; j0 += gtile) push(Work{i, i0, j0, 1}, (int64_t)p->mats[i].mpad);
+      for (int i0 = 0; i0 < p->mats[i].n; i0 += gtm)
+        for (int j0 = 0; j0 < rpad; j0 += gtn) push(Work{i, i0, j0, 1}, (int64_t)p->mats[i].mpad);
   end_kind(W_G2, true, true);
   begin_kind(W_GRAM);
   const int nblk = (rpad + psgd::kBlk - 1) / psgd::kBlk;
