@@ -392,33 +392,37 @@ void k_gs_fdiag(const DevMat* __restrict__ mats, const Work* __restrict__ work, 
 // staged in LDS (op(A) as [row][k], B as [k][col]), the next slice loaded while this one is
 // multiplied. Every read of A and B happens before C is written, so C may alias A or B.
 constexpr int BG_THREADS = 256;
-template <typename T>
+// C (bi x bj, at most TM x TM) = op(A) B (or C -= op(A) B when sub), all row-major with leading
+// dimension ld: op(A) is bi x bk (A itself, or A^T read from a bk x bi block when transA), B is
+// bk x bj. Four waves, each a (TM/2) x (TM/2) quarter of C on v_mfma_f64_16x16x4f64; 16-deep
+// k slices staged in LDS through buffer loads (element offsets relative to the block's first
+// element; masked elements read zero). T is the element type of A and B (fp32 is widened).
+template <typename T, int TM>
 __device__ void bgemm_block(GLOBAL double* C, rsrc_t rA, uint32_t aoff, bool transA, rsrc_t rB,
                             uint32_t boff, bool sub, int ld, int bi, int bj, int bk)
 {
   constexpr int KS = 16;
   constexpr int AP = KS + 1;               // op(A) slice pitch: column reads spread over banks
-  __shared__ double As[kBlk * AP];
-  __shared__ double Bs[KS * kBlk];
+  constexpr int NT = TM / 32;              // 16 x 16 tiles per wave along each side
+  constexpr int EPT = TM * KS / BG_THREADS;   // slice elements per thread and operand
+  __shared__ double As[TM * AP];
+  __shared__ double Bs[KS * TM];
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
   const int wm = wv & 1, wn = wv >> 1;
   const int c = lane & 15, g = lane >> 4;
-  // staging: 2048 elements of each slice, 8 per thread, loaded through buffer descriptors
-  // (element offsets relative to the block's first element; masked elements read zero). op(A)
-  // with transA reads A[k][row] along rows of A (row index fastest).
-  uint32_t oa[8], ob[8];
-  int ka[8], kbb[8];
-  bool va[8], vb[8];
+  uint32_t oa[EPT], ob[EPT];
+  int ka[EPT], kbb[EPT];
+  bool va[EPT], vb[EPT];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
+  for (int e = 0; e < EPT; ++e) {
     const int u = threadIdx.x + e * BG_THREADS;
     int row, kk;
-    if (transA) { kk = u / kBlk; row = u % kBlk; } else { row = u / KS; kk = u % KS; }
+    if (transA) { kk = u / TM; row = u % TM; } else { row = u / KS; kk = u % KS; }
     oa[e] = aoff + (transA ? (uint32_t)kk * ld + row : (uint32_t)row * ld + kk);
     ka[e] = kk;
     va[e] = row < bi;
-    const int bkk = u / kBlk, col = u % kBlk;
+    const int bkk = u / TM, col = u % TM;
     ob[e] = boff + (uint32_t)bkk * ld + col;
     kbb[e] = bkk;
     vb[e] = col < bj;
@@ -428,30 +432,30 @@ __device__ void bgemm_block(GLOBAL double* C, rsrc_t rA, uint32_t aoff, bool tra
     if constexpr (ES == 8) return __builtin_bit_cast(double, bload8(r, off));
     else return (double)__builtin_bit_cast(float, bload4(r, off));
   };
-  double ra[8], rb[8];
+  double ra[EPT], rb[EPT];
   auto load = [&](int k0) {
     const uint32_t astep = transA ? (uint32_t)k0 * ld : (uint32_t)k0, bstep = (uint32_t)k0 * ld;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < EPT; ++e) {
       ra[e] = ld1(rA, va[e] && k0 + ka[e] < bk ? (oa[e] + astep) * ES : kOOB);
       rb[e] = ld1(rB, vb[e] && k0 + kbb[e] < bk ? (ob[e] + bstep) * ES : kOOB);
     }
   };
   auto store = [&]() {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < EPT; ++e) {
       const int u = threadIdx.x + e * BG_THREADS;
       int row, kk;
-      if (transA) { kk = u / kBlk; row = u % kBlk; } else { row = u / KS; kk = u % KS; }
+      if (transA) { kk = u / TM; row = u % TM; } else { row = u / KS; kk = u % KS; }
       As[row * AP + kk] = ra[e];
       Bs[u] = rb[e];                       // [k][col]
     }
   };
-  f64x4 acc[4][4];
+  f64x4 acc[NT][NT];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < NT; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f64x4{0, 0, 0, 0};
+    for (int b = 0; b < NT; ++b) acc[a][b] = f64x4{0, 0, 0, 0};
   load(0);
   for (int k0 = 0; k0 < bk; k0 += KS) {
     __syncthreads();
@@ -461,26 +465,26 @@ __device__ void bgemm_block(GLOBAL double* C, rsrc_t rA, uint32_t aoff, bool tra
 #pragma unroll
     for (int st = 0; st < KS / 4; ++st) {
       const int k = 4 * st + g;
-      double av[4], bv[4];
+      double av[NT], bv[NT];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        av[t] = As[(wm * 64 + t * 16 + c) * AP + k];
-        bv[t] = Bs[k * kBlk + wn * 64 + t * 16 + c];
+      for (int t = 0; t < NT; ++t) {
+        av[t] = As[(wm * (TM / 2) + t * 16 + c) * AP + k];
+        bv[t] = Bs[k * TM + wn * (TM / 2) + t * 16 + c];
       }
 #pragma unroll
-      for (int tm = 0; tm < 4; ++tm)
+      for (int tm = 0; tm < NT; ++tm)
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = mfma_f64(av[tm], bv[tn], acc[tm][tn]);
+        for (int tn = 0; tn < NT; ++tn) acc[tm][tn] = mfma_f64(av[tm], bv[tn], acc[tm][tn]);
     }
   }
   // C layout of v_mfma_f64_16x16x4f64: lane 16g + c, register i holds C[g + 4i][c].
 #pragma unroll
-  for (int tm = 0; tm < 4; ++tm)
+  for (int tm = 0; tm < NT; ++tm)
 #pragma unroll
-    for (int tn = 0; tn < 4; ++tn)
+    for (int tn = 0; tn < NT; ++tn)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = wm * 64 + tm * 16 + g + 4 * i, col = wn * 64 + tn * 16 + c;
+        const int row = wm * (TM / 2) + tm * 16 + g + 4 * i, col = wn * (TM / 2) + tn * 16 + c;
         if (row < bi && col < bj) {
           GLOBAL double* cp = C + (int64_t)row * ld + col;
           *cp = sub ? *cp - acc[tm][tn][i] : acc[tm][tn][i];
@@ -490,10 +494,15 @@ __device__ void bgemm_block(GLOBAL double* C, rsrc_t rA, uint32_t aoff, bool tra
 
 // One work item: matrix `mat`, blocks (i = a, j = b); phase 0 items with j == kb form
 // T_ik = U_ik L, the others R_kj = L^T W_kj; phase 1 items with i <= kb update U, the others W.
+// Phase 0 products overwrite one of their own operands, so one workgroup forms the whole
+// 128 x 128 block (it reads all of its operands before it writes). Phase 1 products write a
+// block that neither operand touches, so four workgroups share each, one 64 x 64 quadrant
+// (c = qi | qj << 1) apiece: four times the workgroups for the few blocks of a step.
+template <int PHASE>
 __global__ __launch_bounds__(BG_THREADS)
-void k_gs_bgemm(const DevMat* __restrict__ mats, const Work* __restrict__ work, int pass, int kb,
-                int phase)
+void k_gs_bgemm(const DevMat* __restrict__ mats, const Work* __restrict__ work, int pass, int kb)
 {
+  constexpr int phase = PHASE;
   const Work wi = work[blockIdx.x];
   if (wi.mat < 0) return;
   const DevMat& d = mats[wi.mat];
@@ -524,7 +533,17 @@ void k_gs_bgemm(const DevMat* __restrict__ mats, const Work* __restrict__ work, 
   } else {                               // W_ij -= R_ki^T R_kj
     C = blk(W, i0, j0); rA = rW; ao = at(k0, i0); transA = true;
   }
-  bgemm_block<double>(C, rA, ao, transA, rB, bo, sub, rp, bi, bj, bsk);
+  if constexpr (PHASE == 0) {
+    bgemm_block<double, kBlk>(C, rA, ao, transA, rB, bo, sub, rp, bi, bj, bsk);
+  } else {
+    const int qi = wi.c & 1, qj = wi.c >> 1;
+    constexpr int H = kBlk / 2;
+    if (qi * H >= bi || qj * H >= bj) return;
+    C += (int64_t)(qi * H) * rp + qj * H;
+    ao += transA ? (uint32_t)(qi * H) : (uint32_t)(qi * H) * (uint32_t)rp;
+    bo += (uint32_t)(qj * H);
+    bgemm_block<double, H>(C, rA, ao, transA, rB, bo, sub, rp, min(H, bi - qi * H), min(H, bj - qj * H), bsk);
+  }
 }
 
 // Gram partial of large ranks through the same block product: one work item is rows
@@ -541,7 +560,7 @@ void k_gs_gram_big(const DevMat* __restrict__ mats, const Work* __restrict__ wor
   const int ci0 = (wi.c & 0xffff) * kBlk, cj0 = (wi.c >> 16) * kBlk;
   const rsrc_t rP = make_rsrc(pass ? d.p2 : d.p_raw, (uint32_t)d.m * (uint32_t)rp * 4u);
   GLOBAL double* __restrict__ out = gbl(d.gram) + (int64_t)wi.b * rp * rp;
-  bgemm_block<float>(out + (int64_t)ci0 * rp + cj0, rP, (uint32_t)(wi.a * rp + ci0), true, rP,
+  bgemm_block<float, kBlk>(out + (int64_t)ci0 * rp + cj0, rP, (uint32_t)(wi.a * rp + ci0), true, rP,
                      (uint32_t)(wi.a * rp + cj0), false, rp, min(kBlk, rp - ci0), min(kBlk, rp - cj0),
                      min(d.gram_rows, d.m - wi.a));
 }
@@ -798,7 +817,8 @@ hipError_t launch_gs_fdiag(int pass, int kb, const DevMat* mats, const Work* wor
 hipError_t launch_gs_bgemm(int pass, int kb, int phase, const DevMat* mats, const Work* work, int n_work,
                            hipStream_t s) {
   if (n_work <= 0) return hipSuccess;
-  k_gs_bgemm<<<dim3(n_work), dim3(BG_THREADS), 0, s>>>(mats, work, pass, kb, phase);
+  if (phase == 0) k_gs_bgemm<0><<<dim3(n_work), dim3(BG_THREADS), 0, s>>>(mats, work, pass, kb);
+  else k_gs_bgemm<1><<<dim3(n_work), dim3(BG_THREADS), 0, s>>>(mats, work, pass, kb);
   return hipGetLastError();
 }
 

@@ -375,11 +375,13 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
           if (ph == 0) {
             for (int ib = 0; ib < kb; ++ib) all.push_back(Work{i, ib, kb, 0});        // T_ik
             for (int jb = kb + 1; jb < nblk; ++jb) all.push_back(Work{i, kb, jb, 0}); // R_kj
-          } else {
+          } else {   // four quadrant items per block (c = qi | qj << 1)
             for (int ib = 0; ib <= kb; ++ib)
-              for (int jb = kb + 1; jb < nblk; ++jb) all.push_back(Work{i, ib, jb, 0});  // U_ij
+              for (int jb = kb + 1; jb < nblk; ++jb)
+                for (int q = 0; q < 4; ++q) all.push_back(Work{i, ib, jb, q});   // U_ij
             for (int ib = kb + 1; ib < nblk; ++ib)
-              for (int jb = ib; jb < nblk; ++jb) all.push_back(Work{i, ib, jb, 0});      // W_ij
+              for (int jb = ib; jb < nblk; ++jb)
+                for (int q = 0; q < 4; ++q) all.push_back(Work{i, ib, jb, q});   // W_ij
           }
         }
         p->bg_cnt[kb][ph] = (int)all.size() - p->off[W_BGEMM] - p->bg_off[kb][ph];
