@@ -73,6 +73,9 @@ def parse(argv=None):
                     help="only measure the block-boundary gradient scaling calls "
                          "(psgd_block_grad_enter / _exit) on residual-stream gradients of one and "
                          "of 16 sequences (1280 tokens x d_model 3968 each); one JSON line")
+    ap.add_argument("--graph", action="store_true",
+                    help="only time the step captured once as a HIP graph and replayed (compress, "
+                         "device-side finite check, decompress/update); one JSON line")
     ap.add_argument("--pmc-summary", metavar="DIR", default=None,
                     help="only summarise rocprofv3 --pmc CSV output: DIR holds pmc_FETCH_SIZE/, "
                          "pmc_WRITE_SIZE/ (bench runs) and pmccopy_FETCH_SIZE/, pmccopy_WRITE_SIZE/ "
@@ -319,6 +322,41 @@ def cpu_baseline(seconds: float):
                       f"{t_total:.1f} s"}
 
 
+def graph_bench(a) -> int:
+    """The step captured once in a HIP graph (no host synchronisation inside) and replayed: the
+    same kernels as the eager step without the per-launch host overhead between them."""
+    import torch
+    w, group, passthrough = build_workload(a.workload, a.n_blocks, not a.no_out, a.inplace, a.rank)
+    for _ in range(a.warmup):
+        group.step(passthrough)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        group.compress()
+        group.check_finite(passthrough)
+        group.decompress_update()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(a.steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    assert int(group.skip.item()) == 0, "a replayed step was skipped"
+    ms = e0.elapsed_time(e1) / a.steps
+    numel = sum(sp.m * sp.n for sp in w.matrices)
+    print(json.dumps({"metric": "gradient GB/s, step replayed from a HIP graph, 1 MI355X",
+                      "value": round(w.grad_bytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+                      "ms_per_step": round(ms, 4), "steps": a.steps, "warmup": a.warmup,
+                      "config": {"workload": workload_name(a.workload, w, numel)}}), flush=True)
+    group.close()
+    return 0
+
+
 def block_scaling_bench(a) -> int:
     """Per-launch time of the block-boundary scaling calls, HIP events on the launch stream.
     Algorithmic bytes per element: entry reads 4 (fp32) and writes 2 (fp16); exit reads 2 + 4
@@ -419,6 +457,8 @@ def main(argv=None) -> int:
     psgd.load_library()
     if a.block_scaling:
         return block_scaling_bench(a)
+    if a.graph:
+        return graph_bench(a)
     hip = Hip()
     log(f"building workload {a.workload} ...")
     w, group, passthrough = build_workload(a.workload, a.n_blocks, not a.no_out, a.inplace, a.rank)
