@@ -320,6 +320,18 @@ def test_invalid_arguments_rejected():
             B.psgd_plan_create(ctx, [B.make_matrix(g, e, q, q.clone(), p, 3)], B.PSGD_F16, 2)
         with pytest.raises(B.PsgdError):   # unknown dtype
             B.psgd_plan_create(ctx, [B.make_matrix(g, e, q, q.clone(), p, 0)], 9, 1)
+        with pytest.raises(B.PsgdError) as ei:   # empty group
+            B.psgd_plan_create(ctx, [], B.PSGD_F16, 1)
+        assert ei.value.status == B.PSGD_EINVAL
+        small = torch.zeros((6, 64), dtype=torch.float16, device="cuda")   # rank 8 > m = 6
+        with pytest.raises(B.PsgdError) as ei:
+            B.psgd_plan_create(ctx, [B.make_matrix(small, torch.zeros((6, 64), device="cuda"), q, q.clone(),
+                                                   torch.zeros((6, 8), device="cuda"), 0)], B.PSGD_F16, 1)
+        assert "exceeds" in str(ei.value)
+        wide = torch.zeros((64, 72), dtype=torch.float32, device="cuda")  # E view with ld 72, offset 2 floats
+        with pytest.raises(B.PsgdError) as ei:
+            B.psgd_plan_create(ctx, [B.make_matrix(g, wide[:, 2:66], q, q.clone(), p, 0)], B.PSGD_F16, 1)
+        assert "aligned" in str(ei.value)
     finally:
         B.psgd_destroy(ctx)
     with pytest.raises(B.PsgdError):
@@ -329,7 +341,7 @@ def test_invalid_arguments_rejected():
 
 
 # ------------------------------------------------------------------------------------------
-# ranks above 128: rank chunks in the two products, blocked orthonormalisation
+# ranks above 128: M split once, the two products as GEMMs, blocked orthonormalisation
 # ------------------------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype,rank", [("f16", 200), ("bf16", 260)])
 def test_large_rank_ragged(dtype, rank):
