@@ -755,7 +755,9 @@ void k_gs_apply(const DevMat* __restrict__ mats, const Work* __restrict__ work, 
 // Row exponents of the decompression operands (ranks above one chunk, or q_next after the
 // caller changed it): for each row of P_hat (which = 0, from p) or of Q' (which = 1, from
 // q_next), the power of two that brings its largest entry into [2^13, 2^14). One work item:
-// 64 rows [a, a + 64) of matrix `mat`, which = b; one wave per row at a time.
+// 64 rows [a, a + 64) of matrix `mat`, which = b; one wave per row at a time, each lane loading
+// up to two 8-rank units of the row at once.
+constexpr int S3_UNITS = kMaxRank / 8 / kWave;   // 8-rank units per lane
 __global__ __launch_bounds__(256)
 void k_split3(const DevMat* __restrict__ mats, const Work* __restrict__ work)
 {
@@ -769,9 +771,23 @@ void k_split3(const DevMat* __restrict__ mats, const Work* __restrict__ work)
   GLOBAL int32_t* __restrict__ ex = gbl(isq ? d.q3_exp : d.p3_exp);
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
+  const bool rvec = (r & 3) == 0;               // rows start 16-byte aligned
   for (int row = wi.a + wv; row < wi.a + 64 && row < rows; row += 4) {
+    const GLOBAL float* __restrict__ x = src + (int64_t)row * r;
     float amax = 0.0f;
-    for (int col = lane; col < r; col += kWave) amax = fmaxf(amax, fabsf(src[(int64_t)row * r + col]));
+#pragma unroll
+    for (int u = 0; u < S3_UNITS; ++u) {
+      const int k = 8 * (lane + kWave * u);
+      if (rvec && k + 8 <= r) {
+        const f32x4 a = *gcast<f32x4>(x + k), b = *gcast<f32x4>(x + k + 4);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) amax = fmaxf(amax, fmaxf(fabsf(a[t]), fabsf(b[t])));
+      } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          if (k + t < r) amax = fmaxf(amax, fabsf(x[k + t]));
+      }
+    }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
     if (lane == 0) ex[row] = fp16_row_exponent(amax);
