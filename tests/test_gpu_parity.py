@@ -343,11 +343,13 @@ def test_invalid_arguments_rejected():
 # ------------------------------------------------------------------------------------------
 # ranks above 128: M split once, the two products as GEMMs, blocked orthonormalisation
 # ------------------------------------------------------------------------------------------
-@pytest.mark.parametrize("dtype,rank", [("f16", 200), ("bf16", 260)])
+@pytest.mark.parametrize("dtype,rank", [("f16", 200), ("bf16", 260), ("f32", 136), ("f16", 1024)])
 def test_large_rank_ragged(dtype, rank):
-    shapes = [(1000, 1536), (700, 520), (300, 264)]
+    """Ranks above 128 with ragged shapes, every gradient dtype; rank 1024 is the largest the
+    library takes (eight 128-column blocks)."""
+    shapes = [(1000, 1536), (700, 520), (300, 264)] if rank <= 300 else [(1100, 1032), (1030, 1088)]
     rng = np.random.default_rng(8000 + rank)
-    blocks = [0, 1, 0]
+    blocks = [0, 1, 0][:len(shapes)]
     scales = np.array([1.0, 0.75], np.float32)
     q0 = [rng.standard_normal((n, rank)).astype(np.float32) for _, n in shapes]
     err0 = [(rng.standard_normal((m, n)) * 0.05).astype(np.float32) for m, n in shapes]
@@ -357,7 +359,8 @@ def test_large_rank_ragged(dtype, rank):
         gs = []
         for m, n in shapes:
             x = rng.standard_normal((m, n)) * np.exp(rng.uniform(-3, 0, size=(m, 1)))
-            gs.append(wl.to_bf16_bits(x) if dtype == "bf16" else wl.to_fp16(x))
+            gs.append(wl.to_bf16_bits(x) if dtype == "bf16" else
+                      x.astype(np.float32) if dtype == "f32" else wl.to_fp16(x))
         case.set_grads(gs)
         assert case.gpu_step() == 0
         compare_step(case.fetch(), case.oracle_step(), f"large rank step {t}")
