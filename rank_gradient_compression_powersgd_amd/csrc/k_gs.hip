@@ -568,23 +568,32 @@ void k_gs_gram_big(const DevMat* __restrict__ mats, const Work* __restrict__ wor
 // ------------------------------------------------------------------------------------------
 // P_hat = P T and the operand layouts of the two products that follow
 // ------------------------------------------------------------------------------------------
-constexpr int GSA_RA = 2;                          // 16-row tiles per wave
-constexpr int GSA_ROWS = GSA_RA * 16 * (GS_THREADS / kWave);   // 128 rows per workgroup
+// 64-row work items, four workgroups per CU (r <= 128): one workgroup's load of P and writes of
+// p and P_hat^T then overlap the fp64 products of the others. With 128-row items and two
+// workgroups per CU the two phases ran about back to back (0.34 ms at r = 112, 0.27 with 64).
+#ifndef GSA_RA_DEF
+#define GSA_RA_DEF 1
+#endif
+#ifndef GSA_OCC
+#define GSA_OCC 4
+#endif
+constexpr int GSA_RA = GSA_RA_DEF;                 // 16-row tiles per wave
+constexpr int GSA_ROWS = GSA_RA * 16 * (GS_THREADS / kWave);   // rows per workgroup (64)
 
-// One work item: rows [a, a + 128) of P_hat and, for large ranks (BIG: RT = 8, rpad > 128),
+// One work item: rows [a, a + GSA_ROWS) of P_hat and, for large ranks (BIG: RT = 8, rpad > 128),
 // its 128-column block b; small ranks (rpad <= 128) take all RT column tiles at once. P is read
 // into LDS by column blocks of RT tiles (one block for small ranks; blocks 0..b for large ones),
 // each with all its 16-byte loads in flight at once. Each wave owns output column tiles
 // {t, RT - 1 - t}: within the diagonal block of T (upper triangular) tile t costs t + 1 k tiles,
 // so every pair costs RT + 1; off-diagonal blocks are dense. A wave computes its pair for all
-// 8 row tiles (or a share of them when there are fewer pairs than waves), so each fragment of
+// the item's row tiles (or a share of them when there are fewer pairs than waves), so each fragment of
 // T, read from L2 one k tile ahead, feeds every row tile of the wave. The k index of an MFMA
 // step is permuted within a 16-k tile (k = 16 kt + 4 g + ks), so that a lane takes its 4 A
 // values of a k tile from one 16-byte LDS read. Products and sums are fp64; P_hat is rounded
 // to fp32 once. Large ranks leave the row exponents of the decompression to split3 (they need
 // every column block).
 template <int RT, bool BIG>
-__global__ __launch_bounds__(GS_THREADS, BIG ? 1 : 2)
+__global__ __launch_bounds__(GS_THREADS, BIG ? 1 : GSA_OCC)
 void k_gs_apply(const DevMat* __restrict__ mats, const Work* __restrict__ work, int pass)
 {
   const Work wi = work[xcd_remap(blockIdx.x, gridDim.x)];
@@ -603,7 +612,7 @@ void k_gs_apply(const DevMat* __restrict__ mats, const Work* __restrict__ work, 
   constexpr int RC = RT * 16;
   constexpr int LD = RC + 4;               // LDS row pitch (floats): rows stay 16-byte aligned
   constexpr int NW = GS_THREADS / kWave;
-  constexpr int NRT = GSA_ROWS / 16;       // row tiles (8)
+  constexpr int NRT = GSA_ROWS / 16;       // row tiles
   const int cb = BIG ? wi.b : 0;           // output column block
   const int c0 = cb * RC;
   const int ncols = BIG ? min(RC, rpad - c0) : RC;   // output columns present (whole tiles)
