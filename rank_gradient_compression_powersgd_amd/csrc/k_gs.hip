@@ -547,8 +547,13 @@ void k_gs_bgemm(const DevMat* __restrict__ mats, const Work* __restrict__ work, 
 }
 
 // Gram partial of large ranks through the same block product: one work item is rows
-// [a, a + gram_rows) of one matrix, partial index b, block pair c = bi | bj << 16 (bi <= bj):
-// W_part(bi, bj) = P_rows(:, bi)^T P_rows(:, bj).
+// [a, a + gram_rows) of one matrix, partial index b, and one 64 x 64 quadrant (qi, qj) of the
+// block pair (bi, bj), bi <= bj, with c = bi | bj << 8 | qi << 16 | qj << 17:
+// W_part(bi, bj)[qi, qj] = P_rows(:, bi half qi)^T P_rows(:, bj half qj). Quadrants instead of
+// whole 128 x 128 blocks give four times the workgroups (784 block items at r = 896 filled the
+// 512 workgroup slots about 1.5 times). The quadrant of a diagonal block below its diagonal is
+// skipped: the factorisation reads only the upper 16 x 16 block triangle of W, the reduction
+// sums it as zeros (the partials are zeroed when the plan is made and never written there).
 __global__ __launch_bounds__(BG_THREADS)
 void k_gs_gram_big(const DevMat* __restrict__ mats, const Work* __restrict__ work, int pass)
 {
@@ -557,12 +562,16 @@ void k_gs_gram_big(const DevMat* __restrict__ mats, const Work* __restrict__ wor
   const DevMat& d = mats[wi.mat];
   if (pass && *d.reorth == 0) return;
   const int rp = d.rpad;
-  const int ci0 = (wi.c & 0xffff) * kBlk, cj0 = (wi.c >> 16) * kBlk;
+  constexpr int H = kBlk / 2;
+  const int bi = wi.c & 0xff, bj = (wi.c >> 8) & 0xff, qi = (wi.c >> 16) & 1, qj = (wi.c >> 17) & 1;
+  if (bi == bj && qi > qj) return;
+  const int ci0 = bi * kBlk + qi * H, cj0 = bj * kBlk + qj * H;
+  if (ci0 >= rp || cj0 >= rp) return;
   const rsrc_t rP = make_rsrc(pass ? d.p2 : d.p_raw, (uint32_t)d.m * (uint32_t)rp * 4u);
   GLOBAL double* __restrict__ out = gbl(d.gram) + (int64_t)wi.b * rp * rp;
-  bgemm_block<float, kBlk>(out + (int64_t)ci0 * rp + cj0, rP, (uint32_t)(wi.a * rp + ci0), true, rP,
-                     (uint32_t)(wi.a * rp + cj0), false, rp, min(kBlk, rp - ci0), min(kBlk, rp - cj0),
-                     min(d.gram_rows, d.m - wi.a));
+  bgemm_block<float, H>(out + (int64_t)ci0 * rp + cj0, rP, (uint32_t)(wi.a * rp + ci0), true, rP,
+                        (uint32_t)(wi.a * rp + cj0), false, rp, min(H, rp - ci0), min(H, rp - cj0),
+                        min(d.gram_rows, d.m - wi.a));
 }
 
 // ------------------------------------------------------------------------------------------

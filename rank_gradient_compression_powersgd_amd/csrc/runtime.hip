@@ -353,7 +353,8 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
     for (int pt = 0; pt < p->mats[i].gram_parts; ++pt)
       for (int bi = 0; bi < (big ? nblk : 1); ++bi)
         for (int bj = bi; bj < (big ? nblk : 1); ++bj)
-          push(Work{i, pt * gr, pt, bi | (bj << 16)}, std::min(gr, p->mats[i].m - pt * gr));
+          for (int q = 0; q < (big ? 4 : 1); ++q)     // 64 x 64 quadrants (qi = q & 1, qj = q >> 1)
+            push(Work{i, pt * gr, pt, bi | (bj << 8) | (q << 16)}, std::min(gr, p->mats[i].m - pt * gr));
   }
   end_kind(W_GRAM, true);
   begin_kind(W_REDUCE);
