@@ -391,8 +391,9 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
   begin_kind(W_APPLY);
   for (int i = 0; i < n_mats; ++i)
     for (int r0 = 0; r0 < p->mats[i].m; r0 += aprows)
-      for (int cb = 0; cb < (big ? nblk : 1); ++cb) push(Work{i, r0, cb, 0}, std::min(aprows, p->mats[i].m - r0));
-  end_kind(W_APPLY, true);
+      for (int cb = 0; cb < (big ? nblk : 1); ++cb)   // output block cb streams cb + 1 blocks of P
+        push(Work{i, r0, cb, 0}, (int64_t)std::min(aprows, p->mats[i].m - r0) * (cb + 1));
+  end_kind(W_APPLY, true, big);
   begin_kind(W_K2);
   if (!big)
     for (int i = 0; i < n_mats; ++i)
