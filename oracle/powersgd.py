@@ -51,7 +51,7 @@ import numpy as np
 
 __all__ = [
     "as_f64", "gram_schmidt", "modified_gram_schmidt", "nonfinite", "MatrixStep",
-    "step_matrix", "GroupStep", "step_group", "subspace_iteration", "truncation_error",
+    "thin_qr_factor", "step_matrix", "GroupStep", "step_group", "subspace_iteration",
     "DataParallelStep", "step_data_parallel",
 ]
 
@@ -98,6 +98,20 @@ def modified_gram_schmidt(P) -> np.ndarray:
     return out
 
 
+def thin_qr_factor(P) -> np.ndarray:
+    """The thin-QR factor of P with a positive R diagonal, from LAPACK's Householder QR with
+    the column signs fixed. For P of full column rank this is the same matrix gram_schmidt
+    defines (that factor is unique); it is the route for panels too long for the column loop
+    to finish in seconds (thousands of rows at ranks in the hundreds). It has no rule for
+    dependent columns, so a rank-deficient P is rejected."""
+    P = as_f64(P)
+    Qf, R = np.linalg.qr(P)
+    d = np.diag(R)
+    if not np.all(np.isfinite(d)) or np.any(np.abs(d) <= 1e-13 * max(1.0, np.abs(d).max())):
+        raise ValueError("thin_qr_factor needs a panel of full column rank; use gram_schmidt")
+    return Qf * np.sign(d)[None, :]
+
+
 def nonfinite(x) -> bool:
     """True when any element of x is +-inf or NaN."""
     return not bool(np.isfinite(as_f64(x)).all())
@@ -113,12 +127,13 @@ class MatrixStep:
     E_next: np.ndarray   # M - D
 
 
-def step_matrix(G, s: float, E, Q) -> MatrixStep:
-    """One PowerSGD step on one gradient matrix (all arithmetic in float64)."""
+def step_matrix(G, s: float, E, Q, orthonormalise=None) -> MatrixStep:
+    """One PowerSGD step on one gradient matrix (all arithmetic in float64).
+    orthonormalise: gram_schmidt (the default) or thin_qr_factor (full-rank panels only)."""
     G, E, Q = as_f64(G), as_f64(E), as_f64(Q)
     M = float(s) * G + E
     P_raw = M @ Q
-    P = gram_schmidt(P_raw)
+    P = (orthonormalise or gram_schmidt)(P_raw)
     Q_next = M.T @ P
     D = P @ Q_next.T
     return MatrixStep(M, P_raw, P, Q_next, D, M - D)
@@ -200,7 +215,3 @@ def subspace_iteration(M, Q0, iters: int):
         Q = M.T @ P
     return P, Q, P @ Q.T
 
-
-def truncation_error(M, D) -> float:
-    """||M - D||_F."""
-    return float(np.linalg.norm(as_f64(M) - as_f64(D)))

@@ -234,33 +234,35 @@ def psgd_reset_errors(ctx: int, plan: int, stream=None) -> None:
     _check(ctx, "psgd_reset_errors", load_library().psgd_reset_errors(ctx, plan, _stream(stream)))
 
 
-def _block_dtype(t) -> int:
+def _block_dtype(t, call: str) -> int:
     import torch
     if t.dtype == torch.float16:
         return PSGD_F16
     if t.dtype == torch.bfloat16:
         return PSGD_BF16
-    raise PsgdError(f"block gradients must be float16 or bfloat16, got {t.dtype}")
+    raise PsgdError(call, PSGD_EDTYPE, f"block gradients must be float16 or bfloat16, got {t.dtype}")
 
 
 def psgd_block_grad_enter(ctx: int, dx, scale, out, stream=None) -> None:
     """out = to16(S_b * dx): a contiguous fp32 gradient entering a resblock, scaled by the
     block's factor (scale: one-element fp32 device tensor) into the 16-bit tensor out."""
     if dx.numel() != out.numel() or not dx.is_contiguous() or not out.is_contiguous():
-        raise PsgdError("dx and out must be contiguous with the same number of elements")
+        raise PsgdError("psgd_block_grad_enter", PSGD_EINVAL,
+                        "dx and out must be contiguous with the same number of elements")
     _check(ctx, "psgd_block_grad_enter",
            load_library().psgd_block_grad_enter(ctx, _ptr(dx), dx.numel(), _ptr(scale), _ptr(out),
-                                                _block_dtype(out), _stream(stream)))
+                                                _block_dtype(out, "psgd_block_grad_enter"), _stream(stream)))
 
 
 def psgd_block_grad_exit(ctx: int, dx, g, scale, flag=None, stream=None) -> None:
     """dx += g / S_b over the finite elements of the 16-bit block output g (Inf/NaN add 0);
     flag (one-element uint8 device tensor, or None) is set to 1 if g held Inf/NaN."""
     if dx.numel() != g.numel() or not dx.is_contiguous() or not g.is_contiguous():
-        raise PsgdError("dx and g must be contiguous with the same number of elements")
+        raise PsgdError("psgd_block_grad_exit", PSGD_EINVAL,
+                        "dx and g must be contiguous with the same number of elements")
     _check(ctx, "psgd_block_grad_exit",
            load_library().psgd_block_grad_exit(ctx, _ptr(dx), _ptr(g), dx.numel(), _ptr(scale),
-                                               _block_dtype(g), None if flag is None else _ptr(flag),
+                                               _block_dtype(g, "psgd_block_grad_exit"), None if flag is None else _ptr(flag),
                                                _stream(stream)))
 
 
@@ -268,12 +270,14 @@ def psgd_block_grad_exit_enter(ctx: int, dx, g, scale_exit, scale_enter, out, fl
     """Leave block b (dx += g / S_b over finite g) and enter block b - 1 (out = to16(S_{b-1} dx))
     in one pass; g and out are 16-bit tensors of the same dtype."""
     if not (dx.numel() == g.numel() == out.numel()) or not (dx.is_contiguous() and g.is_contiguous() and out.is_contiguous()):
-        raise PsgdError("dx, g and out must be contiguous with the same number of elements")
+        raise PsgdError("psgd_block_grad_exit_enter", PSGD_EINVAL,
+                        "dx, g and out must be contiguous with the same number of elements")
     if g.dtype != out.dtype:
-        raise PsgdError("g and out must have the same 16-bit dtype")
+        raise PsgdError("psgd_block_grad_exit_enter", PSGD_EDTYPE, "g and out must have the same 16-bit dtype")
     _check(ctx, "psgd_block_grad_exit_enter",
            load_library().psgd_block_grad_exit_enter(ctx, _ptr(dx), _ptr(g), dx.numel(), _ptr(scale_exit),
-                                                     _ptr(scale_enter), _ptr(out), _block_dtype(g),
+                                                     _ptr(scale_enter), _ptr(out),
+                                                     _block_dtype(g, "psgd_block_grad_exit_enter"),
                                                      _ptr(flag), _stream(stream)))
 
 

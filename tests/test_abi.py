@@ -80,3 +80,31 @@ def test_oracle_is_not_imported_by_the_product():
                 text = open(os.path.join(dirpath, f), errors="ignore").read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), f
                 assert "oracle/" not in text, f
+
+
+@pytest.mark.parametrize("call", ["enter", "exit", "exit_enter"])
+def test_binding_argument_checks_raise_psgd_error(call):
+    """The Python-side checks of the block-scaling wrappers (sizes, contiguity, dtype) run
+    before any library call and raise PsgdError with the call's name and status."""
+    import torch
+    from rank_gradient_compression_powersgd_amd import binding as B
+    dx = torch.zeros(16, dtype=torch.float32)
+    g16 = torch.zeros(16, dtype=torch.float16)
+    short = torch.zeros(8, dtype=torch.float16)
+    f32 = torch.zeros(16, dtype=torch.float32)
+    strided = torch.zeros(32, dtype=torch.float16)[::2]
+    one = torch.ones(1)
+    fn = {
+        "enter": lambda out: B.psgd_block_grad_enter(0, dx, one, out),
+        "exit": lambda g: B.psgd_block_grad_exit(0, dx, g, one),
+        "exit_enter": lambda g: B.psgd_block_grad_exit_enter(0, dx, g, one, one, g16),
+    }[call]
+    name = "psgd_block_grad_" + call
+    for bad, status in ((short, B.PSGD_EINVAL), (strided, B.PSGD_EINVAL), (f32, B.PSGD_EDTYPE)):
+        with pytest.raises(B.PsgdError) as ei:
+            fn(bad)
+        assert ei.value.status == status and name in str(ei.value)
+    if call == "exit_enter":
+        with pytest.raises(B.PsgdError) as ei:
+            B.psgd_block_grad_exit_enter(0, dx, g16, one, one, torch.zeros(16, dtype=torch.bfloat16))
+        assert ei.value.status == B.PSGD_EDTYPE

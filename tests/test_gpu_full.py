@@ -77,51 +77,47 @@ def _device_flags(grads):
 
 
 def test_full_underflow_shard_200_steps():
-    """Rank 80, Student-t(3) gradients near fp16 underflow over all 64 resblocks, 200 warm steps.
-    Each step is non-finite with probability 0.01 (seeded; two forced), the injected value
-    cycling +inf, -inf, NaN into one random element of one random matrix; one extra step has a
-    NaN in a pass-through tensor and one an inf scale. Every step: flags (256 matrices) and skip
-    bit-exact; skipped steps zero every error buffer and keep q. On the steps before, at and
-    after each injection the injected matrix (or, for the pass-through and scale events, one of
-    each shape) is checked against the oracle's step from the GPU's own E and q (one-step
-    protocol)."""
+    """Rank 80, Student-t(3) gradients near fp16 underflow over all 64 resblocks: 200 warm steps,
+    each non-finite with probability 0.01 (workloads.injection_schedule: seeded, at least two
+    forced, the injected value cycling +inf, -inf, NaN into one random element of one random
+    matrix), then step 200 with a NaN in a pass-through tensor and step 201 with an inf scale.
+    Every step: flags (256 matrices) and skip bit-exact against torch's isfinite on the inputs;
+    skipped steps zero every error buffer and keep q. On the steps before, at and after each
+    event the injected matrix (or, for the pass-through and scale events, one matrix of each
+    shape) is checked against the oracle's step from the state the GPU carried into that step
+    (one-step protocol: warm-started error feedback amplifies rounding differences over 200
+    steps, so free-running trajectories cannot be compared this far)."""
     import torch
     w, grads, group = _build(4, write_out=True)
     scales = wl.scales_np(w)
     pt = torch.from_numpy(wl.passthrough_np(4, w.n_blocks)).cuda().reshape(-1)
-    rng = np.random.default_rng(4_000_200)
-    steps = 200
-    inject = [t for t in range(steps) if rng.random() < 0.01]
-    for forced in (50, 120):
-        if len(inject) < 2 and forced not in inject:
-            inject.append(forced)
-    values = (np.inf, -np.inf, np.nan)
-    sched = {t: ("grad", int(rng.integers(len(w.matrices))), k) for k, t in enumerate(sorted(inject))}
-    sched[150] = ("pass", 0, 0)
-    sched[170] = ("scale", 13, 0)
+    events = wl.injection_schedule(w, 200)
+    sched = {e.step: e for e in events}
+    steps = max(sched) + 1
+    assert steps == 202 and sched[200].kind == "passthrough" and sched[201].kind == "scale"
+    assert sum(e.kind == "grad" for e in events) >= 2
     checked = set()
     for t in sched:
         checked.update({t - 1, t, t + 1})
-    log(f"underflow shard: 200 steps, events at {sorted(sched)}")
+    log(f"underflow shard: {steps} steps, events at {sorted(sched)}")
     n_skip = 0
     for step in range(steps):
         for s, g in zip(w.matrices, grads):
             wl.gradient_torch(w, s, step, g.device, out=g)
         ev = sched.get(step)
         ptx = pt
-        if ev and ev[0] == "grad":
-            s = w.matrices[ev[1]]
-            r, c = int(rng.integers(s.m)), int(rng.integers(s.n))
-            grads[ev[1]][r, c] = float(values[ev[2] % 3])
-        if ev and ev[0] == "pass":
+        if ev and ev.kind == "grad":
+            grads[ev.matrix][ev.row, ev.col] = ev.value
+        if ev and ev.kind == "passthrough":
             ptx = pt.clone()
-            ptx[int(rng.integers(ptx.numel()))] = float("nan")
-        if ev and ev[0] == "scale":
-            group.scale[ev[1]] = float("inf")
+            ptx[ev.row] = ev.value
+        if ev and ev.kind == "scale":
+            group.scale[ev.block] = ev.value
         sample = []
         if step in checked:
             near = [e for e in (sched.get(step), sched.get(step - 1), sched.get(step + 1)) if e]
-            sample = sorted({e[1] for e in near if e[0] == "grad"} | ({0, 69, 162, 255} if any(e[0] != "grad" for e in near) else set()))
+            sample = sorted({e.matrix for e in near if e.kind == "grad"}
+                            | ({0, 69, 162, 255} if any(e.kind != "grad" for e in near) else set()))
             host = {i: (grads[i].float().cpu().numpy(), group.err[i].cpu().numpy(), group.q[i].cpu().numpy()) for i in sample}
         expect_flags = _device_flags(grads)
         expect_skip = int(expect_flags.any() or not bool(torch.isfinite(ptx).all())
@@ -150,56 +146,52 @@ def test_full_underflow_shard_200_steps():
                 for k in ("D", "E", "Q"):
                     assert r[k] <= REL_TOL, (step, w.matrices[i].name, k, r[k])
                 assert r["orth"] <= ORTH_TOL
-        if ev and ev[0] == "scale":
-            group.scale[ev[1]] = float(scales[ev[1]])
+        if ev and ev.kind == "scale":
+            group.scale[ev.block] = float(scales[ev.block])
     assert n_skip == len(sched)
     group.close()
 
 
 def test_unsharded_rank896():
     """The unsharded resblock (3968x11904, 3968x3968, 3968x15872, 15872x3968 bf16, planted rank-64
-    component at 10x energy) at rank 896 over 5 warm-started steps. The 3968x3968 matrix is
-    compared with the oracle at every step; for all four matrices the properties that hold at
-    any size are checked: orthonormal P, E + D = M element by element, P^T E = 0, q_next =
-    M^T P on sampled columns."""
+    component at 10x energy) at rank 896 over 5 warm-started steps. Every matrix is compared
+    with its own free-running float64 oracle chain at every step (D, E, q_next and P within the
+    relative Frobenius tolerance, P orthonormal). The panels have full column rank, so the
+    oracle orthonormalises them with LAPACK's Householder QR (sign-fixed thin-QR factor), which
+    finishes in seconds where the column loop takes minutes. The properties that hold at any
+    size are checked as well: E + D = M element by element and P^T E = 0."""
     import torch
     w, grads, group = _build(5)
-    r = w.rank
-    PROJ = 1
-    E_or = np.zeros((w.matrices[PROJ].m, w.matrices[PROJ].n))
-    Q_or = group.q[PROJ].cpu().numpy().astype(np.float64)
-    rng = np.random.default_rng(5)
+    E_or = [np.zeros((s.m, s.n)) for s in w.matrices]
+    Q_or = [q.cpu().numpy().astype(np.float64) for q in group.q]
     for step in range(5):
         if step:
             for s, g in zip(w.matrices, grads):
                 wl.gradient_torch(w, s, step, g.device, out=g)
-        Gs = [g.float().cpu().numpy().astype(np.float64) for g in grads]
-        Es = [e.cpu().numpy().astype(np.float64) for e in group.err]
+        Gs = [g.float().cpu().numpy() for g in grads]
+        Es = [e.cpu().numpy() for e in group.err]
         log(f"unsharded rank 896 step {step}")
         skip = group.step([], host=True)
         torch.cuda.synchronize()
         assert skip == 0
         for i, s in enumerate(w.matrices):
-            M = Gs[i] + Es[i]
             P = group.p[i].cpu().numpy().astype(np.float64)
             E = group.err[i].cpu().numpy().astype(np.float64)
             D = group.out[i].cpu().numpy().astype(np.float64)
             Q = group.q[i].cpu().numpy().astype(np.float64)
-            oe = orth_err(P)
+            M = Gs[i].astype(np.float64) + Es[i]
             ident = float(np.abs(E + D - M).max() / np.abs(M).max())
             pe = float(np.linalg.norm(P.T @ E) / np.linalg.norm(E))
-            cols = rng.choice(r, size=8, replace=False)
-            qs = rel(Q[:, cols], M.T @ P[:, cols])
-            log(f"  {s.name}: orth={oe:.2e} |E+D-M|/|M|max={ident:.2e} |P^T E|/|E|={pe:.2e} q_next={qs:.2e}")
-            assert oe <= ORTH_TOL
+            del M
+            st = oracle.step_matrix(Gs[i], 1.0, E_or[i], Q_or[i], oracle.thin_qr_factor)
+            r_ = dict(D=rel(D, st.D), E=rel(E, st.E_next), Q=rel(Q, st.Q_next), P=rel(P, st.P),
+                      orth=orth_err(P), ident=ident, PtE=pe)
+            log(f"  {s.name}: " + " ".join(f"{k}={v:.2e}" for k, v in r_.items()))
+            for k in ("D", "E", "Q", "P"):
+                assert r_[k] <= REL_TOL, (step, s.name, k, r_[k])
+            assert r_["orth"] <= ORTH_TOL
             assert ident <= 2.0 ** -20
             assert pe <= REL_TOL
-            assert qs <= REL_TOL
-        st = oracle.step_matrix(Gs[PROJ], 1.0, E_or, Q_or)
-        r_ = dict(D=rel(group.out[PROJ].cpu().numpy(), st.D), E=rel(group.err[PROJ].cpu().numpy(), st.E_next),
-                  Q=rel(group.q[PROJ].cpu().numpy(), st.Q_next), P=rel(group.p[PROJ].cpu().numpy(), st.P))
-        log("  oracle proj: " + " ".join(f"{k}={v:.2e}" for k, v in r_.items()))
-        for k in ("D", "E", "Q", "P"):
-            assert r_[k] <= REL_TOL, (step, k, r_[k])
-        E_or, Q_or = st.E_next, st.Q_next
+            E_or[i], Q_or[i] = st.E_next, st.Q_next
+            del st, P, E, D, Q
     group.close()

@@ -241,3 +241,41 @@ def test_data_parallel_mean_error_is_the_step_of_the_mean():
     assert np.abs(sum(dp.E_next) / 3 - one.E_next).max() <= 1e-12 * np.abs(one.E_next).max()
     for G, E, En in zip(Gs, Es, dp.E_next):
         assert np.abs(G + E - dp.D - En).max() == 0.0
+
+
+# ------------------------------------------------------------------------------------------
+# the Householder route of the orthonormalisation, pinned to the definition of the factor
+# ------------------------------------------------------------------------------------------
+def test_thin_qr_factor_meets_its_definition():
+    """thin_qr_factor(P) must be THE thin-QR factor with a positive R diagonal: orthonormal
+    columns, R = F^T P upper triangular with a positive diagonal, and F R = P. These properties
+    fix F uniquely for full-rank P, so it must also equal the (separately pinned) CGS2 column
+    loop; a dependent panel is rejected instead of completed arbitrarily."""
+    rng = np.random.default_rng(31)
+    for m, r, cond in ((50, 9, 1.0), (400, 40, 1e3), (64, 64, 30.0)):
+        U, _ = np.linalg.qr(rng.standard_normal((m, r)))
+        V, _ = np.linalg.qr(rng.standard_normal((r, r)))
+        P = (U * np.geomspace(1.0, 1.0 / cond, r)) @ V.T * 3.0
+        F = oracle.thin_qr_factor(P)
+        R = F.T @ P
+        assert np.abs(F.T @ F - np.eye(r)).max() <= 1e-13
+        assert np.abs(np.tril(R, -1)).max() <= 1e-13 * np.abs(R).max() * cond
+        assert np.diag(R).min() > 0
+        assert np.abs(F @ np.triu(R) - P).max() <= 1e-13 * np.abs(P).max()
+        assert np.abs(F - oracle.gram_schmidt(P)).max() <= 1e-13 * cond
+    Pdep = rng.standard_normal((30, 4))
+    Pdep[:, 3] = Pdep[:, 0] - 2.0 * Pdep[:, 1]
+    with pytest.raises(ValueError):
+        oracle.thin_qr_factor(Pdep)
+
+
+def test_step_matrix_routes_agree():
+    """The step with the Householder route equals the step with the column loop (full rank)."""
+    rng = np.random.default_rng(32)
+    G = rng.standard_normal((120, 56))
+    E = rng.standard_normal((120, 56)) * 0.3
+    Q = rng.standard_normal((56, 12))
+    a = oracle.step_matrix(G, 0.25, E, Q)
+    b = oracle.step_matrix(G, 0.25, E, Q, oracle.thin_qr_factor)
+    for x, y in ((a.P, b.P), (a.Q_next, b.Q_next), (a.D, b.D), (a.E_next, b.E_next)):
+        assert np.abs(x - y).max() <= 1e-12 * max(1.0, np.abs(y).max())

@@ -272,8 +272,10 @@ def injection_schedule(wl: WorkloadSpec, n_steps: int = 200, p: float = 0.01,
     rng = matrix_rng(60_000_000 + wl.config, 0)
     hit = rng.random(n_steps) < p
     forced = rng.choice(n_steps, size=min_events, replace=False)
-    while hit.sum() < min_events:
-        hit[forced[int(hit.sum())]] = True
+    for t in forced:
+        if hit.sum() >= min_events:
+            break
+        hit[t] = True
     values = (math.inf, -math.inf, math.nan)
     out: List[Injection] = []
     for k, t in enumerate(np.nonzero(hit)[0]):
