@@ -257,6 +257,32 @@ psgd_status psgd_block_grad_exit_enter(psgd_ctx* ctx, float* dx, const void* g, 
                                        psgd_dtype dtype, uint8_t* flag, hipStream_t stream);
 
 /*
+ * One whole step (psgd_compress, psgd_check_finite without the host copy, then
+ * psgd_decompress_update) on a group given by its descriptors, with no plan and no device
+ * allocation: for callers that cannot allocate (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc). The results equal those of a plan made from the
+ * same descriptors and the three calls in a row.
+ *  The plan's workspace, descriptor table and work lists are placed in the library's static
+ *  scratch array of 32 MiB per device (held from the first psgd_create on that device until
+ *  the process ends). A group that needs more (about 12 bytes per element of the m x r
+ *  factors plus 8 r^2 bytes per 256 rows at r <= 128: one 3968-wide resblock shard at rank
+ *  112 takes about 19 MiB; ranks above 128 add 8 bytes per gradient element) is rejected with
+ *  PSGD_EINVAL before anything is launched.
+ *  The call launches kernels only (a fill, uploads of the tables as kernel arguments, then the
+ *  step's kernels), all on `stream`, and returns without synchronising. Every call on a device
+ *  shares that device's array and overwrites the previous call's contents: calls on one
+ *  stream are ordered, but calls that overlap on one device (other streams, other threads,
+ *  other contexts) race and corrupt each other's results.
+ *  Arguments as for psgd_plan_create (mats, n_mats, grad_dtype, n_blocks), psgd_compress
+ *  (scale, flags) and psgd_check_finite (pass, n_pass, skip_dev). The caller owns every
+ *  buffer; the descriptors are read during the call only.
+ */
+psgd_status psgd_step_noalloc(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
+                              psgd_dtype grad_dtype, const float* scale, int n_blocks,
+                              const psgd_tensor* pass, int n_pass, uint8_t* flags,
+                              int32_t* skip_dev, hipStream_t stream);
+
+/*
  * Tracing hook. Install an array of n HIP events created by the caller with timing enabled.
  * While installed, the launch of each kernel in slot k is bracketed by hipEventRecord of
  * events[2k] (before) and events[2k+1] (after) on the call's stream; elapsed times between the

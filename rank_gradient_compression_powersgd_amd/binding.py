@@ -87,13 +87,16 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.psgd_refresh_q.argtypes = [vp, vp, vp]
     lib.psgd_factor_buffer.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(i64), ctypes.POINTER(i32)]
     lib.psgd_reset_errors.argtypes = [vp, vp, vp]
+    lib.psgd_step_noalloc.argtypes = [vp, ctypes.POINTER(psgd_matrix), ctypes.c_int, ctypes.c_int, vp,
+                                      ctypes.c_int, ctypes.POINTER(psgd_tensor), ctypes.c_int, vp, vp, vp]
     lib.psgd_block_grad_enter.argtypes = [vp, vp, i64, vp, vp, ctypes.c_int, vp]
     lib.psgd_block_grad_exit.argtypes = [vp, vp, vp, i64, vp, ctypes.c_int, vp, vp]
     lib.psgd_block_grad_exit_enter.argtypes = [vp, vp, vp, i64, vp, vp, vp, ctypes.c_int, vp, vp]
     for name in ("psgd_create", "psgd_destroy", "psgd_plan_create", "psgd_plan_destroy",
                  "psgd_compress", "psgd_check_finite", "psgd_decompress_update",
                  "psgd_debug_buffer", "psgd_profile_events", "psgd_compress_p", "psgd_orthogonalize",
-                 "psgd_compress_q", "psgd_refresh_q", "psgd_factor_buffer", "psgd_reset_errors", "psgd_block_grad_enter",
+                 "psgd_compress_q", "psgd_refresh_q", "psgd_factor_buffer", "psgd_reset_errors",
+                 "psgd_step_noalloc", "psgd_block_grad_enter",
                  "psgd_block_grad_exit", "psgd_block_grad_exit_enter"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
@@ -232,6 +235,18 @@ def psgd_decompress_update(ctx: int, plan: int, scale, skip_dev, stream=None) ->
 def psgd_reset_errors(ctx: int, plan: int, stream=None) -> None:
     """Zero every error buffer of the plan (restart from a checkpoint)."""
     _check(ctx, "psgd_reset_errors", load_library().psgd_reset_errors(ctx, plan, _stream(stream)))
+
+
+def psgd_step_noalloc(ctx: int, mats: Sequence[psgd_matrix], grad_dtype: int, scale, flags,
+                      skip_dev, passthrough: Iterable = (), stream=None) -> None:
+    """One whole step on a group without a plan or any device allocation (the library's static
+    scratch array holds the workspace); calls overlapping on one device race."""
+    arr = (psgd_matrix * len(mats))(*mats)
+    pts = [t for t in passthrough]
+    parr = (psgd_tensor * max(1, len(pts)))(*[psgd_tensor(_ptr(t), t.numel()) for t in pts])
+    _check(ctx, "psgd_step_noalloc",
+           load_library().psgd_step_noalloc(ctx, arr, len(mats), grad_dtype, _ptr(scale), int(scale.numel()),
+                                            parr, len(pts), _ptr(flags), _ptr(skip_dev), _stream(stream)))
 
 
 def _block_dtype(t, call: str) -> int:

@@ -1,4 +1,6 @@
-// Small kernels: fills and the skip decision.
+// Small kernels: fills, uploads through kernel arguments and the skip decision.
+#include <cstring>
+
 #include "psgd_internal.h"
 
 namespace psgd {
@@ -42,7 +44,56 @@ void k_check_finite(const uint8_t* __restrict__ flags, int n_flags,
   if (bad) *skip = 1;
 }
 
+// Zero `n16` 16-byte units (grid-stride, vector stores).
+__global__ __launch_bounds__(256)
+void k_fill_zero16(u32x4* __restrict__ p, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    p[i] = u32x4{0, 0, 0, 0};
+}
+
+// Copy up to kUploadWords 32-bit words handed over as a kernel argument: a host-to-device
+// upload made of kernel launches only (no copy engine, no staging buffer).
+constexpr int kUploadWords = 512;
+struct UploadChunk {
+  uint32_t w[kUploadWords];
+  int n;
+};
+__global__ __launch_bounds__(256)
+void k_upload(uint32_t* __restrict__ dst, UploadChunk c) {
+  for (int i = threadIdx.x; i < c.n; i += blockDim.x) dst[i] = c.w[i];
+}
+
 }  // namespace
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+  if (bytes == 0) return hipSuccess;
+  if ((bytes & 15) != 0 || (reinterpret_cast<uintptr_t>(p) & 15) != 0) return hipErrorInvalidValue;
+  const int64_t n16 = (int64_t)(bytes / 16);
+  int64_t blocks = (n16 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  k_fill_zero16<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(static_cast<u32x4*>(p), n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_upload(void* dst, const void* src, size_t bytes, hipStream_t s) {
+  if ((bytes & 3) != 0 || (reinterpret_cast<uintptr_t>(dst) & 3) != 0) return hipErrorInvalidValue;
+  const uint32_t* w = static_cast<const uint32_t*>(src);
+  uint32_t* d = static_cast<uint32_t*>(dst);
+  size_t left = bytes / 4;
+  while (left > 0) {
+    UploadChunk c;
+    c.n = (int)(left < (size_t)kUploadWords ? left : (size_t)kUploadWords);
+    std::memcpy(c.w, w, (size_t)c.n * 4);
+    k_upload<<<dim3(1), dim3(256), 0, s>>>(d, c);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    w += c.n;
+    d += c.n;
+    left -= (size_t)c.n;
+  }
+  return hipSuccess;
+}
 
 hipError_t launch_zero_u8(uint8_t* p, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;

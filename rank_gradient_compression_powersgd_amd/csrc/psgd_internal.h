@@ -255,6 +255,8 @@ __device__ __forceinline__ f32x8 load_f32x8(const GLOBAL float* p) {
 // ------------------------------------------------------------------------------------------
 namespace psgd {
 hipError_t launch_zero_u8(uint8_t* p, int n, hipStream_t s);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);          // bytes % 16 == 0
+hipError_t launch_upload(void* dst, const void* src, size_t bytes, hipStream_t s);  // bytes % 4 == 0
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
 hipError_t launch_ef_mq(int gt, int rtc, const DevMat* mats, const Work* work, int n_work,
                         const float* scale, uint8_t* flags, hipStream_t s);

@@ -5,6 +5,7 @@
 #include <cstdio>
 #include <cstring>
 #include <memory>
+#include <mutex>
 #include <algorithm>
 #include <new>
 #include <string>
@@ -25,12 +26,32 @@ int decomp_tile_n();
 using psgd::DevMat;
 using psgd::Work;
 
+struct psgd_plan;
+
 struct psgd_ctx {
   int device = 0;
   int rank = 0;
   std::string err;
   std::vector<hipEvent_t> events;   // tracing hook: 2 per slot, empty when off
+  char* scratch = nullptr;          // device address of this device's static scratch array
+  std::unique_ptr<psgd_plan> noalloc_plan;   // host side of psgd_step_noalloc's transient plan
 };
+
+// ------------------------------------------------------------------------------------------
+// Static device scratch for psgd_step_noalloc: the workspace, descriptor table and work lists
+// of one group live here, so that entry point allocates nothing. Each device holds its own
+// copy of the array, from the first context created on it until the process ends. Host code
+// never passes the array's name to a kernel (on the host it is only a stand-in): the device
+// address comes from hipGetSymbolAddress, taken once per device in psgd_create with that
+// device current, and kept in g_scratch_addr.
+// ------------------------------------------------------------------------------------------
+namespace {
+constexpr size_t kScratchBytes = size_t(32) << 20;      // 32 MiB per device
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_addr[kMaxDevices] = {nullptr};
+}  // namespace
+static __device__ __align__(256) char scratch[kScratchBytes];
 
 namespace {
 
@@ -115,10 +136,31 @@ psgd_status psgd_create(psgd_ctx** out, int device, int rank) {
   if (hipGetDeviceCount(&n) != hipSuccess || device < 0 || device >= n) return PSGD_EINVAL;
   if (rank < 1) return PSGD_EINVAL;
   if (rank > psgd::kMaxRank) return PSGD_EUNSUPPORTED;
+  if (device >= kMaxDevices) return PSGD_EUNSUPPORTED;
+  char* scratch_addr = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[device]) {
+      int prev = 0;
+      if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(device) != hipSuccess) return PSGD_EHIP;
+      void* ptr = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      (void)hipSetDevice(prev);
+      if (e != hipSuccess || !ptr) return PSGD_EHIP;
+      g_scratch_addr[device] = static_cast<char*>(ptr);
+    }
+    scratch_addr = g_scratch_addr[device];
+  }
   psgd_ctx* c = new (std::nothrow) psgd_ctx;
   if (!c) return PSGD_ENOMEM;
   c->device = device;
   c->rank = rank;
+  c->scratch = scratch_addr;
+  c->noalloc_plan.reset(new (std::nothrow) psgd_plan);
+  if (!c->noalloc_plan) {
+    delete c;
+    return PSGD_ENOMEM;
+  }
   *out = c;
   return PSGD_OK;
 }
@@ -130,12 +172,28 @@ psgd_status psgd_destroy(psgd_ctx* ctx) {
 
 const char* psgd_last_error(const psgd_ctx* ctx) { return ctx ? ctx->err.c_str() : ""; }
 
-psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
-                             psgd_dtype grad_dtype, int n_blocks, psgd_plan** plan_out) {
-  if (!ctx) return PSGD_EINVAL;
-  ctx->err.clear();
-  if (!plan_out) return fail(ctx, PSGD_EINVAL, "plan pointer is NULL");
-  *plan_out = nullptr;
+}  // extern "C"
+
+namespace {
+
+// Workspace offsets of one matrix's buffers (bytes from the workspace base).
+struct PlanOff {
+  size_t p_raw, pth, ptl, p3e, q3e, gram, tmat, wsum, wdiag, p2, reorth, mh, ml, mth, mtl, qth, qtl;
+};
+struct PlanLayout {
+  std::vector<PlanOff> offs;
+  std::vector<Work> all;       // every work list, concatenated (offsets in psgd_plan::off)
+  size_t ws = 0;               // workspace bytes (a multiple of 256)
+  size_t one_off = 0;          // offset of the constant word 1
+  size_t praw_total = 0;       // bytes of the contiguous raw-factor region at offset 0
+};
+
+// Validate a group and lay out its plan on the host: descriptors (workspace pointers still
+// unbound), grouped work lists and the workspace offsets. Shared by psgd_plan_create, which
+// allocates the workspace, and psgd_step_noalloc, which places it in the library's static
+// scratch array.
+psgd_status plan_layout(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats, psgd_dtype grad_dtype,
+                        int n_blocks, psgd_plan* p, PlanLayout& L) {
   if (!mats || n_mats < 1) return fail(ctx, PSGD_EINVAL, "need at least one matrix");
   if (n_blocks < 1) return fail(ctx, PSGD_EINVAL, "n_blocks must be >= 1");
   int gt = 0;
@@ -145,8 +203,6 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
     case PSGD_F32: gt = psgd::G_F32; break;
     default: return fail(ctx, PSGD_EDTYPE, "unknown gradient dtype %d", (int)grad_dtype);
   }
-  HIPCHK(ctx, hipSetDevice(ctx->device), "hipSetDevice");
-
   // Rank layout. The streaming product kernels carry at most kMaxRankTiles 16-column tiles, so
   // ranks above 128 (which take the split-once GEMM path instead) are laid out as `chunks`
   // equal chunks of `rtc` tiles; rpad = chunks * rtc * 16 >= r, the extra factor columns stay
@@ -159,8 +215,6 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
   const int rpad = rt * 16;
   const int kpad3 = (int)rup(r, 32);
   const bool big = rpad > psgd::kBlk;
-  std::unique_ptr<psgd_plan> p(new (std::nothrow) psgd_plan);
-  if (!p) return fail(ctx, PSGD_ENOMEM, "out of host memory");
   p->ctx = ctx;
   p->n_mats = n_mats;
   p->n_blocks = n_blocks;
@@ -179,8 +233,8 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
   size_t praw_cursor = 0;
   size_t ws = (size_t)rup((int64_t)praw_total, 256);
   auto take = [&](size_t bytes) { size_t o = ws; ws += (size_t)rup((int64_t)bytes, 256); return o; };
-  struct Off { size_t p_raw, pth, ptl, p3e, q3e, gram, tmat, wsum, wdiag, p2, reorth, mh, ml, mth, mtl, qth, qtl; };
-  std::vector<Off> offs(n_mats);
+  std::vector<PlanOff>& offs = L.offs;
+  offs.assign(n_mats, PlanOff{});
   p->mats.resize(n_mats);
   for (int i = 0; i < n_mats; ++i) {
     const psgd_matrix& a = mats[i];
@@ -226,7 +280,7 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
     d.g_bytes = (uint32_t)gb;
     d.e_bytes = (uint32_t)eb;
     d.o_bytes = (uint32_t)ob;
-    Off& o = offs[i];
+    PlanOff& o = offs[i];
     o.p_raw = praw_cursor;
     praw_cursor += (size_t)a.m * rpad * 4;
     o.pth = take((size_t)rpad * d.mpad * 2);
@@ -253,10 +307,11 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
     }
   }
 
-  const size_t one_off = take(4);
+  L.one_off = take(4);
 
   // ---- work lists -------------------------------------------------------------------------
-  std::vector<Work> all;
+  std::vector<Work>& all = L.all;
+  all.clear();
   std::vector<int64_t> cost;   // bytes one item streams (same index as `all`)
   auto begin_kind = [&](int k) { p->off[k] = (int)all.size(); };
   // Padded lists are launched with xcd_remap: XCD x walks the x-th eighth of the list in order.
@@ -420,24 +475,17 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
   end_kind(W_K3, true);
   for (int k = 0; k < W_KINDS; ++k)
     if (p->cnt[k] > 0x7fffffff / 2) return fail(ctx, PSGD_EINVAL, "work list too long");
+  L.ws = ws;
+  L.praw_total = praw_total;
+  return PSGD_OK;
+}
 
-  // ---- device allocations -----------------------------------------------------------------
-  hipError_t e = hipMalloc(&p->workspace, ws ? ws : 256);
-  if (e != hipSuccess) return fail(ctx, PSGD_ENOMEM, "workspace of %zu bytes: %s", ws, hipGetErrorString(e));
-  p->ws_bytes = ws;
-  p->praw_bytes = praw_total;
-  auto cleanup = [&]() {
-    if (p->workspace) (void)hipFree(p->workspace);
-    if (p->d_mats) (void)hipFree(p->d_mats);
-    if (p->d_work) (void)hipFree(p->d_work);
-    p->workspace = nullptr;
-    p->d_mats = nullptr;
-    p->d_work = nullptr;
-  };
-  char* base = static_cast<char*>(p->workspace);
-  for (int i = 0; i < n_mats; ++i) {
+// Point the descriptors at a workspace whose base is `base` (device memory).
+void plan_bind(psgd_plan* p, char* base, const PlanLayout& L) {
+  const bool big = p->big;
+  for (int i = 0; i < p->n_mats; ++i) {
     DevMat& d = p->mats[i];
-    const Off& o = offs[i];
+    const PlanOff& o = L.offs[i];
     d.p_raw = reinterpret_cast<float*>(base + o.p_raw);
     d.pt_hi = reinterpret_cast<uint16_t*>(base + o.pth);
     d.pt_lo = reinterpret_cast<uint16_t*>(base + o.ptl);
@@ -458,8 +506,45 @@ psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
       d.qtl = reinterpret_cast<uint16_t*>(base + o.qtl);
     }
   }
+  p->workspace = base;
+  p->ws_bytes = L.ws;
+  p->praw_bytes = L.praw_total;
+  p->d_one = reinterpret_cast<int32_t*>(base + L.one_off);
+}
+
+}  // namespace
+
+extern "C" {
+
+psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
+                             psgd_dtype grad_dtype, int n_blocks, psgd_plan** plan_out) {
+  if (!ctx) return PSGD_EINVAL;
+  ctx->err.clear();
+  if (!plan_out) return fail(ctx, PSGD_EINVAL, "plan pointer is NULL");
+  *plan_out = nullptr;
+  HIPCHK(ctx, hipSetDevice(ctx->device), "hipSetDevice");
+  std::unique_ptr<psgd_plan> p(new (std::nothrow) psgd_plan);
+  if (!p) return fail(ctx, PSGD_ENOMEM, "out of host memory");
+  PlanLayout L;
+  if (psgd_status st = plan_layout(ctx, mats, n_mats, grad_dtype, n_blocks, p.get(), L); st != PSGD_OK)
+    return st;
+  const size_t ws = L.ws;
+  const std::vector<Work>& all = L.all;
+
+  // ---- device allocations -----------------------------------------------------------------
+  void* wsp = nullptr;
+  hipError_t e = hipMalloc(&wsp, ws ? ws : 256);
+  if (e != hipSuccess) return fail(ctx, PSGD_ENOMEM, "workspace of %zu bytes: %s", ws, hipGetErrorString(e));
+  plan_bind(p.get(), static_cast<char*>(wsp), L);
+  auto cleanup = [&]() {
+    if (p->workspace) (void)hipFree(p->workspace);
+    if (p->d_mats) (void)hipFree(p->d_mats);
+    if (p->d_work) (void)hipFree(p->d_work);
+    p->workspace = nullptr;
+    p->d_mats = nullptr;
+    p->d_work = nullptr;
+  };
   if ((e = hipMemset(p->workspace, 0, ws ? ws : 256)) != hipSuccess) { cleanup(); return hip_fail(ctx, e, "workspace clear"); }
-  p->d_one = reinterpret_cast<int32_t*>(base + one_off);
   const int32_t one = 1;
   if ((e = hipMemcpy(p->d_one, &one, sizeof one, hipMemcpyHostToDevice)) != hipSuccess) { cleanup(); return hip_fail(ctx, e, "constant upload"); }
   if ((e = hipMalloc(&p->d_mats, sizeof(DevMat) * n_mats)) != hipSuccess) { cleanup(); return fail(ctx, PSGD_ENOMEM, "descriptor table"); }
@@ -684,6 +769,46 @@ psgd_status psgd_block_grad_exit_enter(psgd_ctx* ctx, float* dx, const void* g, 
                                             static_cast<const uint16_t*>(g), n, scale_exit, scale_enter,
                                             static_cast<uint16_t*>(out), flag, stream), "block boundary rescaling");
   return PSGD_OK;
+}
+
+psgd_status psgd_step_noalloc(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
+                              psgd_dtype grad_dtype, const float* scale, int n_blocks,
+                              const psgd_tensor* pass, int n_pass, uint8_t* flags,
+                              int32_t* skip_dev, hipStream_t stream) {
+  if (!ctx) return PSGD_EINVAL;
+  ctx->err.clear();
+  if (!scale || !flags || !skip_dev) return fail(ctx, PSGD_EINVAL, "scale, flags and skip_dev are required");
+  if (!ctx->scratch) return fail(ctx, PSGD_EHIP, "no scratch array on device %d", ctx->device);
+  HIPCHK(ctx, hipSetDevice(ctx->device), "hipSetDevice");
+  // Lay the group out exactly as psgd_plan_create does (same descriptors, same work lists, so
+  // the same kernels compute the same results), then place it in the scratch array:
+  // [workspace | descriptor table | work lists].
+  psgd_plan* p = ctx->noalloc_plan.get();
+  PlanLayout L;
+  if (psgd_status st = plan_layout(ctx, mats, n_mats, grad_dtype, n_blocks, p, L); st != PSGD_OK) return st;
+  const size_t mats_off = L.ws;
+  const size_t work_off = mats_off + (size_t)rup((int64_t)(sizeof(DevMat) * n_mats), 256);
+  const size_t total = work_off + (size_t)rup((int64_t)(sizeof(Work) * L.all.size()), 256);
+  if (total > kScratchBytes)
+    return fail(ctx, PSGD_EINVAL,
+                "the group needs %zu bytes of workspace; the allocation-free step holds at most %zu "
+                "(use psgd_plan_create)", total, kScratchBytes);
+  char* base = ctx->scratch;
+  plan_bind(p, base, L);
+  p->d_mats = reinterpret_cast<DevMat*>(base + mats_off);
+  p->d_work = reinterpret_cast<Work*>(base + work_off);
+  // The array keeps the previous call's contents: the workspace padding must read zero (it is
+  // never written by the kernels), so the whole workspace is cleared first. Every step runs on
+  // `stream`, in order; only kernels are launched (the uploads travel as kernel arguments).
+  HIPCHK(ctx, psgd::launch_fill_zero(base, L.ws, stream), "scratch clear");
+  const int32_t one = 1;
+  HIPCHK(ctx, psgd::launch_upload(p->d_one, &one, sizeof one, stream), "constant upload");
+  HIPCHK(ctx, psgd::launch_upload(p->d_mats, p->mats.data(), sizeof(DevMat) * n_mats, stream), "descriptor upload");
+  HIPCHK(ctx, psgd::launch_upload(p->d_work, L.all.data(), sizeof(Work) * L.all.size(), stream), "work list upload");
+  if (psgd_status st = psgd_compress(ctx, p, scale, flags, stream); st != PSGD_OK) return st;
+  if (psgd_status st = psgd_check_finite(ctx, p, flags, pass, n_pass, scale, skip_dev, nullptr, stream); st != PSGD_OK)
+    return st;
+  return psgd_decompress_update(ctx, p, scale, skip_dev, stream);
 }
 
 psgd_status psgd_profile_events(psgd_ctx* ctx, hipEvent_t* events, int n) {

@@ -1,0 +1,121 @@
+"""The allocation-free step (psgd_step_noalloc) against the plan-based step it mirrors
+(psgd_plan_create, then psgd_compress, psgd_check_finite and psgd_decompress_update), through
+the C ABI. Both paths run the same kernels over the same descriptors and work lists, so every
+output must agree bit for bit (stronger than the parity tolerance). Two calls in a row share
+the static scratch array, the second on a smaller group; a group too large for the array is
+rejected before anything is launched.
+"""
+import numpy as np
+import pytest
+
+import workloads as wl
+from tests.gpu_helpers import log
+
+pytestmark = pytest.mark.gpu
+
+RANK = 112
+
+
+def _state(shapes, seed):
+    import torch
+    g, e, q = [], [], []
+    for i, (m, n) in enumerate(shapes):
+        rng = wl.matrix_rng(seed, i)
+        x = rng.standard_normal((m, n)) * np.exp(rng.uniform(np.log(1e-4), 0.0, size=(m, 1)))
+        g.append(torch.from_numpy(wl.to_fp16(x)).cuda())
+        e.append(torch.from_numpy((rng.standard_normal((m, n)) * 0.05).astype(np.float32)).cuda())
+        q.append(torch.from_numpy(rng.standard_normal((n, RANK)).astype(np.float32)).cuda())
+    return g, e, q
+
+
+class _Bufs:
+    """One copy of a group's state and outputs, described to the ABI."""
+
+    def __init__(self, grads, errs, qs, blocks):
+        import torch
+        from rank_gradient_compression_powersgd_amd import binding as B
+        self.err = [x.clone() for x in errs]
+        self.q = [x.clone() for x in qs]
+        self.q_next = [torch.empty_like(x) for x in qs]
+        self.p = [torch.empty((x.shape[0], RANK), dtype=torch.float32, device="cuda") for x in grads]
+        self.out = [torch.empty(x.shape, dtype=torch.float32, device="cuda") for x in grads]
+        self.flags = torch.full((len(grads),), 7, dtype=torch.uint8, device="cuda")
+        self.skip = torch.full((1,), 5, dtype=torch.int32, device="cuda")
+        self.mats = [B.make_matrix(g, e, q, qn, p, b, o) for g, e, q, qn, p, b, o in
+                     zip(grads, self.err, self.q, self.q_next, self.p, blocks, self.out)]
+
+
+def _equal_bits(a, b):
+    import torch
+    if a.dtype in (torch.float32, torch.int32):
+        return bool(torch.equal(a.view(torch.int32), b.view(torch.int32)))
+    return bool(torch.equal(a, b))
+
+
+def _run_both(ctx, shapes, blocks, seed, inject=None):
+    import torch
+    from rank_gradient_compression_powersgd_amd import binding as B
+    grads, errs, qs = _state(shapes, seed)
+    if inject is not None:
+        grads[inject][1, 2] = float("nan")
+    scale = torch.tensor([1.0, 0.5, 0.25], dtype=torch.float32, device="cuda")
+    pt = torch.from_numpy(wl.passthrough_np(2, 3, seed % 1000)).cuda().reshape(-1)
+    ref = _Bufs(grads, errs, qs, blocks)
+    new = _Bufs(grads, errs, qs, blocks)
+    plan = B.psgd_plan_create(ctx, ref.mats, B.PSGD_F16, 3)
+    B.psgd_compress(ctx, plan, scale, ref.flags)
+    B.psgd_check_finite(ctx, plan, ref.flags, [pt], scale, ref.skip)
+    B.psgd_decompress_update(ctx, plan, scale, ref.skip)
+    B.psgd_step_noalloc(ctx, new.mats, B.PSGD_F16, scale, new.flags, new.skip, [pt])
+    torch.cuda.synchronize()
+    B.psgd_plan_destroy(plan)
+    want_skip = 1 if inject is not None else 0
+    assert int(ref.skip.item()) == want_skip and int(new.skip.item()) == want_skip
+    assert _equal_bits(ref.flags, new.flags)
+    for i in range(len(shapes)):
+        pairs = [("E", ref.err[i], new.err[i]), ("q", ref.q[i], new.q[i])]
+        if not want_skip:
+            pairs += [("q_next", ref.q_next[i], new.q_next[i]), ("P", ref.p[i], new.p[i]),
+                      ("D", ref.out[i], new.out[i])]
+        for name, a, b in pairs:
+            assert _equal_bits(a, b), (shapes[i], name, float((a - b).abs().max()))
+    return ref, new
+
+
+def test_noalloc_step_matches_the_plan_step_twice_then_smaller():
+    from rank_gradient_compression_powersgd_amd import binding as B
+    ctx = B.psgd_create(0, RANK)
+    try:
+        big = [(3968, 1488), (496, 3968), (3968, 1984), (1984, 3968)]   # one resblock shard
+        log("no-alloc step: one resblock shard (4 matrices), rank 112")
+        _run_both(ctx, big, [0, 1, 2, 0], 8_100_001)
+        small = [(700, 264), (333, 1024)]
+        log("no-alloc step: smaller group after it (2 matrices)")
+        _run_both(ctx, small, [2, 1], 8_100_002)
+        log("no-alloc step: smaller group with a NaN gradient (skip path)")
+        _run_both(ctx, small, [2, 1], 8_100_003, inject=1)
+        log("no-alloc step: the shard again after the smaller groups")
+        _run_both(ctx, big, [0, 1, 2, 0], 8_100_004)
+    finally:
+        B.psgd_destroy(ctx)
+
+
+def test_noalloc_step_rejects_a_group_beyond_the_scratch_array():
+    import torch
+    from rank_gradient_compression_powersgd_amd import binding as B
+    ctx = B.psgd_create(0, RANK)
+    try:
+        m, n = 32768, 128          # m x 112 factors alone exceed the 32 MiB array
+        g = torch.zeros((m, n), dtype=torch.float16, device="cuda")
+        bufs = _Bufs([g], [torch.zeros((m, n), dtype=torch.float32, device="cuda")],
+                     [torch.zeros((n, RANK), dtype=torch.float32, device="cuda")], [0])
+        scale = torch.ones(1, dtype=torch.float32, device="cuda")
+        log("no-alloc step: oversized group must be rejected")
+        with pytest.raises(B.PsgdError) as ei:
+            B.psgd_step_noalloc(ctx, bufs.mats, B.PSGD_F16, scale, bufs.flags, bufs.skip)
+        assert ei.value.status == B.PSGD_EINVAL and "allocation-free" in str(ei.value)
+        torch.cuda.synchronize()
+        assert int(bufs.skip.item()) == 5            # nothing was launched
+        assert int(bufs.flags[0].item()) == 7
+    finally:
+        B.psgd_destroy(ctx)
