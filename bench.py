@@ -73,6 +73,11 @@ def parse(argv=None):
                     help="only measure the block-boundary gradient scaling calls "
                          "(psgd_block_grad_enter / _exit) on residual-stream gradients of one and "
                          "of 16 sequences (1280 tokens x d_model 3968 each); one JSON line")
+    ap.add_argument("--adam", action="store_true",
+                    help="only time the step with the optimizer: compress, finite check, global "
+                         "norm and clipping, the decompression fused with the Adam update of every "
+                         "matrix (16-bit parameters, bf16 and ue8m8 moments) and fp32 Adam on the "
+                         "pass-through tensors; one JSON line")
     ap.add_argument("--graph", action="store_true",
                     help="only time the step captured once as a HIP graph and replayed (compress, "
                          "device-side finite check, decompress/update); one JSON line")
@@ -321,6 +326,118 @@ def cpu_baseline(seconds: float):
                       f"{nbytes / 1e9:.3f} GB fp16 gradient), float64 numpy oracle, cold start, "
                       f"{t_total:.1f} s"}
 
+ADAM_HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+ADAM_MAX_NORM = 1.0
+
+
+def adam_cpu_baseline(seconds: float, rank: int):
+    """The float64 oracles as they are (PowerSGD step, then the optimizer step with 16-bit
+    storage) on whole resblocks of the per-GPU shard, cold start, for about `seconds`."""
+    import numpy as np
+    import oracle
+    import workloads as wl
+    w = wl.workload(3)
+    hp = oracle.AdamHyper(**ADAM_HP)
+    t_total, nbytes, blocks = 0.0, 0, 0
+    while t_total < seconds and blocks < w.n_blocks:
+        specs = [s for s in w.matrices if s.block == blocks]
+        grads = [wl.gradient_np(w, s, 0).astype(np.float32) for s in specs]
+        errs = [np.zeros((s.m, s.n), np.float32) for s in specs]
+        qs = [wl.initial_q_np(w, s, rank) for s in specs]
+        states = [oracle.AdamState(np.zeros((s.m, s.n)), np.zeros((s.m, s.n)), np.zeros((s.m, s.n)))
+                  for s in specs]
+        t0 = time.perf_counter()
+        st = oracle.step_group(grads, errs, qs, [0] * len(specs), wl.scales_np(w)[blocks:blocks + 1])
+        oracle.adam_group_step(states, st.D, 0, False, hp, max_norm=ADAM_MAX_NORM)
+        t_total += time.perf_counter() - t0
+        nbytes += sum(s.m * s.n * 2 for s in specs)
+        blocks += 1
+    return {"value": nbytes / t_total / 1e9, "unit": "GB/s", "cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle",
+            "sample": f"{blocks} of 64 resblocks ({4 * blocks} matrices, {nbytes / 1e9:.3f} GB fp16 "
+                      f"gradient): float64 PowerSGD step then float64 Adam with 16-bit storage, "
+                      f"cold start, {t_total:.1f} s (the clipping norm over the sampled blocks only)"}
+
+
+def adam_bench(a, hip) -> int:
+    """The step with the optimizer. Per gradient element the fused decompression reads G, E,
+    theta, m1, m2 and writes E, theta, m1, m2 (no D): g + 8 + 3 * 2 * p bytes with 2-byte
+    moments and p-byte parameters (22 bytes for fp16 gradients and parameters)."""
+    import torch
+    import rank_gradient_compression_powersgd_amd as psgd
+    w, group, passthrough = build_workload(a.workload, a.n_blocks, False, a.inplace, a.rank)
+    dev = torch.device("cuda", 0)
+    pdt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+    params, m1s, m2s = [], [], []
+    for i, s in enumerate(w.matrices):
+        g = torch.Generator(device=dev)
+        g.manual_seed(11_000 + i)
+        params.append((torch.randn((s.m, s.n), generator=g, device=dev) * 0.02).to(pdt))
+        m1s.append(torch.zeros((s.m, s.n), dtype=torch.int16, device=dev))
+        m2s.append(torch.zeros((s.m, s.n), dtype=torch.int16, device=dev))
+    group.attach_adam(params, m1s, m2s)
+    pg = passthrough[0]
+    pstate = [(torch.randn_like(pg) * 0.02, torch.zeros_like(pg), torch.zeros_like(pg), pg)]
+    hp = psgd.binding.psgd_adam_hparams(**ADAM_HP)
+    stream = int(torch.cuda.current_stream().cuda_stream)
+    nslot = len(psgd.PROFILE_SLOTS)
+    for _ in range(a.warmup):
+        group.step_adam(hp, pstate, None, ADAM_MAX_NORM)
+    torch.cuda.synchronize()
+    K = a.steps
+    kev = [[hip.event() for _ in range(2 * nslot)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        psgd.psgd_profile_events(group.ctx, kev[k])
+        group.step_adam(hp, pstate, None, ADAM_MAX_NORM)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    psgd.psgd_profile_events(group.ctx, None)
+    assert int(group.skip.item()) == 0, "a timed step was skipped"
+    steps_done = int(group.adam_step.item())
+    assert steps_done == a.warmup + K, steps_done
+    kern = {}
+    for j, name in enumerate(psgd.PROFILE_SLOTS):
+        vals = [hip.elapsed_ms(kev[k][2 * j], kev[k][2 * j + 1]) for k in range(K)]
+        if all(v is not None for v in vals):
+            kern[name] = statistics.mean(vals)
+    for evs in kev:
+        for e in evs:
+            hip.destroy(e)
+    numel = w.numel
+    gsz = 0 if a.inplace else (2 if w.dtype in ("f16", "bf16") else 4)
+    psz = params[0].element_size()
+    per_elem = gsz + 8 + 2 * (psz + 2 + 2)
+    nbytes = per_elem * numel + 4 * w.rank * sum(spec.n for spec in w.matrices)   # + the q commit
+    gbs = nbytes / (kern["decompress_adam"] * 1e-3) / 1e9
+    ms = wall * 1e3 / K
+    norm = group.adam_norm.cpu().tolist()
+    line = {
+        "metric": f"gradient GB/s compressed+decompressed+Adam (rank {w.rank}), 1 MI355X",
+        "value": round(w.grad_bytes * K / wall / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": workload_name(a.workload, w, numel), "grad_dtype": w.dtype,
+                   "param_dtype": str(pdt).replace("torch.", ""), "moments": "m1 bf16, m2 ue8m8",
+                   "passthrough": "gains/biases fp32 Adam", "hparams": ADAM_HP, "max_norm": ADAM_MAX_NORM,
+                   "last_norm": round(norm[0], 4), "last_clip": norm[1]},
+        "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": nbytes,
+                     "bytes_per_element": per_elem, "avg_ms": round(kern["decompress_adam"], 4),
+                     "kernel": "decompress_adam"},
+        "cpu_baseline": None,
+    }
+    group.close()
+    del group, params, m1s, m2s
+    torch.cuda.empty_cache()
+    if not a.no_cpu_baseline:
+        log("timing the CPU oracles ...")
+        line["cpu_baseline"] = adam_cpu_baseline(a.cpu_seconds, w.rank)
+    print(json.dumps(line), flush=True)
+    return 0
+
 
 def graph_bench(a) -> int:
     """The step captured once in a HIP graph (no host synchronisation inside) and replayed: the
@@ -460,6 +577,8 @@ def main(argv=None) -> int:
     if a.graph:
         return graph_bench(a)
     hip = Hip()
+    if a.adam:
+        return adam_bench(a, hip)
     log(f"building workload {a.workload} ...")
     w, group, passthrough = build_workload(a.workload, a.n_blocks, not a.no_out, a.inplace, a.rank)
     stream = int(torch.cuda.current_stream().cuda_stream)

@@ -257,6 +257,77 @@ psgd_status psgd_block_grad_exit_enter(psgd_ctx* ctx, float* dx, const void* g, 
                                        psgd_dtype dtype, uint8_t* flag, hipStream_t stream);
 
 /*
+ * The optimizer that consumes the decompressed gradient: Adam with most moments in a custom
+ * 16-bit format, gradient clipping, and the skip rule for non-finite values ("Zero-Shot
+ * Text-to-Image Generation — 中文验证版", section 方法适配); gains, biases, embeddings and
+ * unembeddings keep 32-bit parameters, gradients and moments (Korean summary of the paper,
+ * section "Mixed-Precision Training"). The update is AdamW ("AIGC 基本功|混合精度与数值稳定性-
+ * AMP", section 6.1), after a global-norm clip of every gradient of the step (section 6.2):
+ *     t <- t + 1;  N = ||all gradients||;  c = min(1, max_norm / N)  (1 when max_norm <= 0)
+ *     g' = c g;  m1 <- b1 m1 + (1 - b1) g';  m2 <- b2 m2 + (1 - b2) g'^2
+ *     theta <- theta - lr ((m1 / (1 - b1^t)) / (sqrt(m2 / (1 - b2^t)) + eps) + wd theta)
+ * using the new moments before they are stored. A skipped step changes nothing (t included).
+ * Storage of a compressed matrix's state: theta in the attached parameter type (fp16, bf16 or
+ * fp32); m1 bfloat16; m2 "ue8m8", a 16-bit code holding bits 30..15 of a non-negative float32
+ * (8 exponent bits, 8 fraction bits: the second moment never needs a sign); every stored
+ * value rounds to nearest even from its float32 value.
+ *
+ * Call order per step (all on one stream, no host sync):
+ *     psgd_compress -> psgd_check_finite -> psgd_adam_prepare
+ *     -> psgd_decompress_adam (instead of psgd_decompress_update) -> psgd_adam_update
+ */
+typedef struct psgd_adam_hparams {
+  float lr, beta1, beta2, eps, weight_decay;   /* 0 <= beta < 1; lr, eps, weight_decay >= 0 */
+} psgd_adam_hparams;
+
+/* Optimizer state of one plan matrix (m x n, row-major): param with leading dimension
+ * ld_param (>= n, multiple of 8), m1 and m2 with leading dimension n. Caller-owned device
+ * memory, 16-byte aligned, each span below 2 GiB; updated in place. */
+typedef struct psgd_adam_matrix {
+  void* param;       int64_t ld_param;
+  uint16_t* m1;      uint16_t* m2;
+} psgd_adam_matrix;
+
+/* A 32-bit pass-through tensor: fp32 param, moments and gradient of numel elements
+ * (device memory; the gradient alone suffices for psgd_adam_prepare). */
+typedef struct psgd_adam_tensor {
+  float* param;  float* m1;  float* m2;  const float* grad;
+  int64_t numel;
+} psgd_adam_tensor;
+
+/* Attach optimizer state to every matrix of the plan (opt has n_mats entries, in plan order);
+ * param_dtype PSGD_F16, PSGD_BF16 or PSGD_F32. Allocates the plan's norm-reduction buffer and
+ * re-uploads its descriptors (synchronises the device). A second call replaces the first. */
+psgd_status psgd_adam_attach(psgd_ctx* ctx, psgd_plan* plan, const psgd_adam_matrix* opt,
+                             psgd_dtype param_dtype);
+
+/* The scalars of a step, after psgd_check_finite and before the updates. Not skipped:
+ * *step_dev += 1, norm_dev[0] = N, norm_dev[1] = c. Skipped: nothing is written.
+ * N covers the decompressed gradient of every plan matrix and the pass-through gradients
+ * (pass[i].grad, numel; at most 8192 * 65536 elements in all). For a plan matrix ||D||_F is
+ * taken as ||q_next||_F, equal to it because P has orthonormal columns, so N is known before
+ * D is formed. Sums run in fp64 in a fixed order (bit-reproducible).
+ *  step_dev  device int32: the optimizer's step count t (caller-owned, checkpointed with the
+ *            moments; 0 before the first step)
+ *  norm_dev  device fp32[2], written */
+psgd_status psgd_adam_prepare(psgd_ctx* ctx, psgd_plan* plan, const psgd_adam_tensor* pass, int n_pass,
+                              float max_norm, const int32_t* skip_dev, int32_t* step_dev,
+                              float* norm_dev, hipStream_t stream);
+
+/* psgd_decompress_update with the Adam update fused in: not skipped, E = M - D, q <- q_next,
+ * and every matrix's param, m1 and m2 take one step on c D (D itself is not written, the
+ * matrices' out buffers are ignored); skipped, E = 0 and nothing else changes. */
+psgd_status psgd_decompress_adam(psgd_ctx* ctx, psgd_plan* plan, const float* scale, const int32_t* skip_dev,
+                                 const int32_t* step_dev, const float* norm_dev,
+                                 const psgd_adam_hparams* hp, hipStream_t stream);
+
+/* The same fp32 step on pass-through tensors (param, m1, m2 fp32, gradient pass[i].grad),
+ * with the scalars psgd_adam_prepare wrote; a skipped step changes nothing. No plan needed. */
+psgd_status psgd_adam_update(psgd_ctx* ctx, const psgd_adam_tensor* pass, int n_pass, const int32_t* skip_dev,
+                             const int32_t* step_dev, const float* norm_dev, const psgd_adam_hparams* hp,
+                             hipStream_t stream);
+
+/*
  * One whole step (psgd_compress, psgd_check_finite without the host copy, then
  * psgd_decompress_update) on a group given by its descriptors, with no plan and no device
  * allocation: for callers that cannot allocate (code under HIP graph capture, tight serving
@@ -291,8 +362,9 @@ psgd_status psgd_step_noalloc(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats
  * 8 decompression + error update + q commit, 9 Gram sum (rank > 128 only), 10 decompression
  * row scales (rank > 128 only, and psgd_refresh_q), 11 second orthonormalisation pass (all
  * four of its launches; they return at once for matrices whose first pass was well
- * conditioned). Slots a call does not launch keep their events unrecorded. n must be at
- * least 24.
+ * conditioned), 12 global gradient norm of psgd_adam_prepare, 13 decompression with the Adam
+ * update, 14 pass-through Adam. Slots a call does not launch keep their events unrecorded.
+ * n must be at least 30.
  * events == NULL (n ignored) removes the hook. The events stay owned by the caller.
  */
 psgd_status psgd_profile_events(psgd_ctx* ctx, hipEvent_t* events, int n);

@@ -7,7 +7,8 @@ include/psgd.h). This package is the thin Python binding over it:
 """
 from .binding import (  # noqa: F401
     LIB_PATH, PROFILE_SLOTS, PSGD_BF16, PSGD_F16, PSGD_F32, PsgdError, load_library,
-    make_matrix, psgd_block_grad_enter, psgd_block_grad_exit, psgd_block_grad_exit_enter,
+    make_adam_matrix, make_adam_tensor, make_matrix, psgd_adam_attach, psgd_adam_prepare,
+    psgd_adam_update, psgd_decompress_adam, psgd_block_grad_enter, psgd_block_grad_exit, psgd_block_grad_exit_enter,
     psgd_check_finite, psgd_compress, psgd_compress_p, psgd_compress_q,
     psgd_create, psgd_debug_buffer, psgd_decompress_update, psgd_destroy, psgd_factor_buffer,
     psgd_last_error, psgd_orthogonalize, psgd_plan_create, psgd_plan_destroy,

@@ -21,7 +21,7 @@ STATUS_NAMES = {0: "PSGD_OK", 1: "PSGD_EINVAL", 2: "PSGD_EDTYPE", 3: "PSGD_ENOME
 # Names of the profiling slots (order of psgd_profile_events).
 PROFILE_SLOTS = ("zero_flags", "ef_mq", "gs_gram", "gs_factor", "gs_apply", "mtp",
                  "zero_skip", "check_finite", "decompress", "gs_reduce", "split3",
-                 "gs_second_pass")
+                 "gs_second_pass", "adam_norm", "decompress_adam", "adam_passthrough")
 
 
 class psgd_matrix(ctypes.Structure):
@@ -40,6 +40,21 @@ class psgd_matrix(ctypes.Structure):
 
 class psgd_tensor(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("numel", ctypes.c_int64)]
+
+
+class psgd_adam_hparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float)]
+
+
+class psgd_adam_matrix(ctypes.Structure):
+    _fields_ = [("param", ctypes.c_void_p), ("ld_param", ctypes.c_int64),
+                ("m1", ctypes.c_void_p), ("m2", ctypes.c_void_p)]
+
+
+class psgd_adam_tensor(ctypes.Structure):
+    _fields_ = [("param", ctypes.c_void_p), ("m1", ctypes.c_void_p), ("m2", ctypes.c_void_p),
+                ("grad", ctypes.c_void_p), ("numel", ctypes.c_int64)]
 
 
 class PsgdError(RuntimeError):
@@ -89,6 +104,12 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.psgd_reset_errors.argtypes = [vp, vp, vp]
     lib.psgd_step_noalloc.argtypes = [vp, ctypes.POINTER(psgd_matrix), ctypes.c_int, ctypes.c_int, vp,
                                       ctypes.c_int, ctypes.POINTER(psgd_tensor), ctypes.c_int, vp, vp, vp]
+    lib.psgd_adam_attach.argtypes = [vp, vp, ctypes.POINTER(psgd_adam_matrix), ctypes.c_int]
+    lib.psgd_adam_prepare.argtypes = [vp, vp, ctypes.POINTER(psgd_adam_tensor), ctypes.c_int, ctypes.c_float,
+                                      vp, vp, vp, vp]
+    lib.psgd_decompress_adam.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(psgd_adam_hparams), vp]
+    lib.psgd_adam_update.argtypes = [vp, ctypes.POINTER(psgd_adam_tensor), ctypes.c_int, vp, vp, vp,
+                                     ctypes.POINTER(psgd_adam_hparams), vp]
     lib.psgd_block_grad_enter.argtypes = [vp, vp, i64, vp, vp, ctypes.c_int, vp]
     lib.psgd_block_grad_exit.argtypes = [vp, vp, vp, i64, vp, ctypes.c_int, vp, vp]
     lib.psgd_block_grad_exit_enter.argtypes = [vp, vp, vp, i64, vp, vp, vp, ctypes.c_int, vp, vp]
@@ -96,7 +117,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                  "psgd_compress", "psgd_check_finite", "psgd_decompress_update",
                  "psgd_debug_buffer", "psgd_profile_events", "psgd_compress_p", "psgd_orthogonalize",
                  "psgd_compress_q", "psgd_refresh_q", "psgd_factor_buffer", "psgd_reset_errors",
-                 "psgd_step_noalloc", "psgd_block_grad_enter",
+                 "psgd_step_noalloc", "psgd_adam_attach", "psgd_adam_prepare", "psgd_decompress_adam",
+                 "psgd_adam_update", "psgd_block_grad_enter",
                  "psgd_block_grad_exit", "psgd_block_grad_exit_enter"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
@@ -247,6 +269,63 @@ def psgd_step_noalloc(ctx: int, mats: Sequence[psgd_matrix], grad_dtype: int, sc
     _check(ctx, "psgd_step_noalloc",
            load_library().psgd_step_noalloc(ctx, arr, len(mats), grad_dtype, _ptr(scale), int(scale.numel()),
                                             parr, len(pts), _ptr(flags), _ptr(skip_dev), _stream(stream)))
+
+
+def make_adam_matrix(param, m1, m2) -> psgd_adam_matrix:
+    """psgd_adam_matrix over torch tensors: param m x n (unit row stride), m1 and m2 contiguous
+    m x n 16-bit tensors (any 2-byte dtype: their bits are the stored codes)."""
+    if param.stride(-1) != 1 or not m1.is_contiguous() or not m2.is_contiguous():
+        raise PsgdError("psgd_adam_attach", PSGD_EINVAL, "param needs unit row stride, m1 and m2 contiguity")
+    if m1.element_size() != 2 or m2.element_size() != 2:
+        raise PsgdError("psgd_adam_attach", PSGD_EDTYPE, "m1 and m2 must be 16-bit tensors")
+    if tuple(m1.shape) != tuple(param.shape) or tuple(m2.shape) != tuple(param.shape):
+        raise PsgdError("psgd_adam_attach", PSGD_EINVAL, "param, m1 and m2 must have the same shape")
+    return psgd_adam_matrix(_ptr(param), param.stride(0), _ptr(m1), _ptr(m2))
+
+
+def make_adam_tensor(param, m1, m2, grad) -> psgd_adam_tensor:
+    """psgd_adam_tensor over contiguous fp32 torch tensors of one size (param, m1, m2 may be
+    None for psgd_adam_prepare, which reads the gradient only)."""
+    for t in (param, m1, m2, grad):
+        if t is not None and (not t.is_contiguous() or t.numel() != grad.numel() or t.element_size() != 4):
+            raise PsgdError("psgd_adam_update", PSGD_EINVAL, "pass-through tensors must be contiguous fp32 of one size")
+    return psgd_adam_tensor(_ptr(param), _ptr(m1), _ptr(m2), _ptr(grad), grad.numel())
+
+
+def _hparams(hp) -> psgd_adam_hparams:
+    if isinstance(hp, psgd_adam_hparams):
+        return hp
+    return psgd_adam_hparams(float(hp.lr), float(hp.beta1), float(hp.beta2), float(hp.eps),
+                             float(hp.weight_decay))
+
+
+def psgd_adam_attach(ctx: int, plan: int, opt: Sequence[psgd_adam_matrix], param_dtype: int) -> None:
+    arr = (psgd_adam_matrix * len(opt))(*opt)
+    _check(ctx, "psgd_adam_attach", load_library().psgd_adam_attach(ctx, plan, arr, param_dtype))
+
+
+def psgd_adam_prepare(ctx: int, plan: int, passthrough: Sequence[psgd_adam_tensor], max_norm: float,
+                      skip_dev, step_dev, norm_dev, stream=None) -> None:
+    arr = (psgd_adam_tensor * max(1, len(passthrough)))(*passthrough)
+    _check(ctx, "psgd_adam_prepare",
+           load_library().psgd_adam_prepare(ctx, plan, arr, len(passthrough), float(max_norm), _ptr(skip_dev),
+                                            _ptr(step_dev), _ptr(norm_dev), _stream(stream)))
+
+
+def psgd_decompress_adam(ctx: int, plan: int, scale, skip_dev, step_dev, norm_dev, hp, stream=None) -> None:
+    h = _hparams(hp)
+    _check(ctx, "psgd_decompress_adam",
+           load_library().psgd_decompress_adam(ctx, plan, _ptr(scale), _ptr(skip_dev), _ptr(step_dev),
+                                               _ptr(norm_dev), ctypes.byref(h), _stream(stream)))
+
+
+def psgd_adam_update(ctx: int, passthrough: Sequence[psgd_adam_tensor], skip_dev, step_dev, norm_dev, hp,
+                     stream=None) -> None:
+    arr = (psgd_adam_tensor * max(1, len(passthrough)))(*passthrough)
+    h = _hparams(hp)
+    _check(ctx, "psgd_adam_update",
+           load_library().psgd_adam_update(ctx, arr, len(passthrough), _ptr(skip_dev), _ptr(step_dev),
+                                           _ptr(norm_dev), ctypes.byref(h), _stream(stream)))
 
 
 def _block_dtype(t, call: str) -> int:

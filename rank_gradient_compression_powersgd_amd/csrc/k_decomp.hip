@@ -68,10 +68,53 @@ template <> struct Raw4<G_F32> {
   __device__ __forceinline__ f32x4 f32() const { return __builtin_bit_cast(f32x4, v); }
 };
 
-template <int GT>
+// Adam variant of the epilogue (PT = parameter type; PT = 0 is the plain decompression). The
+// decompressed gradient is consumed where it is formed instead of being written: for every
+// element, g = c D (c the clipping factor), the moments m1 (bfloat16) and m2 (ue8m8: bits
+// 30..15 of a non-negative float32) are updated, and the parameter takes one AdamW step
+// (Zero-Shot Text-to-Image Generation — 中文验证版, section 方法适配: 16-bit Adam moments with
+// gradient clipping; AIGC 基本功|混合精度与数值稳定性-AMP, section 6.1: the AdamW update).
+// Per element: read G, E, theta, m1, m2; write E, theta, m1, m2 (no D).
+__device__ __forceinline__ float ue8m8_to_f32(uint32_t code) { return __builtin_bit_cast(float, code << 15); }
+__device__ __forceinline__ uint32_t f32_to_ue8m8(float v) {     // v >= 0; round to nearest even
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  return (u + 0x3FFFu + ((u >> 15) & 1u)) >> 15;
+}
+template <int PT> struct ParamIO;
+template <> struct ParamIO<G_F16> {
+  static constexpr uint32_t kBytes = 2;
+  u32x2 v;
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { v = bload8<kPol>(r, off); }
+  __device__ __forceinline__ f32x4 f32() const { return __builtin_convertvector(__builtin_bit_cast(f16x4, v), f32x4); }
+  __device__ __forceinline__ static void store(f32x4 x, rsrc_t r, uint32_t off) {
+    const u32x2 b = __builtin_bit_cast(u32x2, __builtin_convertvector(x, f16x4));
+    __builtin_amdgcn_raw_buffer_store_b64(b, r, off, 0, kPol);
+  }
+};
+template <> struct ParamIO<G_BF16> {
+  static constexpr uint32_t kBytes = 2;
+  u32x2 v;
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { v = bload8<kPol>(r, off); }
+  __device__ __forceinline__ f32x4 f32() const { return __builtin_convertvector(__builtin_bit_cast(bf16x4, v), f32x4); }
+  __device__ __forceinline__ static void store(f32x4 x, rsrc_t r, uint32_t off) {
+    const u32x2 b = __builtin_bit_cast(u32x2, __builtin_convertvector(x, bf16x4));
+    __builtin_amdgcn_raw_buffer_store_b64(b, r, off, 0, kPol);
+  }
+};
+template <> struct ParamIO<G_F32> {
+  static constexpr uint32_t kBytes = 4;
+  u32x4 v;
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t off) { v = bload16<kPol>(r, off); }
+  __device__ __forceinline__ f32x4 f32() const { return __builtin_bit_cast(f32x4, v); }
+  __device__ __forceinline__ static void store(f32x4 x, rsrc_t r, uint32_t off) {
+    bstore16<kPol>(__builtin_bit_cast(u32x4, x), r, off);
+  }
+};
+
+template <int GT, int PT>
 __global__ __launch_bounds__(K3_THREADS, K3_OCC)
 void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
-              const float* __restrict__ scale, const int32_t* __restrict__ skip)
+              const float* __restrict__ scale, const int32_t* __restrict__ skip, AdamArgs aa)
 {
   const Work wi = work[xcd_remap(blockIdx.x, gridDim.x)];
   if (wi.mat < 0) return;
@@ -280,24 +323,87 @@ void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
     __syncthreads();
   }
   const float* Dt = reinterpret_cast<const float*>(lds_raw);
+  if constexpr (PT == 0) {
 #pragma unroll
-  for (int st = 0; st < NS; ++st) {
-    const f32x4 gf = gv[st].f32();
-    const f32x4 ef = __builtin_bit_cast(f32x4, ev[st]);
-    const f32x4 dv = *reinterpret_cast<const f32x4*>(&Dt[(rs + RSTEP * st) * K3_DTP + 4 * cq]);
-    f32x4 en;
+    for (int st = 0; st < NS; ++st) {
+      const f32x4 gf = gv[st].f32();
+      const f32x4 ef = __builtin_bit_cast(f32x4, ev[st]);
+      const f32x4 dv = *reinterpret_cast<const f32x4*>(&Dt[(rs + RSTEP * st) * K3_DTP + 4 * cq]);
+      f32x4 en;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) en[i] = __builtin_fmaf(s, gf[i], ef[i]) - dv[i];
-    bstore16<kPol>(__builtin_bit_cast(u32x4, en), re, offset(st, lde, 4u));
-    bstore16<kPol>(__builtin_bit_cast(u32x4, dv), ro, offset(st, ldo, 4u));
+      for (int i = 0; i < 4; ++i) en[i] = __builtin_fmaf(s, gf[i], ef[i]) - dv[i];
+      bstore16<kPol>(__builtin_bit_cast(u32x4, en), re, offset(st, lde, 4u));
+      bstore16<kPol>(__builtin_bit_cast(u32x4, dv), ro, offset(st, ldo, 4u));
+    }
+  } else {
+    // scalars of this step: clipping factor c and the bias corrections 1 - beta^t
+    const float clipf = *aa.clip;
+    const float t = (float)*aa.step;
+    const float rbc1 = 1.0f / (1.0f - powf(aa.beta1, t));
+    const float rbc2 = 1.0f / (1.0f - powf(aa.beta2, t));
+    const float omb1 = 1.0f - aa.beta1, omb2 = 1.0f - aa.beta2;
+    const rsrc_t rth = make_rsrc(d.param, d.p_bytes);
+    const rsrc_t rm1 = make_rsrc(d.m1, d.mo_bytes);
+    const rsrc_t rm2 = make_rsrc(d.m2, d.mo_bytes);
+    const int ldp = (int)d.ld_param;
+    constexpr int HB = NS / 2;                     // passes per half: state loads in two rounds
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      ParamIO<PT> th[HB];
+      u32x2 v1[HB], v2[HB];
+#pragma unroll
+      for (int j = 0; j < HB; ++j) {
+        const int st = h * HB + j;
+        th[j].load(rth, offset(st, ldp, ParamIO<PT>::kBytes));
+        v1[j] = bload8<kPol>(rm1, offset(st, n, 2u));
+        v2[j] = bload8<kPol>(rm2, offset(st, n, 2u));
+      }
+#pragma unroll
+      for (int j = 0; j < HB; ++j) {
+        const int st = h * HB + j;
+        const f32x4 gf = gv[st].f32();
+        const f32x4 ef = __builtin_bit_cast(f32x4, ev[st]);
+        const f32x4 dv = *reinterpret_cast<const f32x4*>(&Dt[(rs + RSTEP * st) * K3_DTP + 4 * cq]);
+        const f32x4 th0 = th[j].f32();
+        const f32x4 m1o = __builtin_convertvector(__builtin_bit_cast(bf16x4, v1[j]), f32x4);
+        f32x4 en, thn, m1n, m2n;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          en[i] = __builtin_fmaf(s, gf[i], ef[i]) - dv[i];
+          const uint32_t code = i < 2 ? (v2[j][0] >> (16 * i)) & 0xFFFFu : (v2[j][1] >> (16 * (i - 2))) & 0xFFFFu;
+          const float g = clipf * dv[i];
+          m1n[i] = aa.beta1 * m1o[i] + omb1 * g;
+          m2n[i] = aa.beta2 * ue8m8_to_f32(code) + omb2 * (g * g);
+          const float upd = (m1n[i] * rbc1) / (sqrtf(m2n[i] * rbc2) + aa.eps);
+          thn[i] = th0[i] - aa.lr * (upd + aa.weight_decay * th0[i]);
+        }
+        bstore16<kPol>(__builtin_bit_cast(u32x4, en), re, offset(st, lde, 4u));
+        ParamIO<PT>::store(thn, rth, offset(st, ldp, ParamIO<PT>::kBytes));
+        const u32x2 b1 = __builtin_bit_cast(u32x2, __builtin_convertvector(m1n, bf16x4));
+        __builtin_amdgcn_raw_buffer_store_b64(b1, rm1, offset(st, n, 2u), 0, kPol);
+        const u32x2 b2 = u32x2{f32_to_ue8m8(m2n[0]) | (f32_to_ue8m8(m2n[1]) << 16),
+                               f32_to_ue8m8(m2n[2]) | (f32_to_ue8m8(m2n[3]) << 16)};
+        __builtin_amdgcn_raw_buffer_store_b64(b2, rm2, offset(st, n, 2u), 0, kPol);
+      }
+    }
   }
 }
 
-template <int GT>
+template <int GT, int PT>
 hipError_t launch_gt(dim3 grid, hipStream_t s, const DevMat* mats, const Work* work,
-                     const float* scale, const int32_t* skip) {
-  k_decomp<GT><<<grid, dim3(K3_THREADS), 0, s>>>(mats, work, scale, skip);
+                     const float* scale, const int32_t* skip, const AdamArgs& aa) {
+  k_decomp<GT, PT><<<grid, dim3(K3_THREADS), 0, s>>>(mats, work, scale, skip, aa);
   return hipGetLastError();
+}
+template <int PT>
+hipError_t launch_pt(int gt, dim3 grid, hipStream_t s, const DevMat* mats, const Work* work,
+                     const float* scale, const int32_t* skip, const AdamArgs& aa) {
+  switch (gt) {
+    case G_F16: return launch_gt<G_F16, PT>(grid, s, mats, work, scale, skip, aa);
+    case G_BF16: return launch_gt<G_BF16, PT>(grid, s, mats, work, scale, skip, aa);
+    case G_F32: return launch_gt<G_F32, PT>(grid, s, mats, work, scale, skip, aa);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -308,11 +414,17 @@ int decomp_tile_n() { return K3_TN; }
 hipError_t launch_decompress(int gt, const DevMat* mats, const Work* work, int n_work,
                              const float* scale, const int32_t* skip, hipStream_t s) {
   if (n_work <= 0) return hipSuccess;
-  const dim3 grid(n_work);
-  switch (gt) {
-    case G_F16: return launch_gt<G_F16>(grid, s, mats, work, scale, skip);
-    case G_BF16: return launch_gt<G_BF16>(grid, s, mats, work, scale, skip);
-    case G_F32: return launch_gt<G_F32>(grid, s, mats, work, scale, skip);
+  return launch_pt<0>(gt, dim3(n_work), s, mats, work, scale, skip, AdamArgs{});
+}
+
+hipError_t launch_decompress_adam(int gt, int pt, const DevMat* mats, const Work* work, int n_work,
+                                  const float* scale, const int32_t* skip, const AdamArgs& aa,
+                                  hipStream_t s) {
+  if (n_work <= 0) return hipSuccess;
+  switch (pt) {
+    case G_F16: return launch_pt<G_F16>(gt, dim3(n_work), s, mats, work, scale, skip, aa);
+    case G_BF16: return launch_pt<G_BF16>(gt, dim3(n_work), s, mats, work, scale, skip, aa);
+    case G_F32: return launch_pt<G_F32>(gt, dim3(n_work), s, mats, work, scale, skip, aa);
   }
   return hipErrorInvalidValue;
 }

@@ -152,6 +152,35 @@ struct DevMat {
   uint16_t* qth; uint16_t* qtl;        // rpad_b x npad_b: q^T (zero beyond r x n)
   int32_t npad_b;                      // n rounded up to 64
   int32_t rpad_b;                      // rpad rounded up to a whole GEMM tile (128)
+  // optimizer state (psgd_adam_attach; NULL until attached)
+  void* param;       int64_t ld_param; // m x n parameter, type of the attachment
+  uint16_t* m1;      uint16_t* m2;     // m x n 16-bit moments (leading dimension n)
+  uint32_t p_bytes, mo_bytes;          // byte spans of param and of each moment (< 2^31)
+};
+
+// One item of the global-norm reduction: a contiguous fp32 range of a gradient (q_next of a
+// compressed matrix, or a pass-through gradient), at most kNormItem elements.
+struct NormItem {
+  const float* ptr;
+  int64_t n;
+};
+constexpr int64_t kNormItem = 65536;
+// An fp32 tensor updated by the pass-through Adam kernel.
+struct AdamTensor {
+  float* param; float* m1; float* m2; const float* grad; int64_t n;
+};
+constexpr int kAdamTensors = 16;          // tensors per launch (kernel argument)
+struct AdamTensorArgs {
+  AdamTensor t[kAdamTensors];
+  int count;
+};
+
+// Scalars of one Adam step for the fused decompression (hyperparameters by value; the step
+// count and the clipping factor stay on the device).
+struct AdamArgs {
+  float lr, beta1, beta2, eps, weight_decay;
+  const int32_t* step;     // t after this step's increment
+  const float* clip;       // clipping factor c
 };
 
 // One unit of grouped work: a matrix and a block of it. Unused slots have mat = -1.
@@ -272,6 +301,14 @@ hipError_t launch_mtp(int gt, int rtc, const DevMat* mats, const Work* work, int
                       const float* scale, hipStream_t s);
 hipError_t launch_decompress(int gt, const DevMat* mats, const Work* work, int n_work,
                              const float* scale, const int32_t* skip, hipStream_t s);
+hipError_t launch_sqnorm(const NormItem* items, int n_items, double* partial, hipStream_t s);
+hipError_t launch_adam_finalize(const double* partial, int n, float max_norm, const int32_t* skip,
+                                int32_t* step, float* norm_out, hipStream_t s);
+hipError_t launch_adam_f32(const AdamTensor* ts, int n, const AdamArgs& aa, const int32_t* skip,
+                           hipStream_t s);
+hipError_t launch_decompress_adam(int gt, int pt, const DevMat* mats, const Work* work, int n_work,
+                                  const float* scale, const int32_t* skip, const AdamArgs& aa,
+                                  hipStream_t s);
 struct PassList;
 int big_split_tile();
 int big_gemm_tile_m();

@@ -78,6 +78,13 @@ struct psgd_plan {
   int bg_cnt[kMaxBlocks][2] = {{0}};
   int32_t* d_one = nullptr;              // a device word holding 1: the decompression's skip
                                          // word for psgd_reset_errors
+  // optimizer attachment (psgd_adam_attach)
+  int adam_pt = 0;                       // parameter type, 0 = none attached
+  void* adam_buf = nullptr;              // norm items (q_next ranges, then pass-through ranges)
+                                         // and their fp64 sums
+  psgd::NormItem* d_items = nullptr;
+  double* d_partial = nullptr;
+  int n_plan_items = 0;
 };
 
 namespace {
@@ -100,7 +107,8 @@ psgd_status hip_fail(psgd_ctx* ctx, hipError_t e, const char* what) {
 }
 
 enum Slot { S_ZERO_FLAGS, S_K1, S_GRAM, S_FACTOR, S_APPLY, S_K2, S_ZERO_SKIP, S_CHECK,
-            S_K3, S_REDUCE, S_SPLIT3, S_REORTH, S_SLOTS };
+            S_K3, S_REDUCE, S_SPLIT3, S_REORTH, S_ADAM_NORM, S_K3_ADAM, S_ADAM_PASS, S_SLOTS };
+constexpr int kMaxPassItems = 8192;      // norm items of pass-through gradients per call
 
 // Launch `expr` in tracing slot `slot`, bracketed by the hook's events when installed.
 template <typename F>
@@ -563,6 +571,7 @@ psgd_status psgd_plan_destroy(psgd_plan* plan) {
   if (plan->workspace) (void)hipFree(plan->workspace);
   if (plan->d_mats) (void)hipFree(plan->d_mats);
   if (plan->d_work) (void)hipFree(plan->d_work);
+  if (plan->adam_buf) (void)hipFree(plan->adam_buf);
   delete plan;
   return PSGD_OK;
 }
@@ -809,6 +818,151 @@ psgd_status psgd_step_noalloc(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats
   if (psgd_status st = psgd_check_finite(ctx, p, flags, pass, n_pass, scale, skip_dev, nullptr, stream); st != PSGD_OK)
     return st;
   return psgd_decompress_update(ctx, p, scale, skip_dev, stream);
+}
+
+// ------------------------------------------------------------------------------------------
+// the optimizer step that consumes the decompressed gradient
+// ------------------------------------------------------------------------------------------
+psgd_status psgd_adam_attach(psgd_ctx* ctx, psgd_plan* plan, const psgd_adam_matrix* opt,
+                             psgd_dtype param_dtype) {
+  if (psgd_status st = check_call(ctx, plan); st != PSGD_OK) return st;
+  if (!opt) return fail(ctx, PSGD_EINVAL, "optimizer descriptors are required");
+  int pt = 0, psz = 0;
+  switch (param_dtype) {
+    case PSGD_F16: pt = psgd::G_F16; psz = 2; break;
+    case PSGD_BF16: pt = psgd::G_BF16; psz = 2; break;
+    case PSGD_F32: pt = psgd::G_F32; psz = 4; break;
+    default: return fail(ctx, PSGD_EDTYPE, "unknown parameter dtype %d", (int)param_dtype);
+  }
+  std::vector<DevMat> mats = plan->mats;
+  std::vector<psgd::NormItem> items;
+  for (int i = 0; i < plan->n_mats; ++i) {
+    const psgd_adam_matrix& a = opt[i];
+    DevMat& d = mats[i];
+    if (!a.param || !a.m1 || !a.m2) return fail(ctx, PSGD_EINVAL, "matrix %d: param, m1 and m2 are required", i);
+    if (!aligned16(a.param) || !aligned16(a.m1) || !aligned16(a.m2))
+      return fail(ctx, PSGD_EINVAL, "matrix %d: param, m1 and m2 must be 16-byte aligned", i);
+    if (a.ld_param < d.n || a.ld_param % 8 != 0)
+      return fail(ctx, PSGD_EINVAL, "matrix %d: ld_param must be >= n and a multiple of 8", i);
+    const int64_t pb = ((int64_t)(d.m - 1) * a.ld_param + d.n) * psz;
+    const int64_t mb = (int64_t)d.m * d.n * 2;
+    if (pb >= (int64_t(1) << 31) || mb >= (int64_t(1) << 31))
+      return fail(ctx, PSGD_EINVAL, "matrix %d: param and moments must each span less than 2 GiB", i);
+    d.param = a.param;
+    d.ld_param = a.ld_param;
+    d.m1 = a.m1;
+    d.m2 = a.m2;
+    d.p_bytes = (uint32_t)pb;
+    d.mo_bytes = (uint32_t)mb;
+    // the norm of D is that of q_next (n x r): items of at most kNormItem floats
+    const int64_t cnt = (int64_t)d.n * d.r;
+    for (int64_t o = 0; o < cnt; o += psgd::kNormItem)
+      items.push_back(psgd::NormItem{d.q_next + o, std::min<int64_t>(psgd::kNormItem, cnt - o)});
+  }
+  const size_t items_bytes = (size_t)rup((int64_t)((items.size() + kMaxPassItems) * sizeof(psgd::NormItem)), 256);
+  const size_t bytes = items_bytes + (items.size() + kMaxPassItems) * sizeof(double);
+  void* buf = nullptr;
+  hipError_t e = hipDeviceSynchronize();        // no step of this plan may still be running
+  if (e != hipSuccess) return hip_fail(ctx, e, "synchronise before attaching");
+  if ((e = hipMalloc(&buf, bytes)) != hipSuccess) return fail(ctx, PSGD_ENOMEM, "optimizer buffer of %zu bytes", bytes);
+  if ((e = hipMemcpy(buf, items.data(), items.size() * sizeof(psgd::NormItem), hipMemcpyHostToDevice)) != hipSuccess ||
+      (e = hipMemcpy(plan->d_mats, mats.data(), sizeof(DevMat) * plan->n_mats, hipMemcpyHostToDevice)) != hipSuccess ||
+      (e = hipDeviceSynchronize()) != hipSuccess) {
+    (void)hipFree(buf);
+    return hip_fail(ctx, e, "optimizer upload");
+  }
+  if (plan->adam_buf) (void)hipFree(plan->adam_buf);
+  plan->mats = mats;
+  plan->adam_buf = buf;
+  plan->d_items = static_cast<psgd::NormItem*>(buf);
+  plan->d_partial = reinterpret_cast<double*>(static_cast<char*>(buf) + items_bytes);
+  plan->n_plan_items = (int)items.size();
+  plan->adam_pt = pt;
+  return PSGD_OK;
+}
+
+namespace {
+psgd_status check_pass_tensors(psgd_ctx* ctx, const psgd_adam_tensor* pass, int n_pass, bool update) {
+  if (n_pass < 0 || (n_pass > 0 && !pass)) return fail(ctx, PSGD_EINVAL, "bad pass-through list");
+  for (int i = 0; i < n_pass; ++i) {
+    const psgd_adam_tensor& t = pass[i];
+    if (t.numel < 0) return fail(ctx, PSGD_EINVAL, "pass-through tensor %d: negative size", i);
+    if (t.numel == 0) continue;
+    if (!t.grad || (update && (!t.param || !t.m1 || !t.m2)))
+      return fail(ctx, PSGD_EINVAL, "pass-through tensor %d: NULL pointer", i);
+  }
+  return PSGD_OK;
+}
+psgd::AdamArgs adam_args(const psgd_adam_hparams* hp, const int32_t* step, const float* norm) {
+  return psgd::AdamArgs{hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, step, norm + 1};
+}
+psgd_status check_hparams(psgd_ctx* ctx, const psgd_adam_hparams* hp) {
+  if (!hp) return fail(ctx, PSGD_EINVAL, "hyperparameters are required");
+  if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
+    return fail(ctx, PSGD_EINVAL, "betas must lie in [0, 1)");
+  if (!(hp->eps >= 0.0f) || !(hp->lr >= 0.0f) || !(hp->weight_decay >= 0.0f))
+    return fail(ctx, PSGD_EINVAL, "lr, eps and weight_decay must be finite and >= 0");
+  return PSGD_OK;
+}
+}  // namespace
+
+psgd_status psgd_adam_prepare(psgd_ctx* ctx, psgd_plan* plan, const psgd_adam_tensor* pass, int n_pass,
+                              float max_norm, const int32_t* skip_dev, int32_t* step_dev,
+                              float* norm_dev, hipStream_t stream) {
+  if (psgd_status st = check_call(ctx, plan); st != PSGD_OK) return st;
+  if (!plan->adam_pt) return fail(ctx, PSGD_EINVAL, "no optimizer attached to the plan (psgd_adam_attach)");
+  if (!skip_dev || !step_dev || !norm_dev) return fail(ctx, PSGD_EINVAL, "skip_dev, step_dev and norm_dev are required");
+  if (psgd_status st = check_pass_tensors(ctx, pass, n_pass, false); st != PSGD_OK) return st;
+  std::vector<psgd::NormItem> items;
+  for (int i = 0; i < n_pass; ++i)
+    for (int64_t o = 0; o < pass[i].numel; o += psgd::kNormItem)
+      items.push_back(psgd::NormItem{pass[i].grad + o, std::min<int64_t>(psgd::kNormItem, pass[i].numel - o)});
+  if ((int)items.size() > kMaxPassItems)
+    return fail(ctx, PSGD_EINVAL, "pass-through gradients hold more than %lld elements",
+                (long long)kMaxPassItems * psgd::kNormItem);
+  const int n_items = plan->n_plan_items + (int)items.size();
+  HIPCHK(ctx, traced(ctx, S_ADAM_NORM, stream, [&] {
+    hipError_t e = items.empty() ? hipSuccess
+                                 : psgd::launch_upload(plan->d_items + plan->n_plan_items, items.data(),
+                                                       items.size() * sizeof(psgd::NormItem), stream);
+    if (e == hipSuccess) e = psgd::launch_sqnorm(plan->d_items, n_items, plan->d_partial, stream);
+    if (e == hipSuccess) e = psgd::launch_adam_finalize(plan->d_partial, n_items, max_norm, skip_dev, step_dev,
+                                                        norm_dev, stream);
+    return e; }), "global gradient norm");
+  return PSGD_OK;
+}
+
+psgd_status psgd_decompress_adam(psgd_ctx* ctx, psgd_plan* plan, const float* scale, const int32_t* skip_dev,
+                                 const int32_t* step_dev, const float* norm_dev,
+                                 const psgd_adam_hparams* hp, hipStream_t stream) {
+  if (psgd_status st = check_call(ctx, plan); st != PSGD_OK) return st;
+  if (!plan->adam_pt) return fail(ctx, PSGD_EINVAL, "no optimizer attached to the plan (psgd_adam_attach)");
+  if (!scale || !skip_dev || !step_dev || !norm_dev) return fail(ctx, PSGD_EINVAL, "scale, skip_dev, step_dev and norm_dev are required");
+  if (psgd_status st = check_hparams(ctx, hp); st != PSGD_OK) return st;
+  const psgd::AdamArgs aa = adam_args(hp, step_dev, norm_dev);
+  HIPCHK(ctx, traced(ctx, S_K3_ADAM, stream, [&] {
+    return psgd::launch_decompress_adam(plan->gt, plan->adam_pt, plan->d_mats, plan->d_work + plan->off[W_K3],
+                                        plan->cnt[W_K3], scale, skip_dev, aa, stream); }), "decompression with Adam");
+  return PSGD_OK;
+}
+
+psgd_status psgd_adam_update(psgd_ctx* ctx, const psgd_adam_tensor* pass, int n_pass, const int32_t* skip_dev,
+                             const int32_t* step_dev, const float* norm_dev, const psgd_adam_hparams* hp,
+                             hipStream_t stream) {
+  if (!ctx) return PSGD_EINVAL;
+  ctx->err.clear();
+  if (!skip_dev || !step_dev || !norm_dev) return fail(ctx, PSGD_EINVAL, "skip_dev, step_dev and norm_dev are required");
+  if (psgd_status st = check_hparams(ctx, hp); st != PSGD_OK) return st;
+  if (psgd_status st = check_pass_tensors(ctx, pass, n_pass, true); st != PSGD_OK) return st;
+  std::vector<psgd::AdamTensor> ts;
+  for (int i = 0; i < n_pass; ++i)
+    if (pass[i].numel > 0)
+      ts.push_back(psgd::AdamTensor{pass[i].param, pass[i].m1, pass[i].m2, pass[i].grad, pass[i].numel});
+  HIPCHK(ctx, hipSetDevice(ctx->device), "hipSetDevice");
+  const psgd::AdamArgs aa = adam_args(hp, step_dev, norm_dev);
+  HIPCHK(ctx, traced(ctx, S_ADAM_PASS, stream, [&] {
+    return psgd::launch_adam_f32(ts.data(), (int)ts.size(), aa, skip_dev, stream); }), "pass-through Adam");
+  return PSGD_OK;
 }
 
 psgd_status psgd_profile_events(psgd_ctx* ctx, hipEvent_t* events, int n) {

@@ -67,6 +67,35 @@ class PowerSGDGroup:
         """E = 0 for every matrix: resuming from a checkpoint, which holds no error buffers."""
         B.psgd_reset_errors(self.ctx, self.plan, stream)
 
+    # ---- optimizer ---------------------------------------------------------------------
+    def attach_adam(self, params: Sequence, m1: Sequence, m2: Sequence):
+        """Attach per-matrix optimizer state (caller-owned device tensors, updated in place):
+        params m x n (fp16, bf16 or fp32), m1 and m2 m x n 16-bit codes (bf16 and ue8m8)."""
+        torch = self.torch
+        self.params, self.m1, self.m2 = list(params), list(m1), list(m2)
+        opt = [B.make_adam_matrix(p, a, b) for p, a, b in zip(self.params, self.m1, self.m2)]
+        B.psgd_adam_attach(self.ctx, self.plan, opt, B.dtype_code(self.params[0].dtype))
+        dev = self.flags.device
+        self.adam_step = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.adam_norm = torch.zeros(2, dtype=torch.float32, device=dev)
+
+    def step_adam(self, hp, passthrough: Sequence = (), hp_pass=None, max_norm: float = 0.0,
+                  host: bool = False, stream=None):
+        """One step with the optimizer: compress, finite check, global norm and clipping,
+        decompression fused with the matrices' Adam update, fp32 Adam on the pass-through
+        tensors. passthrough: (param, m1, m2, grad) fp32 tensors; their gradients take part in
+        the finite check and the global norm."""
+        self.compress(stream)
+        grads = [t[3] for t in passthrough]
+        s = self.check_finite(grads, host, stream)
+        ts = [B.make_adam_tensor(*t) for t in passthrough]
+        B.psgd_adam_prepare(self.ctx, self.plan, ts, max_norm, self.skip, self.adam_step, self.adam_norm, stream)
+        B.psgd_decompress_adam(self.ctx, self.plan, self.scale, self.skip, self.adam_step, self.adam_norm, hp,
+                               stream)
+        if ts:
+            B.psgd_adam_update(self.ctx, ts, self.skip, self.adam_step, self.adam_norm, hp_pass or hp, stream)
+        return s
+
     def step(self, passthrough: Sequence = (), host: bool = False, stream=None):
         self.compress(stream)
         s = self.check_finite(passthrough, host, stream)

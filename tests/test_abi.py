@@ -24,7 +24,8 @@ def test_header_declares_the_step_calls():
               "psgd_destroy", "psgd_plan_create", "psgd_plan_destroy", "psgd_last_error",
               "psgd_compress_p", "psgd_orthogonalize", "psgd_compress_q", "psgd_refresh_q",
               "psgd_factor_buffer", "psgd_reset_errors", "psgd_block_grad_enter", "psgd_block_grad_exit",
-              "psgd_block_grad_exit_enter"):
+              "psgd_block_grad_exit_enter", "psgd_step_noalloc", "psgd_adam_attach", "psgd_adam_prepare",
+              "psgd_decompress_adam", "psgd_adam_update"):
         assert n in names
 
 
@@ -46,24 +47,30 @@ def test_binding_names_match_header():
 
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
 def test_struct_layout_matches_c(tmp_path):
-    from rank_gradient_compression_powersgd_amd.binding import psgd_matrix, psgd_tensor
+    from rank_gradient_compression_powersgd_amd.binding import (
+        psgd_adam_hparams, psgd_adam_matrix, psgd_adam_tensor, psgd_matrix, psgd_tensor)
+    structs = (psgd_matrix, psgd_tensor, psgd_adam_hparams, psgd_adam_matrix, psgd_adam_tensor)
     src = tmp_path / "layout.c"
-    src.write_text(
-        '#include <stdio.h>\n#include <stddef.h>\n#include "psgd.h"\n'
-        "int main(void){\n"
-        ' printf("%zu %zu\\n", sizeof(psgd_matrix), sizeof(psgd_tensor));\n'
-        + "".join(f' printf("%zu\\n", offsetof(psgd_matrix, {f}));\n' for f, _ in psgd_matrix._fields_)
-        + " return 0; }\n")
+    body = ""
+    for st in structs:
+        body += f' printf("%zu\\n", sizeof({st.__name__}));\n'
+        body += "".join(f' printf("%zu\\n", offsetof({st.__name__}, {f}));\n' for f, _ in st._fields_)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "psgd.h"\nint main(void){\n'
+                   + body + " return 0; }\n")
     exe = tmp_path / "layout"
     r = subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
                         "-I", "/opt/rocm/include", str(src), "-o", str(exe)],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
-    vals = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()
-    assert int(vals[0]) == ctypes.sizeof(psgd_matrix)
-    assert int(vals[1]) == ctypes.sizeof(psgd_tensor)
-    for (f, _), off in zip(psgd_matrix._fields_, vals[2:]):
-        assert getattr(psgd_matrix, f).offset == int(off), f
+    vals = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    k = 0
+    for st in structs:
+        assert vals[k] == ctypes.sizeof(st), st.__name__
+        k += 1
+        for f, _ in st._fields_:
+            assert getattr(st, f).offset == vals[k], (st.__name__, f)
+            k += 1
+    assert k == len(vals)
 
 
 def test_product_path_fails_loudly_without_library(tmp_path):

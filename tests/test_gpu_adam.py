@@ -1,0 +1,258 @@
+"""The optimizer step through the C ABI (psgd_adam_prepare, psgd_decompress_adam,
+psgd_adam_update) against the float64 oracle (oracle/adam.py).
+
+Two protocols:
+  * exact inputs: matrices whose G and E are zero have D = 0 exactly on both sides, and the
+    pass-through tensors take seeded fp32 gradients directly, so the oracle sees exactly the
+    GPU's inputs (seeded parameters, moment codes and step count, fresh for every case). The global norm, the
+    clipping factor, the step count and every fp32 value then agree to a few float32 units;
+    each 16-bit stored code is the oracle's or (at a rounding midpoint within float32 error) a
+    neighbour, in at most 1e-3 of the elements;
+  * free-running: a one-resblock shard (fp16 gradients, rank 112) takes three steps with
+    clipping active and weight decay; the oracle runs its own PowerSGD step (float64) and its
+    own optimizer step from the same seeded state. The applied parameter update and both
+    moments must agree within the relative Frobenius tolerance of the compression (2e-3): their
+    differences come from the decompressed gradients, which agree to that bound.
+Both protocols end with a skipped step: nothing changes, the step count included, and the
+error buffers are zero.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from tests.gpu_helpers import REL_TOL, log, rel
+
+pytestmark = pytest.mark.gpu
+
+HP = oracle.AdamHyper(lr=2e-3, beta1=0.9, beta2=0.96, eps=1e-8, weight_decay=0.05)
+HP_PASS = oracle.AdamHyper(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
+
+
+def _f32(hp):
+    """The hyperparameters as the ABI holds them (float32), for the oracle."""
+    return oracle.AdamHyper(*[float(np.float32(v)) for v in (hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay)])
+
+
+def _decode(t, fmt):
+    """Stored values as float64: floating tensors exactly, 16-bit code tensors by format."""
+    import torch
+    if t.dtype in (torch.float16, torch.bfloat16, torch.float32):
+        return t.float().cpu().numpy().astype(np.float64)
+    bits = t.cpu().view(torch.int16).numpy().view(np.uint16)
+    if fmt == "bf16":
+        return oracle.bf16_bits_to_f64(bits)
+    return oracle.ue8m8_decode(bits)
+
+
+def _codes_close(got, want, fmt, what, frac=1e-3):
+    """Stored values equal, or neighbouring codes in at most `frac` of the elements."""
+    diff = got != want
+    if not diff.any():
+        return 0.0
+    g, w = got[diff], want[diff]
+    if fmt == "f16":
+        step = np.abs(np.spacing(np.maximum(np.abs(g), np.abs(w)).astype(np.float16)).astype(np.float64))
+    elif fmt == "bf16":
+        step = np.exp2(np.floor(np.log2(np.maximum(np.abs(g), np.abs(w)))) - 7)
+    else:
+        step = np.exp2(np.floor(np.log2(np.maximum(np.abs(g), np.abs(w)))) - 8)
+    assert np.all(np.abs(g - w) <= step * (1 + 1e-12)), (what, "codes further apart than one step")
+    f = float(diff.mean())
+    assert f <= frac, (what, f)
+    return f
+
+
+def _seed_state(shape, seed, param_dtype):
+    import torch
+    rng = wl.matrix_rng(seed, 0)
+    th = rng.standard_normal(shape) * 0.02
+    m1 = rng.standard_normal(shape) * 1e-3
+    m2 = (rng.standard_normal(shape) * 1e-3) ** 2
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[param_dtype]
+    th_t = torch.from_numpy(th.astype(np.float32)).to(tdt).cuda()
+    m1_t = torch.from_numpy(oracle.f32_to_bf16_bits(m1.astype(np.float32)).view(np.int16)).cuda()
+    m2_t = torch.from_numpy(oracle.ue8m8_encode(m2.astype(np.float32)).view(np.int16)).cuda()
+    return th_t, m1_t, m2_t
+
+
+def _oracle_states(params, m1s, m2s, param_dtype, pass_state):
+    st = [oracle.AdamState(_decode(p, param_dtype), _decode(a, "bf16"), _decode(b, "ue8m8"), param_dtype)
+          for p, a, b in zip(params, m1s, m2s)]
+    for p, a, b, _ in pass_state:
+        st.append(oracle.AdamState(_decode(p, "f32"), _decode(a, "f32"), _decode(b, "f32"), "f32", "f32", "f32"))
+    return st
+
+
+def _pass_tensors(seed, sizes, step):
+    import torch
+    out = []
+    for k, n in enumerate(sizes):
+        rng = wl.matrix_rng(seed + 17, k)
+        p = torch.from_numpy((rng.standard_normal(n) * 0.1).astype(np.float32)).cuda()
+        a = torch.from_numpy((rng.standard_normal(n) * 1e-2).astype(np.float32)).cuda()
+        b = torch.from_numpy(((rng.standard_normal(n) * 1e-2) ** 2).astype(np.float32)).cuda()
+        g = torch.empty(n, dtype=torch.float32, device="cuda")
+        out.append([p, a, b, g])
+    return out
+
+
+def _set_pass_grads(pts, seed, step):
+    import torch
+    for k, t in enumerate(pts):
+        rng = wl.matrix_rng(seed + 1000 * (step + 1), k)
+        t[3].copy_(torch.from_numpy((rng.standard_normal(t[3].numel()) * (0.5 + k)).astype(np.float32)))
+
+
+@pytest.mark.parametrize("param_dtype", ["f16", "bf16", "f32"])
+def test_exact_inputs_against_oracle(param_dtype):
+    """D = 0 matrices plus pass-through tensors: every input of the optimizer is known exactly.
+    Each case starts from freshly seeded parameters, moment codes, gradients and step count
+    (so no stored value carries an earlier rounding decision into the next comparison); the
+    cases alternate clipping on and off, and one carries a NaN pass-through gradient."""
+    import torch
+    from rank_gradient_compression_powersgd_amd import PowerSGDGroup
+    shapes = [(300, 264), (129, 520)]
+    rank = 16
+    seed = 9_100_000 + {"f16": 1, "bf16": 2, "f32": 3}[param_dtype]
+    grads = [torch.zeros(s, dtype=torch.float16, device="cuda") for s in shapes]
+    q0 = [torch.from_numpy(wl.matrix_rng(seed, 50 + i).standard_normal((s[1], rank)).astype(np.float32))
+          for i, s in enumerate(shapes)]
+    scale = torch.ones(1, dtype=torch.float32, device="cuda")
+    group = PowerSGDGroup(grads, [0, 0], scale, rank, q0, None, False)
+    st = [_seed_state(s, seed + i, param_dtype) for i, s in enumerate(shapes)]
+    params, m1s, m2s = [x[0] for x in st], [x[1] for x in st], [x[2] for x in st]
+    group.attach_adam(params, m1s, m2s)
+    pts = _pass_tensors(seed, [2 * 3968, 1000, 13], 0)
+    for case, (t0, max_norm, skip_now) in enumerate(((0, 5.0, False), (1, 0.0, False), (6, 5.0, False),
+                                                    (6, 5.0, True), (99, 1e9, False))):
+        cs = seed + 100 * (case + 1)
+        for i, s in enumerate(shapes):
+            fresh = _seed_state(s, cs + i, param_dtype)
+            for dst, src in zip((params[i], m1s[i], m2s[i]), fresh):
+                dst.copy_(src)
+        for k, p in enumerate(_pass_tensors(cs, [t[3].numel() for t in pts], 0)):
+            for dst, src in zip(pts[k][:3], p[:3]):
+                dst.copy_(src)
+        _set_pass_grads(pts, cs, case)
+        if skip_now:
+            pts[1][3][7] = float("nan")
+        group.adam_step.fill_(t0)
+        ost = _oracle_states(params, m1s, m2s, param_dtype, pts)
+        before = [(p.clone(), a.clone(), b.clone()) for p, a, b in zip(params, m1s, m2s)]
+        before_pass = [[x.clone() for x in p[:3]] for p in pts]
+        log(f"adam exact inputs {param_dtype} case {case}: t {t0} -> {t0 + (0 if skip_now else 1)}, "
+            f"max_norm {max_norm}, skip {skip_now}")
+        skip = group.step_adam(HP, pts, HP_PASS, max_norm, host=True)
+        torch.cuda.synchronize()
+        assert skip == int(skip_now)
+        gr = [np.zeros(s) for s in shapes] + [p[3].cpu().numpy().astype(np.float64) for p in pts]
+        ost, t_new, n_or, c_or = oracle.adam_group_step(ost, gr, t0, skip_now, _f32(HP), _f32(HP_PASS),
+                                                        n_mats=len(shapes), max_norm=max_norm)
+        assert int(group.adam_step.item()) == t_new
+        if skip_now:
+            for (p0, a0, b0), p, a, b in zip(before, params, m1s, m2s):
+                assert torch.equal(p0, p) and torch.equal(a0, a) and torch.equal(b0, b)
+            for b4, p in zip(before_pass, pts):
+                for x0, x in zip(b4, p[:3]):
+                    assert torch.equal(x0, x)
+            for e in group.err:
+                assert float(e.abs().max()) == 0.0
+            continue
+        nrm = group.adam_norm.cpu().numpy().astype(np.float64)
+        assert abs(nrm[0] - n_or) <= 2e-7 * n_or, (nrm[0], n_or)
+        assert abs(nrm[1] - c_or) <= 2e-7 * c_or, (nrm[1], c_or)
+        for i in range(len(shapes)):
+            th = _decode(params[i], param_dtype)
+            if param_dtype == "f32":
+                err = np.abs(th - ost[i].theta).max()
+                tol = 4e-7 * np.abs(ost[i].theta).max() + 1e-5 * HP.lr
+                assert err <= tol, (i, "theta", err, tol)
+                f1 = float((th != ost[i].theta).mean())
+            else:
+                f1 = _codes_close(th, ost[i].theta, param_dtype, ("theta", i))
+            f2 = _codes_close(_decode(m1s[i], "bf16"), ost[i].m1, "bf16", ("m1", i))
+            f3 = _codes_close(_decode(m2s[i], "ue8m8"), ost[i].m2, "ue8m8", ("m2", i))
+            log(f"  matrix {i}: stored values differing theta {f1:.1e} m1 {f2:.1e} m2 {f3:.1e}")
+        for k, p in enumerate(pts):
+            o = ost[len(shapes) + k]
+            for name, got, want in (("theta", p[0], o.theta), ("m1", p[1], o.m1), ("m2", p[2], o.m2)):
+                g = got.cpu().numpy().astype(np.float64)
+                tol = 4e-7 * np.abs(want).max() + (1e-5 * HP_PASS.lr if name == "theta" else 0.0)
+                assert np.abs(g - want).max() <= tol, (k, name, np.abs(g - want).max(), tol)
+    group.close()
+
+
+def test_free_running_shard_against_oracle():
+    """One resblock shard (fp16 gradients and parameters, rank 112), three optimizer steps with
+    clipping active and weight decay, then a skipped step."""
+    import torch
+    from rank_gradient_compression_powersgd_amd import PowerSGDGroup
+    w = wl.workload(2)
+    seed = 9_200_000
+    grads = [torch.from_numpy(wl.gradient_np(w, s, 0)).cuda() for s in w.matrices]
+    q0 = [wl.initial_q_np(w, s) for s in w.matrices]
+    scale = torch.ones(1, dtype=torch.float32, device="cuda")
+    group = PowerSGDGroup(grads, [0] * 4, scale, w.rank, [torch.from_numpy(q) for q in q0], None, False)
+    params = []
+    for i, s in enumerate(w.matrices):
+        rng = wl.matrix_rng(seed, i)
+        params.append(torch.from_numpy((rng.standard_normal((s.m, s.n)) * 0.02).astype(np.float16)).cuda())
+    m1s = [torch.zeros((s.m, s.n), dtype=torch.int16, device="cuda") for s in w.matrices]
+    m2s = [torch.zeros((s.m, s.n), dtype=torch.int16, device="cuda") for s in w.matrices]
+    group.attach_adam(params, m1s, m2s)
+    pts = _pass_tensors(seed, [2 * 3968], 0)
+    ost = _oracle_states(params, m1s, m2s, "f16", pts)
+    E_or = [np.zeros((s.m, s.n)) for s in w.matrices]
+    Q_or = [q.astype(np.float64) for q in q0]
+    t = 0
+    max_norm = 20.0
+    for step in range(4):
+        skip_now = step == 3
+        if step:
+            for s, g in zip(w.matrices, grads):
+                g.copy_(torch.from_numpy(wl.gradient_np(w, s, step)))
+        if skip_now:
+            grads[2][5, 9] = float("inf")
+        _set_pass_grads(pts, seed, step)
+        G = [g.float().cpu().numpy() for g in grads]
+        th_before = [_decode(p, "f16") for p in params]
+        log(f"adam free-running shard step {step}")
+        skip = group.step_adam(HP, pts, HP_PASS, max_norm, host=True)
+        torch.cuda.synchronize()
+        assert skip == int(skip_now)
+        gs = oracle.step_group(G, E_or, Q_or, [0] * 4, np.ones(1, np.float32),
+                               [p[3].cpu().numpy() for p in pts])
+        assert gs.skip == skip_now
+        gr = (gs.D if not skip_now else [None] * 4) + [p[3].cpu().numpy().astype(np.float64) for p in pts]
+        prev = [oracle.AdamState(s.theta.copy(), s.m1.copy(), s.m2.copy(), s.param_fmt, s.m1_fmt, s.m2_fmt)
+                for s in ost]
+        ost, t, n_or, c_or = oracle.adam_group_step(ost, gr, t, skip_now, _f32(HP), _f32(HP_PASS),
+                                                    n_mats=4, max_norm=max_norm)
+        E_or, Q_or = gs.E_next, gs.Q_next
+        assert int(group.adam_step.item()) == t
+        if skip_now:
+            for i in range(4):
+                assert np.array_equal(_decode(params[i], "f16"), th_before[i])
+            for e in group.err:
+                assert float(e.abs().max()) == 0.0
+            break
+        nrm = group.adam_norm.cpu().numpy().astype(np.float64)
+        assert c_or < 1.0, "the step was meant to clip"
+        assert abs(nrm[0] - n_or) <= REL_TOL * n_or and abs(nrm[1] - c_or) <= REL_TOL * c_or, (nrm, n_or, c_or)
+        worst = {}
+        for i, s in enumerate(w.matrices):
+            th = _decode(params[i], "f16")
+            r = dict(dtheta=rel(th - th_before[i], ost[i].theta - prev[i].theta),
+                     m1=rel(_decode(m1s[i], "bf16"), ost[i].m1), m2=rel(_decode(m2s[i], "ue8m8"), ost[i].m2),
+                     theta_values_differing=float((th != ost[i].theta).mean()))
+            for k, v in r.items():
+                worst[k] = max(worst.get(k, 0.0), v)
+            for k in ("dtheta", "m1", "m2"):
+                assert r[k] <= REL_TOL, (step, s.name, k, r[k])
+        o = ost[4]
+        for name, got, want in (("theta", pts[0][0], o.theta), ("m1", pts[0][1], o.m1), ("m2", pts[0][2], o.m2)):
+            assert rel(got.cpu().numpy(), want) <= REL_TOL, (step, "pass-through", name)
+        log(f"  norm {nrm[0]:.6g} (oracle {n_or:.6g}) clip {nrm[1]:.4g}: "
+            + " ".join(f"{k}={v:.2e}" for k, v in worst.items()))
+    group.close()
