@@ -3,10 +3,10 @@
 // The factor product comes from the P·Q decomposition of the Korean summary of the DALL·E
 // paper (section "Distributed Optimization"). The contraction runs over the m rows of M, so an
 // MFMA B-fragment needs 8 consecutive rows of one column. Reading that directly would
-// stride through memory. Instead every lane loads an 8-row x 4-column block of M: each load
-// is 4 consecutive columns of one row, and a wave instruction covers 4 rows x 64 columns,
-// contiguous along the row. The lane then holds the B-fragments of 4 column tiles at once.
-// Column tile t of a wave holds columns {4j + t : j = 0..15} of its 64-column strip.
+// stride through memory. Instead every lane loads an 8-row x TC-column block of M: each load
+// is TC consecutive columns of one row, and a wave instruction covers 4 rows x 16 TC columns,
+// contiguous along the row. The lane then holds the B-fragments of TC column tiles at once.
+// Column tile t of a wave holds columns {TC j + t : j = 0..15} of its 16 TC-column strip.
 // The shared operand P^T, split into bf16 hi/lo by the orthonormalisation kernel, is staged
 // in LDS 32 rows of m at a time and double-buffered. Products use the same three-term bf16
 // split as K1. G and E are read through buffer descriptors (out-of-range reads give zeros),
@@ -20,11 +20,16 @@
 namespace psgd {
 namespace {
 
+// Eight waves of two column tiles (256 columns per workgroup) with one 32-row k group per
+// stage keep each wave at 188 VGPRs, so a CU holds two waves per SIMD; four waves of four
+// tiles (two k groups) needed 422 registers and ran one wave per SIMD, 1.89 -> 1.80 ms on the
+// 64-resblock rank-112 shard (the accumulators shrink with TC, and the second wave per SIMD
+// covers the loads of the first).
 #ifndef K2_W
-#define K2_W 4       // waves per workgroup
+#define K2_W 8       // waves per workgroup
 #endif
 #ifndef K2_TC
-#define K2_TC 4      // consecutive columns per lane = column tiles per wave (2 or 4)
+#define K2_TC 2      // consecutive columns per lane = column tiles per wave (2 or 4)
 #endif
 #ifndef K2_POLG
 #define K2_POLG 0
@@ -36,7 +41,7 @@ namespace {
 #define K2_OCC 1     // workgroups per CU the register budget is sized for
 #endif
 #ifndef K2_KSUB
-#define K2_KSUB 2    // 32-row MFMA k groups per pipeline stage (rows of M in flight per stage)
+#define K2_KSUB 1    // 32-row MFMA k groups per pipeline stage (rows of M in flight per stage)
 #endif
 constexpr int KR = 32 * K2_KSUB;          // rows of M per stage
 constexpr int LDS_K = KR;                 // LDS row = KR bf16, 16-byte units XOR-swizzled
