@@ -354,6 +354,16 @@ psgd_status psgd_step_noalloc(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats
                               int32_t* skip_dev, hipStream_t stream);
 
 /*
+ * Step counters of a plan, for monitoring (the skip count is the figure a mixed-precision run
+ * is watched by: "AIGC 基本功|混合精度与数值稳定性-AMP", section 6.5). *counters receives the
+ * device address of two int64: [0] steps decompressed (psgd_decompress_update or
+ * psgd_decompress_adam calls that ran), [1] of those, steps skipped on non-finite values. The
+ * decompression kernel updates them on the device in stream order (no host sync); they start
+ * at 0 when the plan is made and psgd_reset_errors does not count. Owned by the plan.
+ */
+psgd_status psgd_plan_counters(psgd_plan* plan, const int64_t** counters);
+
+/*
  * Tracing hook. Install an array of n HIP events created by the caller with timing enabled.
  * While installed, the launch of each kernel in slot k is bracketed by hipEventRecord of
  * events[2k] (before) and events[2k+1] (after) on the call's stream; elapsed times between the

@@ -11,7 +11,7 @@ from .binding import (  # noqa: F401
     psgd_adam_update, psgd_decompress_adam, psgd_block_grad_enter, psgd_block_grad_exit, psgd_block_grad_exit_enter,
     psgd_check_finite, psgd_compress, psgd_compress_p, psgd_compress_q,
     psgd_create, psgd_debug_buffer, psgd_decompress_update, psgd_destroy, psgd_factor_buffer,
-    psgd_last_error, psgd_orthogonalize, psgd_plan_create, psgd_plan_destroy,
+    psgd_last_error, psgd_orthogonalize, psgd_plan_counters, psgd_plan_create, psgd_plan_destroy,
     psgd_profile_events, psgd_refresh_q, psgd_reset_errors, psgd_step_noalloc, psgd_version,
 )
 from .group import PowerSGDGroup  # noqa: F401

@@ -104,6 +104,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.psgd_reset_errors.argtypes = [vp, vp, vp]
     lib.psgd_step_noalloc.argtypes = [vp, ctypes.POINTER(psgd_matrix), ctypes.c_int, ctypes.c_int, vp,
                                       ctypes.c_int, ctypes.POINTER(psgd_tensor), ctypes.c_int, vp, vp, vp]
+    lib.psgd_plan_counters.argtypes = [vp, ctypes.POINTER(vp)]
     lib.psgd_adam_attach.argtypes = [vp, vp, ctypes.POINTER(psgd_adam_matrix), ctypes.c_int]
     lib.psgd_adam_prepare.argtypes = [vp, vp, ctypes.POINTER(psgd_adam_tensor), ctypes.c_int, ctypes.c_float,
                                       vp, vp, vp, vp]
@@ -117,7 +118,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                  "psgd_compress", "psgd_check_finite", "psgd_decompress_update",
                  "psgd_debug_buffer", "psgd_profile_events", "psgd_compress_p", "psgd_orthogonalize",
                  "psgd_compress_q", "psgd_refresh_q", "psgd_factor_buffer", "psgd_reset_errors",
-                 "psgd_step_noalloc", "psgd_adam_attach", "psgd_adam_prepare", "psgd_decompress_adam",
+                 "psgd_step_noalloc", "psgd_plan_counters", "psgd_adam_attach", "psgd_adam_prepare", "psgd_decompress_adam",
                  "psgd_adam_update", "psgd_block_grad_enter",
                  "psgd_block_grad_exit", "psgd_block_grad_exit_enter"):
         getattr(lib, name).restype = ctypes.c_int
@@ -226,6 +227,13 @@ def psgd_compress_q(ctx: int, plan: int, scale, stream=None) -> None:
 
 def psgd_refresh_q(ctx: int, plan: int, stream=None) -> None:
     _check(ctx, "psgd_refresh_q", load_library().psgd_refresh_q(ctx, plan, _stream(stream)))
+
+
+def psgd_plan_counters(plan: int) -> int:
+    """Device address of the plan's two int64 step counters (steps decompressed, steps skipped)."""
+    ptr = ctypes.c_void_p()
+    _check(None, "psgd_plan_counters", load_library().psgd_plan_counters(plan, ctypes.byref(ptr)))
+    return ptr.value
 
 
 def psgd_factor_buffer(plan: int):

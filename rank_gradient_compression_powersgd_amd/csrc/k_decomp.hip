@@ -114,8 +114,14 @@ template <> struct ParamIO<G_F32> {
 template <int GT, int PT>
 __global__ __launch_bounds__(K3_THREADS, K3_OCC)
 void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
-              const float* __restrict__ scale, const int32_t* __restrict__ skip, AdamArgs aa)
+              const float* __restrict__ scale, const int32_t* __restrict__ skip, AdamArgs aa,
+              int64_t* __restrict__ counters)
 {
+  // step counters of the plan: steps decompressed and steps skipped (one thread of the grid)
+  if (counters != nullptr && blockIdx.x == 0 && threadIdx.x == 0) {
+    counters[0] += 1;
+    counters[1] += *skip != 0 ? 1 : 0;
+  }
   const Work wi = work[xcd_remap(blockIdx.x, gridDim.x)];
   if (wi.mat < 0) return;
   const DevMat& d = mats[wi.mat];
@@ -391,17 +397,17 @@ void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
 
 template <int GT, int PT>
 hipError_t launch_gt(dim3 grid, hipStream_t s, const DevMat* mats, const Work* work,
-                     const float* scale, const int32_t* skip, const AdamArgs& aa) {
-  k_decomp<GT, PT><<<grid, dim3(K3_THREADS), 0, s>>>(mats, work, scale, skip, aa);
+                     const float* scale, const int32_t* skip, const AdamArgs& aa, int64_t* counters) {
+  k_decomp<GT, PT><<<grid, dim3(K3_THREADS), 0, s>>>(mats, work, scale, skip, aa, counters);
   return hipGetLastError();
 }
 template <int PT>
 hipError_t launch_pt(int gt, dim3 grid, hipStream_t s, const DevMat* mats, const Work* work,
-                     const float* scale, const int32_t* skip, const AdamArgs& aa) {
+                     const float* scale, const int32_t* skip, const AdamArgs& aa, int64_t* counters) {
   switch (gt) {
-    case G_F16: return launch_gt<G_F16, PT>(grid, s, mats, work, scale, skip, aa);
-    case G_BF16: return launch_gt<G_BF16, PT>(grid, s, mats, work, scale, skip, aa);
-    case G_F32: return launch_gt<G_F32, PT>(grid, s, mats, work, scale, skip, aa);
+    case G_F16: return launch_gt<G_F16, PT>(grid, s, mats, work, scale, skip, aa, counters);
+    case G_BF16: return launch_gt<G_BF16, PT>(grid, s, mats, work, scale, skip, aa, counters);
+    case G_F32: return launch_gt<G_F32, PT>(grid, s, mats, work, scale, skip, aa, counters);
   }
   return hipErrorInvalidValue;
 }
@@ -412,19 +418,19 @@ int decomp_tile_m() { return K3_TM; }
 int decomp_tile_n() { return K3_TN; }
 
 hipError_t launch_decompress(int gt, const DevMat* mats, const Work* work, int n_work,
-                             const float* scale, const int32_t* skip, hipStream_t s) {
+                             const float* scale, const int32_t* skip, int64_t* counters, hipStream_t s) {
   if (n_work <= 0) return hipSuccess;
-  return launch_pt<0>(gt, dim3(n_work), s, mats, work, scale, skip, AdamArgs{});
+  return launch_pt<0>(gt, dim3(n_work), s, mats, work, scale, skip, AdamArgs{}, counters);
 }
 
 hipError_t launch_decompress_adam(int gt, int pt, const DevMat* mats, const Work* work, int n_work,
                                   const float* scale, const int32_t* skip, const AdamArgs& aa,
-                                  hipStream_t s) {
+                                  int64_t* counters, hipStream_t s) {
   if (n_work <= 0) return hipSuccess;
   switch (pt) {
-    case G_F16: return launch_pt<G_F16>(gt, dim3(n_work), s, mats, work, scale, skip, aa);
-    case G_BF16: return launch_pt<G_BF16>(gt, dim3(n_work), s, mats, work, scale, skip, aa);
-    case G_F32: return launch_pt<G_F32>(gt, dim3(n_work), s, mats, work, scale, skip, aa);
+    case G_F16: return launch_pt<G_F16>(gt, dim3(n_work), s, mats, work, scale, skip, aa, counters);
+    case G_BF16: return launch_pt<G_BF16>(gt, dim3(n_work), s, mats, work, scale, skip, aa, counters);
+    case G_F32: return launch_pt<G_F32>(gt, dim3(n_work), s, mats, work, scale, skip, aa, counters);
   }
   return hipErrorInvalidValue;
 }

@@ -300,7 +300,7 @@ hipError_t launch_split3(const DevMat* mats, const Work* work, int n_work, hipSt
 hipError_t launch_mtp(int gt, int rtc, const DevMat* mats, const Work* work, int n_work,
                       const float* scale, hipStream_t s);
 hipError_t launch_decompress(int gt, const DevMat* mats, const Work* work, int n_work,
-                             const float* scale, const int32_t* skip, hipStream_t s);
+                             const float* scale, const int32_t* skip, int64_t* counters, hipStream_t s);
 hipError_t launch_sqnorm(const NormItem* items, int n_items, double* partial, hipStream_t s);
 hipError_t launch_adam_finalize(const double* partial, int n, float max_norm, const int32_t* skip,
                                 int32_t* step, float* norm_out, hipStream_t s);
@@ -308,7 +308,7 @@ hipError_t launch_adam_f32(const AdamTensor* ts, int n, const AdamArgs& aa, cons
                            hipStream_t s);
 hipError_t launch_decompress_adam(int gt, int pt, const DevMat* mats, const Work* work, int n_work,
                                   const float* scale, const int32_t* skip, const AdamArgs& aa,
-                                  hipStream_t s);
+                                  int64_t* counters, hipStream_t s);
 struct PassList;
 int big_split_tile();
 int big_gemm_tile_m();

@@ -78,6 +78,7 @@ struct psgd_plan {
   int bg_cnt[kMaxBlocks][2] = {{0}};
   int32_t* d_one = nullptr;              // a device word holding 1: the decompression's skip
                                          // word for psgd_reset_errors
+  int64_t* d_counters = nullptr;         // steps decompressed, steps skipped
   // optimizer attachment (psgd_adam_attach)
   int adam_pt = 0;                       // parameter type, 0 = none attached
   void* adam_buf = nullptr;              // norm items (q_next ranges, then pass-through ranges)
@@ -193,6 +194,7 @@ struct PlanLayout {
   std::vector<Work> all;       // every work list, concatenated (offsets in psgd_plan::off)
   size_t ws = 0;               // workspace bytes (a multiple of 256)
   size_t one_off = 0;          // offset of the constant word 1
+  size_t counters_off = 0;     // offset of the two step counters
   size_t praw_total = 0;       // bytes of the contiguous raw-factor region at offset 0
 };
 
@@ -316,6 +318,7 @@ psgd_status plan_layout(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats, psgd
   }
 
   L.one_off = take(4);
+  L.counters_off = take(16);
 
   // ---- work lists -------------------------------------------------------------------------
   std::vector<Work>& all = L.all;
@@ -518,6 +521,7 @@ void plan_bind(psgd_plan* p, char* base, const PlanLayout& L) {
   p->ws_bytes = L.ws;
   p->praw_bytes = L.praw_total;
   p->d_one = reinterpret_cast<int32_t*>(base + L.one_off);
+  p->d_counters = reinterpret_cast<int64_t*>(base + L.counters_off);
 }
 
 }  // namespace
@@ -718,7 +722,7 @@ psgd_status psgd_decompress_update(psgd_ctx* ctx, psgd_plan* plan, const float* 
   HIPCHK(ctx, hipSetDevice(ctx->device), "hipSetDevice");
   const DevMat* dm = plan->d_mats;
   auto W = [&](int k) { return plan->d_work + plan->off[k]; };
-  HIPCHK(ctx, traced(ctx, S_K3, stream, [&] { return psgd::launch_decompress(plan->gt, dm, W(W_K3), plan->cnt[W_K3], scale, skip_dev, stream); }), "decompress");
+  HIPCHK(ctx, traced(ctx, S_K3, stream, [&] { return psgd::launch_decompress(plan->gt, dm, W(W_K3), plan->cnt[W_K3], scale, skip_dev, plan->d_counters, stream); }), "decompress");
   return PSGD_OK;
 }
 
@@ -730,7 +734,7 @@ psgd_status psgd_reset_errors(psgd_ctx* ctx, psgd_plan* plan, hipStream_t stream
   // the decompression's skipped form zeroes every error buffer and touches nothing else (no
   // scale is read on that path; the pointer only has to be valid)
   const float* any_scale = reinterpret_cast<const float*>(plan->d_one);
-  HIPCHK(ctx, traced(ctx, S_K3, stream, [&] { return psgd::launch_decompress(plan->gt, plan->d_mats, plan->d_work + plan->off[W_K3], plan->cnt[W_K3], any_scale, plan->d_one, stream); }), "error buffer reset");
+  HIPCHK(ctx, traced(ctx, S_K3, stream, [&] { return psgd::launch_decompress(plan->gt, plan->d_mats, plan->d_work + plan->off[W_K3], plan->cnt[W_K3], any_scale, plan->d_one, nullptr, stream); }), "error buffer reset");
   return PSGD_OK;
 }
 
@@ -942,7 +946,7 @@ psgd_status psgd_decompress_adam(psgd_ctx* ctx, psgd_plan* plan, const float* sc
   const psgd::AdamArgs aa = adam_args(hp, step_dev, norm_dev);
   HIPCHK(ctx, traced(ctx, S_K3_ADAM, stream, [&] {
     return psgd::launch_decompress_adam(plan->gt, plan->adam_pt, plan->d_mats, plan->d_work + plan->off[W_K3],
-                                        plan->cnt[W_K3], scale, skip_dev, aa, stream); }), "decompression with Adam");
+                                        plan->cnt[W_K3], scale, skip_dev, aa, plan->d_counters, stream); }), "decompression with Adam");
   return PSGD_OK;
 }
 
@@ -974,6 +978,12 @@ psgd_status psgd_profile_events(psgd_ctx* ctx, hipEvent_t* events, int n) {
   }
   if (n < 2 * S_SLOTS) return fail(ctx, PSGD_EINVAL, "need at least %d events, got %d", 2 * S_SLOTS, n);
   ctx->events.assign(events, events + 2 * S_SLOTS);
+  return PSGD_OK;
+}
+
+psgd_status psgd_plan_counters(psgd_plan* plan, const int64_t** counters) {
+  if (!plan || !counters) return PSGD_EINVAL;
+  *counters = plan->d_counters;
   return PSGD_OK;
 }
 

@@ -63,6 +63,20 @@ class PowerSGDGroup:
     def decompress_update(self, stream=None):
         B.psgd_decompress_update(self.ctx, self.plan, self.scale, self.skip, stream)
 
+    def counters(self):
+        """(steps decompressed, steps skipped): the plan's device counters, copied to the host
+        after a device synchronisation."""
+        import ctypes
+        self.torch.cuda.synchronize()
+        addr = B.psgd_plan_counters(self.plan)
+        out = (ctypes.c_int64 * 2)()
+        hip = ctypes.CDLL("libamdhip64.so.7")
+        hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+        err = hip.hipMemcpy(ctypes.addressof(out), addr, 16, 2)          # device to host
+        if err != 0:
+            raise RuntimeError(f"hipMemcpy of the step counters failed ({err})")
+        return int(out[0]), int(out[1])
+
     def reset_errors(self, stream=None):
         """E = 0 for every matrix: resuming from a checkpoint, which holds no error buffers."""
         B.psgd_reset_errors(self.ctx, self.plan, stream)
