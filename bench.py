@@ -81,10 +81,14 @@ def parse(argv=None):
     ap.add_argument("--graph", action="store_true",
                     help="only time the step captured once as a HIP graph and replayed (compress, "
                          "device-side finite check, decompress/update); one JSON line")
+    ap.add_argument("--trace-summary", metavar="CSV", default=None,
+                    help="only summarise a rocprofv3 --kernel-trace CSV: launches, average and "
+                         "per-step time of each library kernel")
     ap.add_argument("--pmc-summary", metavar="DIR", default=None,
-                    help="only summarise rocprofv3 --pmc CSV output: DIR holds pmc_FETCH_SIZE/, "
-                         "pmc_WRITE_SIZE/ (bench runs) and pmccopy_FETCH_SIZE/, pmccopy_WRITE_SIZE/ "
-                         "(copy calibration runs); prints per-kernel HBM bytes per launch")
+                    help="only summarise rocprofv3 --pmc CSV output found under DIR: pmc_FETCH_SIZE/, "
+                         "pmc_WRITE_SIZE/ (bench runs) with pmccopy_FETCH_SIZE/, "
+                         "pmccopy_WRITE_SIZE/ (copy calibration runs) give per-kernel HBM bytes "
+                         "per launch; pmc_MFMA/ MFMA use; pmc_LDS/ LDS bank conflicts")
     return ap.parse_args(argv)
 
 
@@ -141,6 +145,27 @@ def _pmc_means(path: str, counter: str):
 
 
 def pmc_summary(d: str) -> int:
+    """Summarise the counter runs found under d: HBM traffic (pmc_FETCH_SIZE/, pmc_WRITE_SIZE/
+    with the copy calibration in pmccopy_FETCH_SIZE/, pmccopy_WRITE_SIZE/), MFMA use
+    (pmc_MFMA/) and LDS bank conflicts (pmc_LDS/)."""
+    done = False
+    if os.path.isdir(os.path.join(d, "pmc_FETCH_SIZE")):
+        if traffic_summary(d):
+            return 1
+        done = True
+    if os.path.isdir(os.path.join(d, "pmc_MFMA")):
+        mfma_summary(os.path.join(d, "pmc_MFMA"))
+        done = True
+    if os.path.isdir(os.path.join(d, "pmc_LDS")):
+        lds_summary(os.path.join(d, "pmc_LDS"))
+        done = True
+    if not done:
+        print(f"no counter runs under {d}", file=sys.stderr)
+        return 1
+    return 0
+
+
+def traffic_summary(d: str) -> int:
     fe = _pmc_means(os.path.join(d, "pmc_FETCH_SIZE"), "FETCH_SIZE")
     wr = _pmc_means(os.path.join(d, "pmc_WRITE_SIZE"), "WRITE_SIZE")
     cf = _pmc_means(os.path.join(d, "pmccopy_FETCH_SIZE"), "FETCH_SIZE")
@@ -159,7 +184,8 @@ def pmc_summary(d: str) -> int:
     numel = 1511522304
     qcommit = 4 * 81772544             # the decompression also writes q <- q_next (sum of n x r fp32)
     algo = {"k_ef_mq": 6 * numel, "k_mtp": 6 * numel, "k_decomp": 14 * numel + qcommit}
-    print(f"{'kernel':34s} {'launches':>8s} {'fetch GB':>9s} {'write GB':>9s} {'total GB':>9s} {'algorithmic GB':>15s}")
+    print(f"{'kernel':34s} {'launches':>8s} {'fetch GB':>9s} {'write GB':>9s} {'total GB':>9s} "
+          f"{'algorithmic GB':>15s} {'ratio':>6s}")
     for k in sorted(fe):
         if not k.startswith("k_"):
             continue
@@ -168,34 +194,90 @@ def pmc_summary(d: str) -> int:
         base = k.split("<")[0]
         a = algo.get(base)
         print(f"{k:34s} {fe[k][1]:8d} {f / 1e9:9.3f} {w / 1e9:9.3f} {(f + w) / 1e9:9.3f} "
-              f"{(a / 1e9 if a else float('nan')):15.3f}")
+              f"{(a / 1e9 if a else float('nan')):15.3f} {((f + w) / a if a else float('nan')):6.3f}")
         if base in ("k_ef_mq", "k_mtp", "k_decomp"):
             print(f"TRAFFIC {KERNEL_SLOT[base]} {int(f + w)} fetch {int(f)} write {int(w)} source {kernel_source_hash()}")
-    mf = os.path.join(d, "pmc_MFMA")
-    if os.path.isdir(mf):
-        busy = _pmc_values(mf, "SQ_VALU_MFMA_BUSY_CYCLES")
-        gui = _pmc_values(mf, "GRBM_GUI_ACTIVE")
-        mops = {t: _pmc_values(mf, f"SQ_INSTS_VALU_MFMA_MOPS_{t.upper()}") for t in ("bf16", "f16", "f64")}
-        print()
-        print("MFMA counters, mean over the launches that multiply (a second-pass launch that returns at")
-        print("once is left out): busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs);")
-        print("flops = 512 x SQ_INSTS_VALU_MFMA_MOPS_<type>")
-        print(f"{'kernel':34s} {'launches':>8s} {'busy':>6s} {'bf16 GFLOP':>11s} {'f16 GFLOP':>10s} {'f64 GFLOP':>10s}")
-        for k in sorted(busy):
-            if not k.startswith("k_") or k not in gui:
-                continue
-            ids = [i for i in busy[k] if sum(mops[t].get(k, {}).get(i, 0.0) for t in mops) > 0]
-            if not ids:
-                continue
-            cyc = sum(gui[k][i] for i in ids) / 8.0
-            frac = sum(busy[k][i] for i in ids) / (cyc * 1024.0) if cyc > 0 else 0.0
-            fl = {t: sum(mops[t].get(k, {}).get(i, 0.0) for i in ids) / len(ids) * 512.0 for t in mops}
-            print(f"{k:34s} {len(ids):8d} {frac:6.3f} {fl['bf16'] / 1e9:11.1f} {fl['f16'] / 1e9:10.1f} "
-                  f"{fl['f64'] / 1e9:10.1f}")
-            base = k.split("<")[0]
-            if base in KERNEL_SLOT and any(fl.values()):
-                print(f"MFMA {KERNEL_SLOT[base]} busy {frac:.4f} bf16 {int(fl['bf16'])} f16 {int(fl['f16'])} "
-                      f"f64 {int(fl['f64'])} source {kernel_source_hash()}")
+    return 0
+
+
+def mfma_summary(mf: str) -> None:
+    busy = _pmc_values(mf, "SQ_VALU_MFMA_BUSY_CYCLES")
+    gui = _pmc_values(mf, "GRBM_GUI_ACTIVE")
+    mops = {t: _pmc_values(mf, f"SQ_INSTS_VALU_MFMA_MOPS_{t.upper()}") for t in ("bf16", "f16", "f64")}
+    print()
+    print("MFMA counters, mean over the launches that multiply (a second-pass launch that returns at")
+    print("once is left out): busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs);")
+    print("flops = 512 x SQ_INSTS_VALU_MFMA_MOPS_<type>")
+    print(f"{'kernel':34s} {'launches':>8s} {'busy':>6s} {'bf16 GFLOP':>11s} {'f16 GFLOP':>10s} {'f64 GFLOP':>10s}")
+    for k in sorted(busy):
+        if not k.startswith("k_") or k not in gui:
+            continue
+        ids = [i for i in busy[k] if sum(mops[t].get(k, {}).get(i, 0.0) for t in mops) > 0]
+        if not ids:
+            continue
+        cyc = sum(gui[k][i] for i in ids) / 8.0
+        frac = sum(busy[k][i] for i in ids) / (cyc * 1024.0) if cyc > 0 else 0.0
+        fl = {t: sum(mops[t].get(k, {}).get(i, 0.0) for i in ids) / len(ids) * 512.0 for t in mops}
+        print(f"{k:34s} {len(ids):8d} {frac:6.3f} {fl['bf16'] / 1e9:11.1f} {fl['f16'] / 1e9:10.1f} "
+              f"{fl['f64'] / 1e9:10.1f}")
+        base = k.split("<")[0]
+        if base in KERNEL_SLOT and any(fl.values()):
+            print(f"MFMA {KERNEL_SLOT[base]} busy {frac:.4f} bf16 {int(fl['bf16'])} f16 {int(fl['f16'])} "
+                  f"f64 {int(fl['f64'])} source {kernel_source_hash()}")
+
+
+def lds_summary(ld: str) -> None:
+    conf = _pmc_values(ld, "SQ_LDS_BANK_CONFLICT")
+    act = _pmc_values(ld, "SQ_LDS_IDX_ACTIVE")
+    insts = _pmc_values(ld, "SQ_INSTS_LDS")
+    print()
+    print("LDS counters, summed over the launches that use LDS: conflict = SQ_LDS_BANK_CONFLICT /")
+    print("SQ_LDS_IDX_ACTIVE (share of the cycles the LDS spent on indexed accesses that were bank-")
+    print("conflict stalls); instructions = SQ_INSTS_LDS per launch")
+    print(f"{'kernel':34s} {'launches':>8s} {'conflict':>9s} {'active Mcyc':>12s} {'LDS Minst':>10s}")
+    for k in sorted(act):
+        if not k.startswith("k_"):
+            continue
+        ids = [i for i in act[k] if act[k][i] > 0]
+        if not ids:
+            continue
+        a = sum(act[k][i] for i in ids)
+        c = sum(conf.get(k, {}).get(i, 0.0) for i in ids)
+        n = sum(insts.get(k, {}).get(i, 0.0) for i in ids) / len(ids)
+        print(f"{k:34s} {len(ids):8d} {c / a:9.3f} {a / len(ids) / 1e6:12.2f} {n / 1e6:10.2f}")
+
+
+def trace_summary(path: str) -> int:
+    """Per-kernel table of a rocprofv3 --kernel-trace CSV (library kernels only). Steps are
+    counted by the finite check, which runs once per step; k_gemm_nt, launched twice per step
+    (M q, then M^T P_hat), is split by launch order."""
+    import csv
+    rows = []
+    for row in csv.DictReader(open(path)):
+        if "psgd::" not in row["Kernel_Name"]:
+            continue
+        rows.append((int(row["Start_Timestamp"]), _short_kernel(row["Kernel_Name"]),
+                     (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) * 1e-3))
+    rows.sort()
+    steps = sum(1 for r in rows if r[1] == "k_check_finite")
+    if steps == 0:
+        print("no library step in the trace", file=sys.stderr)
+        return 1
+    per = {}
+    gemm = 0
+    for _, k, us in rows:
+        if k == "k_gemm_nt":
+            k = "k_gemm_nt (M q)" if gemm % 2 == 0 else "k_gemm_nt (M^T P_hat)"
+            gemm += 1
+        per.setdefault(k, []).append(us)
+    tot = sum(sum(v) for v in per.values())
+    print(f"{steps} steps (warm-up included), {len(rows)} library kernel launches")
+    print("| kernel | launches | average us | ms per step | share |")
+    print("|---|---|---|---|---|")
+    for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        print(f"| {k} | {len(v)} | {sum(v) / len(v):.1f} | {sum(v) / steps / 1e3:.3f} | "
+              f"{100 * sum(v) / tot:.1f}% |")
+    print(f"| all library kernels | {len(rows)} | | {tot / steps / 1e3:.3f} | |")
     return 0
 
 
@@ -552,6 +634,8 @@ def main(argv=None) -> int:
     a = parse(argv)
     if a.pmc_summary:
         return pmc_summary(a.pmc_summary)
+    if a.trace_summary:
+        return trace_summary(a.trace_summary)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (--gpus {a.gpus}, WORLD_SIZE {world}): the "

@@ -137,6 +137,9 @@ psgd_status psgd_plan_destroy(psgd_plan* plan);
 
 /*
  * Compression: for every matrix, M = s_b G + E, P = orthonormalise(M q), q_next = M^T P.
+ * This is the low-rank factorisation of the gradient with an error buffer and a warm-started
+ * factor ("Zero-Shot Text-to-Image Generation — 中文验证版", section 方法适配; Korean summary
+ * of the paper, section "Distributed Optimization"), at the rank of the plan.
  * Writes p, q_next and flags[i] = 1 when any element of G_i or E_i is +-inf or NaN (else 0).
  * Reads E and q without modifying them.
  *  scale  device fp32[n_blocks], the per-resblock multipliers s_b.
