@@ -53,9 +53,14 @@ constexpr int K1_THREADS = K1_W * kWave;
 constexpr int KS = 32 * K1_KSUB;       // k columns per stage
 constexpr int LDS_K = KS;              // LDS row = KS bf16; 16-byte units XOR-swizzled by row
 static_assert(KS == 64, "the LDS swizzle assumes 8 units per row");
-// Physical 16-byte unit of logical unit q in row rr: with 128-byte rows, the 16 lanes of an
-// MFMA fragment read (16 consecutive rows, one unit each) hit 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int swz1(int rr, int q) { return q ^ ((rr >> 1) & 7); }
+// Physical 16-byte unit of logical unit q in row rr. The LDS serves a 16-byte read 8 lanes
+// per pass over 32 four-byte banks, and every 128-byte row starts on bank 0, so an MFMA
+// fragment read (8 consecutive rows from a multiple of 8, one logical unit) is conflict-free
+// when those rows land on 8 distinct units: rr & 7 runs over 0..7 and rr >> 2 takes two values
+// that differ only in bit 0, so XOR-ing them permutes the 8 units. The same mixing spreads the
+// transposed warm-start stores (rows 4 g + e for consecutive rank groups g) over all 8 units
+// of a k position; (rr >> 1) & 7 reached only 4.
+__device__ __forceinline__ int swz1(int rr, int q) { return q ^ ((rr ^ (rr >> 2)) & 7); }
 
 // coalesced M loads: 16 lanes per row, 4 columns per lane
 constexpr int LCOL = KS / 4;                    // lanes per row (16)
@@ -102,8 +107,11 @@ void k_ef_mq(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   // rc0 + RC - 1, split into bf16 hi + lo and transposed into ldq[hi/lo][rank][k]. A unit is 4
   // consecutive ranks of the two rows k, k + 1: consecutive threads take consecutive rank
   // groups of a row pair (coalesced reads of q), and every rank's (k, k + 1) pair becomes one
-  // 4-byte LDS store. Rows past n and ranks past r read zeros. Threads past the last unit
-  // repeat it (same values to the same LDS addresses), so the code has no branch.
+  // 4-byte LDS store. The threads of a store pass share k, so those stores keep a few-way bank
+  // conflict; giving consecutive threads 4 consecutive row pairs instead removes it but cuts
+  // the reads of q into 256-byte pieces, and the kernel ran slower (1.93 -> 2.06 ms on the
+  // 64-resblock rank-112 shard). Rows past n and ranks past r read zeros. Threads past the last
+  // unit repeat it (same values to the same LDS addresses), so the code has no branch.
   constexpr int RG = RC / 4;                    // rank groups per row
   constexpr int QUNITS = (KS / 2) * RG;
   constexpr int UPT = (QUNITS + K1_THREADS - 1) / K1_THREADS;

@@ -46,11 +46,13 @@ namespace {
 constexpr int KR = 32 * K2_KSUB;          // rows of M per stage
 constexpr int LDS_K = KR;                 // LDS row = KR bf16, 16-byte units XOR-swizzled
 constexpr int UPR = KR / 8;               // 16-byte units per LDS row
-// Physical unit of logical unit q in row rr: the 16 lanes of a fragment read (16 consecutive
-// rows, one unit each) hit 16 distinct 16-byte bank groups.
+// Physical unit of logical unit q in row rr. The LDS serves a 16-byte read 8 lanes per pass
+// over 32 four-byte banks (128 bytes), so the 8 consecutive rows a fragment read takes in one
+// pass must land on 8 distinct 16-byte groups: with 64-byte rows, rr & 1 picks the half of the
+// 128 bytes and (rr >> 1) & 3 the unit in it; with 128-byte rows, the low 3 bits of rr do.
 __device__ __forceinline__ int swz2(int rr, int q) {
-  if constexpr (UPR == 4) return q ^ ((rr >> 2) & 3);
-  else return q ^ ((rr >> 1) & 7);
+  if constexpr (UPR == 4) return q ^ ((rr >> 1) & 3);
+  else return q ^ (rr & 7);
 }
 static_assert(UPR == 4 || UPR == 8, "stage of 32 or 64 rows");
 constexpr int TC = K2_TC;
