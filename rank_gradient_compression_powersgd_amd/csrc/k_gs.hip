@@ -15,7 +15,9 @@
 //              from the running Gram matrix, which is updated as columns are projected out.
 //              This gives the upper-triangular T with P T orthonormal, T = R^-1 of the thin
 //              QR. fp64, one workgroup per matrix, W and T resident in LDS, in 16-column
-//              panels (one wave per diagonal panel, fp64 MFMA block updates).
+//              panels (one wave per diagonal panel, its pivots read through the scalar
+//              unit and its column values moved by DPP row broadcasts; fp64 MFMA block
+//              updates).
 //              A column whose remaining squared norm is at most 2^-40 of its original squared
 //              norm (or zero, or not finite) is dependent: its column of T is set to zero.
 //   second pass The Gram form loses orthogonality as eps_64 times the squared condition
@@ -200,20 +202,60 @@ __device__ __forceinline__ void fblock_mm(double* C, const double* A, bool trans
   }
 }
 
+// Value of x in lane `lane` (wave-uniform lane index), through the scalar unit.
+__device__ __forceinline__ double readlane_f64(double x, int lane) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Value of x in lane l (0..15) of the calling lane's 16-lane row (DPP row_newbcast; l must
+// fold to a constant).
+__device__ __forceinline__ int row_bcast_i32(int v, int l) {
+  switch (l) {
+#define RB(L) case L: return __builtin_amdgcn_update_dpp(0, v, 0x150 + L, 0xF, 0xF, false);
+    RB(0) RB(1) RB(2) RB(3) RB(4) RB(5) RB(6) RB(7)
+    RB(8) RB(9) RB(10) RB(11) RB(12) RB(13) RB(14) RB(15)
+#undef RB
+  }
+  return v;
+}
+__device__ __forceinline__ double row_bcast_f64(double x, int l) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)row_bcast_i32((int)(uint32_t)u, l);
+  const uint32_t hi = (uint32_t)row_bcast_i32((int)(uint32_t)(u >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// 1 / sqrt(x) for a positive normal x: the hardware estimate refined by two Newton steps
+// (e = 1 - x y^2, y += y e / 2), within a few ulp. The steps commute with scaling x by a power
+// of 4, so scaled inputs give exactly scaled results.
+__device__ __forceinline__ double rsqrt_f64(double x) {
+  double y = __builtin_amdgcn_rsq(x);
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const double e = __builtin_fma(-x, y * y, 1.0);
+    y = __builtin_fma(0.5 * y, e, y);
+  }
+  return y;
+}
+
 // The panel recurrence on nb panels held in LDS: Wb (upper block triangle of the residual
 // Gram matrix), Ub (I on entry; T on return), d0 (each column's squared norm before any
-// projection). All GSF_THREADS threads call it; wave 0 returns the smallest squared residual
-// ratio of a kept column (1 if none is kept), the other waves 1.
-__device__ __forceinline__ double factor_panels(double* Wb, double* Ub, double* Lsh, const double* d0, int nb)
+// projection). All GSF_THREADS threads call it; wave 0 returns whether a kept column retained
+// less than 2^-20 of its squared norm (the second-pass test), the other waves false.
+__device__ __forceinline__ bool factor_panels(double* Wb, double* Ub, double* Lsh, const double* d0, int nb)
 {
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
   constexpr int NWV = GSF_THREADS / kWave;
   const int c = lane & 15, g = lane >> 4;
-  double minratio = 1.0;
+  bool again = false;
   for (int p = 0; p < nb; ++p) {
     // (A) diagonal block: lane 16g + c holds rows g + 4i, column c, of the residual Gram block
-    // (a) and of the local factor (l).
+    // (a) and of the local factor (l). The pivot and its inverse square root are wave-uniform:
+    // the pivot is read through the scalar unit and the scaling is branch-free.
     if (wv == 0) {
       const double* Wpp = &Wb[fblk(p, p, nb) * FBS];
       double a[4], l[4];
@@ -222,29 +264,35 @@ __device__ __forceinline__ double factor_panels(double* Wb, double* Ub, double* 
         a[i] = Wpp[(g + 4 * i) * FBP + c];
         l[i] = (g + 4 * i == c) ? 1.0 : 0.0;
       }
-#pragma unroll
+#pragma clang loop unroll(full)
       for (int jj = 0; jj < FB; ++jj) {
         const int gj = jj & 3, ij = jj >> 2;       // holder of row jj: lanes 16 gj + x, register ij
-        const double dj = __shfl(a[ij], 16 * gj + jj);
+        // The lane's coordinates pass through an empty asm statement each step, so that the
+        // per-lane conditions of the step are formed where they are used: hoisted out of the
+        // unrolled steps they took 96 lane masks and spilled scalar registers.
+        int cs = c, gs = g;
+        asm volatile("" : "+v"(cs), "+v"(gs));
+        const double dj = readlane_f64(a[ij], 16 * gj + jj);
         const double dz = d0[p * FB + jj];
         const bool ok = (dz > 0.0) && (dj > kDegenerate * dz) && (dj <= 1.0e300);
-        const double inv = ok ? 1.0 / sqrt(dj) : 0.0;
-        if (ok) minratio = fmin(minratio, dj / dz);
-        // row jj of the residual block, scaled: r[x] = a[jj][x] / ||v_jj||
-        const double rc = __shfl(a[ij], 16 * gj + c) * inv;
+        const double y = rsqrt_f64(ok ? dj : 1.0);
+        const double inv = ok ? y : 0.0;
+        again |= ok && dj < kReorth * dz;
+        // row jj of the residual block, scaled: r[x] = a[jj][x] / ||v_jj||. Lane 16g + c needs
+        // r[c] (held in row group gj: a shuffle across rows) and r[g + 4i] = a[g + 4i][jj] (the
+        // block is symmetric), held by lane jj of its own row group (a row broadcast).
+        const double rc = __shfl(a[ij], 16 * gj + cs) * inv;
         double rrow[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rrow[i] = __shfl(a[ij], 16 * gj + g + 4 * i) * inv;
+        for (int i = 0; i < 4; ++i) rrow[i] = row_bcast_f64(a[i], jj) * inv;
         // local factor: column jj scaled, then removed from the later columns
-        if (c == jj) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) l[i] *= inv;
-        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const double lj = __shfl(l[i], 16 * g + jj);
-          if (c > jj) l[i] -= rc * lj;
-          if (c > jj && g + 4 * i > jj) a[i] -= rrow[i] * rc;
+          const double lj = row_bcast_f64(l[i], jj) * inv;   // L[g + 4i][jj], scaled
+          const double ls = cs == jj ? lj : l[i];
+          l[i] = cs > jj ? l[i] - rc * lj : ls;
+          const double as = a[i] - rrow[i] * rc;
+          a[i] = (cs > jj && gs + 4 * i > jj) ? as : a[i];
         }
       }
 #pragma unroll
@@ -280,7 +328,7 @@ __device__ __forceinline__ double factor_panels(double* Wb, double* Ub, double* 
     }
     __syncthreads();
   }
-  return minratio;
+  return again;
 }
 
 // row-major element (row, col) of the block layout (upper block triangle only)
@@ -323,8 +371,8 @@ void k_gs_factor(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   }
   __syncthreads();
 
-  const double minratio = factor_panels(Wb, Ub, Lsh, diag0, nb);
-  if (pass == 0 && threadIdx.x == 0) *gbl(d.reorth) = minratio < kReorth ? 1 : 0;
+  const bool again = factor_panels(Wb, Ub, Lsh, diag0, nb);
+  if (pass == 0 && threadIdx.x == 0) *gbl(d.reorth) = again ? 1 : 0;
 
   // T (row-major rpad x rpad; zero below the block diagonal)
   for (int e = threadIdx.x; e < rp * rp; e += GSF_THREADS) {
@@ -374,10 +422,9 @@ void k_gs_fdiag(const DevMat* __restrict__ mats, const Work* __restrict__ work, 
   for (int i = threadIdx.x; i < bs; i += GSF_THREADS) diag0[i] = wd[k0 + i];
   __syncthreads();
 
-  const double minratio = factor_panels(Wb, Ub, Lsh, diag0, nb);
+  const bool again = factor_panels(Wb, Ub, Lsh, diag0, nb);
   if (pass == 0 && threadIdx.x == 0) {
-    const int again = minratio < kReorth ? 1 : 0;
-    if (kb == 0) *gbl(d.reorth) = again;
+    if (kb == 0) *gbl(d.reorth) = again ? 1 : 0;
     else if (again) *gbl(d.reorth) = 1;
   }
   for (int e = threadIdx.x; e < bs * bs; e += GSF_THREADS) {
