@@ -1,5 +1,6 @@
 // C ABI of libpsgd.so: contexts, plans (validated descriptor tables + workspace) and the three
 // step calls, each enqueuing grouped kernels on the caller's stream.
+#include <cmath>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -904,7 +905,8 @@ psgd_status check_hparams(psgd_ctx* ctx, const psgd_adam_hparams* hp) {
   if (!hp) return fail(ctx, PSGD_EINVAL, "hyperparameters are required");
   if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
     return fail(ctx, PSGD_EINVAL, "betas must lie in [0, 1)");
-  if (!(hp->eps >= 0.0f) || !(hp->lr >= 0.0f) || !(hp->weight_decay >= 0.0f))
+  if (!(hp->eps >= 0.0f) || !(hp->lr >= 0.0f) || !(hp->weight_decay >= 0.0f) ||
+      !std::isfinite(hp->eps) || !std::isfinite(hp->lr) || !std::isfinite(hp->weight_decay))
     return fail(ctx, PSGD_EINVAL, "lr, eps and weight_decay must be finite and >= 0");
   return PSGD_OK;
 }

@@ -377,3 +377,59 @@ def test_fp32_gradients_fp16_params_counters_and_reset():
     import torch
     counts = _free_running([(130, 96), (64, 200)], "f32", "f16", 24, 4, 9_400_000)
     assert counts == (4, 1), counts
+
+
+def test_optimizer_arguments_rejected():
+    """Bad optimizer calls return PSGD_EINVAL / PSGD_EDTYPE before anything is launched: calls
+    before an attachment, unknown or mismatched parameter formats, hyperparameters outside
+    their ranges (beta = 1, negative or infinite lr, NaN eps), missing device words; the
+    optimizer state and the step count are untouched."""
+    import torch
+    from rank_gradient_compression_powersgd_amd import PowerSGDGroup
+    from rank_gradient_compression_powersgd_amd import binding as B
+    dev = torch.device("cuda", 0)
+    shape, rank = (64, 96), 8
+    rng = np.random.default_rng(9_500_000)
+    g = torch.from_numpy(wl.to_fp16(rng.standard_normal(shape))).to(dev)
+    q0 = [torch.from_numpy(rng.standard_normal((shape[1], rank)).astype(np.float32))]
+    scale = torch.ones(1, dtype=torch.float32, device=dev)
+    group = PowerSGDGroup([g], [0], scale, rank, q0)
+    step = torch.zeros(1, dtype=torch.int32, device=dev)
+    norm = torch.zeros(2, dtype=torch.float32, device=dev)
+    try:
+        with pytest.raises(B.PsgdError) as ei:        # nothing attached yet
+            B.psgd_adam_prepare(group.ctx, group.plan, [], 1.0, group.skip, step, norm)
+        assert ei.value.status == B.PSGD_EINVAL and "attach" in str(ei.value)
+        with pytest.raises(B.PsgdError) as ei:
+            B.psgd_decompress_adam(group.ctx, group.plan, scale, group.skip, step, norm, HP)
+        assert ei.value.status == B.PSGD_EINVAL
+        param = torch.zeros(shape, dtype=torch.float16, device=dev)
+        m1 = torch.zeros(shape, dtype=torch.int16, device=dev)
+        m2 = torch.zeros(shape, dtype=torch.int16, device=dev)
+        opt = [B.make_adam_matrix(param, m1, m2)]
+        with pytest.raises(B.PsgdError) as ei:        # unknown parameter format
+            B.psgd_adam_attach(group.ctx, group.plan, opt, 9)
+        assert ei.value.status == B.PSGD_EDTYPE
+        with pytest.raises(B.PsgdError):              # moments of another shape
+            B.make_adam_matrix(param, m1[:, :64], m2)
+        group.attach_adam([param], [m1], [m2])
+        group.compress()
+        group.check_finite()
+        for bad in (oracle.AdamHyper(beta1=1.0), oracle.AdamHyper(beta2=-0.1), oracle.AdamHyper(lr=-1e-3),
+                    oracle.AdamHyper(lr=float("inf")), oracle.AdamHyper(eps=float("nan")),
+                    oracle.AdamHyper(weight_decay=float("inf"))):
+            with pytest.raises(B.PsgdError) as ei:
+                B.psgd_decompress_adam(group.ctx, group.plan, scale, group.skip, group.adam_step,
+                                       group.adam_norm, bad)
+            assert ei.value.status == B.PSGD_EINVAL, bad
+            with pytest.raises(B.PsgdError) as ei:
+                B.psgd_adam_update(group.ctx, [], group.skip, group.adam_step, group.adam_norm, bad)
+            assert ei.value.status == B.PSGD_EINVAL, bad
+        with pytest.raises(B.PsgdError) as ei:        # no device step word
+            B.psgd_adam_prepare(group.ctx, group.plan, [], 1.0, group.skip, None, group.adam_norm)
+        assert ei.value.status == B.PSGD_EINVAL
+        torch.cuda.synchronize()
+        assert int(group.adam_step.item()) == 0
+        assert int(param.abs().max().item()) == 0 and int(m1.abs().max()) == 0 and int(m2.abs().max()) == 0
+    finally:
+        group.close()
