@@ -369,6 +369,46 @@ psgd_status plan_layout(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats, psgd
     }
     p->cnt[k] = (int)all.size() - p->off[k];
   };
+  // GEMM lists: the rank tiles of one row tile form a group that shares its A tile in one XCD's
+  // L2. Groups go to the XCD with the least work so far, longest first, so that each XCD gets
+  // its share of the long items (contiguous eighths of the matrix-ordered list gave the XCDs
+  // holding the 15872-long products up to twice the others' work at r = 896); each XCD's
+  // segment, longest first, is then padded to the longest segment.
+  auto end_kind_groups = [&](int k, int gsize) {
+    cost.resize(all.size(), 0);
+    const int beg = p->off[k], n = (int)all.size() - beg;
+    std::vector<int> gstart;
+    for (int j = 0; j < n; j += gsize) gstart.push_back(j);
+    auto gcost = [&](int gi) {
+      int64_t c = 0;
+      for (int j = gstart[gi]; j < std::min(n, gstart[gi] + gsize); ++j) c += cost[beg + j];
+      return c;
+    };
+    std::vector<int> order(gstart.size());
+    for (size_t gi = 0; gi < order.size(); ++gi) order[gi] = (int)gi;
+    std::stable_sort(order.begin(), order.end(), [&](int u, int v) { return gcost(u) > gcost(v); });
+    std::vector<std::vector<int>> seg(psgd::kXcds);
+    int64_t load[psgd::kXcds] = {};
+    for (int gi : order) {
+      int x = 0;
+      for (int y = 1; y < psgd::kXcds; ++y) if (load[y] < load[x]) x = y;
+      load[x] += gcost(gi);
+      for (int j = gstart[gi]; j < std::min(n, gstart[gi] + gsize); ++j) seg[x].push_back(beg + j);
+    }
+    size_t per = 0;
+    for (const auto& sg : seg) per = std::max(per, sg.size());
+    std::vector<Work> out;
+    std::vector<int64_t> oc;
+    for (const auto& sg : seg) {
+      for (int u : sg) { out.push_back(all[u]); oc.push_back(cost[u]); }
+      for (size_t j = sg.size(); j < per; ++j) { out.push_back(Work{-1, 0, 0, 0}); oc.push_back(0); }
+    }
+    all.resize(beg);
+    cost.resize(beg);
+    all.insert(all.end(), out.begin(), out.end());
+    cost.insert(cost.end(), oc.begin(), oc.end());
+    p->cnt[k] = (int)all.size() - p->off[k];
+  };
   auto push = [&](Work w, int64_t c) {
     all.push_back(w);
     cost.resize(all.size(), 0);
@@ -406,13 +446,13 @@ psgd_status plan_layout(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats, psgd
     for (int i = 0; i < n_mats; ++i)
       for (int i0 = 0; i0 < p->mats[i].m; i0 += gtm)
         for (int j0 = 0; j0 < rpad; j0 += gtn) push(Work{i, i0, j0, 0}, (int64_t)p->mats[i].n);
-  end_kind(W_G1, true, true);
+  end_kind_groups(W_G1, (rpad + gtn - 1) / gtn);
   begin_kind(W_G2);
   if (big)
     for (int i = 0; i < n_mats; ++i)
       for (int i0 = 0; i0 < p->mats[i].n; i0 += gtm)
         for (int j0 = 0; j0 < rpad; j0 += gtn) push(Work{i, i0, j0, 1}, (int64_t)p->mats[i].mpad);
-  end_kind(W_G2, true, true);
+  end_kind_groups(W_G2, (rpad + gtn - 1) / gtn);
   begin_kind(W_GRAM);
   const int nblk = (rpad + psgd::kBlk - 1) / psgd::kBlk;
   for (int i = 0; i < n_mats; ++i) {
