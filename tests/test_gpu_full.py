@@ -195,3 +195,56 @@ def test_unsharded_rank896():
             E_or[i], Q_or[i] = st.E_next, st.Q_next
             del st, P, E, D, Q
     group.close()
+
+
+@pytest.mark.parametrize("rank", [112, 256])
+def test_largest_matrix_at_the_buffer_limit(rank):
+    """One fp16 gradient matrix whose error buffer and decompressed output come within 3% of the
+    2 GiB buffer-range limit (16000 x 32760: 2.097e9 bytes of fp32), at rank 112 (the streaming
+    products) and rank 256 (M split once, the GEMM path, and the blocked factorisation), one
+    step from a seeded error buffer and warm start, against the float64 oracle: D, E, q_next
+    and P within the relative Frobenius tolerance, P orthonormal, E + D = M. Every byte offset
+    of the kernels stays below 2^32 here; a 32-bit overflow in any of them would show."""
+    import torch
+    from rank_gradient_compression_powersgd_amd import PowerSGDGroup
+    m, n = 16000, 32760
+    assert m * n * 4 < 2 ** 31 and m * n * 4 > 0.97 * 2 ** 31
+    rng = np.random.default_rng(9_600_000 + rank)
+    dev = torch.device("cuda", 0)
+    x = rng.standard_normal((m, n), dtype=np.float32)
+    x *= np.exp(rng.uniform(-3.0, 0.0, size=(m, 1))).astype(np.float32)
+    G16 = x.astype(np.float16)
+    del x
+    E0 = (rng.standard_normal((m, n), dtype=np.float32) * np.float32(0.05))
+    Q0 = rng.standard_normal((n, rank), dtype=np.float32)
+    log(f"largest matrix {m}x{n} rank {rank}: inputs generated")
+    g = torch.from_numpy(G16).to(dev)
+    e = torch.from_numpy(E0).to(dev)
+    group = PowerSGDGroup([g], [0], torch.ones(1, device=dev), rank, [torch.from_numpy(Q0)], [e])
+    skip = group.step([], host=True)
+    torch.cuda.synchronize()
+    assert skip == 0
+    P = group.p[0].cpu().numpy().astype(np.float64)
+    E = group.err[0].cpu().numpy()
+    D = group.out[0].cpu().numpy()
+    Q = group.q[0].cpu().numpy().astype(np.float64)
+    group.close()
+    del g, e, group
+    torch.cuda.empty_cache()
+    log("  GPU step done; oracle step")
+    G = G16.astype(np.float32)
+    del G16
+    st = oracle.step_matrix(G, 1.0, E0, Q0, oracle.thin_qr_factor)
+    r_ = dict(D=rel(D, st.D), E=rel(E, st.E_next), Q=rel(Q, st.Q_next), P=rel(P, st.P), orth=orth_err(P))
+    log(f"  rank {rank}: " + " ".join(f"{k}={v:.2e}" for k, v in r_.items()))
+    for k in ("D", "E", "Q", "P"):
+        assert r_[k] <= REL_TOL, (rank, k, r_[k])
+    assert r_["orth"] <= ORTH_TOL
+    del st
+    # E + D = M, row block by row block (M in fp64 would take another 4 GB at once)
+    worst, mmax = 0.0, 0.0
+    for r0 in range(0, m, 2000):
+        M = G[r0:r0 + 2000].astype(np.float64) + E0[r0:r0 + 2000]
+        worst = max(worst, float(np.abs(E[r0:r0 + 2000].astype(np.float64) + D[r0:r0 + 2000] - M).max()))
+        mmax = max(mmax, float(np.abs(M).max()))
+    assert worst <= 2.0 ** -20 * mmax, (worst, mmax)
