@@ -148,7 +148,10 @@ def compare_step(res, st, what="", exact_rank: bool = False, check_p: bool = Tru
     for i in range(len(res["E"])):
         rD = rel(res["D"][i], st.D[i]) if res["D"][i] is not None else 0.0
         nm = float(np.linalg.norm(st.D[i] + st.E_next[i]))       # ||M||
-        if exact_rank or np.linalg.norm(st.E_next[i]) <= 1e-8 * nm:
+        if nm == 0.0:
+            # M = 0: E must be exactly zero (no relative measure exists)
+            rE = float(np.linalg.norm(res["E"][i]))
+        elif exact_rank or np.linalg.norm(st.E_next[i]) <= 1e-8 * nm:
             # M lies in span(P) (rank(M) <= r): the oracle's E is round-off, so E is measured
             # against ||M|| instead of against itself
             rE = float(np.linalg.norm(res["E"][i] - st.E_next[i]) / nm)

@@ -156,6 +156,35 @@ def test_ragged_shapes(dtype, rank):
     case.close()
 
 
+@pytest.mark.parametrize("rank,shapes", [
+    (1, [(1, 8), (1, 64), (7, 8), (33, 16), (40, 24)]),
+    (8, [(8, 8), (9, 8), (8, 4096), (17, 24), (40, 24)]),
+], ids=["r1", "r8"])
+def test_degenerate_shapes_and_a_zero_matrix(rank, shapes):
+    """Shapes at the edges of the tiles: one-row matrices, fewer rows than one MFMA tile, the
+    narrowest n (8), r = m = n (P square and orthogonal, D = M, E at round-off), and a matrix
+    whose G and E stay zero (every column of P dependent: P, D, E and q_next zero), three
+    warm-started steps in one group against the oracle."""
+    rng = np.random.default_rng(7300 + rank)
+    blocks = [0] * len(shapes)
+    scales = np.array([1.0], np.float32)
+    q0 = [rng.standard_normal((n, rank)).astype(np.float32) for _, n in shapes]
+    err0 = [(rng.standard_normal((m, n)) * 0.05).astype(np.float32) for m, n in shapes]
+    err0[-1][:] = 0.0                                    # the zero matrix
+    log(f"degenerate shapes r={rank}: {shapes}")
+    case = Case(shapes, blocks, "f16", rank, scales, q0, err0)
+    for t in range(3):
+        gs = [wl.to_fp16(rng.standard_normal((m, n))) for m, n in shapes]
+        gs[-1] = np.zeros(shapes[-1], np.float16)
+        case.set_grads(gs)
+        assert case.gpu_step() == 0
+        res = case.fetch()
+        compare_step(res, case.oracle_step(), f"degenerate r={rank} step {t}")
+        for key in ("P", "D", "E", "Qn"):
+            assert float(np.abs(res[key][-1]).max()) == 0.0, (t, key)
+    case.close()
+
+
 # ------------------------------------------------------------------------------------------
 # the flag reports non-finite G or E only: a finite M whose product overflows sets none
 # ------------------------------------------------------------------------------------------
