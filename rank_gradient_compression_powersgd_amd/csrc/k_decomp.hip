@@ -352,31 +352,34 @@ void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
     const rsrc_t rm1 = make_rsrc(d.m1, d.mo_bytes);
     const rsrc_t rm2 = make_rsrc(d.m2, d.mo_bytes);
     const int ldp = (int)d.ld_param;
-    constexpr int HB = NS / 2;                     // passes per half: state loads in two rounds
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      ParamIO<PT> th[HB];
-      u32x2 v1[HB], v2[HB];
+    // The optimizer state is read in four quarters of the tile, each quarter's loads issued
+    // while the previous quarter is updated.
+    constexpr int QN = 4, HB = NS / QN;
+    static_assert(HB * QN == NS, "quarters of whole passes");
+    struct State { ParamIO<PT> th[HB]; u32x2 v1[HB], v2[HB]; };
+    auto load_state = [&](State& S, int q) {
 #pragma unroll
       for (int j = 0; j < HB; ++j) {
-        const int st = h * HB + j;
-        th[j].load(rth, offset(st, ldp, ParamIO<PT>::kBytes));
-        v1[j] = bload8<kPol>(rm1, offset(st, n, 2u));
-        v2[j] = bload8<kPol>(rm2, offset(st, n, 2u));
+        const int st = q * HB + j;
+        S.th[j].load(rth, offset(st, ldp, ParamIO<PT>::kBytes));
+        S.v1[j] = bload8<kPol>(rm1, offset(st, n, 2u));
+        S.v2[j] = bload8<kPol>(rm2, offset(st, n, 2u));
       }
+    };
+    auto update = [&](const State& S, int q) {
 #pragma unroll
       for (int j = 0; j < HB; ++j) {
-        const int st = h * HB + j;
+        const int st = q * HB + j;
         const f32x4 gf = gv[st].f32();
         const f32x4 ef = __builtin_bit_cast(f32x4, ev[st]);
         const f32x4 dv = *reinterpret_cast<const f32x4*>(&Dt[(rs + RSTEP * st) * K3_DTP + 4 * cq]);
-        const f32x4 th0 = th[j].f32();
-        const f32x4 m1o = __builtin_convertvector(__builtin_bit_cast(bf16x4, v1[j]), f32x4);
+        const f32x4 th0 = S.th[j].f32();
+        const f32x4 m1o = __builtin_convertvector(__builtin_bit_cast(bf16x4, S.v1[j]), f32x4);
         f32x4 en, thn, m1n, m2n;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           en[i] = __builtin_fmaf(s, gf[i], ef[i]) - dv[i];
-          const uint32_t code = i < 2 ? (v2[j][0] >> (16 * i)) & 0xFFFFu : (v2[j][1] >> (16 * (i - 2))) & 0xFFFFu;
+          const uint32_t code = i < 2 ? (S.v2[j][0] >> (16 * i)) & 0xFFFFu : (S.v2[j][1] >> (16 * (i - 2))) & 0xFFFFu;
           const float g = clipf * dv[i];
           m1n[i] = aa.beta1 * m1o[i] + omb1 * g;
           m2n[i] = aa.beta2 * ue8m8_to_f32(code) + omb2 * (g * g);
@@ -391,7 +394,16 @@ void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
                                f32_to_ue8m8(m2n[2]) | (f32_to_ue8m8(m2n[3]) << 16)};
         __builtin_amdgcn_raw_buffer_store_b64(b2, rm2, offset(st, n, 2u), 0, kPol);
       }
-    }
+    };
+    State S0, S1;
+    load_state(S0, 0);
+    load_state(S1, 1);
+    update(S0, 0);
+    load_state(S0, 2);
+    update(S1, 1);
+    load_state(S1, 3);
+    update(S0, 2);
+    update(S1, 3);
   }
 }
 
