@@ -73,3 +73,52 @@ def test_parse_defaults(mode):
     a = bench.parse([] if mode == "default" else ["--block-scaling"])
     assert a.gpus == 1 and a.workload == 3 and a.steps > 0 and a.warmup >= 3
     assert a.block_scaling == (mode == "block")
+
+
+def test_lds_summary_ratio(tmp_path, capsys):
+    """The LDS table divides conflict cycles by indexed-access cycles, per kernel, over the
+    launches that used the LDS."""
+    name = "void psgd::(anonymous namespace)::k_ef_mq<1, 7>(psgd::DevMat const*)"
+    _write_counter_csv(tmp_path / "pmc_LDS" / "x", [
+        (1, name, "SQ_LDS_BANK_CONFLICT", 30.0), (1, name, "SQ_LDS_IDX_ACTIVE", 100.0),
+        (1, name, "SQ_INSTS_LDS", 2e6),
+        (2, name, "SQ_LDS_BANK_CONFLICT", 10.0), (2, name, "SQ_LDS_IDX_ACTIVE", 100.0),
+        (2, name, "SQ_INSTS_LDS", 4e6)])
+    assert bench.pmc_summary(str(tmp_path)) == 0
+    row = next(l for l in capsys.readouterr().out.splitlines() if l.startswith("k_ef_mq<1, 7>"))
+    f = row.split()
+    assert f[2] == "2" and float(f[3]) == pytest.approx(0.2) and float(f[5]) == pytest.approx(3.0)
+
+
+def test_pmc_summary_needs_some_counter_run(tmp_path):
+    assert bench.pmc_summary(str(tmp_path)) == 1
+
+
+def test_trace_summary_counts_steps_and_splits_the_two_gemms(tmp_path, capsys):
+    """Steps are counted by the finite check; k_gemm_nt launches alternate between M q and
+    M^T P_hat; per-step times are totals over the steps."""
+    p = tmp_path / "b_kernel_trace.csv"
+    ns = 0
+    rows = []
+    def add(kernel, us):
+        nonlocal ns
+        rows.append({"Kernel_Name": f"void psgd::(anonymous namespace)::{kernel}(int)",
+                     "Start_Timestamp": ns, "End_Timestamp": ns + int(us * 1000)})
+        ns += int(us * 1000) + 10
+    for _ in range(3):
+        add("k_gemm_nt", 100.0)
+        add("k_gemm_nt", 50.0)
+        add("k_check_finite", 2.0)
+        rows.append({"Kernel_Name": "void at::native::other(int)", "Start_Timestamp": ns,
+                     "End_Timestamp": ns + 5})
+    with open(p, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        w.writerows(rows)
+    assert bench.trace_summary(str(p)) == 0
+    out = capsys.readouterr().out
+    assert out.startswith("3 steps")
+    mq = next(l for l in out.splitlines() if l.startswith("| k_gemm_nt (M q)"))
+    mtp = next(l for l in out.splitlines() if l.startswith("| k_gemm_nt (M^T P_hat)"))
+    assert mq.split("|")[2].strip() == "3" and float(mq.split("|")[3]) == pytest.approx(100.0)
+    assert float(mtp.split("|")[4]) == pytest.approx(0.05)
