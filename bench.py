@@ -182,8 +182,9 @@ def traffic_summary(d: str) -> int:
           f"{f_copy / 2**30:.3f} GiB -> scale {sf:.3f}; WRITE_SIZE reads {w_copy / 2**30:.3f} GiB -> "
           f"scale {sw:.3f}")
     numel = 1511522304
-    qcommit = 4 * 81772544             # the decompression also writes q <- q_next (sum of n x r fp32)
-    algo = {"k_ef_mq": 6 * numel, "k_mtp": 6 * numel, "k_decomp": 14 * numel + qcommit}
+    # the factors each kernel reads or writes once (fp32, rank 112): sum of m x r and of n x r
+    sm, sn = 4 * 112 * 666624, 4 * 81772544
+    algo = {"k_ef_mq": 6 * numel + sn + sm, "k_mtp": 6 * numel + sm + sn, "k_decomp": 14 * numel + sm + 2 * sn}
     print(f"{'kernel':34s} {'launches':>8s} {'fetch GB':>9s} {'write GB':>9s} {'total GB':>9s} "
           f"{'algorithmic GB':>15s} {'ratio':>6s}")
     for k in sorted(fe):
@@ -279,6 +280,16 @@ def trace_summary(path: str) -> int:
               f"{100 * sum(v) / tot:.1f}% |")
     print(f"| all library kernels | {len(rows)} | | {tot / steps / 1e3:.3f} | |")
     return 0
+
+
+def factor_bytes(kernel: str, w) -> int:
+    """Bytes of the low-rank factors a streaming kernel must read or write once per launch (fp32,
+    r = the workload's rank): M Q reads q (n x r) and writes P (m x r); M^T P reads P^T (m x r,
+    as two 16-bit halves) and writes q_next (n x r); the decompression reads P (m x r) and q_next
+    (n x r) and writes q <- q_next (n x r)."""
+    sm = sum(spec.m for spec in w.matrices) * w.rank * 4
+    sn = sum(spec.n for spec in w.matrices) * w.rank * 4
+    return {"ef_mq": sn + sm, "mtp": sm + sn, "decompress": sm + 2 * sn}[kernel]
 
 
 def recorded_mfma(slot: str):
@@ -444,7 +455,8 @@ def adam_cpu_baseline(seconds: float, rank: int):
 def adam_bench(a, hip) -> int:
     """The step with the optimizer. Per gradient element the fused decompression reads G, E,
     theta, m1, m2 and writes E, theta, m1, m2 (no D): g + 8 + 3 * 2 * p bytes with 2-byte
-    moments and p-byte parameters (22 bytes for fp16 gradients and parameters)."""
+    moments and p-byte parameters (22 bytes for fp16 gradients and parameters), plus the factors
+    it reads (P, q_next) and the q commit."""
     import torch
     import rank_gradient_compression_powersgd_amd as psgd
     w, group, passthrough = build_workload(a.workload, a.n_blocks, False, a.inplace, a.rank)
@@ -491,7 +503,8 @@ def adam_bench(a, hip) -> int:
     gsz = 0 if a.inplace else (2 if w.dtype in ("f16", "bf16") else 4)
     psz = params[0].element_size()
     per_elem = gsz + 8 + 2 * (psz + 2 + 2)
-    nbytes = per_elem * numel + 4 * w.rank * sum(spec.n for spec in w.matrices)   # + the q commit
+    ebytes = per_elem * numel
+    nbytes = ebytes + factor_bytes("decompress", w)   # + P and q_next read, q <- q_next written
     gbs = nbytes / (kern["decompress_adam"] * 1e-3) / 1e9
     ms = wall * 1e3 / K
     norm = group.adam_norm.cpu().tolist()
@@ -507,8 +520,9 @@ def adam_bench(a, hip) -> int:
         "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": nbytes,
-                     "bytes_per_element": per_elem, "avg_ms": round(kern["decompress_adam"], 4),
-                     "kernel": "decompress_adam"},
+                     "bytes_per_element": per_elem, "element_bytes": ebytes, "factor_bytes": nbytes - ebytes,
+                     "frac_elements_only": round(ebytes / (kern["decompress_adam"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "avg_ms": round(kern["decompress_adam"], 4), "kernel": "decompress_adam"},
         "cpu_baseline": None,
     }
     group.close()
@@ -707,13 +721,15 @@ def main(argv=None) -> int:
     per_elem = {"ef_mq": gsz + 4, "mtp": gsz + 4, "decompress": gsz + 8 + (0 if a.no_out else 4)}
     rooflines = {}
     for name in STREAMING:
-        nbytes = per_elem[name] * numel
-        if name == "decompress":       # and commits q <- q_next: n x r fp32 written per matrix
-            nbytes += 4 * w.rank * sum(spec.n for spec in w.matrices)
+        ebytes = per_elem[name] * numel
+        fbytes = factor_bytes(name, w)
+        nbytes = ebytes + fbytes
         gbs = nbytes / (kern[name] * 1e-3) / 1e9
         rooflines[name] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                           "bytes_per_launch": nbytes, "avg_ms": round(kern[name], 4)}
+                           "bytes_per_launch": nbytes, "element_bytes": ebytes, "factor_bytes": fbytes,
+                           "frac_elements_only": round(ebytes / (kern[name] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                           "avg_ms": round(kern[name], 4)}
     if w.rank > 128:
         # Above rank 128 the products are GEMMs on split operands: bound by MFMA, not HBM. The
         # achieved rate counts the method's own flops, 2 m n r per product (the split runs three
