@@ -81,3 +81,67 @@ def test_step_graph_replays_match_eager(rank):
         assert torch.equal(a, b)
     eager.close()
     cap.close()
+
+
+def test_step_with_optimizer_graph_replays_match_eager():
+    """The step with the optimizer (compress, finite check, global norm and clip, decompression
+    fused with the matrices' Adam update, fp32 Adam on a pass-through tensor) captured once and
+    replayed three times with new gradients: parameters, moments, step count, norm, error
+    buffers and warm starts equal the eager run bit for bit after every replay."""
+    import torch
+    from rank_gradient_compression_powersgd_amd import PowerSGDGroup
+    from rank_gradient_compression_powersgd_amd.binding import psgd_adam_hparams
+    dev = torch.device("cuda", 0)
+    rank = 24
+    shapes = [(520, 264), (300, 512)]
+    rng = np.random.default_rng(5170)
+    q0 = [rng.standard_normal((n, rank)).astype(np.float32) for _, n in shapes]
+    grads = [[wl.to_fp16(rng.standard_normal(sh)) for sh in shapes] for _ in range(3)]
+    pgrads = [(rng.standard_normal(4096) * 1e-2).astype(np.float32) for _ in range(3)]
+    th0 = [wl.to_fp16(rng.standard_normal(sh) * 0.02) for sh in shapes]
+    hp = psgd_adam_hparams(1e-3, 0.9, 0.999, 1e-8, 0.01)
+    scale = torch.tensor([1.0], device=dev)
+
+    def group():
+        g = PowerSGDGroup([torch.from_numpy(grads[0][i]).to(dev) for i in range(len(shapes))], [0, 0],
+                          scale, rank, [torch.from_numpy(q) for q in q0])
+        g.attach_adam([torch.from_numpy(t).to(dev) for t in th0],
+                      [torch.zeros(sh, dtype=torch.int16, device=dev) for sh in shapes],
+                      [torch.zeros(sh, dtype=torch.int16, device=dev) for sh in shapes])
+        g.pass_state = (torch.full((4096,), 0.5, device=dev), torch.zeros(4096, device=dev),
+                        torch.zeros(4096, device=dev), torch.from_numpy(pgrads[0]).to(dev))
+        return g
+
+    warm = group()
+    warm.step_adam(hp, [warm.pass_state], max_norm=1.0)
+    torch.cuda.synchronize()
+    warm.close()
+    eager, cap = group(), group()
+    torch.cuda.synchronize()
+    log("graph capture of the step with the optimizer")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        cap.step_adam(hp, [cap.pass_state], max_norm=1.0)
+    torch.cuda.synchronize()
+    assert int(cap.adam_step.item()) == 0             # capturing ran nothing
+    for t in range(3):
+        for i in range(len(shapes)):
+            src = torch.from_numpy(grads[t][i]).to(dev)
+            eager.grads[i].copy_(src)
+            cap.grads[i].copy_(src)
+        eager.pass_state[3].copy_(torch.from_numpy(pgrads[t]).to(dev))
+        cap.pass_state[3].copy_(eager.pass_state[3])
+        eager.step_adam(hp, [eager.pass_state], max_norm=1.0)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert int(cap.adam_step.item()) == t + 1 == int(eager.adam_step.item())
+        assert torch.equal(eager.adam_norm, cap.adam_norm), t
+        for name in ("params", "m1", "m2", "err", "q"):
+            for a, b in zip(getattr(eager, name), getattr(cap, name)):
+                assert torch.equal(a, b), (t, name)
+        for a, b in zip(eager.pass_state[:3], cap.pass_state[:3]):
+            assert torch.equal(a, b), (t, "pass-through")
+    eager.close()
+    cap.close()
