@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 RANK = 112
 
 
-def _state(shapes, seed):
+def _state(shapes, seed, rank=RANK):
     import torch
     g, e, q = [], [], []
     for i, (m, n) in enumerate(shapes):
@@ -24,20 +24,20 @@ def _state(shapes, seed):
         x = rng.standard_normal((m, n)) * np.exp(rng.uniform(np.log(1e-4), 0.0, size=(m, 1)))
         g.append(torch.from_numpy(wl.to_fp16(x)).cuda())
         e.append(torch.from_numpy((rng.standard_normal((m, n)) * 0.05).astype(np.float32)).cuda())
-        q.append(torch.from_numpy(rng.standard_normal((n, RANK)).astype(np.float32)).cuda())
+        q.append(torch.from_numpy(rng.standard_normal((n, rank)).astype(np.float32)).cuda())
     return g, e, q
 
 
 class _Bufs:
     """One copy of a group's state and outputs, described to the ABI."""
 
-    def __init__(self, grads, errs, qs, blocks):
+    def __init__(self, grads, errs, qs, blocks, rank=RANK):
         import torch
         from rank_gradient_compression_powersgd_amd import binding as B
         self.err = [x.clone() for x in errs]
         self.q = [x.clone() for x in qs]
         self.q_next = [torch.empty_like(x) for x in qs]
-        self.p = [torch.empty((x.shape[0], RANK), dtype=torch.float32, device="cuda") for x in grads]
+        self.p = [torch.empty((x.shape[0], rank), dtype=torch.float32, device="cuda") for x in grads]
         self.out = [torch.empty(x.shape, dtype=torch.float32, device="cuda") for x in grads]
         self.flags = torch.full((len(grads),), 7, dtype=torch.uint8, device="cuda")
         self.skip = torch.full((1,), 5, dtype=torch.int32, device="cuda")
@@ -52,16 +52,16 @@ def _equal_bits(a, b):
     return bool(torch.equal(a, b))
 
 
-def _run_both(ctx, shapes, blocks, seed, inject=None):
+def _run_both(ctx, shapes, blocks, seed, inject=None, rank=RANK):
     import torch
     from rank_gradient_compression_powersgd_amd import binding as B
-    grads, errs, qs = _state(shapes, seed)
+    grads, errs, qs = _state(shapes, seed, rank)
     if inject is not None:
         grads[inject][1, 2] = float("nan")
     scale = torch.tensor([1.0, 0.5, 0.25], dtype=torch.float32, device="cuda")
     pt = torch.from_numpy(wl.passthrough_np(2, 3, seed % 1000)).cuda().reshape(-1)
-    ref = _Bufs(grads, errs, qs, blocks)
-    new = _Bufs(grads, errs, qs, blocks)
+    ref = _Bufs(grads, errs, qs, blocks, rank)
+    new = _Bufs(grads, errs, qs, blocks, rank)
     plan = B.psgd_plan_create(ctx, ref.mats, B.PSGD_F16, 3)
     B.psgd_compress(ctx, plan, scale, ref.flags)
     B.psgd_check_finite(ctx, plan, ref.flags, [pt], scale, ref.skip)
@@ -96,6 +96,20 @@ def test_noalloc_step_matches_the_plan_step_twice_then_smaller():
         _run_both(ctx, small, [2, 1], 8_100_003, inject=1)
         log("no-alloc step: the shard again after the smaller groups")
         _run_both(ctx, big, [0, 1, 2, 0], 8_100_004)
+    finally:
+        B.psgd_destroy(ctx)
+
+
+def test_noalloc_step_large_rank_matches_the_plan_step():
+    """Rank 160: the split-once GEMM path (M and M^T split into the scratch array, the balanced
+    GEMM lists) and the blocked factorisation, twice in a row, the second group smaller."""
+    from rank_gradient_compression_powersgd_amd import binding as B
+    ctx = B.psgd_create(0, 160)
+    try:
+        log("no-alloc step: rank 160, three matrices")
+        _run_both(ctx, [(600, 512), (257, 768), (320, 264)], [0, 1, 2], 8_100_011, rank=160)
+        log("no-alloc step: rank 160, one matrix after it")
+        _run_both(ctx, [(200, 776)], [1], 8_100_012, rank=160)
     finally:
         B.psgd_destroy(ctx)
 
