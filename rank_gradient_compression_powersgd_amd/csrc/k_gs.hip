@@ -270,32 +270,33 @@ __device__ __forceinline__ bool factor_panels(double* Wb, double* Ub, double* Ls
 #pragma clang loop unroll(full)
       for (int jj = 0; jj < FB; ++jj) {
         const int gj = jj & 3, ij = jj >> 2;       // holder of row jj: lanes 16 gj + x, register ij
-        // The lane's coordinates pass through an empty asm statement each step, so that the
+        // The lane's column passes through an empty asm statement each step, so that the
         // per-lane conditions of the step are formed where they are used: hoisted out of the
         // unrolled steps they took 96 lane masks and spilled scalar registers.
-        int cs = c, gs = g;
-        asm volatile("" : "+v"(cs), "+v"(gs));
+        int cs = c;
+        asm volatile("" : "+v"(cs));
         const double dj = readlane_f64(a[ij], 16 * gj + jj);
         const double dz = d0[p * FB + jj];
         const bool ok = (dz > 0.0) && (dj > kDegenerate * dz) && (dj <= 1.0e300);
         const double y = rsqrt_f64(ok ? dj : 1.0);
         const double inv = ok ? y : 0.0;
         again |= ok && dj < kReorth * dz;
-        // row jj of the residual block, scaled: r[x] = a[jj][x] / ||v_jj||. Lane 16g + c needs
-        // r[c] (held in row group gj: a shuffle across rows) and r[g + 4i] = a[g + 4i][jj] (the
-        // block is symmetric), held by lane jj of its own row group (a row broadcast).
-        const double rc = __shfl(a[ij], 16 * gj + cs) * inv;
-        double rrow[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rrow[i] = row_bcast_f64(a[i], jj) * inv;
-        // local factor: column jj scaled, then removed from the later columns
+        // Row jj of the residual block scaled by 1 / ||v_jj|| is r[x] = a[jj][x] inv. The
+        // rank-one update a[y][x] -= r[y] r[x] and the removal of column jj from the later
+        // columns of L, L[y][x] -= L[y][jj] inv r[x], both take s[x] = a[jj][x] inv^2: lane
+        // 16g + c needs a[jj][c] (held in row group gj: a shuffle across rows), and a[g + 4i][jj]
+        // = a[jj][g + 4i] (the block is symmetric) and L[g + 4i][jj], held by lane jj of its own
+        // row group (row broadcasts). Only the later columns (c > jj) are updated; the rows up
+        // to jj are updated too, which leaves them near zero and unread by the later steps.
+        const double s = __shfl(a[ij], 16 * gj + cs) * inv * inv;
+        const double sa = cs > jj ? s : 0.0;                 // later columns only
+        const double beta = cs == jj ? inv : -sa;            // L: column jj scaled, later ones reduced
+        const double alpha = cs == jj ? 0.0 : 1.0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const double lj = row_bcast_f64(l[i], jj) * inv;   // L[g + 4i][jj], scaled
-          const double ls = cs == jj ? lj : l[i];
-          l[i] = cs > jj ? l[i] - rc * lj : ls;
-          const double as = a[i] - rrow[i] * rc;
-          a[i] = (cs > jj && gs + 4 * i > jj) ? as : a[i];
+          const double bl = row_bcast_f64(l[i], jj), ba = row_bcast_f64(a[i], jj);
+          l[i] = __builtin_fma(bl, beta, l[i] * alpha);
+          a[i] = __builtin_fma(-ba, sa, a[i]);
         }
       }
 #pragma unroll
