@@ -255,54 +255,56 @@ __device__ __forceinline__ bool factor_panels(double* Wb, double* Ub, double* Ls
   constexpr int NWV = GSF_THREADS / kWave;
   const int c = lane & 15, g = lane >> 4;
   bool again = false;
-  for (int p = 0; p < nb; ++p) {
-    // (A) diagonal block: lane 16g + c holds rows g + 4i, column c, of the residual Gram block
-    // (a) and of the local factor (l). The pivot and its inverse square root are wave-uniform:
-    // the pivot is read through the scalar unit and the scaling is branch-free.
-    if (wv == 0) {
-      const double* Wpp = &Wb[fblk(p, p, nb) * FBS];
-      double a[4], l[4];
+  // (A) diagonal block of panel q (wave 0): lane 16g + c holds rows g + 4i, column c, of the
+  // residual Gram block (a) and of the local factor (l), which goes to Lsh. The pivot and its
+  // inverse square root are wave-uniform: the pivot is read through the scalar unit and the
+  // scaling is branch-free.
+  auto diag = [&](int q) {
+    const double* Wpp = &Wb[fblk(q, q, nb) * FBS];
+    double a[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = Wpp[(g + 4 * i) * FBP + c];
+      l[i] = (g + 4 * i == c) ? 1.0 : 0.0;
+    }
+#pragma clang loop unroll(full)
+    for (int jj = 0; jj < FB; ++jj) {
+      const int gj = jj & 3, ij = jj >> 2;       // holder of row jj: lanes 16 gj + x, register ij
+      // The lane's column passes through an empty asm statement each step, so that the
+      // per-lane conditions of the step are formed where they are used: hoisted out of the
+      // unrolled steps they took 96 lane masks and spilled scalar registers.
+      int cs = c;
+      asm volatile("" : "+v"(cs));
+      const double dj = readlane_f64(a[ij], 16 * gj + jj);
+      const double dz = d0[q * FB + jj];
+      const bool ok = (dz > 0.0) && (dj > kDegenerate * dz) && (dj <= 1.0e300);
+      const double y = rsqrt_f64(ok ? dj : 1.0);
+      const double inv = ok ? y : 0.0;
+      again |= ok && dj < kReorth * dz;
+      // Row jj of the residual block scaled by 1 / ||v_jj|| is r[x] = a[jj][x] inv. The
+      // rank-one update a[y][x] -= r[y] r[x] and the removal of column jj from the later
+      // columns of L, L[y][x] -= L[y][jj] inv r[x], both take s[x] = a[jj][x] inv^2: lane
+      // 16g + c needs a[jj][c] (held in row group gj: a shuffle across rows), and a[g + 4i][jj]
+      // = a[jj][g + 4i] (the block is symmetric) and L[g + 4i][jj], held by lane jj of its own
+      // row group (row broadcasts). Only the later columns (c > jj) are updated; the rows up
+      // to jj are updated too, which leaves them near zero and unread by the later steps.
+      const double s = __shfl(a[ij], 16 * gj + cs) * inv * inv;
+      const double sa = cs > jj ? s : 0.0;                 // later columns only
+      const double beta = cs == jj ? inv : -sa;            // L: column jj scaled, later ones reduced
+      const double alpha = cs == jj ? 0.0 : 1.0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        a[i] = Wpp[(g + 4 * i) * FBP + c];
-        l[i] = (g + 4 * i == c) ? 1.0 : 0.0;
+        const double bl = row_bcast_f64(l[i], jj), ba = row_bcast_f64(a[i], jj);
+        l[i] = __builtin_fma(bl, beta, l[i] * alpha);
+        a[i] = __builtin_fma(-ba, sa, a[i]);
       }
-#pragma clang loop unroll(full)
-      for (int jj = 0; jj < FB; ++jj) {
-        const int gj = jj & 3, ij = jj >> 2;       // holder of row jj: lanes 16 gj + x, register ij
-        // The lane's column passes through an empty asm statement each step, so that the
-        // per-lane conditions of the step are formed where they are used: hoisted out of the
-        // unrolled steps they took 96 lane masks and spilled scalar registers.
-        int cs = c;
-        asm volatile("" : "+v"(cs));
-        const double dj = readlane_f64(a[ij], 16 * gj + jj);
-        const double dz = d0[p * FB + jj];
-        const bool ok = (dz > 0.0) && (dj > kDegenerate * dz) && (dj <= 1.0e300);
-        const double y = rsqrt_f64(ok ? dj : 1.0);
-        const double inv = ok ? y : 0.0;
-        again |= ok && dj < kReorth * dz;
-        // Row jj of the residual block scaled by 1 / ||v_jj|| is r[x] = a[jj][x] inv. The
-        // rank-one update a[y][x] -= r[y] r[x] and the removal of column jj from the later
-        // columns of L, L[y][x] -= L[y][jj] inv r[x], both take s[x] = a[jj][x] inv^2: lane
-        // 16g + c needs a[jj][c] (held in row group gj: a shuffle across rows), and a[g + 4i][jj]
-        // = a[jj][g + 4i] (the block is symmetric) and L[g + 4i][jj], held by lane jj of its own
-        // row group (row broadcasts). Only the later columns (c > jj) are updated; the rows up
-        // to jj are updated too, which leaves them near zero and unread by the later steps.
-        const double s = __shfl(a[ij], 16 * gj + cs) * inv * inv;
-        const double sa = cs > jj ? s : 0.0;                 // later columns only
-        const double beta = cs == jj ? inv : -sa;            // L: column jj scaled, later ones reduced
-        const double alpha = cs == jj ? 0.0 : 1.0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const double bl = row_bcast_f64(l[i], jj), ba = row_bcast_f64(a[i], jj);
-          l[i] = __builtin_fma(bl, beta, l[i] * alpha);
-          a[i] = __builtin_fma(-ba, sa, a[i]);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Lsh[(g + 4 * i) * FBP + c] = l[i];
     }
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Lsh[(g + 4 * i) * FBP + c] = l[i];
+  };
+  if (wv == 0) diag(0);
+  __syncthreads();
+  for (int p = 0; p < nb; ++p) {
     // (B) T_ip = U_ip L (in place, i <= p) and R_pj = L^T W_pj (in place, j > p)
     for (int t = wv; t < nb; t += NWV) {
       if (t <= p) {
@@ -314,20 +316,31 @@ __device__ __forceinline__ bool factor_panels(double* Wb, double* Ub, double* Ls
       }
     }
     __syncthreads();
-    // (C) U_ij -= T_ip R_pj (i <= p < j); W_ij -= R_pi^T R_pj (p < i <= j)
+    // (C) U_ij -= T_ip R_pj (i <= p < j); W_ij -= R_pi^T R_pj (p < i <= j). Look-ahead: wave 0
+    // updates the next diagonal block W_{p+1,p+1} and factors it while the other waves update
+    // the remaining blocks (item nu, that diagonal block, is skipped in their list).
     const int nr = nb - p - 1;                     // block columns right of the panel
     const int nu = (p + 1) * nr, nw = nr * (nr + 1) / 2;
-    for (int t = wv; t < nu + nw; t += NWV) {
-      if (t < nu) {
-        const int i = t / nr, j = p + 1 + t % nr;
-        fblock_mm(&Ub[fblk(i, j, nb) * FBS], &Ub[fblk(i, p, nb) * FBS], false,
-                  &Wb[fblk(p, j, nb) * FBS], true, c, g);
+    if (nr > 0) {
+      if (wv == 0) {
+        double* Rn = &Wb[fblk(p, p + 1, nb) * FBS];
+        fblock_mm(&Wb[fblk(p + 1, p + 1, nb) * FBS], Rn, true, Rn, true, c, g);
+        diag(p + 1);
       } else {
-        int u = t - nu, i = p + 1;
-        while (u >= nb - i) { u -= nb - i; ++i; }
-        const int j = i + u;
-        fblock_mm(&Wb[fblk(i, j, nb) * FBS], &Wb[fblk(p, i, nb) * FBS], true,
-                  &Wb[fblk(p, j, nb) * FBS], true, c, g);
+        for (int t0 = wv - 1; t0 < nu + nw - 1; t0 += NWV - 1) {
+          const int t = t0 < nu ? t0 : t0 + 1;
+          if (t < nu) {
+            const int i = t / nr, j = p + 1 + t % nr;
+            fblock_mm(&Ub[fblk(i, j, nb) * FBS], &Ub[fblk(i, p, nb) * FBS], false,
+                      &Wb[fblk(p, j, nb) * FBS], true, c, g);
+          } else {
+            int u = t - nu, i = p + 1;
+            while (u >= nb - i) { u -= nb - i; ++i; }
+            const int j = i + u;
+            fblock_mm(&Wb[fblk(i, j, nb) * FBS], &Wb[fblk(p, i, nb) * FBS], true,
+                      &Wb[fblk(p, j, nb) * FBS], true, c, g);
+          }
+        }
       }
     }
     __syncthreads();
