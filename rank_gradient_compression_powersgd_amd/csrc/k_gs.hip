@@ -129,8 +129,9 @@ void k_gs_gram(const DevMat* __restrict__ mats, const Work* __restrict__ work, i
 
 // W = sum of the Gram partials in part order (large ranks); also U = I (tmat) and the
 // diagonal of W saved in wdiag for the factorisation's dependence test. One work item: 4096
-// consecutive elements of the rpad x rpad matrix starting at a * 4096. Elements of blocks below
-// the diagonal were never written and sum to zero.
+// consecutive elements of the rpad x rpad matrix starting at a * 4096. Only the 128-column
+// blocks on and above the diagonal are formed: the partials hold nothing below it, and the
+// factorisation and the product P T read W and T there only.
 __global__ __launch_bounds__(256)
 void k_gs_reduce(const DevMat* __restrict__ mats, const Work* __restrict__ work, int pass)
 {
@@ -146,6 +147,7 @@ void k_gs_reduce(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   GLOBAL double* __restrict__ tmat = gbl(d.tmat);
   GLOBAL double* __restrict__ wdiag = gbl(d.wdiag);
   for (int64_t e = (int64_t)wi.a * 4096 + threadIdx.x; e < tot && e < (int64_t)(wi.a + 1) * 4096; e += 256) {
+    if ((e % rp) / kBlk < (e / rp) / kBlk) continue;   // below the block diagonal
     double sum = 0.0;
 #pragma unroll 8
     for (int pt = 0; pt < parts; ++pt) sum += gram[(int64_t)pt * tot + e];
