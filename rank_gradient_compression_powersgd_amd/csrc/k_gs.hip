@@ -684,7 +684,7 @@ void k_gs_apply(const DevMat* __restrict__ mats, const Work* __restrict__ work, 
   const GLOBAL float* __restrict__ P = gbl(pass ? d.p2 : d.p_raw);
   const GLOBAL double* __restrict__ Tm = gbl(d.tmat);
   const int lane = threadIdx.x & (kWave - 1);
-  const int wv = threadIdx.x / kWave;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // uniform: scalar branches
   const int c = lane & 15, g = lane >> 4;
   const int row0 = wi.a;
   const int rows = min(GSA_ROWS, m - row0);
@@ -751,9 +751,8 @@ void k_gs_apply(const DevMat* __restrict__ mats, const Work* __restrict__ work, 
           nA[ks] = kt <= endA ? Tm[krow + 16 * tA + c] : 0.0;
         }
       };
-      fetch(0);
-#pragma unroll 1
-      for (int kt = 0; kt <= kend; ++kt) {
+      // one k tile: UA / UB (compile-time) say which of the pair's tiles take part
+      auto step = [&](int kt, auto UA, auto UB) {
         double bB[4], bA[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) { bB[ks] = nB[ks]; bA[ks] = nA[ks]; }
@@ -762,13 +761,49 @@ void k_gs_apply(const DevMat* __restrict__ mats, const Work* __restrict__ work, 
 #pragma unroll
         for (int a = 0; a < RPW; ++a)
           av[a] = *reinterpret_cast<const f32x4*>(&S[((rs + a * WPG) * 16 + c) * LD + 16 * kt + 4 * g]);
-        const bool useB = !BIG || kt <= endB, useA = kt <= endA;   // small ranks: kend == endB
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
           for (int a = 0; a < RPW; ++a) {
-            if (useB) acc[1][a] = mfma_f64((double)av[a][ks], bB[ks], acc[1][a]);
-            if (useA) acc[0][a] = mfma_f64((double)av[a][ks], bA[ks], acc[0][a]);
+            if constexpr (decltype(UB)::value) acc[1][a] = mfma_f64((double)av[a][ks], bB[ks], acc[1][a]);
+            if constexpr (decltype(UA)::value) acc[0][a] = mfma_f64((double)av[a][ks], bA[ks], acc[0][a]);
+          }
+        }
+      };
+      fetch(0);
+      if constexpr (BIG) {
+        // k tiles where both tiles of the pair take part, then those of one of them alone (the
+        // longer tile of a diagonal block, or the only one present)
+        const int kboth = endA < endB ? endA : endB;
+        int kt = 0;
+#pragma unroll 1
+        for (; kt <= kboth; ++kt) step(kt, std::true_type{}, std::true_type{});
+#pragma unroll 1
+        for (; kt <= endB; ++kt) step(kt, std::false_type{}, std::true_type{});
+#pragma unroll 1
+        for (; kt <= endA; ++kt) step(kt, std::true_type{}, std::false_type{});
+      } else {
+        // small ranks: tile B takes part at every k tile (kend == endB); one loop body, with the
+        // test for tile A at each of its products, keeps the registers within four workgroups
+        // per CU (split loops spilled)
+#pragma unroll 1
+        for (int kt = 0; kt <= kend; ++kt) {
+          double bB[4], bA[4];
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) { bB[ks] = nB[ks]; bA[ks] = nA[ks]; }
+          if (kt < kend) fetch(kt + 1);
+          f32x4 av[RPW];
+#pragma unroll
+          for (int a = 0; a < RPW; ++a)
+            av[a] = *reinterpret_cast<const f32x4*>(&S[((rs + a * WPG) * 16 + c) * LD + 16 * kt + 4 * g]);
+          const bool useA = kt <= endA;
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+            for (int a = 0; a < RPW; ++a) {
+              acc[1][a] = mfma_f64((double)av[a][ks], bB[ks], acc[1][a]);
+              if (useA) acc[0][a] = mfma_f64((double)av[a][ks], bA[ks], acc[0][a]);
+            }
           }
         }
       }
