@@ -396,6 +396,28 @@ def test_large_rank_ragged(dtype, rank):
     case.close()
 
 
+def test_large_rank_many_matrices():
+    """Rank 144 (a full 128-column block and a ragged 16-column one) over 24 matrices of mixed
+    shapes: the block factorisation's per-step work lists, its diagonal blocks and the GEMM
+    lists all carry many matrices at once."""
+    rank = 144
+    rng = np.random.default_rng(8144)
+    shapes = [(int(rng.integers(150, 700)), 8 * int(rng.integers(19, 90))) for _ in range(24)]
+    blocks = [i % 3 for i in range(len(shapes))]
+    scales = np.array([1.0, 0.5, 2.0], np.float32)
+    q0 = [rng.standard_normal((n, rank)).astype(np.float32) for _, n in shapes]
+    err0 = [(rng.standard_normal((m, n)) * 0.05).astype(np.float32) for m, n in shapes]
+    log(f"large rank, {len(shapes)} matrices, r={rank}")
+    case = Case(shapes, blocks, "f16", rank, scales, q0, err0)
+    for t in range(2):
+        gs = [wl.to_fp16(rng.standard_normal((m, n)) * np.exp(rng.uniform(-3, 0, size=(m, 1))))
+              for m, n in shapes]
+        case.set_grads(gs)
+        assert case.gpu_step() == 0
+        compare_step(case.fetch(), case.oracle_step(), f"many matrices step {t}")
+    case.close()
+
+
 @pytest.mark.parametrize("rank,true_rank", [(100, 60), (200, 150)])
 def test_rank_deficient_second_pass(rank, true_rank):
     """rank(M) < r: one step recovers M (E vanishes relative to M). The surplus columns of M q
