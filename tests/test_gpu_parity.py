@@ -210,10 +210,14 @@ def test_product_overflow_is_not_a_flag():
 # ------------------------------------------------------------------------------------------
 # non-finite values: flags and skip bit-exact, error buffers zeroed, q kept
 # ------------------------------------------------------------------------------------------
-def test_nonfinite_flags_skip_and_zeroing():
+@pytest.mark.parametrize("rank,shapes", [(16, [(300, 256), (64, 512), (200, 104)]),
+                                         (160, [(300, 256), (200, 512), (200, 176)])],
+                         ids=["r16", "r160"])
+def test_nonfinite_flags_skip_and_zeroing(rank, shapes):
+    """Each non-finite event flags exactly its matrix (or only skips, for a pass-through NaN or a
+    non-finite scale), the step is skipped, E is zeroed and q and out are kept; rank 160 takes
+    the path where M is split once and the flag comes from that split."""
     import torch
-    shapes = [(300, 256), (64, 512), (200, 104)]
-    rank = 16
     rng = np.random.default_rng(99)
     q0 = [rng.standard_normal((n, rank)).astype(np.float32) for _, n in shapes]
     err0 = [(rng.standard_normal((m, n)) * 0.1).astype(np.float32) for m, n in shapes]
