@@ -175,6 +175,8 @@ constexpr int GSF_THREADS = 1024;
 //   (B) T_ip = U_ip L for i <= p, and the panel row of R, R_pj = L^T W_pj for j > p;
 //   (C) U_ij -= T_ip R_pj (i <= p < j) and W_ij -= R_pi^T R_pj (p < i <= j).
 // (B) and (C) are 16 x 16 x 16 block products on v_mfma_f64_16x16x4f64, one block per wave.
+// In (C) wave 0 updates only W_{p+1,p+1} and then runs (A) of panel p + 1 on it, while the other
+// waves update the remaining blocks (look-ahead).
 // This is the right-looking blocked form of the column recurrence: every column still sees
 // the residual Gram entries of its own step, so dependent columns are dropped by the same test.
 constexpr int FB = 16;                 // panel width
