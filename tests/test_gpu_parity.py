@@ -614,14 +614,16 @@ def test_split_calls_two_simulated_ranks(rank):
         grp.close()
 
 
-def test_split_calls_equal_the_fused_call():
+@pytest.mark.parametrize("rank", [None, 160])
+def test_split_calls_equal_the_fused_call(rank):
     """On one GPU the exchanges are the identity: the split calls must give bit-identical
-    results to psgd_compress."""
+    results to psgd_compress. Above rank 128 the fused call forms M^T on a second stream while
+    the split calls run everything on one, so this also checks that fork and join."""
     import torch
     from rank_gradient_compression_powersgd_amd import binding as B
     outs = []
     for split in (False, True):
-        w, specs, case = _shard_case(2, None, err_warm=True)
+        w, specs, case = _shard_case(2, None, err_warm=True, rank=rank)
         case.set_grads([wl.gradient_np(w, s, 2) for s in specs])
         g = case.group
         if split:
