@@ -9,13 +9,15 @@
 // (the M q and M^T P kernels). At higher ranks those kernels walk G and E once per 128-rank
 // chunk and convert M to bf16 halves in every pass; the conversions, not the bytes, then
 // bound them. Here M is formed and split once:
-//   k_split_m   M = s_b G + E -> M_hi, M_lo (m x n, row-major) and their transposes (n x m),
-//               bf16, zero-padded; the per-matrix flag "G or E holds inf/NaN";
+//   k_split_m   M = s_b G + E -> M_hi, M_lo (m x n, row-major, bf16, zero-padded) and the
+//               per-matrix flag "G or E holds inf/NaN";
 //   k_split_qt  q (n x r fp32) -> q^T split into bf16 halves (rpad x n);
-//   k_gemm_nt   C = A B^T over K with A and B both K-contiguous bf16 halves, three products
-//               A_hi B_hi + A_hi B_lo + A_lo B_hi accumulated in fp32 (as the streaming
-//               kernels do): P_raw = M (q^T)^T and q_next = M^T (P^T)^T, P^T being the halves
-//               the orthonormal-factor kernel writes.
+//   k_gemm_nt   C = A B^T over K with bf16 halves, three products A_hi B_hi + A_hi B_lo +
+//               A_lo B_hi accumulated in fp32 (as the streaming kernels do): P_raw = M (q^T)^T
+//               with both operands K-contiguous, and q_next = M^T (P^T)^T, P^T being the halves
+//               the orthonormal-factor kernel writes and A = M^T read from M's row-major halves
+//               (K-outer) through gfx950's transposing LDS read, so no transposed copy of M is
+//               written.
 #include "psgd_internal.h"
 
 namespace psgd {
@@ -23,11 +25,11 @@ namespace {
 
 constexpr int ST = 64;          // split tile: 64 x 64 elements
 constexpr int ST_THREADS = 256;
-constexpr int STP = ST + 8;     // LDS row pitch of the transpose tile (bf16), 16-byte rows apart
+constexpr int STP = ST + 8;     // LDS row pitch of the q transpose tile (bf16), 16-byte rows apart
 
 // 64 x 64 tile (rows i0.., columns j0..) of the padded M range: 16 lanes per row, 4 columns
 // each, 16 rows per step, 4 steps. Rows past m and columns past n read zeros (buffer
-// descriptors), so the padding of M and M^T is written as zeros.
+// descriptors), so the padding of M is written as zeros.
 template <int GT>
 __global__ __launch_bounds__(ST_THREADS)
 void k_split_m(const DevMat* __restrict__ mats, const Work* __restrict__ work,
@@ -38,13 +40,12 @@ void k_split_m(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   const DevMat& d = mats[wi.mat];
   const int m = d.m, n = d.n, i0 = wi.a, j0 = wi.b;
   const int ldg = (int)d.ld_grad, lde = (int)d.ld_err;
-  const int ldm = d.npad_b, ldt = d.mpad;
+  const int ldm = d.npad_b;
   const rsrc_t rg = make_rsrc(d.grad, d.g_bytes);
   const rsrc_t re = make_rsrc(d.err, d.e_bytes);
   const float s = d.grad ? scale[d.block] : 0.0f;   // in-place matrices: E already holds M
   constexpr int GB = GradIO<GT>::kBytes;
   const int lu = threadIdx.x & 15, lr = threadIdx.x >> 4;
-  __shared__ __attribute__((aligned(16))) uint16_t th[ST][STP], tl[ST][STP];
   GLOBAL uint16_t* __restrict__ mh = gbl(d.mh);
   GLOBAL uint16_t* __restrict__ ml = gbl(d.ml);
   bool bad = false;
@@ -59,7 +60,7 @@ void k_split_m(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   }
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
-    const int rr = lr + 16 * st, row = i0 + rr, col = j0 + 4 * lu;
+    const int row = i0 + lr + 16 * st, col = j0 + 4 * lu;
     const f32x4 gf = gv[st].f32(), ef = ev[st].f32();
     f32x4 mv;
 #pragma unroll
@@ -71,23 +72,6 @@ void k_split_m(const DevMat* __restrict__ mats, const Work* __restrict__ work,
     const bf16x4 lo = __builtin_convertvector(mv - __builtin_convertvector(hi, f32x4), bf16x4);
     *gcast<u32x2>(mh + (int64_t)row * ldm + col) = __builtin_bit_cast(u32x2, hi);
     *gcast<u32x2>(ml + (int64_t)row * ldm + col) = __builtin_bit_cast(u32x2, lo);
-    *reinterpret_cast<bf16x4*>(&th[rr][4 * lu]) = hi;
-    *reinterpret_cast<bf16x4*>(&tl[rr][4 * lu]) = lo;
-  }
-  __syncthreads();
-  // transposed: row j0 + jj of M^T holds column j0 + jj of M; 4 consecutive rows of M per lane
-  GLOBAL uint16_t* __restrict__ mth = gbl(d.mth);
-  GLOBAL uint16_t* __restrict__ mtl = gbl(d.mtl);
-#pragma unroll
-  for (int st = 0; st < 4; ++st) {
-    const int jj = lr + 16 * st, ii = 4 * lu;
-    uint16_t h[4], l[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) { h[e] = th[ii + e][jj]; l[e] = tl[ii + e][jj]; }
-    const u32x2 hv = {(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
-    const u32x2 lv = {(uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16)};
-    *gcast<u32x2>(mth + (int64_t)(j0 + jj) * ldt + i0 + ii) = hv;
-    *gcast<u32x2>(mtl + (int64_t)(j0 + jj) * ldt + i0 + ii) = lv;
   }
   if (__builtin_amdgcn_ballot_w64(bad) != 0 && (threadIdx.x & (kWave - 1)) == 0) gbl(flags)[wi.mat] = 1;
 }
@@ -146,7 +130,7 @@ constexpr int GK = 32;                         // K per stage: LDS row = 32 bf16
 __device__ __forceinline__ int swzg(int rr, int q) { return q ^ ((rr >> 1) & 3); }
 
 struct GemmArgs {
-  rsrc_t ah, al, bh, bl;        // operand halves: A rows x K, B rows x K, K-contiguous
+  rsrc_t ah, al, bh, bl;        // operand halves: A rows x K (K x A rows when K-outer), B rows x K
   int lda, ldb, K;              // leading dimensions (elements), K a multiple of GK
   GLOBAL float* c; int ldc, crows, ccols;
 };
@@ -159,17 +143,31 @@ __device__ __forceinline__ GemmArgs gemm_args(const DevMat& d, int which) {
     g.bh = make_rsrc(d.qth, bb); g.bl = make_rsrc(d.qtl, bb);
     g.lda = d.npad_b; g.ldb = d.npad_b; g.K = d.npad_b;
     g.c = gbl(d.p_raw); g.ldc = d.rpad; g.crows = d.m; g.ccols = d.rpad;
-  } else {                      // q_next (n x r) = M^T P:  A = M^T (npad_b x mpad), B = P^T (rpad x mpad)
-    const uint32_t ab = (uint32_t)d.npad_b * (uint32_t)d.mpad * 2u, bb = (uint32_t)d.rpad * (uint32_t)d.mpad * 2u;
-    g.ah = make_rsrc(d.mth, ab); g.al = make_rsrc(d.mtl, ab);
+  } else {                      // q_next (n x r) = M^T P:  A = M^T, K-outer (M, mpad x npad_b), B = P^T (rpad x mpad)
+    const uint32_t ab = (uint32_t)d.mpad * (uint32_t)d.npad_b * 2u, bb = (uint32_t)d.rpad * (uint32_t)d.mpad * 2u;
+    g.ah = make_rsrc(d.mh, ab); g.al = make_rsrc(d.ml, ab);
     g.bh = make_rsrc(d.pt_hi, bb); g.bl = make_rsrc(d.pt_lo, bb);
-    g.lda = d.mpad; g.ldb = d.mpad; g.K = d.mpad;
+    g.lda = d.npad_b; g.ldb = d.mpad; g.K = d.mpad;
     g.c = gbl(d.q_next); g.ldc = d.r; g.crows = d.n; g.ccols = d.r;
   }
   return g;
 }
 
+// gfx950's transposing LDS read (ds_read_b64_tr_b16): each lane names 8 bytes (4 consecutive
+// 16-bit elements of one LDS row); within every 16 lanes, lane j receives element j % 4 of the
+// 8-byte pieces named by lanes j / 4, j / 4 + 4, j / 4 + 8 and j / 4 + 12, in that order. If
+// lane s of the 16 names row k0 + s / 4 at column c0 + 4 (s % 4), lane j therefore receives
+// rows k0 .. k0 + 3 of column c0 + j: 4 consecutive k of one row of A^T, as an MFMA operand
+// takes them.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+}
+
 // One work item: matrix `mat`, C tile rows a.., columns b.., product c (0: M q, 1: M^T P).
+// AT: A is stored K-outer (row k of the source holds A[.][k]); staged as GK LDS rows of GT_M
+// elements and read with the transposing LDS read.
+template <bool AT>
 __global__ __launch_bounds__(GM_THREADS, WRT == 4 ? 2 : 1)
 void k_gemm_nt(const DevMat* __restrict__ mats, const Work* __restrict__ work)
 {
@@ -182,22 +180,37 @@ void k_gemm_nt(const DevMat* __restrict__ mats, const Work* __restrict__ work)
   const int wm = wv & 1, wn = wv >> 1;
   const int c = lane & 15, g = lane >> 4;
 
-  __shared__ __attribute__((aligned(16))) uint16_t ldsA[2][2][GT_M][GK];   // [buf][hi/lo][row][k]
+  // K-outer A: LDS row = one k, GT_M elements plus 16 of padding (the 4 rows one 16-lane
+  // transposing read touches then start 32 bytes apart in the banks)
+  constexpr int ATP = GT_M + 16;
+  constexpr int A_ELEMS = AT ? GK * ATP : GT_M * GK;              // one buffer, one half
+  __shared__ __attribute__((aligned(16))) uint16_t ldsA[2][2][A_ELEMS];     // [buf][hi/lo][...]
   __shared__ __attribute__((aligned(16))) uint16_t ldsB[2][2][GT_N][GK];
 
   // staging: a 16-byte unit is 8 consecutive k of one row; 4 units per row, UA (UB) per
   // thread and operand half. Rows past the operand's padded extent read zeros. Two register
   // sets hold the next two stages, so a stage's loads have two stages of products to arrive.
+  // K-outer A: a unit is 8 consecutive A rows at one k; 16 units per k (GT_M / 8 = 16), and
+  // A rows past lda (the padded row length of the source) read zeros.
   struct Regs { u32x4 a[UA][2], b[UB][2]; };     // [unit][hi/lo]
   Regs R0, R1;
   uint32_t aoff[UA], boff[UB];
   int arow[UA], aq[UA], brow[UB], bq[UB];
+  bool aok[UA];
 #pragma unroll
   for (int j = 0; j < UA; ++j) {
     const int u = threadIdx.x + GM_THREADS * j;
-    arow[j] = u >> 2;
-    aq[j] = u & 3;
-    aoff[j] = ((uint32_t)(i0 + arow[j]) * (uint32_t)ga.lda + 8u * aq[j]) * 2u;
+    if constexpr (AT) {
+      arow[j] = u >> 4;                           // k within the stage
+      aq[j] = u & 15;                             // unit along the A rows
+      aok[j] = i0 + 8 * aq[j] < ga.lda;
+      aoff[j] = ((uint32_t)arow[j] * (uint32_t)ga.lda + (uint32_t)(i0 + 8 * aq[j])) * 2u;
+    } else {
+      arow[j] = u >> 2;
+      aq[j] = u & 3;
+      aok[j] = true;
+      aoff[j] = ((uint32_t)(i0 + arow[j]) * (uint32_t)ga.lda + 8u * aq[j]) * 2u;
+    }
   }
 #pragma unroll
   for (int j = 0; j < UB; ++j) {
@@ -208,10 +221,11 @@ void k_gemm_nt(const DevMat* __restrict__ mats, const Work* __restrict__ work)
   }
   auto load_stage = [&](Regs& R, int k0) {
     const uint32_t kb = (uint32_t)k0 * 2u;
+    const uint32_t kba = AT ? (uint32_t)k0 * (uint32_t)ga.lda * 2u : kb;
 #pragma unroll
     for (int j = 0; j < UA; ++j) {
-      R.a[j][0] = bload16(ga.ah, aoff[j] + kb);
-      R.a[j][1] = bload16(ga.al, aoff[j] + kb);
+      R.a[j][0] = bload16(ga.ah, aok[j] ? aoff[j] + kba : kOOB);
+      R.a[j][1] = bload16(ga.al, aok[j] ? aoff[j] + kba : kOOB);
     }
 #pragma unroll
     for (int j = 0; j < UB; ++j) {
@@ -223,8 +237,10 @@ void k_gemm_nt(const DevMat* __restrict__ mats, const Work* __restrict__ work)
 #pragma unroll
     for (int j = 0; j < UA; ++j)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        *reinterpret_cast<u32x4*>(&ldsA[buf][h][arow[j]][8 * swzg(arow[j], aq[j])]) = R.a[j][h];
+      for (int h = 0; h < 2; ++h) {
+        const int off = AT ? arow[j] * ATP + 8 * aq[j] : arow[j] * GK + 8 * swzg(arow[j], aq[j]);
+        *reinterpret_cast<u32x4*>(&ldsA[buf][h][off]) = R.a[j][h];
+      }
 #pragma unroll
     for (int j = 0; j < UB; ++j)
 #pragma unroll
@@ -247,9 +263,19 @@ void k_gemm_nt(const DevMat* __restrict__ mats, const Work* __restrict__ work)
     }
 #pragma unroll
     for (int im = 0; im < WRT; ++im) {
-      const int ra = wm * (WRT * 16) + im * 16 + c;
-      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&ldsA[buf][0][ra][8 * swzg(ra, g)]);
-      const bf16x8 al = *reinterpret_cast<const bf16x8*>(&ldsA[buf][1][ra][8 * swzg(ra, g)]);
+      bf16x8 ah, al;
+      if constexpr (AT) {
+        // rows k = 8 g .. 8 g + 7 of A row wm * 16 WRT + 16 im + c, in two transposing reads
+        const int off = (8 * g + (c >> 2)) * ATP + wm * (WRT * 16) + im * 16 + 4 * (c & 3);
+        const i16x4 h0 = lds_read_tr16(&ldsA[buf][0][off]), h1 = lds_read_tr16(&ldsA[buf][0][off + 4 * ATP]);
+        const i16x4 l0 = lds_read_tr16(&ldsA[buf][1][off]), l1 = lds_read_tr16(&ldsA[buf][1][off + 4 * ATP]);
+        ah = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+        al = __builtin_bit_cast(bf16x8, __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7));
+      } else {
+        const int ra = wm * (WRT * 16) + im * 16 + c;
+        ah = *reinterpret_cast<const bf16x8*>(&ldsA[buf][0][ra * GK + 8 * swzg(ra, g)]);
+        al = *reinterpret_cast<const bf16x8*>(&ldsA[buf][1][ra * GK + 8 * swzg(ra, g)]);
+      }
 #pragma unroll
       for (int jn = 0; jn < 4; ++jn) {
         acc[im][jn] = mfma_bf16(ah, bh[jn], acc[im][jn]);
@@ -317,9 +343,10 @@ hipError_t launch_split_qt(const DevMat* mats, const Work* work, int n_work, hip
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_nt(const DevMat* mats, const Work* work, int n_work, hipStream_t s) {
+hipError_t launch_gemm_nt(const DevMat* mats, const Work* work, int n_work, bool a_k_outer, hipStream_t s) {
   if (n_work <= 0) return hipSuccess;
-  k_gemm_nt<<<dim3(n_work), dim3(GM_THREADS), 0, s>>>(mats, work);
+  if (a_k_outer) k_gemm_nt<true><<<dim3(n_work), dim3(GM_THREADS), 0, s>>>(mats, work);
+  else k_gemm_nt<false><<<dim3(n_work), dim3(GM_THREADS), 0, s>>>(mats, work);
   return hipGetLastError();
 }
 

@@ -148,7 +148,6 @@ struct DevMat {
   int32_t* reorth;                     // 1: this step's factor needs a second pass
   // r > 128: M split once per step into bf16 halves for the two factor GEMMs
   uint16_t* mh; uint16_t* ml;          // mpad x npad_b: M (zero beyond m x n)
-  uint16_t* mth; uint16_t* mtl;        // npad_b x mpad: M^T
   uint16_t* qth; uint16_t* qtl;        // rpad_b x npad_b: q^T (zero beyond r x n)
   int32_t npad_b;                      // n rounded up to 64
   int32_t rpad_b;                      // rpad rounded up to a whole GEMM tile (128)
@@ -316,7 +315,7 @@ int big_gemm_tile_n();
 hipError_t launch_split_m(int gt, const DevMat* mats, const Work* work, int n_work, const float* scale,
                           uint8_t* flags, hipStream_t s);
 hipError_t launch_split_qt(const DevMat* mats, const Work* work, int n_work, hipStream_t s);
-hipError_t launch_gemm_nt(const DevMat* mats, const Work* work, int n_work, hipStream_t s);
+hipError_t launch_gemm_nt(const DevMat* mats, const Work* work, int n_work, bool a_k_outer, hipStream_t s);
 hipError_t launch_block_enter(int dt, const float* dx, int64_t n, const float* scale, uint16_t* out,
                               hipStream_t s);
 hipError_t launch_block_exit(int dt, float* dx, const uint16_t* g, int64_t n, const float* scale,

@@ -188,7 +188,7 @@ namespace {
 
 // Workspace offsets of one matrix's buffers (bytes from the workspace base).
 struct PlanOff {
-  size_t p_raw, pth, ptl, p3e, q3e, gram, tmat, wsum, wdiag, p2, reorth, mh, ml, mth, mtl, qth, qtl;
+  size_t p_raw, pth, ptl, p3e, q3e, gram, tmat, wsum, wdiag, p2, reorth, mh, ml, qth, qtl;
 };
 struct PlanLayout {
   std::vector<PlanOff> offs;
@@ -308,12 +308,13 @@ psgd_status plan_layout(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats, psgd
     d.npad_b = (int)rup(a.n, psgd::big_split_tile());
     d.rpad_b = (int)rup(rpad, psgd::big_gemm_tile_n());
     if (big) {
-      // the split operands of the two factor GEMMs: M and M^T (2 x 4 bytes per element of the
-      // padded matrix) and q^T; each half addressed through a buffer range below 2 GiB
+      // the split operands of the two factor GEMMs: M (4 bytes per element of the padded
+      // matrix; M^T P reads it K-outer) and q^T; each half addressed through a buffer range
+      // below 2 GiB
       const size_t mb = (size_t)d.mpad * d.npad_b * 2, qb = (size_t)d.rpad_b * d.npad_b * 2;
       if (mb >= (size_t(1) << 31))
         return fail(ctx, PSGD_EINVAL, "matrix %d: %d x %d is too large for ranks above 128 (each bf16 half of M must span less than 2 GiB)", i, (int)a.m, (int)a.n);
-      o.mh = take(mb); o.ml = take(mb); o.mth = take(mb); o.mtl = take(mb);
+      o.mh = take(mb); o.ml = take(mb);
       o.qth = take(qb); o.qtl = take(qb);
     }
   }
@@ -552,8 +553,6 @@ void plan_bind(psgd_plan* p, char* base, const PlanLayout& L) {
     if (big) {
       d.mh = reinterpret_cast<uint16_t*>(base + o.mh);
       d.ml = reinterpret_cast<uint16_t*>(base + o.ml);
-      d.mth = reinterpret_cast<uint16_t*>(base + o.mth);
-      d.mtl = reinterpret_cast<uint16_t*>(base + o.mtl);
       d.qth = reinterpret_cast<uint16_t*>(base + o.qth);
       d.qtl = reinterpret_cast<uint16_t*>(base + o.qtl);
     }
@@ -642,7 +641,7 @@ psgd_status psgd_compress_p(psgd_ctx* ctx, psgd_plan* plan, const float* scale, 
     HIPCHK(ctx, traced(ctx, S_K1, stream, [&] {
       hipError_t e = psgd::launch_split_m(plan->gt, dm, W(W_SPLITM), plan->cnt[W_SPLITM], scale, flags, stream);
       if (e == hipSuccess) e = psgd::launch_split_qt(dm, W(W_SPLITQT), plan->cnt[W_SPLITQT], stream);
-      if (e == hipSuccess) e = psgd::launch_gemm_nt(dm, W(W_G1), plan->cnt[W_G1], stream);
+      if (e == hipSuccess) e = psgd::launch_gemm_nt(dm, W(W_G1), plan->cnt[W_G1], false, stream);
       return e; }), "M Q");
     return PSGD_OK;
   }
@@ -694,7 +693,7 @@ psgd_status psgd_compress_q(psgd_ctx* ctx, psgd_plan* plan, const float* scale, 
   const DevMat* dm = plan->d_mats;
   auto W = [&](int k) { return plan->d_work + plan->off[k]; };
   if (plan->big)
-    HIPCHK(ctx, traced(ctx, S_K2, stream, [&] { return psgd::launch_gemm_nt(dm, W(W_G2), plan->cnt[W_G2], stream); }), "M^T P");
+    HIPCHK(ctx, traced(ctx, S_K2, stream, [&] { return psgd::launch_gemm_nt(dm, W(W_G2), plan->cnt[W_G2], true, stream); }), "M^T P");
   else
     HIPCHK(ctx, traced(ctx, S_K2, stream, [&] { return psgd::launch_mtp(plan->gt, plan->rtc, dm, W(W_K2), plan->cnt[W_K2], scale, stream); }), "M^T P");
   if (plan->big)
