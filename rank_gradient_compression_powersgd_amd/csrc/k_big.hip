@@ -128,6 +128,12 @@ constexpr int GK = 32;                         // K per stage: LDS row = 32 bf16
 // physical 16-byte unit of logical unit q in LDS row rr (64-byte rows): the 8 lanes of one LDS
 // pass read 8 consecutive rows and hit the 8 distinct 16-byte groups of the 32 banks
 __device__ __forceinline__ int swzg(int rr, int q) { return q ^ ((rr >> 1) & 3); }
+// K-outer A (LDS row = one k, 128 bf16 = 256 bytes = all 64 banks): physical 16-byte unit of
+// logical unit q in row k. A transposing read touches 32 bytes (a pair of units) in each of
+// 16 rows, k = 8 g + 4 h + t (g, t = 0..3); the pair index is XOR-ed with t + 4 (g & 1), so the
+// 8 rows of lanes 0..31 (g = 0, 1), and those of lanes 32..63, land on 8 distinct pairs: all
+// 64 banks once. Stores of whole rows stay conflict-free (a permutation within the row).
+__device__ __forceinline__ int swzt(int k, int q) { return q ^ (2 * ((k & 3) | (((k >> 3) & 1) << 2))); }
 
 struct GemmArgs {
   rsrc_t ah, al, bh, bl;        // operand halves: A rows x K (K x A rows when K-outer), B rows x K
@@ -180,9 +186,7 @@ void k_gemm_nt(const DevMat* __restrict__ mats, const Work* __restrict__ work)
   const int wm = wv & 1, wn = wv >> 1;
   const int c = lane & 15, g = lane >> 4;
 
-  // K-outer A: LDS row = one k, GT_M elements plus 16 of padding (the 4 rows one 16-lane
-  // transposing read touches then start 32 bytes apart in the banks)
-  constexpr int ATP = GT_M + 16;
+  constexpr int ATP = GT_M;                                       // K-outer A: LDS row pitch
   constexpr int A_ELEMS = AT ? GK * ATP : GT_M * GK;              // one buffer, one half
   __shared__ __attribute__((aligned(16))) uint16_t ldsA[2][2][A_ELEMS];     // [buf][hi/lo][...]
   __shared__ __attribute__((aligned(16))) uint16_t ldsB[2][2][GT_N][GK];
@@ -238,7 +242,7 @@ void k_gemm_nt(const DevMat* __restrict__ mats, const Work* __restrict__ work)
     for (int j = 0; j < UA; ++j)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int off = AT ? arow[j] * ATP + 8 * aq[j] : arow[j] * GK + 8 * swzg(arow[j], aq[j]);
+        const int off = AT ? arow[j] * ATP + 8 * swzt(arow[j], aq[j]) : arow[j] * GK + 8 * swzg(arow[j], aq[j]);
         *reinterpret_cast<u32x4*>(&ldsA[buf][h][off]) = R.a[j][h];
       }
 #pragma unroll
@@ -266,7 +270,9 @@ void k_gemm_nt(const DevMat* __restrict__ mats, const Work* __restrict__ work)
       bf16x8 ah, al;
       if constexpr (AT) {
         // rows k = 8 g .. 8 g + 7 of A row wm * 16 WRT + 16 im + c, in two transposing reads
-        const int off = (8 * g + (c >> 2)) * ATP + wm * (WRT * 16) + im * 16 + 4 * (c & 3);
+        // (rows k and k + 4 share their swizzle)
+        const int k = 8 * g + (c >> 2), q = (wm * (WRT * 16) + im * 16) / 8 + ((c & 3) >> 1);
+        const int off = k * ATP + 8 * swzt(k, q) + 4 * (c & 1);
         const i16x4 h0 = lds_read_tr16(&ldsA[buf][0][off]), h1 = lds_read_tr16(&ldsA[buf][0][off + 4 * ATP]);
         const i16x4 l0 = lds_read_tr16(&ldsA[buf][1][off]), l1 = lds_read_tr16(&ldsA[buf][1][off + 4 * ATP]);
         ah = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
