@@ -101,7 +101,7 @@ def test_noalloc_step_matches_the_plan_step_twice_then_smaller():
 
 
 def test_noalloc_step_large_rank_matches_the_plan_step():
-    """Rank 160: the split-once GEMM path (M and M^T split into the scratch array, the balanced
+    """Rank 160: the split-once GEMM path (M split into the scratch array, the balanced
     GEMM lists) and the blocked factorisation, twice in a row, the second group smaller."""
     from rank_gradient_compression_powersgd_amd import binding as B
     ctx = B.psgd_create(0, 160)
