@@ -18,6 +18,12 @@
 // The workgroups of the first row of tiles also copy the q_next rows they stage into q (the
 // warm start of the next step), so a non-skipped step commits q without a pass of its own.
 //
+// PS (ranks above one chunk): the factors arrive already scaled and split into fp16 halves
+// (written once per step with the row exponents), and a stage is a plain copy into LDS. Each
+// factor row is otherwise split again in every tile that uses it, about 14 conversions per
+// output element at r = 896. q then comes from q_next directly, each tile of a column block
+// copying its share of the block's rows, so that no row of tiles carries the whole copy.
+//
 // Skip: the device-side skip word is read first. A skipped step zeroes the error buffer over
 // the tile and writes nothing else (the error buffer is zeroed on non-finite values: Korean
 // summary of the paper, section "Distributed Optimization").
@@ -111,7 +117,7 @@ template <> struct ParamIO<G_F32> {
   }
 };
 
-template <int GT, int PT>
+template <int GT, int PT, bool PS>
 __global__ __launch_bounds__(K3_THREADS, K3_OCC)
 void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
               const float* __restrict__ scale, const int32_t* __restrict__ skip, AdamArgs aa,
@@ -189,7 +195,21 @@ void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
       v[e] = __builtin_bit_cast(float, bload4(rs_, k + e < r ? rowoff + 4u * (k + e) : kOOB));
     return v;
   };
+  // split factors: a row holds kpad3 ranks as 16-byte (hi, lo) pairs per 8 ranks, so the 8
+  // threads of a row read the stage's 128 bytes in order: thread hq the hi (hq even) or lo
+  // half of ranks k0 + 8 (hq / 2) ..; the buffers cover whole tiles (zero rows past m, n)
+  const rsrc_t rsqh = make_rsrc(d.q3h, PS ? (uint32_t)((n + K3_TN - 1) / K3_TN * K3_TN) * (uint32_t)kpad3 * 4u : 0u);
+  const rsrc_t rsph = make_rsrc(d.p3h, PS ? (uint32_t)((m + K3_TM - 1) / K3_TM * K3_TM) * (uint32_t)kpad3 * 4u : 0u);
   auto load_stage = [&](int k0) {
+    if constexpr (PS) {
+#pragma unroll
+      for (int j = 0; j < QG; ++j)
+        sq[j] = __builtin_bit_cast(f32x4, bload16(rsqh, ((uint32_t)(n0 + rq0 + RSTEP3 * j) * (uint32_t)kpad3 + (uint32_t)k0) * 4u + 16u * hq));
+#pragma unroll
+      for (int j = 0; j < PG; ++j)
+        sp[j] = __builtin_bit_cast(f32x4, bload16(rsph, ((uint32_t)(m0 + rq0 + RSTEP3 * j) * (uint32_t)kpad3 + (uint32_t)k0) * 4u + 16u * hq));
+      return;
+    }
     const int k = k0 + 4 * hq;
 #pragma unroll
     for (int j = 0; j < QG; ++j) sq[j] = load_group(rsq, qrow[j], k);
@@ -209,9 +229,23 @@ void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   };
   // The first row of tiles also commits q <- q_next (the step is not skipped here): it writes
   // the fp32 groups of q_next it has just read to the same place in q.
-  const bool commit = m0 == 0;
+  const bool commit = !PS && m0 == 0;
   const rsrc_t rqc = make_rsrc(d.q, commit ? (uint32_t)n * (uint32_t)r * 4u : 0u);
   auto store_stage = [&](int buf, int k0) {
+    if constexpr (PS) {
+      const int h = hq & 1;
+#pragma unroll
+      for (int j = 0; j < QG; ++j) {
+        const int rr = rq0 + RSTEP3 * j;
+        *reinterpret_cast<f32x4*>(&ldq[buf][h][rr][8 * swz3(rr, hq >> 1)]) = sq[j];
+      }
+#pragma unroll
+      for (int j = 0; j < PG; ++j) {
+        const int rr = rq0 + RSTEP3 * j;
+        *reinterpret_cast<f32x4*>(&ldp[buf][h][rr][8 * swz3(rr, hq >> 1)]) = sp[j];
+      }
+      return;
+    }
     const int k = k0 + 4 * hq;
 #pragma unroll
     for (int j = 0; j < QG; ++j) {
@@ -264,6 +298,23 @@ void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
     }
   };
 
+  if constexpr (PS) {
+    // q <- q_next: the tiles of this column block share its rows, in order of their row block
+    const int mt = (m + K3_TM - 1) / K3_TM, share = (K3_TN + mt - 1) / mt;
+    const int rb = n0 + (m0 / K3_TM) * share;
+    const int re_ = min(min(rb + share, n0 + K3_TN), n);
+    if (rb < re_) {
+      const GLOBAL float* __restrict__ qn = gbl(d.q_next);
+      GLOBAL float* __restrict__ qc = gbl(d.q);
+      const int64_t b = (int64_t)rb * r, e = (int64_t)re_ * r;
+      if (rvec) {
+        for (int64_t i = b / 4 + threadIdx.x; i < e / 4; i += K3_THREADS)
+          *gcast<f32x4>(qc + 4 * i) = *gcast<f32x4>(qn + 4 * i);
+      } else {
+        for (int64_t i = b + threadIdx.x; i < e; i += K3_THREADS) qc[i] = qn[i];
+      }
+    }
+  }
   const int nsteps = kpad3 / 32;
   load_stage(0);
   store_stage(0, 0);
@@ -408,18 +459,19 @@ void k_decomp(const DevMat* __restrict__ mats, const Work* __restrict__ work,
 }
 
 template <int GT, int PT>
-hipError_t launch_gt(dim3 grid, hipStream_t s, const DevMat* mats, const Work* work,
+hipError_t launch_gt(bool ps, dim3 grid, hipStream_t s, const DevMat* mats, const Work* work,
                      const float* scale, const int32_t* skip, const AdamArgs& aa, int64_t* counters) {
-  k_decomp<GT, PT><<<grid, dim3(K3_THREADS), 0, s>>>(mats, work, scale, skip, aa, counters);
+  if (ps) k_decomp<GT, PT, true><<<grid, dim3(K3_THREADS), 0, s>>>(mats, work, scale, skip, aa, counters);
+  else k_decomp<GT, PT, false><<<grid, dim3(K3_THREADS), 0, s>>>(mats, work, scale, skip, aa, counters);
   return hipGetLastError();
 }
 template <int PT>
-hipError_t launch_pt(int gt, dim3 grid, hipStream_t s, const DevMat* mats, const Work* work,
+hipError_t launch_pt(int gt, bool ps, dim3 grid, hipStream_t s, const DevMat* mats, const Work* work,
                      const float* scale, const int32_t* skip, const AdamArgs& aa, int64_t* counters) {
   switch (gt) {
-    case G_F16: return launch_gt<G_F16, PT>(grid, s, mats, work, scale, skip, aa, counters);
-    case G_BF16: return launch_gt<G_BF16, PT>(grid, s, mats, work, scale, skip, aa, counters);
-    case G_F32: return launch_gt<G_F32, PT>(grid, s, mats, work, scale, skip, aa, counters);
+    case G_F16: return launch_gt<G_F16, PT>(ps, grid, s, mats, work, scale, skip, aa, counters);
+    case G_BF16: return launch_gt<G_BF16, PT>(ps, grid, s, mats, work, scale, skip, aa, counters);
+    case G_F32: return launch_gt<G_F32, PT>(ps, grid, s, mats, work, scale, skip, aa, counters);
   }
   return hipErrorInvalidValue;
 }
@@ -429,20 +481,20 @@ hipError_t launch_pt(int gt, dim3 grid, hipStream_t s, const DevMat* mats, const
 int decomp_tile_m() { return K3_TM; }
 int decomp_tile_n() { return K3_TN; }
 
-hipError_t launch_decompress(int gt, const DevMat* mats, const Work* work, int n_work,
+hipError_t launch_decompress(int gt, bool presplit, const DevMat* mats, const Work* work, int n_work,
                              const float* scale, const int32_t* skip, int64_t* counters, hipStream_t s) {
   if (n_work <= 0) return hipSuccess;
-  return launch_pt<0>(gt, dim3(n_work), s, mats, work, scale, skip, AdamArgs{}, counters);
+  return launch_pt<0>(gt, presplit, dim3(n_work), s, mats, work, scale, skip, AdamArgs{}, counters);
 }
 
-hipError_t launch_decompress_adam(int gt, int pt, const DevMat* mats, const Work* work, int n_work,
+hipError_t launch_decompress_adam(int gt, int pt, bool presplit, const DevMat* mats, const Work* work, int n_work,
                                   const float* scale, const int32_t* skip, const AdamArgs& aa,
                                   int64_t* counters, hipStream_t s) {
   if (n_work <= 0) return hipSuccess;
   switch (pt) {
-    case G_F16: return launch_pt<G_F16>(gt, dim3(n_work), s, mats, work, scale, skip, aa, counters);
-    case G_BF16: return launch_pt<G_BF16>(gt, dim3(n_work), s, mats, work, scale, skip, aa, counters);
-    case G_F32: return launch_pt<G_F32>(gt, dim3(n_work), s, mats, work, scale, skip, aa, counters);
+    case G_F16: return launch_pt<G_F16>(gt, presplit, dim3(n_work), s, mats, work, scale, skip, aa, counters);
+    case G_BF16: return launch_pt<G_BF16>(gt, presplit, dim3(n_work), s, mats, work, scale, skip, aa, counters);
+    case G_F32: return launch_pt<G_F32>(gt, presplit, dim3(n_work), s, mats, work, scale, skip, aa, counters);
   }
   return hipErrorInvalidValue;
 }

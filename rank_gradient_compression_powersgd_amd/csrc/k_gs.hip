@@ -879,9 +879,12 @@ void k_gs_apply(const DevMat* __restrict__ mats, const Work* __restrict__ work, 
 
 // Row exponents of the decompression operands (ranks above one chunk, or q_next after the
 // caller changed it): for each row of P_hat (which = 0, from p) or of Q' (which = 1, from
-// q_next), the power of two that brings its largest entry into [2^13, 2^14). One work item:
-// 64 rows [a, a + 64) of matrix `mat`, which = b; one wave per row at a time, each lane loading
-// up to two 8-rank units of the row at once.
+// q_next), the power of two that brings its largest entry into [2^13, 2^14). Ranks above one
+// chunk also get the row, scaled by that power, split into fp16 hi + lo once here, for the
+// decompression to copy into its stages: kpad3 ranks per row as 16-byte pairs per 8 ranks (hi,
+// then lo), ranks past r zero; the same arithmetic as the decompression's own split of fp32
+// factors. One work item: 64 rows [a, a + 64) of matrix `mat`, which = b; one wave per row at
+// a time, each lane holding up to two 8-rank units of the row.
 constexpr int S3_UNITS = kMaxRank / 8 / kWave;   // 8-rank units per lane
 __global__ __launch_bounds__(256)
 void k_split3(const DevMat* __restrict__ mats, const Work* __restrict__ work)
@@ -889,33 +892,54 @@ void k_split3(const DevMat* __restrict__ mats, const Work* __restrict__ work)
   const Work wi = work[blockIdx.x];
   if (wi.mat < 0) return;
   const DevMat& d = mats[wi.mat];
-  const int r = d.r;
+  const int r = d.r, kpad3 = d.kpad3;
   const bool isq = wi.b != 0;
   const int rows = isq ? d.n : d.m;
   const GLOBAL float* __restrict__ src = gbl(isq ? d.q_next : d.p);
   GLOBAL int32_t* __restrict__ ex = gbl(isq ? d.q3_exp : d.p3_exp);
+  GLOBAL uint16_t* __restrict__ halves = gbl(isq ? d.q3h : d.p3h);   // NULL: exponents only
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
   const bool rvec = (r & 3) == 0;               // rows start 16-byte aligned
   for (int row = wi.a + wv; row < wi.a + 64 && row < rows; row += 4) {
     const GLOBAL float* __restrict__ x = src + (int64_t)row * r;
     float amax = 0.0f;
+    f32x4 v[S3_UNITS][2];
 #pragma unroll
     for (int u = 0; u < S3_UNITS; ++u) {
       const int k = 8 * (lane + kWave * u);
       if (rvec && k + 8 <= r) {
-        const f32x4 a = *gcast<f32x4>(x + k), b = *gcast<f32x4>(x + k + 4);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) amax = fmaxf(amax, fmaxf(fabsf(a[t]), fabsf(b[t])));
+        v[u][0] = *gcast<f32x4>(x + k);
+        v[u][1] = *gcast<f32x4>(x + k + 4);
       } else {
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
-          if (k + t < r) amax = fmaxf(amax, fabsf(x[k + t]));
+        for (int t = 0; t < 8; ++t) v[u][t >> 2][t & 3] = k + t < r ? x[k + t] : 0.0f;
       }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) amax = fmaxf(amax, fmaxf(fabsf(v[u][0][t]), fabsf(v[u][1][t])));
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-    if (lane == 0) ex[row] = fp16_row_exponent(amax);
+    const int e = fp16_row_exponent(amax);
+    if (lane == 0) ex[row] = e;
+    if (halves != nullptr) {
+      GLOBAL uint16_t* __restrict__ hrow = halves + (int64_t)row * kpad3 * 2;
+#pragma unroll
+      for (int u = 0; u < S3_UNITS; ++u) {
+        const int k = 8 * (lane + kWave * u);
+        if (k >= kpad3) continue;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          f32x4 xs;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) xs[t] = ldexpf(v[u][h][t], e);
+          const f16x4 hi = __builtin_convertvector(xs, f16x4);
+          const f16x4 lo = __builtin_convertvector(xs - __builtin_convertvector(hi, f32x4), f16x4);
+          *gcast<f16x4>(hrow + 2 * k + 4 * h) = hi;
+          *gcast<f16x4>(hrow + 2 * k + 8 + 4 * h) = lo;
+        }
+      }
+    }
   }
 }
 

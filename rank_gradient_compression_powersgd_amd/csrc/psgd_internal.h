@@ -138,6 +138,10 @@ struct DevMat {
   int32_t* p3_exp;                     // m3 (m rounded up to a decompression tile; zero rows):
                                        // row exponent of P for the decompression's fp16 split
   int32_t* q3_exp;                     // n3 likewise for q_next
+  uint16_t* p3h;                       // r > 128 (else NULL): m3 rows of kpad3 ranks, P_hat scaled
+                                       // by its row exponent and split into fp16 hi + lo, as
+                                       // 16-byte pairs per 8 ranks (hi, then lo); zero rows past m
+  uint16_t* q3h;                       // n3 rows likewise for q_next
   double* gram;                        // gram_parts x rpad x rpad fp64 partial Gram matrices
   double* tmat;                        // rpad x rpad fp64 upper-triangular T, P = (M q) T
   double* wsum;                        // rpad x rpad fp64 summed Gram matrix, updated in place by
@@ -298,14 +302,14 @@ hipError_t launch_gs_apply(int rt, bool big, int pass, const DevMat* mats, const
 hipError_t launch_split3(const DevMat* mats, const Work* work, int n_work, hipStream_t s);
 hipError_t launch_mtp(int gt, int rtc, const DevMat* mats, const Work* work, int n_work,
                       const float* scale, hipStream_t s);
-hipError_t launch_decompress(int gt, const DevMat* mats, const Work* work, int n_work,
+hipError_t launch_decompress(int gt, bool presplit, const DevMat* mats, const Work* work, int n_work,
                              const float* scale, const int32_t* skip, int64_t* counters, hipStream_t s);
 hipError_t launch_sqnorm(const NormItem* items, int n_items, double* partial, hipStream_t s);
 hipError_t launch_adam_finalize(const double* partial, int n, float max_norm, const int32_t* skip,
                                 int32_t* step, float* norm_out, hipStream_t s);
 hipError_t launch_adam_f32(const AdamTensor* ts, int n, const AdamArgs& aa, const int32_t* skip,
                            hipStream_t s);
-hipError_t launch_decompress_adam(int gt, int pt, const DevMat* mats, const Work* work, int n_work,
+hipError_t launch_decompress_adam(int gt, int pt, bool presplit, const DevMat* mats, const Work* work, int n_work,
                                   const float* scale, const int32_t* skip, const AdamArgs& aa,
                                   int64_t* counters, hipStream_t s);
 struct PassList;

@@ -188,7 +188,7 @@ namespace {
 
 // Workspace offsets of one matrix's buffers (bytes from the workspace base).
 struct PlanOff {
-  size_t p_raw, pth, ptl, p3e, q3e, gram, tmat, wsum, wdiag, p2, reorth, mh, ml, qth, qtl;
+  size_t p_raw, pth, ptl, p3e, q3e, p3h, q3h, gram, tmat, wsum, wdiag, p2, reorth, mh, ml, qth, qtl;
 };
 struct PlanLayout {
   std::vector<PlanOff> offs;
@@ -299,6 +299,13 @@ psgd_status plan_layout(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats, psgd
     const int64_t m3 = rup(a.m, psgd::decomp_tile_m()), n3 = rup(a.n, psgd::decomp_tile_n());
     o.p3e = take((size_t)m3 * 4);              // zero rows up to a whole decompression tile
     o.q3e = take((size_t)n3 * 4);
+    if (big) {
+      // the decompression's factors split once per step (fp16 hi + lo, 4 bytes per entry)
+      if (m3 * kpad3 * 4 >= (int64_t(1) << 31) || n3 * kpad3 * 4 >= (int64_t(1) << 31))
+        return fail(ctx, PSGD_EINVAL, "matrix %d: the split decompression factors must each span less than 2 GiB", i);
+      o.p3h = take((size_t)m3 * kpad3 * 4);
+      o.q3h = take((size_t)n3 * kpad3 * 4);
+    }
     o.gram = take((size_t)d.gram_parts * rpad * rpad * 8);
     o.tmat = take((size_t)rpad * rpad * 8);
     o.wsum = big ? take((size_t)rpad * rpad * 8) : 0;
@@ -544,6 +551,8 @@ void plan_bind(psgd_plan* p, char* base, const PlanLayout& L) {
     d.pt_lo = reinterpret_cast<uint16_t*>(base + o.ptl);
     d.p3_exp = reinterpret_cast<int32_t*>(base + o.p3e);
     d.q3_exp = reinterpret_cast<int32_t*>(base + o.q3e);
+    d.p3h = big ? reinterpret_cast<uint16_t*>(base + o.p3h) : nullptr;
+    d.q3h = big ? reinterpret_cast<uint16_t*>(base + o.q3h) : nullptr;
     d.gram = reinterpret_cast<double*>(base + o.gram);
     d.tmat = reinterpret_cast<double*>(base + o.tmat);
     d.wsum = big ? reinterpret_cast<double*>(base + o.wsum) : nullptr;
@@ -762,7 +771,7 @@ psgd_status psgd_decompress_update(psgd_ctx* ctx, psgd_plan* plan, const float* 
   HIPCHK(ctx, hipSetDevice(ctx->device), "hipSetDevice");
   const DevMat* dm = plan->d_mats;
   auto W = [&](int k) { return plan->d_work + plan->off[k]; };
-  HIPCHK(ctx, traced(ctx, S_K3, stream, [&] { return psgd::launch_decompress(plan->gt, dm, W(W_K3), plan->cnt[W_K3], scale, skip_dev, plan->d_counters, stream); }), "decompress");
+  HIPCHK(ctx, traced(ctx, S_K3, stream, [&] { return psgd::launch_decompress(plan->gt, plan->big, dm, W(W_K3), plan->cnt[W_K3], scale, skip_dev, plan->d_counters, stream); }), "decompress");
   return PSGD_OK;
 }
 
@@ -774,7 +783,7 @@ psgd_status psgd_reset_errors(psgd_ctx* ctx, psgd_plan* plan, hipStream_t stream
   // the decompression's skipped form zeroes every error buffer and touches nothing else (no
   // scale is read on that path; the pointer only has to be valid)
   const float* any_scale = reinterpret_cast<const float*>(plan->d_one);
-  HIPCHK(ctx, traced(ctx, S_K3, stream, [&] { return psgd::launch_decompress(plan->gt, plan->d_mats, plan->d_work + plan->off[W_K3], plan->cnt[W_K3], any_scale, plan->d_one, nullptr, stream); }), "error buffer reset");
+  HIPCHK(ctx, traced(ctx, S_K3, stream, [&] { return psgd::launch_decompress(plan->gt, plan->big, plan->d_mats, plan->d_work + plan->off[W_K3], plan->cnt[W_K3], any_scale, plan->d_one, nullptr, stream); }), "error buffer reset");
   return PSGD_OK;
 }
 
@@ -986,7 +995,7 @@ psgd_status psgd_decompress_adam(psgd_ctx* ctx, psgd_plan* plan, const float* sc
   if (psgd_status st = check_hparams(ctx, hp); st != PSGD_OK) return st;
   const psgd::AdamArgs aa = adam_args(hp, step_dev, norm_dev);
   HIPCHK(ctx, traced(ctx, S_K3_ADAM, stream, [&] {
-    return psgd::launch_decompress_adam(plan->gt, plan->adam_pt, plan->d_mats, plan->d_work + plan->off[W_K3],
+    return psgd::launch_decompress_adam(plan->gt, plan->adam_pt, plan->big, plan->d_mats, plan->d_work + plan->off[W_K3],
                                         plan->cnt[W_K3], scale, skip_dev, aa, plan->d_counters, stream); }), "decompression with Adam");
   return PSGD_OK;
 }
