@@ -125,10 +125,9 @@ psgd_status psgd_destroy(psgd_ctx* ctx);
  * (the grouped all-reduce of "Zero-Shot Text-to-Image Generation — 中文验证版", section 证据).
  * Validates every matrix, allocates and zeroes the plan workspace (about 16 bytes per element
  * of the m x r factors, plus 4 per gradient element and 4 per factor element when the rank is
- * above 128), and uploads
- * the descriptor tables once (synchronously, on the null stream). The pointers in `mats` are
- * captured: the same buffers are used by every later call on the plan. n_blocks is the length
- * of the scale array later calls pass.
+ * above 128), and uploads the descriptor tables once (synchronously, on the null stream). The
+ * pointers in `mats` are captured: the same buffers are used by every later call on the plan.
+ * n_blocks is the length of the scale array later calls pass.
  */
 psgd_status psgd_plan_create(psgd_ctx* ctx, const psgd_matrix* mats, int n_mats,
                              psgd_dtype grad_dtype, int n_blocks, psgd_plan** plan);
@@ -342,8 +341,7 @@ psgd_status psgd_adam_update(psgd_ctx* ctx, const psgd_adam_tensor* pass, int n_
  *  the process ends). A group that needs more (about 12 bytes per element of the m x r
  *  factors plus 8 r^2 bytes per 256 rows at r <= 128: one 3968-wide resblock shard at rank
  *  112 takes about 19 MiB; ranks above 128 add 4 bytes per gradient element and 4 per factor
- *  element) is rejected with
- *  PSGD_EINVAL before anything is launched.
+ *  element) is rejected with PSGD_EINVAL before anything is launched.
  *  The call launches kernels only (a fill, uploads of the tables as kernel arguments, then the
  *  step's kernels), all on `stream`, and returns without synchronising. Every call on a device
  *  shares that device's array and overwrites the previous call's contents: calls on one
