@@ -170,9 +170,9 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
 }
 
-// One work item: matrix `mat`, C tile rows a.., columns b.., product c (0: M q, 1: M^T P).
-// AT: A is stored K-outer (row k of the source holds A[.][k]); staged as GK LDS rows of GT_M
-// elements and read with the transposing LDS read.
+// One work item: matrix `mat`, C tile rows a.., columns b.. of the product AT selects: M q
+// (AT false) or M^T P (AT true, A stored K-outer: row k of M holds A[.][k]; staged as GK LDS
+// rows of GT_M elements and read with the transposing LDS read).
 template <bool AT>
 __global__ __launch_bounds__(GM_THREADS, WRT == 4 ? 2 : 1)
 void k_gemm_nt(const DevMat* __restrict__ mats, const Work* __restrict__ work)
@@ -180,7 +180,7 @@ void k_gemm_nt(const DevMat* __restrict__ mats, const Work* __restrict__ work)
   const Work wi = work[xcd_remap(blockIdx.x, gridDim.x)];
   if (wi.mat < 0) return;
   const DevMat& d = mats[wi.mat];
-  const GemmArgs ga = gemm_args(d, wi.c);
+  const GemmArgs ga = gemm_args(d, AT ? 1 : 0);
   const int i0 = wi.a, j0 = wi.b;
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
   const int wm = wv & 1, wn = wv >> 1;
