@@ -376,10 +376,11 @@ def test_invalid_arguments_rejected():
 # ------------------------------------------------------------------------------------------
 # ranks above 128: M split once, the two products as GEMMs, blocked orthonormalisation
 # ------------------------------------------------------------------------------------------
-@pytest.mark.parametrize("dtype,rank", [("f16", 200), ("bf16", 260), ("f32", 136), ("f16", 1024)])
+@pytest.mark.parametrize("dtype,rank", [("f16", 200), ("bf16", 260), ("f32", 136), ("f16", 1024), ("bf16", 201)])
 def test_large_rank_ragged(dtype, rank):
     """Ranks above 128 with ragged shapes, every gradient dtype; rank 1024 is the largest the
-    library takes (eight 128-column blocks)."""
+    library takes (eight 128-column blocks), and the odd rank 201 leaves factor rows that are not
+    whole 16-byte units."""
     shapes = [(1000, 1536), (700, 520), (300, 264)] if rank <= 300 else [(1100, 1032), (1030, 1088)]
     rng = np.random.default_rng(8000 + rank)
     blocks = [0, 1, 0][:len(shapes)]
