@@ -133,3 +133,23 @@ def test_noalloc_step_rejects_a_group_beyond_the_scratch_array():
         assert int(bufs.flags[0].item()) == 7
     finally:
         B.psgd_destroy(ctx)
+
+
+@pytest.mark.parametrize("rank", [80, 129])
+def test_noalloc_step_over_random_groups_in_a_row(rank):
+    """Ten seeded random groups in a row on one context (one to three ragged matrices, blocks
+    and a NaN-gradient skip step drawn per group), each against the plan path bit for bit: the
+    scratch array is re-laid out for every group and must hold no state from the one before."""
+    from rank_gradient_compression_powersgd_amd import binding as B
+    rng = np.random.default_rng(8_200_000 + rank)
+    ctx = B.psgd_create(0, rank)
+    try:
+        for k in range(10):
+            shapes = [(int(rng.integers(rank, rank + 600)), 8 * int(rng.integers((rank + 7) // 8, (rank + 7) // 8 + 90)))
+                      for _ in range(int(rng.integers(1, 4)))]
+            blocks = [int(b) for b in rng.integers(0, 3, len(shapes))]
+            inject = int(rng.integers(0, len(shapes))) if k % 4 == 3 else None
+            log(f"no-alloc step, rank {rank}, group {k}: {shapes}, blocks {blocks}, NaN in {inject}")
+            _run_both(ctx, shapes, blocks, 8_300_000 + 100 * rank + k, inject=inject, rank=rank)
+    finally:
+        B.psgd_destroy(ctx)
