@@ -20,7 +20,8 @@
 //     them to an LDS tile (rows x 64 columns, 16-byte units XOR-swizzled by row); the MFMA
 //     A-fragments are read from there;
 //   * the shared operand, 64 rows of q, is read in fp32, split into bf16 hi/lo and staged in
-//     LDS beside it, transposed;
+//     LDS beside it as it lies in q (one LDS row per k); the MFMA B-fragments, which need 8
+//     consecutive k of one rank, come from gfx950's transposing LDS read;
 //   * the flag test runs on the finished P rows: a non-finite element of M makes its row of
 //     P non-finite (inf times a nonzero factor entry is inf, times zero is NaN, and NaN
 //     propagates; the split of inf has a NaN low half). Only when the workgroup's P is
@@ -57,9 +58,7 @@ static_assert(KS == 64, "the LDS swizzle assumes 8 units per row");
 // per pass over 32 four-byte banks, and every 128-byte row starts on bank 0, so an MFMA
 // fragment read (8 consecutive rows from a multiple of 8, one logical unit) is conflict-free
 // when those rows land on 8 distinct units: rr & 7 runs over 0..7 and rr >> 2 takes two values
-// that differ only in bit 0, so XOR-ing them permutes the 8 units. The same mixing spreads the
-// transposed warm-start stores (rows 4 g + e for consecutive rank groups g) over all 8 units
-// of a k position; (rr >> 1) & 7 reached only 4.
+// that differ only in bit 0, so XOR-ing them permutes the 8 units.
 __device__ __forceinline__ int swz1(int rr, int q) { return q ^ ((rr ^ (rr >> 2)) & 7); }
 
 // coalesced M loads: 16 lanes per row, 4 columns per lane
@@ -94,71 +93,61 @@ void k_ef_mq(const DevMat* __restrict__ mats, const Work* __restrict__ work,
   // One LDS arena: the staged operands during the main loop, the output tile afterwards.
   constexpr int RC = RTC * 16;                      // rank columns of this chunk
   constexpr int PT_LD = RC + 4;                     // output tile row (padded against bank conflicts)
-  constexpr int kQBytes = 2 * RC * LDS_K * 2;
+  constexpr int kQBytes = 2 * KS * 128 * 2;         // q halves K-outer: KS rows of 128 ranks
   constexpr int kMBytes = 2 * K1_ROWS * LDS_K * 2;
   constexpr int kPBytes = K1_ROWS * PT_LD * 4;
   constexpr int kArena = kQBytes + kMBytes > kPBytes ? kQBytes + kMBytes : kPBytes;
   __shared__ __attribute__((aligned(16))) unsigned char lds_raw[kArena];
-  auto& ldq = *reinterpret_cast<uint16_t (*)[2][RC][LDS_K]>(lds_raw);             // Q^T hi, lo
+  auto& ldq = *reinterpret_cast<uint16_t (*)[2][KS * 128]>(lds_raw);              // q hi, lo (K-outer)
   auto& ldm = *reinterpret_cast<uint16_t (*)[2][K1_ROWS][LDS_K]>(lds_raw + kQBytes);  // M hi, lo
   __shared__ int s_bad;
 
   // Warm-start staging: rows k0 .. k0 + KS - 1 of q (n x r fp32, row-major), ranks rc0 ..
-  // rc0 + RC - 1, split into bf16 hi + lo and transposed into ldq[hi/lo][rank][k]. A unit is 4
-  // consecutive ranks of the two rows k, k + 1: consecutive threads take consecutive rank
-  // groups of a row pair (coalesced reads of q), and every rank's (k, k + 1) pair becomes one
-  // 4-byte LDS store. The threads of a store pass share k, so those stores keep a few-way bank
-  // conflict; giving consecutive threads 4 consecutive row pairs instead removes it but cuts
-  // the reads of q into 256-byte pieces, and the kernel ran slower (1.93 -> 2.06 ms on the
-  // 64-resblock rank-112 shard). Rows past n and ranks past r read zeros. Threads past the last
-  // unit repeat it (same values to the same LDS addresses), so the code has no branch.
+  // rc0 + RC - 1, split into bf16 hi + lo and stored as they lie: LDS row k holds 128 ranks
+  // (256 bytes), in 16-byte units of 8 ranks. A unit of work is 4 consecutive ranks of one row
+  // (one 16-byte read of q, coalesced across consecutive threads). A B-fragment read touches
+  // 32 bytes in each of the 16 rows 32 j + 8 g + 4 h + t (g, t = 0..3, h = 0, 1); XOR-ing a
+  // row's unit pairs with t + 4 (g & 1) puts the 8 rows of each half-wave on 8 distinct pairs,
+  // all 64 banks once. Rows past n and ranks past r read zeros; threads past the last unit
+  // repeat it (same values to the same LDS addresses), so the code has no branch.
   constexpr int RG = RC / 4;                    // rank groups per row
-  constexpr int QUNITS = (KS / 2) * RG;
+  constexpr int QUNITS = KS * RG;
   constexpr int UPT = (QUNITS + K1_THREADS - 1) / K1_THREADS;
   const bool qvec = (r & 3) == 0;               // rows of q are whole 16-byte units
-  f32x4 stq[UPT][2];
-  auto qunit = [&](int j, int& kp, int& rg) {
+  f32x4 stq[UPT];
+  auto qunit = [&](int j, int& kq, int& rg) {
     int u = threadIdx.x + j * K1_THREADS;
     u = u < QUNITS ? u : QUNITS - 1;
-    kp = u / RG;
-    rg = u - kp * RG;
+    kq = u / RG;
+    rg = u - kq * RG;
   };
+  auto swzt = [](int k, int q) { return q ^ (2 * ((k & 3) | (((k >> 3) & 1) << 2))); };
   auto load_stage = [&](int k0) {
 #pragma unroll
     for (int j = 0; j < UPT; ++j) {
-      int kp, rg;
-      qunit(j, kp, rg);
-      const int rank = rc0 + 4 * rg;
+      int kq, rg;
+      qunit(j, kq, rg);
+      const int rank = rc0 + 4 * rg, row = k0 + kq;
+      const bool ok = row < n;
+      if (qvec) {
+        stq[j] = __builtin_bit_cast(f32x4, bload16(rq, ok && rank < r ? (uint32_t)(row * r + rank) * 4u : kOOB));
+      } else {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int row = k0 + 2 * kp + h;
-        const bool ok = row < n;
-        if (qvec) {
-          stq[j][h] = __builtin_bit_cast(f32x4, bload16(rq, ok && rank < r ? (uint32_t)(row * r + rank) * 4u : kOOB));
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            stq[j][h][e] = __builtin_bit_cast(float, bload4(rq, ok && rank + e < r ? (uint32_t)(row * r + rank + e) * 4u : kOOB));
-        }
+        for (int e = 0; e < 4; ++e)
+          stq[j][e] = __builtin_bit_cast(float, bload4(rq, ok && rank + e < r ? (uint32_t)(row * r + rank + e) * 4u : kOOB));
       }
     }
   };
   auto store_stage = [&]() {
 #pragma unroll
     for (int j = 0; j < UPT; ++j) {
-      int kp, rg;
-      qunit(j, kp, rg);
-      const int qq = kp >> 2, w = (2 * kp) & 7;   // 16-byte unit of k = 2 kp, bf16 offset in it
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int rr = 4 * rg + e;
-        const f32x2 x = {stq[j][0][e], stq[j][1][e]};
-        const bf16x2 hi = __builtin_convertvector(x, bf16x2);
-        const bf16x2 lo = __builtin_convertvector(x - __builtin_convertvector(hi, f32x2), bf16x2);
-        const int off = 8 * swz1(rr, qq) + w;
-        *reinterpret_cast<bf16x2*>(&ldq[0][rr][off]) = hi;
-        *reinterpret_cast<bf16x2*>(&ldq[1][rr][off]) = lo;
-      }
+      int kq, rg;
+      qunit(j, kq, rg);
+      const bf16x4 hi = __builtin_convertvector(stq[j], bf16x4);
+      const bf16x4 lo = __builtin_convertvector(stq[j] - __builtin_convertvector(hi, f32x4), bf16x4);
+      const int off = kq * 128 + 8 * swzt(kq, rg >> 1) + 4 * (rg & 1);
+      *reinterpret_cast<bf16x4*>(&ldq[0][off]) = hi;
+      *reinterpret_cast<bf16x4*>(&ldq[1][off]) = lo;
     }
   };
 
@@ -213,9 +202,16 @@ void k_ef_mq(const DevMat* __restrict__ mats, const Work* __restrict__ work,
       }
 #pragma unroll
       for (int cc = 0; cc < RTC; ++cc) {
-        const int pq = 8 * swz1(cc * 16 + c, 4 * j + g);
-        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&ldq[0][cc * 16 + c][pq]);
-        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&ldq[1][cc * 16 + c][pq]);
+        // ranks cc 16 .. of rows 32 j + 8 g .. + 7, in two transposing reads of 4 rows each
+        // (rows k and k + 4 share their swizzle)
+        const int k = 32 * j + 8 * g + (c >> 2), q = 2 * cc + ((c & 3) >> 1);
+        const int off = k * 128 + 8 * swzt(k, q) + 4 * (c & 1);
+        typedef short i16x4 __attribute__((ext_vector_type(4)));
+        auto tr = [](const uint16_t* p) {
+          return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+        };
+        const bf16x8 bh = __builtin_bit_cast(bf16x8, __builtin_shufflevector(tr(&ldq[0][off]), tr(&ldq[0][off + 4 * 128]), 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8 bl = __builtin_bit_cast(bf16x8, __builtin_shufflevector(tr(&ldq[1][off]), tr(&ldq[1][off + 4 * 128]), 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int a = 0; a < K1_RA; ++a) {
           acc[a][cc] = mfma_bf16(ah[a], bh, acc[a][cc]);
