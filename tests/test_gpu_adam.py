@@ -433,3 +433,19 @@ def test_optimizer_arguments_rejected():
         assert int(param.abs().max().item()) == 0 and int(m1.abs().max()) == 0 and int(m2.abs().max()) == 0
     finally:
         group.close()
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_configuration_with_optimizer(seed):
+    """Seeded random groups with the fused optimizer: rank on both sides of the 128-column chunk
+    (odd ranks among them), one to three ragged matrices, gradient and parameter dtypes, and
+    an in-place matrix or none; three steps against the oracle, the last skipped."""
+    rng = np.random.default_rng(9_500_000 + seed)
+    rank = int(rng.choice([5, 24, 64, 112, 129, 200]))
+    shapes = [(int(rng.integers(rank, rank + 400)), 8 * int(rng.integers((rank + 7) // 8, (rank + 7) // 8 + 60)))
+              for _ in range(int(rng.integers(1, 4)))]
+    gdt = str(rng.choice(["f16", "bf16", "f32"]))
+    pdt = str(rng.choice(["f16", "bf16", "f32"]))
+    inplace = (int(rng.integers(0, len(shapes))),) if rng.random() < 0.4 else ()
+    counts = _free_running(shapes, gdt, pdt, rank, 3, 9_600_000 + 1000 * seed, inplace=inplace)
+    assert counts == (3, 1), counts
