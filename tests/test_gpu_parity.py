@@ -550,24 +550,23 @@ def _dev_copy(dst: int, src: int, nbytes: int):
     assert lib.hipMemcpy(dst, src, nbytes, 3) == 0       # device to device
 
 
-@pytest.mark.parametrize("rank", [16, 160])
-def test_split_calls_two_simulated_ranks(rank):
+def _simulated_data_parallel(rank, shapes, n_ranks, rng, dtype="f16"):
     """psgd_compress_p -> mean of the factor buffers -> psgd_orthogonalize -> psgd_compress_q ->
-    mean of q_next -> psgd_refresh_q -> check -> decompress, for two ranks holding different
-    gradients of the same matrices (two plans on one GPU, torch doing the means), against the
-    oracle's data-parallel step: P and D identical on both ranks, each rank's own E."""
+    mean of q_next -> psgd_refresh_q -> check -> decompress, for n_ranks ranks holding
+    different gradients of the same matrices (one plan each on one GPU, torch doing the means),
+    against the oracle's data-parallel step: P and D identical on every rank, each rank's own
+    E."""
     import torch
     from rank_gradient_compression_powersgd_amd import PowerSGDGroup
     from rank_gradient_compression_powersgd_amd import binding as B
-    shapes = [(520, 264), (300, 512)]
-    rng = np.random.default_rng(77)
     q0 = [rng.standard_normal((n, rank)).astype(np.float32) for _, n in shapes]
     scale = torch.tensor([0.5], device="cuda")
     ranks = []
-    for k in range(2):
-        gs = [wl.to_fp16(rng.standard_normal(sh)) for sh in shapes]
+    for k in range(n_ranks):
+        x = [rng.standard_normal(sh) for sh in shapes]
+        gs = [wl.to_fp16(v) if dtype == "f16" else v.astype(np.float32) for v in x]
         es = [(rng.standard_normal(sh) * 0.05).astype(np.float32) for sh in shapes]
-        grp = PowerSGDGroup([torch.from_numpy(g).cuda() for g in gs], [0, 0], scale, rank,
+        grp = PowerSGDGroup([torch.from_numpy(g).cuda() for g in gs], [0] * len(shapes), scale, rank,
                             [torch.from_numpy(q) for q in q0],
                             [torch.from_numpy(e).cuda() for e in es], True)
         ranks.append((grp, gs, es))
@@ -580,7 +579,7 @@ def test_split_calls_two_simulated_ranks(rank):
     for t, (ptr, cnt, _) in zip(f, bufs):
         assert cnt == count
         _dev_copy(t.data_ptr(), ptr, 4 * count)
-    mean = (f[0] + f[1]) / 2
+    mean = sum(f) / n_ranks
     torch.cuda.synchronize()
     for ptr, _, _ in bufs:
         _dev_copy(ptr, mean.data_ptr(), 4 * count)
@@ -589,7 +588,7 @@ def test_split_calls_two_simulated_ranks(rank):
         B.psgd_compress_q(grp.ctx, grp.plan, grp.scale)
     torch.cuda.synchronize()
     for i in range(len(shapes)):
-        qm = (ranks[0][0].q_next[i] + ranks[1][0].q_next[i]) / 2
+        qm = sum(grp.q_next[i] for grp, _, _ in ranks) / n_ranks
         for grp, _, _ in ranks:
             grp.q_next[i].copy_(qm)
     torch.cuda.synchronize()
@@ -599,20 +598,44 @@ def test_split_calls_two_simulated_ranks(rank):
         grp.decompress_update()
     torch.cuda.synchronize()
     for i, sh in enumerate(shapes):
-        st = oracle.step_data_parallel([ranks[k][1][i].astype(np.float32) for k in range(2)],
-                                       [ranks[k][2][i] for k in range(2)], q0[i], 0.5)
+        st = oracle.step_data_parallel([ranks[k][1][i].astype(np.float32) for k in range(n_ranks)],
+                                       [ranks[k][2][i] for k in range(n_ranks)], q0[i], 0.5)
         P = [grp.p[i].cpu().numpy() for grp, _, _ in ranks]
         D = [grp.out[i].cpu().numpy() for grp, _, _ in ranks]
-        assert np.array_equal(P[0], P[1]) and np.array_equal(D[0], D[1])
+        for k in range(1, n_ranks):
+            assert np.array_equal(P[0], P[k]) and np.array_equal(D[0], D[k])
         r = dict(P=rel(P[0], st.P), D=rel(D[0], st.D), Q=rel(ranks[0][0].q[i].cpu().numpy(), st.Q_next),
-                 E0=rel(ranks[0][0].err[i].cpu().numpy(), st.E_next[0]),
-                 E1=rel(ranks[1][0].err[i].cpu().numpy(), st.E_next[1]), orth=orth_err(P[0]))
+                 orth=orth_err(P[0]))
+        for k in range(n_ranks):
+            r[f"E{k}"] = rel(ranks[k][0].err[i].cpu().numpy(), st.E_next[k])
         log(f"  matrix {i} {sh}: " + " ".join(f"{k}={v:.2e}" for k, v in r.items()))
-        for k in ("P", "D", "Q", "E0", "E1"):
-            assert r[k] <= REL_TOL, (i, k, r[k])
+        for k, v in r.items():
+            if k != "orth":
+                assert v <= REL_TOL, (i, k, v)
         assert r["orth"] <= ORTH_TOL
     for grp, _, _ in ranks:
         grp.close()
+
+
+@pytest.mark.parametrize("rank", [16, 160])
+def test_split_calls_two_simulated_ranks(rank):
+    """Two simulated ranks of a data-parallel group on one GPU, against the oracle's
+    data-parallel step (the split calls with the means taken between them)."""
+    _simulated_data_parallel(rank, [(520, 264), (300, 512)], 2, np.random.default_rng(77))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_split_calls_random_simulated_groups(seed):
+    """Seeded random data-parallel groups: two to four simulated ranks, a rank on either side of
+    the 128-column chunk, ragged shapes, fp16 or fp32 gradients."""
+    rng = np.random.default_rng(7_900_000 + seed)
+    rank = int(rng.choice([7, 48, 112, 144, 200]))
+    shapes = [(int(rng.integers(rank, rank + 500)), 8 * int(rng.integers((rank + 7) // 8, (rank + 7) // 8 + 70)))
+              for _ in range(int(rng.integers(1, 3)))]
+    n_ranks = int(rng.integers(2, 5))
+    dtype = str(rng.choice(["f16", "f32"]))
+    log(f"simulated group {seed}: {n_ranks} ranks, rank {rank}, {dtype}, shapes {shapes}")
+    _simulated_data_parallel(rank, shapes, n_ranks, rng, dtype)
 
 
 @pytest.mark.parametrize("rank", [None, 160])
