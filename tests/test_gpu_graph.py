@@ -13,7 +13,7 @@ from tests.gpu_helpers import log
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("rank", [16, 160])
+@pytest.mark.parametrize("rank", [16, 160, 37, 255])
 def test_step_graph_replays_match_eager(rank):
     import torch
     from rank_gradient_compression_powersgd_amd import PowerSGDGroup
